@@ -1,0 +1,190 @@
+/*
+ * sharq.h -- C ABI of the SharQ hot path on AMD Instinct MI355X (gfx950).
+ *
+ * Method (SharQ: Bridging Activation Sparsity and FP4 Quantization for LLM Inference, Abstract; arXiv 2606.26587): each activation tensor of a linear
+ * layer is cut into two FP4 parts.  An N:M mask chosen from the tensor's own
+ * values keeps the large-magnitude elements (where the outliers live); those
+ * form a sparse backbone that is quantized to FP4.  What the quantized
+ * backbone fails to represent -- the masked-out elements plus the backbone's
+ * own rounding error -- is a dense residual, also quantized to FP4.  The
+ * layer output adds the backbone product and the residual product, both
+ * against one FP4 copy of the weight.  Normalization, masking and residual
+ * formation run as one fused operator.
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers are HIP device (or managed) memory; the library never
+ *     allocates or frees memory.  Scratch space comes from the caller as a
+ *     workspace argument sized by the *_workspace_size() helpers.
+ *   - All work is enqueued on `stream` (a hipStream_t, NULL = the default
+ *     stream) and runs asynchronously; no call synchronizes with the host.
+ *   - Arguments are validated on the host before any HIP call; a failed check
+ *     returns its status code and enqueues nothing.  SHARQ_ERR_HIP reports a
+ *     failed launch; faults inside a kernel surface at the caller's next
+ *     synchronization, as usual with HIP.  On any error the outputs are
+ *     unspecified.
+ *   - Element formats:
+ *       E2M1   FP4 code: bit 3 sign, bits 0-2 magnitude index into
+ *              {0, 0.5, 1, 1.5, 2, 3, 4, 6}; a zero magnitude is always 0x0.
+ *              Two codes per byte, element k in the low nibble when k is even.
+ *       MXFP4  E2M1 + one E8M0 scale byte per 32 elements along K:
+ *              scale 2^(byte-127), exponent floor(log2 amax) - 2 (OCP MX v1.0).
+ *       NVFP4  E2M1 + one E4M3 scale byte per 16 elements along K, times one
+ *              FP32 scale per tensor, amax(tensor)/2688.
+ *   - The N:M mask keeps, in every group of M consecutive elements along K,
+ *     the N elements of largest magnitude; equal magnitudes favour the lower
+ *     index.  Mask bitmap: bit k%8 of byte k/8 of the row.
+ */
+#ifndef SHARQ_H
+#define SHARQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SHARQ_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define SHARQ_API __attribute__((visibility("default")))
+#else
+#define SHARQ_API
+#endif
+
+typedef enum {
+    SHARQ_OK = 0,
+    SHARQ_ERR_NULL = 1,        /* a required pointer is NULL                    */
+    SHARQ_ERR_SHAPE = 2,       /* a size is negative, K not a multiple of the   */
+                               /* block (32 MX / 16 NV) or of 128 for products, */
+                               /* or a leading dimension is too small           */
+    SHARQ_ERR_NM = 3,          /* not 0 <= N <= M, or M not in {1,2,4,8,16}, or */
+                               /* M does not divide K                           */
+    SHARQ_ERR_DTYPE = 4,       /* unsupported element type                      */
+    SHARQ_ERR_ALIGN = 5,       /* pointer or row stride not 16-byte aligned     */
+    SHARQ_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required       */
+    SHARQ_ERR_UNSUPPORTED = 7, /* format / norm / combination not built         */
+    SHARQ_ERR_HIP = 8          /* a HIP call or kernel launch failed            */
+} sharq_status;
+
+typedef enum { SHARQ_F16 = 0, SHARQ_BF16 = 1, SHARQ_F32 = 2 } sharq_dtype;
+typedef enum { SHARQ_NORM_NONE = 0, SHARQ_NORM_RMS = 1, SHARQ_NORM_LAYER = 2 } sharq_norm;
+typedef enum { SHARQ_MXFP4 = 0, SHARQ_NVFP4 = 1 } sharq_format;
+
+/* Version of this ABI (SHARQ_ABI_VERSION). */
+SHARQ_API int sharq_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+SHARQ_API const char *sharq_status_string(int status);
+
+/* Bytes of workspace sharq_prepare needs for T rows (0 for MXFP4). */
+SHARQ_API size_t sharq_prepare_workspace_size(int64_t T, int64_t K, int32_t fmt);
+
+/*
+ * sharq_prepare -- the fused preparation operator (SharQ: Bridging Activation Sparsity and FP4 Quantization for LLM Inference, Abstract:
+ * normalization, mask generation and residual construction in one
+ * operator; backbone and residual as in the decomposition it describes).
+ *
+ * Per row t of X (T rows, K columns, row stride ldx elements):
+ *   xhat = norm(x)           NONE: x;  RMS: x * r * gamma with
+ *                            r = fl32(1/sqrt(sum(x^2)/K + eps)) (sum in FP64);
+ *                            LAYER: ((x - mu) * r) * gamma + beta
+ *   mask = top-N |xhat| of every M-group along K
+ *   S    = mask ? xhat : 0;             backbone = Q(S)
+ *   R    = xhat - deq(backbone);        residual = Q(R)
+ * where Q is MXFP4 or NVFP4 (the NVFP4 tensor scale G = amax(xhat)/2688 is
+ * shared by backbone and residual and written to *global_scale).
+ *
+ *   x            [T][ldx] F16 or BF16, 16-byte aligned, ldx*2 % 16 == 0
+ *   gamma, beta  [K] same type as x; gamma required for RMS and LAYER, beta
+ *                optional for LAYER (NULL = 0), both ignored for NONE
+ *   eps          added to the mean square / variance
+ *   n, m         N:M mask, 0 <= n <= m, m in {1,2,4,8,16}, K % m == 0
+ *   fmt          SHARQ_MXFP4 (K % 32 == 0) or SHARQ_NVFP4 (K % 16 == 0)
+ *   mask         [T][K/8] bitmap or NULL (not written)
+ *   b_codes      [T][K/2] backbone E2M1 codes, 4-byte aligned
+ *   b_scales     [T][K/B] backbone block scales (E8M0 or E4M3 bytes)
+ *   r_codes      [T][K/2] residual codes, 4-byte aligned
+ *   r_scales     [T][K/B] residual block scales
+ *   global_scale one device float: NVFP4 tensor scale (written); MXFP4: may
+ *                be NULL, otherwise 1.0f is written
+ *   workspace    sharq_prepare_workspace_size() bytes (NVFP4 only)
+ * All outputs are dense row-major arrays owned by the caller.  T == 0 is a
+ * valid no-op.
+ */
+SHARQ_API sharq_status sharq_prepare(const void *x, int32_t x_dtype, int64_t T, int64_t K, int64_t ldx,
+                           int32_t norm, const void *gamma, const void *beta, float eps,
+                           int32_t n, int32_t m, int32_t fmt, uint8_t *mask, uint8_t *b_codes,
+                           uint8_t *b_scales, uint8_t *r_codes, uint8_t *r_scales,
+                           float *global_scale, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Bytes of workspace sharq_quantize_weight needs. */
+SHARQ_API size_t sharq_quantize_weight_workspace_size(int64_t experts, int64_t nout, int64_t K, int32_t fmt);
+
+/*
+ * sharq_quantize_weight -- the single FP4 weight payload that both paths
+ * read (SharQ: Bridging Activation Sparsity and FP4 Quantization for LLM Inference, Abstract: one weight payload, a scale view per path).
+ * Round-to-nearest-even quantization, run once per weight, offline.
+ *
+ *   w            [experts][nout][K] F16 or BF16 (PyTorch Linear layout,
+ *                Y = X W^T), contiguous, 16-byte aligned
+ *   codes        [experts][nout][K/2] E2M1 codes
+ *   scales       [experts][nout][K/B] block scales
+ *   global_scale [experts] device floats: NVFP4 per-expert tensor scale
+ *                amax/2688 (written); MXFP4: may be NULL, else 1.0f written
+ *   workspace    sharq_quantize_weight_workspace_size() bytes
+ */
+SHARQ_API sharq_status sharq_quantize_weight(const void *w, int32_t w_dtype, int64_t experts, int64_t nout,
+                                   int64_t K, int32_t fmt, uint8_t *codes, uint8_t *scales,
+                                   float *global_scale, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
+/* Bytes of workspace sharq_linear needs (currently always 0). */
+SHARQ_API size_t sharq_linear_workspace_size(int64_t rows, int64_t K, int64_t nout, int64_t experts,
+                                   int32_t fmt);
+
+/*
+ * sharq_linear -- the dual-path FP4 linear layer (SharQ: Bridging Activation Sparsity and FP4 Quantization for LLM Inference, Abstract: a sparse FP4
+ * product on the backbone plus a dense FP4 product on the residual, which
+ * restores what masking dropped and what backbone rounding lost).
+ *
+ *   Y[r][o] = sum_k ( deq(backbone)[src(r)][k] + deq(residual)[src(r)][k] )
+ *                   * deq(W[e(r)])[o][k]
+ * in FP32 accumulation, with NVFP4 tensor scales applied as
+ * x_global_scale * w_global_scale[e] in the epilogue.  Both paths read the
+ * same weight codes and scales.  The backbone is multiplied densely on its
+ * zero-filled form (gfx950 has no block-scaled sparse FP4 matrix
+ * instruction).
+ *
+ *   b_codes, b_scales, r_codes, r_scales  prepared activations, T rows,
+ *                as written by sharq_prepare (dense row-major)
+ *   x_global_scale  device float (NVFP4), NULL for MXFP4
+ *   T, K         prepared rows and reduction length (K % 128 == 0)
+ *   w_codes, w_scales, w_global_scale  payload of sharq_quantize_weight
+ *   experts, nout  weight shape
+ *   group_offsets  experts == 1: NULL.  experts > 1: device int32
+ *                [experts+1], non-decreasing, offsets[0] = 0,
+ *                offsets[experts] = rows; output rows
+ *                offsets[e]..offsets[e+1]-1 use expert e
+ *   row_index    device int32 [rows] or NULL: output row r reads prepared row
+ *                row_index[r] (0 <= row_index[r] < T); NULL reads row r
+ *   rows         output rows (T when row_index is NULL and experts == 1)
+ *   y            [rows][ldy] FP32, ldy >= nout, 4-byte aligned (128-bit
+ *                stores are used when y is 16-byte aligned and ldy % 4 == 0)
+ * Contents of group_offsets and row_index are trusted (device memory is not
+ * read on the host); out-of-range values are undefined behaviour.
+ */
+SHARQ_API sharq_status sharq_linear(const uint8_t *b_codes, const uint8_t *b_scales, const uint8_t *r_codes,
+                          const uint8_t *r_scales, const float *x_global_scale, int64_t T,
+                          int64_t K, int32_t fmt, const uint8_t *w_codes, const uint8_t *w_scales,
+                          const float *w_global_scale, int64_t experts, int64_t nout,
+                          const int32_t *group_offsets, const int32_t *row_index, int64_t rows,
+                          float *y, int64_t ldy, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHARQ_H */

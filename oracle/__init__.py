@@ -5,8 +5,8 @@ the benchmark's CPU-baseline leg, never by the product library or its
 Python binding.  The arithmetic lives in ``sharq_oracle.c`` (plain scalar C,
 each step documented there); this module builds and loads it, and adds the
 layer product Y = deq(backbone).W^T + deq(residual).W^T in float64 with
-numpy (SharQ abstract: a sparse FP4 GEMM on the backbone plus a dense FP4
-GEMM on the residual, both against one weight payload).
+numpy (SharQ: Bridging Activation Sparsity and FP4 Quantization for LLM Inference, Abstract: a sparse FP4 product on the
+backbone plus a dense FP4 product on the residual, one weight payload).
 """
 from __future__ import annotations
 
@@ -73,7 +73,9 @@ def lib():
         L.or_e4m3_encode_n.restype = None
         L.or_quantize_weight.argtypes = [p, i32, i64, i64, i64, i64, i32, p, p, p]
         L.or_dequant.argtypes = [p, p, i64, i64, i32, f32, p]
-        for fn in (L.or_normalize, L.or_prepare, L.or_quantize_weight, L.or_dequant):
+        L.or_quantize_rows.argtypes = [p, i32, i64, i64, i32, f32, p, p]
+        for fn in (L.or_normalize, L.or_prepare, L.or_quantize_weight, L.or_dequant,
+                   L.or_quantize_rows):
             fn.restype = i32
         _lib = L
     return _lib
@@ -224,6 +226,18 @@ def quantize_weight(w: np.ndarray, dtype: str, fmt: int) -> QWeight:
                                   _ptr(q.codes), _ptr(q.scales), _ptr(q.gscale))
     _check(rc, "quantize_weight")
     return q
+
+
+def quantize_rows(w_rows: np.ndarray, dtype: str, fmt: int, G: float = 1.0):
+    """Quantize a sample of weight rows [n][K] with a known tensor scale G."""
+    w_rows = np.ascontiguousarray(w_rows)
+    n, K = w_rows.shape
+    B = block_size(fmt)
+    codes = np.zeros((n, K // 2), np.uint8)
+    scales = np.zeros((n, K // B), np.uint8)
+    _check(lib().or_quantize_rows(_ptr(w_rows), DTYPE_CODE[dtype], n, K, fmt, float(G),
+                                  _ptr(codes), _ptr(scales)), "quantize_rows")
+    return codes, scales
 
 
 def dequant(codes: np.ndarray, scales: np.ndarray, K: int, fmt: int, G: float = 1.0) -> np.ndarray:

@@ -6,11 +6,12 @@
  * code, header, table or constant with the HIP library, and the HIP library
  * never calls it.
  *
- * What it computes (SharQ abstract, method sentences): for every activation
- * tensor, normalize it, build an input-adaptive N:M mask that keeps the
- * outlier-dominated sparse backbone, quantize the backbone to FP4 with block
- * scales, form the dense residual against the *quantized* (dequantized)
- * backbone, and quantize that residual to FP4 as well; the layer output is
+ * What it computes (SharQ: Bridging Activation Sparsity and FP4 Quantization for LLM Inference, Abstract): for every
+ * activation tensor, normalize it, choose an N:M mask from its own
+ * magnitudes so that the large (outlier) elements form a sparse backbone,
+ * quantize that backbone to FP4 with block scales, subtract the
+ * dequantized backbone from the normalized tensor to get the dense residual,
+ * and quantize the residual to FP4 too; the layer output is
  * backbone.W + residual.W with one FP4 weight payload.  The pages give no
  * formulas, so every step below takes the plainest reading:
  *
@@ -423,6 +424,23 @@ int or_quantize_weight(const void *w, int wdt, int64_t E, int64_t Nout, int64_t 
             quantize_row(row, K, fmt, G, codes + (e * Nout + n) * (K / 2),
                          scales + (e * Nout + n) * (K / B), NULL);
         }
+    }
+    free(row);
+    return OR_OK;
+}
+
+/* Quantize rows W[nrows][K] (row stride K) with a given tensor scale G
+ * (NVFP4; ignored for MXFP4) -- used to check a sample of a large weight. */
+int or_quantize_rows(const void *w, int wdt, int64_t nrows, int64_t K, int fmt, float G,
+                     uint8_t *codes, uint8_t *scales)
+{
+    if (check_shape(K, 1, 1, fmt) != OR_OK || nrows < 0) return OR_EINVAL;
+    int B = fmt == OR_FMT_MXFP4 ? 32 : 16;
+    float *row = malloc(sizeof(float) * K);
+    if (!row) return OR_ENOMEM;
+    for (int64_t n = 0; n < nrows; n++) {
+        for (int64_t k = 0; k < K; k++) row[k] = load_elem(w, wdt, n * K + k);
+        quantize_row(row, K, fmt, G, codes + n * (K / 2), scales + n * (K / B), NULL);
     }
     free(row);
     return OR_OK;

@@ -1,0 +1,133 @@
+// Device helpers shared by the gfx950 kernels of the SharQ hot path.
+//
+// Element formats (OCP MX v1.0 for E2M1/E8M0; E4M3 as used by NVFP4):
+//   E2M1 magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}, code bit 3 = sign;
+//   E8M0 byte b = 2^(b-127); E4M3 bias 7, 3 fraction bits, max 448.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sharq {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- 16-bit loads
+// Two 16-bit elements packed in a 32-bit word, element 0 in the low half.
+template <bool BF16>
+__device__ __forceinline__ float elem_lo(uint32_t w) {
+    if constexpr (BF16) {
+        return __uint_as_float(w << 16);
+    } else {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+    }
+}
+template <bool BF16>
+__device__ __forceinline__ float elem_hi(uint32_t w) {
+    if constexpr (BF16) {
+        return __uint_as_float(w & 0xFFFF0000u);
+    } else {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    }
+}
+
+// Eight consecutive elements from one 128-bit word.
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const uint4 &q, float v[8]) {
+    v[0] = elem_lo<BF16>(q.x); v[1] = elem_hi<BF16>(q.x);
+    v[2] = elem_lo<BF16>(q.y); v[3] = elem_hi<BF16>(q.y);
+    v[4] = elem_lo<BF16>(q.z); v[5] = elem_hi<BF16>(q.z);
+    v[6] = elem_lo<BF16>(q.w); v[7] = elem_hi<BF16>(q.w);
+}
+
+// ---------------------------------------------------------------- lane exchange
+// DPP quad permutations: lane i of every group of four reads lane perm[i].
+constexpr int kDppQuadXor1 = 0xB1;  // [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // [2,3,0,1]
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// ---------------------------------------------------------------- E2M1
+// Round |u| to the E2M1 grid (nearest, ties to even, saturating at 6).
+// Returns the 3-bit magnitude code and the rounded magnitude.
+// For |u| >= 1 the float is rounded to one fraction bit in its own binade by
+// integer arithmetic on the bit pattern; below 1 the grid step is 0.5.
+__device__ __forceinline__ uint32_t e2m1_round(float u, float &qmag) {
+    const uint32_t b = __float_as_uint(u) & 0x7FFFFFFFu;
+    const float a = __uint_as_float(b);
+    uint32_t code;
+    if (a >= 1.0f) {
+        const uint32_t r = (b + 0x1FFFFFu + ((b >> 22) & 1u)) >> 22;  // exponent:1-bit fraction
+        code = min(r - 252u, 7u);                                        // 1.0 -> 254 -> code 2
+        qmag = code == 7u ? 6.0f : __uint_as_float(r << 22);
+    } else {
+        code = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f);
+        qmag = 0.5f * (float)code;
+    }
+    return code;
+}
+
+// Signed 4-bit code of u (canonical +0 for a zero magnitude) and the signed
+// rounded value (+0 when the code is 0).
+__device__ __forceinline__ uint32_t e2m1_encode(float u, float &q) {
+    float qmag;
+    uint32_t c = e2m1_round(u, qmag);
+    const uint32_t neg = (c != 0u) ? (__float_as_uint(u) >> 31) : 0u;
+    q = __uint_as_float(__float_as_uint(qmag) | (neg << 31));
+    return c | (neg << 3);
+}
+
+// ---------------------------------------------------------------- E8M0 (MX)
+// floor(log2 a) for a finite a > 0, subnormals included.
+__device__ __forceinline__ int floor_log2_f32(float a) {
+    const uint32_t b = __float_as_uint(a);
+    return b >= 0x00800000u ? (int)(b >> 23) - 127 : (31 - (int)__clz((int)b)) - 149;
+}
+
+// OCP MX shared exponent for E2M1 elements: floor(log2 amax) - 2, or -127
+// for amax == 0 (never below -127; at most 125 for finite floats).
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+    if (amax == 0.0f) return -127;
+    const int e = floor_log2_f32(amax) - 2;
+    return e < -127 ? -127 : e;
+}
+
+// 2^-E as a normal float for E in [-127, 125].
+__device__ __forceinline__ float pow2_neg(int E) { return __uint_as_float((uint32_t)(127 - E) << 23); }
+// 2^E for E in [-127, 125] (2^-127 is subnormal).
+__device__ __forceinline__ float pow2(int E) {
+    return E >= -126 ? __uint_as_float((uint32_t)(E + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// ---------------------------------------------------------------- E4M3 (NVFP4 scales)
+// Nearest E4M3 (ties to even), saturating at 448; t >= 0 and finite.
+__device__ __forceinline__ uint32_t e4m3_encode_sat(float t) {
+    if (!(t > 0.0f)) return 0u;
+    if (t >= 448.0f) return 0x7Eu;
+    const uint32_t b = __float_as_uint(t);
+    if (b < 0x3C800000u) {                      // t < 2^-6: subnormal step 2^-9
+        return (uint32_t)__builtin_rintf(t * 512.0f);  // 8 lands on 0x08 = 2^-6
+    }
+    const uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;  // 3 fraction bits, RNE
+    return ((r >> 3) - 120u) << 3 | (r & 7u);
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t s) {
+    const uint32_t e = (s >> 3) & 15u, f = s & 7u;
+    return e == 0u ? (float)f * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (f << 20));
+}
+
+}  // namespace sharq

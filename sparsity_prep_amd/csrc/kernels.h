@@ -1,0 +1,57 @@
+// Internal launcher interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sharq {
+
+enum { kNormNone = 0, kNormRms = 1, kNormLayer = 2 };
+enum { kFmtMx = 0, kFmtNv = 1 };
+
+struct PrepArgs {
+    const uint16_t *x;
+    int64_t T, K, ldx;
+    const uint16_t *gamma, *beta;
+    float eps;
+    int n, m, norm, fmt;
+    bool bf16;
+    uint8_t *mask, *b_codes, *b_scales, *r_codes, *r_scales;
+    float *global_scale;
+};
+
+hipError_t launch_prepare(const PrepArgs &a, void *ws, hipStream_t st);
+size_t prepare_workspace_bytes(int64_t T, int fmt);
+
+struct QuantWArgs {
+    const uint16_t *w;
+    int64_t E, nout, K;
+    int fmt;
+    bool bf16;
+    uint8_t *codes, *scales;
+    float *global_scale;
+};
+
+hipError_t launch_quantize_weight(const QuantWArgs &a, void *ws, hipStream_t st);
+size_t quantize_weight_workspace_bytes(int64_t E, int64_t nout, int fmt);
+
+struct LinearArgs {
+    const uint8_t *b_codes, *b_scales, *r_codes, *r_scales;
+    const float *x_gscale;
+    int64_t T, K;
+    int fmt;
+    const uint8_t *w_codes, *w_scales;
+    const float *w_gscale;
+    int64_t E, nout;
+    const int32_t *offsets, *row_index;
+    int64_t rows;
+    float *y;
+    int64_t ldy;
+    bool y_vec;  // rows of y are 16-byte aligned: 128-bit stores
+};
+
+hipError_t launch_linear(const LinearArgs &a, void *ws, size_t ws_bytes, hipStream_t st);
+size_t linear_workspace_bytes(int64_t rows, int64_t K, int64_t nout, int64_t E, int fmt);
+
+}  // namespace sharq

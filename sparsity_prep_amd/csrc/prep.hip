@@ -1,0 +1,490 @@
+// Fused SharQ preparation kernels for gfx950.
+//
+// Source: SharQ: Bridging Activation Sparsity and FP4 Quantization for LLM Inference, Abstract.
+// One operator normalizes a row, picks the N:M mask from the row's own
+// magnitudes, quantizes the masked backbone to FP4, subtracts the
+// dequantized backbone to get the dense residual and quantizes that too.
+//
+// Work decomposition: one wavefront per row task.  Lane l of a wave owns the
+// eight consecutive elements [(c*64 + l)*8, +8) of chunk c of the row, so
+// every global load is one coalesced 128-bit word per lane (1 KiB per wave),
+// an N:M group with M <= 8 sits inside one lane, an MXFP4 block (32) spans
+// the four lanes of a DPP quad and an NVFP4 block (16) a lane pair.  The row
+// is read from HBM exactly once; everything else happens in registers.
+//
+//   MX + norm, K <= 8*512: the row stays in registers across the FP64 norm
+//                          reduction and the quantization pass;
+//   MX + norm, larger K:   the quantization pass re-reads the row (L2 hit);
+//   no norm:               tasks are (row, group of chunks), fully parallel;
+//   NVFP4:                 a pre-pass writes per-row norm statistics and
+//                          amax, a one-block kernel reduces the tensor scale,
+//                          then the main pass streams (row, chunk-group) tasks.
+#include "device_util.h"
+#include "kernels.h"
+
+namespace sharq {
+
+constexpr int kPrepWaves = 4;        // waves per workgroup
+constexpr int kChunk = 512;          // elements per wave-wide 128-bit load
+constexpr int kStreamChunks = 4;     // chunks per task when rows are split
+constexpr int kRegChunks = 8;        // register-resident row: K <= 4096
+
+struct RowStats {  // per-row statistics written by the NVFP4 pre-pass
+    float r, mu, amax, pad;
+};
+
+// ---------------------------------------------------------------- selection
+// keep bit i of the result is set when element i (of the 8 owned by the lane)
+// is among the N largest magnitudes of its M-group; equal magnitudes favour
+// the lower index.  M in {1,2,4,8}: groups lie inside the lane.
+template <int M>
+__device__ __forceinline__ uint32_t select_in_lane(const float v[8], int n) {
+    uint32_t key[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) key[i] = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+    uint32_t keep = 0;
+#pragma unroll
+    for (int g = 0; g < 8; g += M) {
+#pragma unroll
+        for (int i = 0; i < M; i++) {
+            int rank = 0;
+#pragma unroll
+            for (int j = 0; j < M; j++) {
+                if (j == i) continue;
+                const bool beats = j < i ? key[g + j] >= key[g + i] : key[g + j] > key[g + i];
+                rank += beats ? 1 : 0;
+            }
+            keep |= (rank < n ? 1u : 0u) << (g + i);
+        }
+    }
+    return keep;
+}
+
+// M = 16: a group spans the lane and its quad neighbour (lane ^ 1); the lower
+// lane of the pair holds group elements 0..7.
+__device__ __forceinline__ uint32_t select_m16(const float v[8], int n, int lane) {
+    uint32_t key[8], other[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        key[i] = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+        other[i] = dpp_u32<kDppQuadXor1>(key[i]);
+    }
+    const bool low = (lane & 1) == 0;
+    uint32_t keep = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        int rank = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            if (j != i) rank += (j < i ? key[j] >= key[i] : key[j] > key[i]) ? 1 : 0;
+            // partner elements come before ours when we are the upper lane
+            rank += (low ? other[j] > key[i] : other[j] >= key[i]) ? 1 : 0;
+        }
+        keep |= (rank < n ? 1u : 0u) << i;
+    }
+    return keep;
+}
+
+template <int M>
+__device__ __forceinline__ uint32_t select8(const float v[8], int n, int lane) {
+    if constexpr (M == 16) return select_m16(v, n, lane);
+    else return select_in_lane<M>(v, n);
+}
+
+// ---------------------------------------------------------------- block quantizers
+// MXFP4: 32-element block across a quad.  Writes packed codes of the lane's
+// eight elements, the dequantized values, and returns the E8M0 byte.
+__device__ __forceinline__ uint32_t quant_mx8(const float s[8], uint32_t &codes, float deq[8]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(s[i]));
+    m = fmaxf(m, dpp_f32<kDppQuadXor1>(m));
+    m = fmaxf(m, dpp_f32<kDppQuadXor2>(m));
+    const int E = mx_shared_exp(m);
+    const float inv = pow2_neg(E), sc = pow2(E);
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        float q;
+        c |= e2m1_encode(__fmul_rn(s[i], inv), q) << (4 * i);
+        deq[i] = __fmul_rn(q, sc);
+    }
+    codes = c;
+    return (uint32_t)(E + 127);
+}
+
+// NVFP4: 16-element block across a lane pair, tensor scale G (G6 = fl32(6G)).
+__device__ __forceinline__ uint32_t quant_nv8(const float s[8], float G, float G6, uint32_t &codes,
+                                              float deq[8]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(s[i]));
+    m = fmaxf(m, dpp_f32<kDppQuadXor1>(m));
+    const uint32_t sb = e4m3_encode_sat(__fdiv_rn(m, G6));
+    const float D = __fmul_rn(e4m3_value(sb), G);
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        float q = 0.0f;
+        if (sb != 0u) c |= e2m1_encode(__fdiv_rn(s[i], D), q) << (4 * i);
+        deq[i] = __fmul_rn(q, D);
+    }
+    codes = c;
+    return sb;
+}
+
+// ---------------------------------------------------------------- normalization
+template <int NORM>
+__device__ __forceinline__ void normalize8(float v[8], const float g[8], const float b[8], float r,
+                                           float mu) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        if constexpr (NORM == kNormRms) {
+            v[i] = __fmul_rn(__fmul_rn(v[i], r), g[i]);
+        } else if constexpr (NORM == kNormLayer) {
+            v[i] = __fadd_rn(__fmul_rn(__fmul_rn(__fsub_rn(v[i], mu), r), g[i]), b[i]);
+        }
+    }
+}
+
+template <bool BF16, bool HAS>
+__device__ __forceinline__ void load_param8(const uint16_t *p, int64_t e0, float out[8], float dflt) {
+    if (HAS && p != nullptr) {
+        unpack8<BF16>(*reinterpret_cast<const uint4 *>(p + e0), out);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) out[i] = dflt;
+    }
+}
+
+// ---------------------------------------------------------------- per-chunk body
+// Normalized values v of one lane -> mask byte, backbone and residual codes
+// and scales, stored at element offset e0 of row `row`.
+template <int FMT, int M>
+__device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, int64_t e0, int lane,
+                                                const float v[8], float G, float G6) {
+    const uint32_t keep = select8<M>(v, a.n, lane);
+    float S[8], dq[8], R[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) S[i] = (keep >> i) & 1u ? v[i] : 0.0f;
+    uint32_t bc, rc, bs, rs;
+    if constexpr (FMT == kFmtMx) bs = quant_mx8(S, bc, dq);
+    else bs = quant_nv8(S, G, G6, bc, dq);
+#pragma unroll
+    for (int i = 0; i < 8; i++) R[i] = __fsub_rn(v[i], dq[i]);
+    float unused[8];
+    if constexpr (FMT == kFmtMx) rs = quant_mx8(R, rc, unused);
+    else rs = quant_nv8(R, G, G6, rc, unused);
+
+    const int64_t K = a.K;
+    if (a.mask) a.mask[row * (K / 8) + e0 / 8] = (uint8_t)keep;
+    *reinterpret_cast<uint32_t *>(a.b_codes + row * (K / 2) + e0 / 2) = bc;
+    *reinterpret_cast<uint32_t *>(a.r_codes + row * (K / 2) + e0 / 2) = rc;
+    constexpr int LPB = FMT == kFmtMx ? 4 : 2;  // lanes per scale block
+    constexpr int B = FMT == kFmtMx ? 32 : 16;
+    if ((lane % LPB) == 0) {
+        a.b_scales[row * (K / B) + e0 / B] = (uint8_t)bs;
+        a.r_scales[row * (K / B) + e0 / B] = (uint8_t)rs;
+    }
+}
+
+// ---------------------------------------------------------------- MX, norm, row in registers
+template <bool BF16, int NORM, int M>
+__global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_reg(PrepArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
+    if (row >= a.T) return;
+    const uint16_t *xr = a.x + row * a.ldx;
+    const int64_t K = a.K;
+    const int nch = (int)((K + kChunk - 1) / kChunk);
+
+    uint4 raw[kRegChunks];
+#pragma unroll
+    for (int c = 0; c < kRegChunks; c++) {
+        const int64_t e0 = (int64_t)(c * kWave + lane) * 8;
+        raw[c] = (c < nch && e0 < K) ? *reinterpret_cast<const uint4 *>(xr + e0) : make_uint4(0, 0, 0, 0);
+    }
+    // FP64 statistics (each lane serial over its elements, then a wave tree)
+    double s1 = 0.0;
+    float v[8];
+#pragma unroll
+    for (int c = 0; c < kRegChunks; c++) {
+        unpack8<BF16>(raw[c], v);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            if constexpr (NORM == kNormRms) s1 += (double)v[i] * (double)v[i];
+            else s1 += (double)v[i];
+        }
+    }
+    s1 = wave_sum_f64(s1);
+    float r, mu = 0.0f;
+    if constexpr (NORM == kNormRms) {
+        r = (float)(1.0 / sqrt(s1 / (double)K + (double)a.eps));
+    } else {
+        const double mud = s1 / (double)K;
+        double s2 = 0.0;
+#pragma unroll
+        for (int c = 0; c < kRegChunks; c++) {
+            const int64_t e0 = (int64_t)(c * kWave + lane) * 8;
+            if (c < nch && e0 < K) {
+                unpack8<BF16>(raw[c], v);
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const double d = (double)v[i] - mud;
+                    s2 += d * d;
+                }
+            }
+        }
+        s2 = wave_sum_f64(s2);
+        mu = (float)mud;
+        r = (float)(1.0 / sqrt(s2 / (double)K + (double)a.eps));
+    }
+#pragma unroll
+    for (int c = 0; c < kRegChunks; c++) {
+        const int64_t e0 = (int64_t)(c * kWave + lane) * 8;
+        if (c < nch && e0 < K) {
+            float g[8], b[8];
+            load_param8<BF16, true>(a.gamma, e0, g, 1.0f);
+            load_param8<BF16, NORM == kNormLayer>(a.beta, e0, b, 0.0f);
+            unpack8<BF16>(raw[c], v);
+            normalize8<NORM>(v, g, b, r, mu);
+            decompose_store<kFmtMx, M>(a, row, e0, lane, v, 1.0f, 6.0f);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- MX, norm, two reads
+template <bool BF16, int NORM, int M>
+__global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_2pass(PrepArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
+    if (row >= a.T) return;
+    const uint16_t *xr = a.x + row * a.ldx;
+    const int64_t K = a.K;
+    float v[8];
+    double s1 = 0.0;
+    for (int64_t e0 = (int64_t)lane * 8; e0 < K; e0 += kChunk) {
+        unpack8<BF16>(*reinterpret_cast<const uint4 *>(xr + e0), v);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            if constexpr (NORM == kNormRms) s1 += (double)v[i] * (double)v[i];
+            else s1 += (double)v[i];
+        }
+    }
+    s1 = wave_sum_f64(s1);
+    float r, mu = 0.0f;
+    if constexpr (NORM == kNormRms) {
+        r = (float)(1.0 / sqrt(s1 / (double)K + (double)a.eps));
+    } else {
+        const double mud = s1 / (double)K;
+        double s2 = 0.0;
+        for (int64_t e0 = (int64_t)lane * 8; e0 < K; e0 += kChunk) {
+            unpack8<BF16>(*reinterpret_cast<const uint4 *>(xr + e0), v);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const double d = (double)v[i] - mud;
+                s2 += d * d;
+            }
+        }
+        s2 = wave_sum_f64(s2);
+        mu = (float)mud;
+        r = (float)(1.0 / sqrt(s2 / (double)K + (double)a.eps));
+    }
+    for (int64_t e0 = (int64_t)lane * 8; e0 < K; e0 += kChunk) {
+        float g[8], b[8];
+        load_param8<BF16, true>(a.gamma, e0, g, 1.0f);
+        load_param8<BF16, NORM == kNormLayer>(a.beta, e0, b, 0.0f);
+        unpack8<BF16>(*reinterpret_cast<const uint4 *>(xr + e0), v);
+        normalize8<NORM>(v, g, b, r, mu);
+        decompose_store<kFmtMx, M>(a, row, e0, lane, v, 1.0f, 6.0f);
+    }
+}
+
+// ---------------------------------------------------------------- streaming tasks
+// Row-split tasks: (row, kStreamChunks chunks).  Normalization statistics
+// come from the NVFP4 pre-pass (stats != nullptr) or there is no norm.
+template <bool BF16, int NORM, int FMT, int M>
+__global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_stream(PrepArgs a, const RowStats *stats) {
+    const int lane = threadIdx.x & 63;
+    const int64_t K = a.K;
+    const int64_t tasks_per_row = (K + (int64_t)kChunk * kStreamChunks - 1) / ((int64_t)kChunk * kStreamChunks);
+    const int64_t task = (int64_t)blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
+    const int64_t row = task / tasks_per_row;
+    if (row >= a.T) return;
+    const int64_t c0 = (task - row * tasks_per_row) * kStreamChunks;
+    const uint16_t *xr = a.x + row * a.ldx;
+    float r = 1.0f, mu = 0.0f, G = 1.0f, G6 = 6.0f;
+    if constexpr (NORM != kNormNone) {
+        r = stats[row].r;
+        mu = stats[row].mu;
+    }
+    if constexpr (FMT == kFmtNv) {
+        G = *a.global_scale;
+        G6 = __fmul_rn(6.0f, G);
+    }
+    uint4 raw[kStreamChunks];
+#pragma unroll
+    for (int c = 0; c < kStreamChunks; c++) {
+        const int64_t e0 = ((c0 + c) * kWave + lane) * 8;
+        raw[c] = e0 < K ? *reinterpret_cast<const uint4 *>(xr + e0) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < kStreamChunks; c++) {
+        const int64_t e0 = ((c0 + c) * kWave + lane) * 8;
+        if (e0 < K) {
+            float v[8], g[8], b[8];
+            unpack8<BF16>(raw[c], v);
+            if constexpr (NORM != kNormNone) {
+                load_param8<BF16, true>(a.gamma, e0, g, 1.0f);
+                load_param8<BF16, NORM == kNormLayer>(a.beta, e0, b, 0.0f);
+                normalize8<NORM>(v, g, b, r, mu);
+            }
+            decompose_store<FMT, M>(a, row, e0, lane, v, G, G6);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- NVFP4 pre-pass
+// Per row: norm statistics and amax of the normalized row.
+template <bool BF16, int NORM>
+__global__ __launch_bounds__(kPrepWaves * kWave) void k_nv_rowstats(PrepArgs a, RowStats *stats) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
+    if (row >= a.T) return;
+    const uint16_t *xr = a.x + row * a.ldx;
+    const int64_t K = a.K;
+    float v[8];
+    float r = 1.0f, mu = 0.0f;
+    if constexpr (NORM != kNormNone) {
+        double s1 = 0.0;
+        for (int64_t e0 = (int64_t)lane * 8; e0 < K; e0 += kChunk) {
+            unpack8<BF16>(*reinterpret_cast<const uint4 *>(xr + e0), v);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                if constexpr (NORM == kNormRms) s1 += (double)v[i] * (double)v[i];
+                else s1 += (double)v[i];
+            }
+        }
+        s1 = wave_sum_f64(s1);
+        if constexpr (NORM == kNormRms) {
+            r = (float)(1.0 / sqrt(s1 / (double)K + (double)a.eps));
+        } else {
+            const double mud = s1 / (double)K;
+            double s2 = 0.0;
+            for (int64_t e0 = (int64_t)lane * 8; e0 < K; e0 += kChunk) {
+                unpack8<BF16>(*reinterpret_cast<const uint4 *>(xr + e0), v);
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const double d = (double)v[i] - mud;
+                    s2 += d * d;
+                }
+            }
+            s2 = wave_sum_f64(s2);
+            mu = (float)mud;
+            r = (float)(1.0 / sqrt(s2 / (double)K + (double)a.eps));
+        }
+    }
+    float m = 0.0f;
+    for (int64_t e0 = (int64_t)lane * 8; e0 < K; e0 += kChunk) {
+        float g[8], b[8];
+        unpack8<BF16>(*reinterpret_cast<const uint4 *>(xr + e0), v);
+        if constexpr (NORM != kNormNone) {
+            load_param8<BF16, true>(a.gamma, e0, g, 1.0f);
+            load_param8<BF16, NORM == kNormLayer>(a.beta, e0, b, 0.0f);
+            normalize8<NORM>(v, g, b, r, mu);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    if (lane == 0) stats[row] = RowStats{r, mu, m, 0.0f};
+}
+
+// Tensor scale G = fl32(amax / 2688), or 1 when that is not positive.
+__global__ __launch_bounds__(1024) void k_nv_tensor_scale(const RowStats *stats, int64_t T, float *G) {
+    __shared__ float part[1024 / kWave];
+    float m = 0.0f;
+    for (int64_t i = threadIdx.x; i < T; i += blockDim.x) m = fmaxf(m, stats[i].amax);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.0f;
+        for (int i = 0; i < (int)(blockDim.x / kWave); i++) t = fmaxf(t, part[i]);
+        float g = __fdiv_rn(t, 2688.0f);
+        *G = g > 0.0f ? g : 1.0f;
+    }
+}
+
+__global__ void k_fill_f32(float *p, float v) { *p = v; }
+
+// ---------------------------------------------------------------- launcher
+template <bool BF16, int NORM, int FMT, int M>
+static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
+    const dim3 blk(kPrepWaves * kWave);
+    const int64_t K = a.K;
+    if constexpr (FMT == kFmtMx && NORM != kNormNone) {
+        const dim3 grid((unsigned)((a.T + kPrepWaves - 1) / kPrepWaves));
+        if (K <= (int64_t)kChunk * kRegChunks)
+            hipLaunchKernelGGL((k_prep_mx_reg<BF16, NORM, M>), grid, blk, 0, st, a);
+        else
+            hipLaunchKernelGGL((k_prep_mx_2pass<BF16, NORM, M>), grid, blk, 0, st, a);
+        if (a.global_scale) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, a.global_scale, 1.0f);
+        return hipGetLastError();
+    }
+    RowStats *stats = reinterpret_cast<RowStats *>(ws);
+    if constexpr (FMT == kFmtNv) {
+        const dim3 grid((unsigned)((a.T + kPrepWaves - 1) / kPrepWaves));
+        hipLaunchKernelGGL((k_nv_rowstats<BF16, NORM>), grid, blk, 0, st, a, stats);
+        hipLaunchKernelGGL(k_nv_tensor_scale, dim3(1), dim3(1024), 0, st, stats, a.T, a.global_scale);
+    } else if (a.global_scale) {
+        hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, a.global_scale, 1.0f);
+    }
+    const int64_t tasks_per_row = (K + (int64_t)kChunk * kStreamChunks - 1) / ((int64_t)kChunk * kStreamChunks);
+    const int64_t tasks = a.T * tasks_per_row;
+    const dim3 grid((unsigned)((tasks + kPrepWaves - 1) / kPrepWaves));
+    if constexpr (FMT == kFmtNv || NORM == kNormNone)
+        hipLaunchKernelGGL((k_prep_stream<BF16, NORM, FMT, M>), grid, blk, 0, st, a, stats);
+    return hipGetLastError();
+}
+
+template <bool BF16, int NORM, int FMT>
+static hipError_t launch_prep_m(const PrepArgs &a, void *ws, hipStream_t st) {
+    switch (a.m) {
+        case 1: return launch_prep_t<BF16, NORM, FMT, 1>(a, ws, st);
+        case 2: return launch_prep_t<BF16, NORM, FMT, 2>(a, ws, st);
+        case 4: return launch_prep_t<BF16, NORM, FMT, 4>(a, ws, st);
+        case 8: return launch_prep_t<BF16, NORM, FMT, 8>(a, ws, st);
+        case 16: return launch_prep_t<BF16, NORM, FMT, 16>(a, ws, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool BF16, int NORM>
+static hipError_t launch_prep_f(const PrepArgs &a, void *ws, hipStream_t st) {
+    return a.fmt == kFmtMx ? launch_prep_m<BF16, NORM, kFmtMx>(a, ws, st)
+                           : launch_prep_m<BF16, NORM, kFmtNv>(a, ws, st);
+}
+
+template <bool BF16>
+static hipError_t launch_prep_n(const PrepArgs &a, void *ws, hipStream_t st) {
+    switch (a.norm) {
+        case kNormNone: return launch_prep_f<BF16, kNormNone>(a, ws, st);
+        case kNormRms: return launch_prep_f<BF16, kNormRms>(a, ws, st);
+        case kNormLayer: return launch_prep_f<BF16, kNormLayer>(a, ws, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prepare(const PrepArgs &a, void *ws, hipStream_t st) {
+    if (a.T == 0) return hipSuccess;
+    return a.bf16 ? launch_prep_n<true>(a, ws, st) : launch_prep_n<false>(a, ws, st);
+}
+
+size_t prepare_workspace_bytes(int64_t T, int fmt) {
+    return fmt == kFmtNv ? (size_t)(T > 0 ? T : 1) * sizeof(RowStats) : 0;
+}
+
+}  // namespace sharq

@@ -4,12 +4,13 @@ This module only draws random numbers and lays them out; it holds none of
 the method's arithmetic (no norm, no mask, no quantization).  Both the CPU
 oracle and the HIP path are fed from here, so the same bytes reach both.
 
-The pages evaluate SharQ on Llama-3.1-8B, Qwen2.5-7B and Qwen3-30B-A3B
-(SharQ abstract, evaluation sentence).  No weights or activations of those
-models are available, so seeded tensors with their layer shapes stand in:
-Gaussian (or Student-t) activations with a few outlier channels, which is
-the "input-dependent outliers that dominate block scales" situation the
-abstract describes, and N(0, 0.02) weights.
+SharQ is evaluated on Llama-3.1-8B, Qwen2.5-7B and Qwen3-30B-A3B (SharQ:
+Bridging Activation Sparsity and FP4 Quantization for LLM Inference,
+Abstract).  No weights or activations of those models are available, so
+seeded tensors with their layer shapes stand in: Gaussian (or Student-t)
+activations with a few outlier channels -- the case the abstract describes,
+where a handful of large values set the FP4 block scales -- and N(0, 0.02)
+weights.
 
 Every array is returned as raw 16-bit patterns (numpy uint16) plus a dtype
 tag ("bf16" or "f16"), because numpy has no bfloat16.  Values are drawn in

@@ -1,0 +1,153 @@
+"""CPU checks of the C ABI: the library loads without a GPU, exports every
+entry point include/sharq.h declares, and rejects invalid arguments with the
+documented status code before making any HIP call (so nothing here touches a
+device).  Also records the sparse-MFMA decision as a compile probe."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sharq.h")
+LIB = os.path.join(ROOT, "sparsity_prep_amd", "libsharq.so")
+
+OK, NULL, SHAPE, NM, DTYPE, ALIGN, WORKSPACE, UNSUPPORTED = 0, 1, 2, 3, 4, 5, 6, 7
+BF16, F16, F32 = 1, 0, 2
+MX, NV = 0, 1
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} not built (python -m sparsity_prep_amd.build)")
+    import sparsity_prep_amd
+    return sparsity_prep_amd.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SHARQ_API[^;(]*?\b(sharq_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_symbols()
+    for n in ("sharq_prepare", "sharq_linear", "sharq_quantize_weight"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)", out))
+    assert set(declared_symbols()) == {s for s in exported if s.startswith("sharq_")}
+
+
+def test_version_and_strings(L):
+    assert L.sharq_abi_version() == 1
+    for code in range(9):
+        assert L.sharq_status_string(code)
+    assert L.sharq_status_string(99) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10002)
+
+
+def prep(L, x=FAKE, dt=BF16, T=4, K=256, ldx=None, norm=1, gamma=FAKE, beta=None, n=2, m=4,
+         fmt=MX, mask=FAKE, bc=FAKE, bs=FAKE, rc=FAKE, rs=FAKE, G=None, ws=None, wsb=0):
+    return L.sharq_prepare(x, dt, T, K, K if ldx is None else ldx, norm, gamma, beta, 1e-5, n, m,
+                           fmt, mask, bc, bs, rc, rs, G, ws, wsb, None)
+
+
+def test_prepare_validation(L):
+    assert prep(L, fmt=3) == UNSUPPORTED
+    assert prep(L, dt=F32) == DTYPE
+    assert prep(L, norm=7) == UNSUPPORTED
+    assert prep(L, K=100) == SHAPE                # not a multiple of 32
+    assert prep(L, K=256, ldx=128) == SHAPE
+    assert prep(L, T=-1) == SHAPE
+    assert prep(L, n=5, m=4) == NM
+    assert prep(L, n=-1, m=4) == NM
+    assert prep(L, n=2, m=3) == NM
+    assert prep(L, n=2, m=32) == NM
+    assert prep(L, K=40, fmt=NV, G=FAKE) == SHAPE  # not a multiple of 16
+    assert prep(L, x=None) == NULL
+    assert prep(L, gamma=None) == NULL
+    assert prep(L, norm=0, gamma=None, x=MISALIGNED) == ALIGN
+    assert prep(L, ldx=256 + 4) == ALIGN
+    assert prep(L, fmt=NV) == NULL                 # NVFP4 needs the tensor-scale output
+    assert prep(L, fmt=NV, G=FAKE) == WORKSPACE
+    assert prep(L, fmt=NV, G=FAKE, ws=FAKE, wsb=1) == WORKSPACE
+    assert prep(L, T=0, x=None) == OK              # empty tensor is a no-op, no HIP call
+
+
+def test_quantize_weight_validation(L):
+    q = L.sharq_quantize_weight
+    assert q(FAKE, BF16, 1, 16, 256, 9, FAKE, FAKE, None, None, 0, None) == UNSUPPORTED
+    assert q(FAKE, F32, 1, 16, 256, MX, FAKE, FAKE, None, None, 0, None) == DTYPE
+    assert q(FAKE, BF16, 0, 16, 256, MX, FAKE, FAKE, None, None, 0, None) == SHAPE
+    assert q(FAKE, BF16, 1, 16, 40, MX, FAKE, FAKE, None, None, 0, None) == SHAPE
+    assert q(None, BF16, 1, 16, 256, MX, FAKE, FAKE, None, None, 0, None) == NULL
+    assert q(FAKE, BF16, 1, 16, 256, NV, FAKE, FAKE, None, None, 0, None) == NULL
+    assert q(FAKE, BF16, 1, 16, 256, NV, FAKE, FAKE, FAKE, None, 0, None) == WORKSPACE
+    assert q(MISALIGNED, BF16, 1, 16, 256, MX, FAKE, FAKE, None, None, 0, None) == ALIGN
+    assert q(None, BF16, 1, 0, 256, MX, None, None, None, None, 0, None) == OK
+
+
+def lin(L, T=4, K=256, fmt=MX, E=1, nout=64, offs=None, ridx=None, rows=None, y=FAKE, ldy=None,
+        bc=FAKE, xg=None, wg=None):
+    return L.sharq_linear(bc, FAKE, FAKE, FAKE, xg, T, K, fmt, FAKE, FAKE, wg, E, nout, offs, ridx,
+                          T if rows is None else rows, y, nout if ldy is None else ldy, None, 0, None)
+
+
+def test_linear_validation(L):
+    assert lin(L, fmt=5) == UNSUPPORTED
+    assert lin(L, K=160) == SHAPE                 # not a multiple of 128
+    assert lin(L, ldy=10) == SHAPE
+    assert lin(L, rows=7) == SHAPE                # dense rows must equal T without a gather
+    assert lin(L, E=4) == NULL                    # grouped needs offsets
+    assert lin(L, bc=None) == NULL
+    assert lin(L, fmt=NV) == NULL                 # NVFP4 needs both tensor scales
+    assert lin(L, y=MISALIGNED) == ALIGN
+    assert lin(L, rows=0, T=0) == OK
+    assert lin(L, T=0, rows=3, ridx=FAKE) == SHAPE
+
+
+def test_workspace_sizes(L):
+    assert L.sharq_prepare_workspace_size(100, 256, MX) == 0
+    assert L.sharq_prepare_workspace_size(100, 256, NV) >= 100 * 12
+    assert L.sharq_quantize_weight_workspace_size(2, 64, 256, NV) >= 128 * 4
+    assert L.sharq_linear_workspace_size(64, 256, 64, 1, MX) == 0
+
+
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+def _compiles(tmp_path, body):
+    src = tmp_path / "probe.hip"
+    src.write_text("#include <hip/hip_runtime.h>\n"
+                   "typedef int v4i __attribute__((ext_vector_type(4)));\n"
+                   "typedef int v8i __attribute__((ext_vector_type(8)));\n"
+                   "typedef float v4f __attribute__((ext_vector_type(4)));\n" + body)
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "--offload-device-only", "-c", str(src),
+                        "-o", str(tmp_path / "p.o")], capture_output=True, text=True)
+    return r.returncode == 0
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_gfx950_has_block_scaled_fp4_mfma_but_no_sparse_fp4(tmp_path):
+    """The backbone runs dense on its zero-filled form because gfx950's sparse
+    matrix instructions take fp8/bf8/f16/bf16 operands only and no block
+    scale; the block-scaled FP4 instruction is dense."""
+    assert _compiles(tmp_path, "__global__ void k(v8i*a,v8i*b,v4f*c){int i=threadIdx.x;"
+                     "c[i]=__builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i],b[i],c[i],4,4,0,127,0,127);}")
+    assert _compiles(tmp_path, "__global__ void k(v4i*a,v8i*b,v4f*c,int*x){int i=threadIdx.x;"
+                     "c[i]=__builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a[i],b[i],c[i],x[i],0,0);}")
+    for name in ("smfmac_f32_16x16x128_fp4_fp4", "smfmac_f32_16x16x256_fp4_fp4",
+                 "smfmac_scale_f32_16x16x128_f8f6f4", "smfmac_f32_16x16x128_f8f6f4"):
+        assert not _compiles(tmp_path, "__global__ void k(v4i*a,v8i*b,v4f*c,int*x){int i=threadIdx.x;"
+                             f"c[i]=__builtin_amdgcn_{name}(a[i],b[i],c[i],x[i],0,0);}}"), name

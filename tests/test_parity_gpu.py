@@ -1,0 +1,353 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Prepared masks, codes and scales must be bit-exact (tie allowance in
+parity_util); layer outputs must be within relative Frobenius error 1e-3 of
+the oracle's FP64 product of the same dequantized codes.  Small cases span
+several tiles and ragged tails; full-size workloads (Llama-3.1-8B prefill
+and decode, Qwen2.5-7B NVFP4 prefill, Qwen3-30B-A3B MoE experts) are checked
+in full for the prepared tensors where the oracle is fast enough, otherwise
+on sampled rows, with the launch configuration the benchmark uses.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from golden_io import load as load_golden
+from parity_util import compare_prepared, dev16, host, prepared_to_host, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparsity_prep_amd as sq
+    sq.lib()
+    return sq
+
+
+def sq():
+    import sparsity_prep_amd
+    return sparsity_prep_amd
+
+
+def gpu_prepare(x_bits, dtype, K, norm, g_bits, b_bits, eps, n, m, fmt, with_mask=True):
+    x = dev16(x_bits, dtype)
+    g = dev16(g_bits, dtype) if g_bits is not None else None
+    b = dev16(b_bits, dtype) if b_bits is not None else None
+    p = sq().prepare(x, norm=norm, gamma=g, beta=b, eps=eps, n=n, m=m, fmt=fmt, with_mask=with_mask)
+    torch.cuda.synchronize()
+    return p
+
+
+def check_prep(x, dtype, K, norm, g, b, eps, n, m, fmt, rows=None, what=""):
+    p = gpu_prepare(x, dtype, K, norm, g, b, eps, n, m, fmt)
+    gh = prepared_to_host(p)
+    o = oracle.prepare(x, dtype, K, norm, g, b, eps, n, m, fmt, rows=rows, trace=True)
+    if rows is not None:
+        gh = {k: (v[rows] if isinstance(v, np.ndarray) else v) for k, v in gh.items()}
+    stats = compare_prepared(gh, o, n, m, what)
+    if fmt == oracle.FMT_NVFP4:
+        assert gh["G"] == o.G, (what, gh["G"], o.G)
+    return p, gh, o, stats
+
+
+# ---------------------------------------------------------------- hand-worked rows
+
+@pytest.mark.parametrize("name", ["worked_mxfp4_2of4.txt", "worked_nvfp4_2of4.txt"])
+def test_golden_rows(name):
+    g = load_golden(name)
+    p = gpu_prepare(g["x"], g["dtype"], g["K"], g["norm"], None, None, g["eps"], g["N"], g["M"], g["fmt"])
+    gh = prepared_to_host(p)
+    for key in ("mask", "b_codes", "b_scales", "r_codes", "r_scales"):
+        assert np.array_equal(gh[key], g[key]), (key, gh[key], g[key])
+    if g["fmt"] == oracle.FMT_NVFP4:
+        assert gh["G"] == g["gscale"]
+
+
+# ---------------------------------------------------------------- prep sweeps
+
+PREP_CASES = [
+    # (fmt, norm, dtype, n, m, T, K)
+    (0, 1, "bf16", 2, 4, 5, 256),
+    (0, 1, "f16", 2, 4, 16, 256),
+    (0, 0, "bf16", 2, 4, 37, 2560),
+    (0, 2, "bf16", 2, 4, 7, 1024),
+    (0, 1, "bf16", 1, 4, 3, 4096),
+    (0, 1, "bf16", 3, 4, 9, 3584),
+    (0, 1, "bf16", 4, 8, 4, 512),
+    (0, 1, "bf16", 1, 2, 4, 96),
+    (0, 1, "bf16", 8, 16, 6, 1536),
+    (0, 0, "bf16", 5, 16, 6, 2048 + 32),
+    (0, 1, "bf16", 1, 1, 2, 64),
+    (0, 1, "bf16", 0, 4, 2, 128),
+    (0, 1, "bf16", 4, 4, 3, 800),
+    (0, 1, "bf16", 2, 4, 5, 4608),      # norm with a re-read of the row
+    (0, 2, "f16", 2, 4, 3, 5120 + 32),
+    (0, 0, "f16", 2, 4, 40, 768),
+    (1, 1, "bf16", 2, 4, 9, 256),
+    (1, 0, "bf16", 2, 4, 33, 2048 + 16),
+    (1, 2, "bf16", 2, 4, 4, 1024),
+    (1, 1, "f16", 1, 2, 5, 3584),
+    (1, 1, "bf16", 8, 16, 3, 4608),
+    (1, 0, "bf16", 4, 4, 2, 48),
+]
+
+
+@pytest.mark.parametrize("case", PREP_CASES, ids=lambda c: "fmt%d-norm%d-%s-%d:%d-T%d-K%d" % c)
+def test_prep_sweep(case):
+    fmt, norm, dtype, n, m, T, K = case
+    tag = PREP_CASES.index(case)
+    x = synth.small_case(K, T, dtype, outliers=max(1, K // 200), mult=40.0,
+                         dist="t" if fmt else "normal", tag=tag)
+    g = synth.small_gamma(K, dtype, tag=tag) if norm else None
+    b = synth.small_gamma(K, dtype, tag=tag + 1) if norm == 2 else None
+    _, _, _, stats = check_prep(x, dtype, K, norm, g, b, 1e-5, n, m, fmt, what=str(case))
+    assert stats["mismatched"] == 0, stats
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_prep_edge_values(fmt):
+    K, T = 512, 8
+    rng = np.random.default_rng(11)
+    x = np.zeros((T, K), np.float32)
+    x[1] = rng.standard_normal(K) * 2.0 ** -130           # subnormal range (bf16 keeps them)
+    x[2] = rng.standard_normal(K) * 2.0 ** 120             # near the top of the range
+    x[3] = 1.0                                              # every magnitude tied
+    x[4] = np.where(np.arange(K) % 2, -1.0, 1.0) * 0.75     # E2M1 midpoints everywhere
+    x[5, ::7] = 3.0e38
+    x[6] = rng.integers(-3, 4, K) * 0.5                     # heavy ties, small integers
+    x[7] = -0.0
+    bits = synth.to_bits(x, "bf16")
+    _, _, _, stats = check_prep(bits, "bf16", K, 0, None, None, 0.0, 2, 4, fmt, what=f"edge fmt{fmt}")
+    assert stats["mismatched"] == 0
+
+
+def test_prep_zero_rows_is_noop():
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
+    p = sq().prepare(x, norm=0, n=2, m=4, fmt=0)
+    assert p.b_codes.shape == (0, 128)
+
+
+def test_prep_strided_rows():
+    K, T, ld = 512, 6, 512 + 64
+    x = synth.small_case(ld, T, "bf16", tag=77)
+    xt = dev16(x, "bf16")[:, :K]
+    p = sq().prepare(xt, norm=0, n=2, m=4, fmt=0)
+    torch.cuda.synchronize()
+    o = oracle.prepare(np.ascontiguousarray(x[:, :K]), "bf16", K, 0, None, None, 0.0, 2, 4, 0, trace=True)
+    compare_prepared(prepared_to_host(p), o, 2, 4, "strided")
+
+
+# ---------------------------------------------------------------- weight quantization
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("shape", [(1, 48, 256), (3, 40, 640), (1, 257, 4096)])
+def test_quantize_weight(fmt, shape):
+    E, nout, K = shape
+    w = synth.small_weight(nout, K, experts=E, tag=E * 7 + K)
+    q = sq().quantize_weight(dev16(w, "bf16"), fmt=fmt)
+    torch.cuda.synchronize()
+    o = oracle.quantize_weight(w, "bf16", fmt)
+    assert np.array_equal(host(q.codes), o.codes)
+    assert np.array_equal(host(q.scales), o.scales)
+    if fmt == 1:
+        assert np.array_equal(host(q.global_scale), o.gscale)
+
+
+# ---------------------------------------------------------------- layer product
+
+def ref_linear(pg, qw, row_index=None, offsets=None, out_rows=None, expert_of_row=None):
+    """Oracle FP64 product of the GPU's own codes (decoded by the oracle)."""
+    K, fmt = pg.K, pg.fmt
+    G = float(host(pg.global_scale)[0]) if pg.global_scale is not None else 1.0
+    bc, bs, rc, rs = host(pg.b_codes), host(pg.b_scales), host(pg.r_codes), host(pg.r_scales)
+    wc, ws = host(qw.codes), host(qw.scales)
+    wG = host(qw.global_scale) if qw.global_scale is not None else np.ones(qw.E, np.float32)
+    rows = np.arange(pg.T if row_index is None and offsets is None else
+                     (len(row_index) if row_index is not None else int(offsets[-1])))
+    if out_rows is not None:
+        rows = np.asarray(out_rows)
+    src = rows if row_index is None else row_index[rows]
+    if offsets is None:
+        ex = np.zeros(len(rows), np.int64)
+    else:
+        ex = np.searchsorted(offsets, rows, side="right") - 1
+    y = np.zeros((len(rows), qw.nout))
+    for e in np.unique(ex):
+        sel = np.nonzero(ex == e)[0]
+        a = oracle.dequant(bc[src[sel]], bs[src[sel]], K, fmt, G) + 0.0
+        r = oracle.dequant(rc[src[sel]], rs[src[sel]], K, fmt, G)
+        w = oracle.dequant(wc[e], ws[e], K, fmt, float(wG[e]))
+        y[sel] = a @ w.T + r @ w.T
+    return rows, y
+
+
+LINEAR_CASES = [
+    # (fmt, T, K, nout)
+    (0, 16, 256, 256), (0, 300, 640, 272), (0, 513, 1024, 520), (0, 1, 512, 64), (0, 5, 768, 48),
+    (0, 17, 1280, 100), (0, 64, 4096, 256), (0, 65, 384, 1000), (0, 2, 14336, 64),
+    (1, 16, 256, 256), (1, 300, 640, 272), (1, 1, 512, 64), (1, 70, 1024, 130), (1, 257, 3584, 256),
+]
+
+
+@pytest.mark.parametrize("case", LINEAR_CASES, ids=lambda c: "fmt%d-T%d-K%d-N%d" % c)
+def test_linear(case):
+    fmt, T, K, nout = case
+    x = synth.small_case(K, T, "bf16", outliers=3, mult=40.0, tag=T + K)
+    g = synth.small_gamma(K, "bf16", tag=T)
+    pg = gpu_prepare(x, "bf16", K, 1, g, None, 1e-5, 2, 4, fmt)
+    w = synth.small_weight(nout, K, tag=nout + K)
+    qw = sq().quantize_weight(dev16(w, "bf16"), fmt=fmt)
+    y = host(sq().linear(pg, qw))
+    _, ref = ref_linear(pg, qw)
+    err = rel_fro(y, ref)
+    assert err <= TOL, err
+    # and against the oracle end to end (its own prep and weight)
+    o = oracle.prepare(x, "bf16", K, 1, g, None, 1e-5, 2, 4, fmt)
+    ow = oracle.quantize_weight(w, "bf16", fmt)
+    assert rel_fro(y, oracle.linear(o, ow)) <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_linear_grouped(fmt):
+    K, nout, E, T = 640, 96, 5, 90
+    x = synth.small_case(K, T, "bf16", outliers=3, tag=5)
+    pg = gpu_prepare(x, "bf16", K, 0, None, None, 0.0, 2, 4, fmt)
+    w = synth.small_weight(nout, K, experts=E, tag=6)
+    qw = sq().quantize_weight(dev16(w, "bf16"), fmt=fmt)
+    offsets = np.array([0, 130, 130, 141, 400, 401], np.int32)   # an empty expert, ragged sizes
+    rng = np.random.default_rng(3)
+    row_index = rng.integers(0, T, offsets[-1]).astype(np.int32)
+    y = host(sq().linear(pg, qw, group_offsets=torch.from_numpy(offsets).cuda(),
+                         row_index=torch.from_numpy(row_index).cuda(), rows=int(offsets[-1])))
+    _, ref = ref_linear(pg, qw, row_index=row_index, offsets=offsets)
+    assert rel_fro(y, ref) <= TOL
+    # contiguous grouped rows, no gather
+    pg2 = gpu_prepare(synth.small_case(K, 401, "bf16", tag=9), "bf16", K, 0, None, None, 0.0, 2, 4, fmt)
+    y2 = host(sq().linear(pg2, qw, group_offsets=torch.from_numpy(offsets).cuda(), rows=401))
+    _, ref2 = ref_linear(pg2, qw, offsets=offsets)
+    assert rel_fro(y2, ref2) <= TOL
+
+
+def test_determinism():
+    K, T, nout = 4096, 512, 512
+    x = synth.small_case(K, T, "bf16", tag=21)
+    g = synth.small_gamma(K, "bf16", tag=21)
+    w = synth.small_weight(nout, K, tag=21)
+    qw = sq().quantize_weight(dev16(w, "bf16"), fmt=0)
+    outs = []
+    for _ in range(2):
+        pg = gpu_prepare(x, "bf16", K, 1, g, None, 1e-5, 2, 4, 0)
+        outs.append((prepared_to_host(pg), host(sq().linear(pg, qw))))
+    for key in ("mask", "b_codes", "b_scales", "r_codes", "r_scales"):
+        assert np.array_equal(outs[0][0][key], outs[1][0][key])
+    assert np.array_equal(outs[0][1], outs[1][1])
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+def _weight_sample_check(wl, lin, qw, w_bits, nrows=128, seed=0):
+    rng = np.random.default_rng(seed)
+    E = qw.E
+    codes, scales = host(qw.codes), host(qw.scales)
+    for e in sorted(set([0, E - 1])):
+        rows = np.sort(rng.choice(qw.nout, size=min(nrows, qw.nout), replace=False))
+        G = 1.0
+        if wl.fmt == oracle.FMT_NVFP4:
+            amax = float(np.abs(synth.bits_to_f32(w_bits[e], wl.dtype)).max())
+            G = oracle.nv_global_scale(amax)
+            assert host(qw.global_scale)[e] == np.float32(G)
+        c, s = oracle.quantize_rows(w_bits[e][rows], wl.dtype, wl.fmt, G)
+        assert np.array_equal(codes[e][rows], c), (lin.name, e)
+        assert np.array_equal(scales[e][rows], s), (lin.name, e)
+
+
+def _run_layer(wl, lin, tokens, prep_rows=None, out_rows=64, seed=0):
+    x = synth.activation(wl, lin, tokens)
+    g = synth.gamma(wl, lin) if lin.norm else None
+    p, gh, o, stats = check_prep(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.n, wl.m, wl.fmt,
+                                 rows=prep_rows, what=f"{wl.name}/{lin.name}/T{tokens}")
+    assert stats["mismatched"] <= 1e-5 * stats["elements"]
+    w = synth.weight(wl, lin)
+    qw = sq().quantize_weight(dev16(w, wl.dtype), fmt=wl.fmt)
+    torch.cuda.synchronize()
+    _weight_sample_check(wl, lin, qw, w)
+    y = host(sq().linear(p, qw))
+    rng = np.random.default_rng(seed)
+    rows = np.arange(tokens) if tokens <= out_rows else np.sort(rng.choice(tokens, out_rows, replace=False))
+    rows, ref = ref_linear(p, qw, out_rows=rows)
+    err = rel_fro(y[rows], ref)
+    print(f"{wl.name}/{lin.name} T={tokens}: prep mismatches {stats['mismatched']} "
+          f"of {stats['elements']}, GEMM rel err {err:.2e}", flush=True)
+    assert err <= TOL
+    return err
+
+
+@pytest.mark.parametrize("lin", [0, 1, 2], ids=["qkv", "gate_up", "down"])
+def test_llama8b_prefill_full(lin):
+    wl = synth.WORKLOADS[1]
+    _run_layer(wl, wl.linears[lin], wl.tokens)
+
+
+@pytest.mark.parametrize("tokens", synth.DECODE_TOKENS)
+@pytest.mark.parametrize("lin", [0, 1, 2], ids=["qkv", "gate_up", "down"])
+def test_llama8b_decode_full(lin, tokens):
+    wl = synth.WORKLOADS[2]
+    _run_layer(wl, wl.linears[lin], tokens)
+
+
+@pytest.mark.parametrize("lin", [0, 1, 2], ids=["qkv", "gate_up", "down"])
+def test_qwen25_7b_nvfp4_full(lin):
+    wl = synth.WORKLOADS[3]
+    rng = np.random.default_rng(lin)
+    rows = np.unique(np.concatenate([[0, wl.tokens - 1], rng.choice(wl.tokens, 254, replace=False)]))
+    _run_layer(wl, wl.linears[lin], wl.tokens, prep_rows=rows)
+
+
+def test_single_linear_c0():
+    wl = synth.WORKLOADS[0]
+    _run_layer(wl, wl.linears[0], wl.tokens)
+
+
+def test_qwen3_moe_full():
+    wl = synth.WORKLOADS[4]
+    route = synth.moe_routing(wl)
+    offs = torch.from_numpy(route.offsets).cuda()
+    ridx = torch.from_numpy(route.row_index).cuda()
+    nrows = int(route.offsets[-1])
+    rng = np.random.default_rng(4)
+    sample = np.sort(rng.choice(nrows, 96, replace=False))
+    # gate_up: RMSNorm on the unique tokens, grouped product gathers rows
+    lin = wl.linears[0]
+    x = synth.activation(wl, lin, wl.tokens)
+    g = synth.gamma(wl, lin)
+    p, gh, o, stats = check_prep(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.n, wl.m, wl.fmt,
+                                 what="moe gate_up")
+    w = synth.weight(wl, lin)
+    qw = sq().quantize_weight(dev16(w, wl.dtype), fmt=wl.fmt)
+    _weight_sample_check(wl, lin, qw, w, nrows=32)
+    y = host(sq().linear(p, qw, group_offsets=offs, row_index=ridx, rows=nrows))
+    _, ref = ref_linear(p, qw, row_index=route.row_index, offsets=route.offsets, out_rows=sample)
+    err = rel_fro(y[sample], ref)
+    print(f"moe gate_up rel err {err:.2e}", flush=True)
+    assert err <= TOL
+    # down: rows already sorted by expert, no norm
+    lin = wl.linears[1]
+    x = synth.activation(wl, lin, nrows)
+    rows = np.unique(np.concatenate([[0, nrows - 1], rng.choice(nrows, 510, replace=False)]))
+    p, gh, o, stats = check_prep(x, wl.dtype, lin.k, lin.norm, None, None, wl.eps, wl.n, wl.m, wl.fmt,
+                                 rows=rows, what="moe down")
+    w = synth.weight(wl, lin)
+    qw = sq().quantize_weight(dev16(w, wl.dtype), fmt=wl.fmt)
+    _weight_sample_check(wl, lin, qw, w, nrows=32)
+    y = host(sq().linear(p, qw, group_offsets=offs, rows=nrows))
+    _, ref = ref_linear(p, qw, offsets=route.offsets, out_rows=sample)
+    err = rel_fro(y[sample], ref)
+    print(f"moe down rel err {err:.2e}", flush=True)
+    assert err <= TOL

@@ -160,7 +160,8 @@ SHARQ_API size_t sharq_linear_workspace_size(int64_t rows, int64_t K, int64_t no
  *   b_codes, b_scales, r_codes, r_scales  prepared activations, T rows,
  *                as written by sharq_prepare (dense row-major)
  *   x_global_scale  device float (NVFP4), NULL for MXFP4
- *   T, K         prepared rows and reduction length (K % 128 == 0)
+ *   T, K         prepared rows and reduction length (K % 128 == 0); each
+ *                operand (T*K/2 code bytes, one expert's nout*K/2) < 2 GiB
  *   w_codes, w_scales, w_global_scale  payload of sharq_quantize_weight
  *   experts, nout  weight shape
  *   group_offsets  experts == 1: NULL.  experts > 1: device int32

@@ -151,6 +151,9 @@ sharq_status sharq_linear(const uint8_t *b_codes, const uint8_t *b_scales, const
         !aligned(b_scales, 4) || !aligned(r_scales, 4) || !aligned(w_scales, 4))
         return SHARQ_ERR_ALIGN;
     if (!aligned(y, 4)) return SHARQ_ERR_ALIGN;
+    // operands are addressed with 32-bit buffer offsets
+    const int64_t limit = (int64_t)1 << 31;
+    if (T * (K / 2) >= limit || nout * (K / 2) >= limit) return SHARQ_ERR_SHAPE;
     const size_t need = linear_workspace_bytes(rows, K, nout, experts, fmt);
     if (need > 0 && (!workspace || workspace_bytes < need)) return SHARQ_ERR_WORKSPACE;
     LinearArgs a;

@@ -40,6 +40,34 @@ __device__ __forceinline__ void unpack8(const uint4 &q, float v[8]) {
     v[6] = elem_lo<BF16>(q.w); v[7] = elem_hi<BF16>(q.w);
 }
 
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer resources: loads at offsets >= the resource's byte count return
+// zeros, so out-of-range rows of a tile need no branch.  Offsets are 32-bit;
+// the C ABI keeps every operand below 2 GiB.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint2 bload64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
+// Direct buffer -> LDS loads: lane i's bytes land at lds + i*size (lds is
+// wave-uniform); out-of-range lanes write zeros.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, off, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- lane exchange
 // DPP quad permutations: lane i of every group of four reads lane perm[i].
 constexpr int kDppQuadXor1 = 0xB1;  // [1,0,3,2]
@@ -90,6 +118,39 @@ __device__ __forceinline__ uint32_t e2m1_encode(float u, float &q) {
     return c | (neg << 3);
 }
 
+// Hardware E2M1 conversion of eight values (element i -> nibble i) divided
+// by a power-of-two scale.  The scale operand carries an E8M0 exponent E as
+// the float bit pattern (E+127) << 23 (so 2^-127 is the pattern 0).
+// v_cvt_scalef32_pk_fp4_f32 then yields exactly the nearest-even, saturating
+// E2M1 code of v*2^-E (checked on the MI355X against the software rounding
+// for all 2^32 inputs at unit scale and for every E in [-127, 125]), except
+// that a negative value rounding to zero keeps its sign (code 0x8); those
+// sign bits are cleared so that a zero magnitude is always the code 0x0.
+__device__ __forceinline__ uint32_t e2m1_cvt8(const float u[8], float scale) {
+    uint32_t p = 0;
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, u[0], u[1], scale, 0);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, u[2], u[3], scale, 1);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, u[4], u[5], scale, 2);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, u[6], u[7], scale, 3);
+    const uint32_t zero_mag = ~(p | (p >> 1) | (p >> 2)) & 0x11111111u;
+    return p & ~(zero_mag << 3);
+}
+
+typedef float sharq_v2f __attribute__((ext_vector_type(2)));
+
+// Values of eight E2M1 codes times the power-of-two scale (same encoding as
+// above); exact, +0 for code 0.
+__device__ __forceinline__ void e2m1_dec8(uint32_t p, float scale, float q[8]) {
+    sharq_v2f t;
+    t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, scale, 0); q[0] = t.x; q[1] = t.y;
+    t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, scale, 1); q[2] = t.x; q[3] = t.y;
+    t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, scale, 2); q[4] = t.x; q[5] = t.y;
+    t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, scale, 3); q[6] = t.x; q[7] = t.y;
+}
+
+// E8M0 exponent E as the scale operand of the conversions above.
+__device__ __forceinline__ float e8m0_operand(int E) { return __uint_as_float((uint32_t)(E + 127) << 23); }
+
 // ---------------------------------------------------------------- E8M0 (MX)
 // floor(log2 a) for a finite a > 0, subnormals included.
 __device__ __forceinline__ int floor_log2_f32(float a) {
@@ -99,10 +160,25 @@ __device__ __forceinline__ int floor_log2_f32(float a) {
 
 // OCP MX shared exponent for E2M1 elements: floor(log2 amax) - 2, or -127
 // for amax == 0 (never below -127; at most 125 for finite floats).
+// Branch-free: amax == 0 lands on the subnormal formula (-150 - 2), which
+// the clamp maps to -127.
 __device__ __forceinline__ int mx_shared_exp(float amax) {
-    if (amax == 0.0f) return -127;
     const int e = floor_log2_f32(amax) - 2;
     return e < -127 ? -127 : e;
+}
+
+// Max over the four lanes of a quad (MX block) / a lane pair (NVFP4 block)
+// of a non-negative float, done on the bit pattern (same order as the value).
+__device__ __forceinline__ float quad_max_nonneg(float m) {
+    uint32_t b = __float_as_uint(m);
+    b = max(b, dpp_u32<kDppQuadXor1>(b));
+    b = max(b, dpp_u32<kDppQuadXor2>(b));
+    return __uint_as_float(b);
+}
+__device__ __forceinline__ float pair_max_nonneg(float m) {
+    uint32_t b = __float_as_uint(m);
+    b = max(b, dpp_u32<kDppQuadXor1>(b));
+    return __uint_as_float(b);
 }
 
 // 2^-E as a normal float for E in [-127, 125].

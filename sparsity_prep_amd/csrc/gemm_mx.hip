@@ -12,12 +12,13 @@
 // zero-filled form: gfx950's sparse matrix instructions (smfmac) take fp8,
 // bf8, f16 or bf16 operands without block scales, so none holds MXFP4.
 //
-// Operand mapping for one 16x16x128 MFMA: the weight fragment is the A
-// operand (16 weight rows), the activation fragment is the B operand (16
-// token rows), so each lane's four accumulator values are four consecutive
-// output columns of one token row and leave as one 128-bit store.  Lane l
-// feeds row l%16 and the 32-element block l/16 of the 128-wide K step (16
-// bytes of codes, one scale byte).
+// Operand mapping: the weight fragment is the A operand, the activation
+// fragment the B operand, so every group of four accumulator values is four
+// consecutive output columns of one token row and leaves as one 128-bit
+// store.  Each lane feeds 16 bytes of codes (one 32-element block of one
+// row) and that block's scale byte.  The prefill kernel uses the 32x32x64
+// shape, the small-T kernel the 16x16x128 shape (lane l: row l%16, block
+// l/16).
 #include "device_util.h"
 #include "kernels.h"
 
@@ -26,6 +27,7 @@ namespace sharq {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kCbszFp4 = 4;  // MFMA operand format code for E2M1
 
@@ -33,6 +35,18 @@ __device__ __forceinline__ v4f mfma_fp4(v4i a, v4i b, v4f c, int sa, int sb) {
     const v8i a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
     const v8i b8 = {b.x, b.y, b.z, b.w, 0, 0, 0, 0};
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, kCbszFp4, kCbszFp4, 0, sa, 0, sb);
+}
+
+// 32x32x64 block-scaled FP4 MFMA: lane l feeds row l%32 and the 32-element
+// block l/32 of the 64-wide K step; lane l, accumulator r holds
+// C[8*(r/4) + 4*(l/32) + r%4][l%32].  On gfx950 this shape runs FP4 at twice
+// the FP8 rate (about 9.3 PFLOP/s measured), the 16x16x128 shape does not.
+// OPSEL picks which byte of the scale registers this MFMA uses.
+template <int OPSEL>
+__device__ __forceinline__ v16f mfma32_fp4(v4i a, v4i b, v16f c, int sa, int sb) {
+    const v8i a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+    const v8i b8 = {b.x, b.y, b.z, b.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, kCbszFp4, kCbszFp4, OPSEL, sa, OPSEL, sb);
 }
 
 template <int OPSEL>
@@ -44,15 +58,25 @@ __device__ __forceinline__ v4f mfma_fp4_sel(v4i a, v4i b, v4f c, int sa, int sb)
 }
 
 // ============================================================================
-// Prefill: LDS-tiled, double-buffered.  Block tile BM token rows x BN weight
-// rows, K step 128 (64 bytes of codes per row).  LDS row of 4 x 16-byte
-// units, unit u of row r stored at u ^ ((r >> 2) & 3) so that the 16 rows
-// read by one MFMA operand fetch hit disjoint banks.
+// Prefill: LDS-tiled, three-stage pipeline fed by direct global->LDS buffer
+// loads (no register staging).  Block tile BM token rows x BN weight rows,
+// four waves in a 2x2 grid, K step 128 (64 bytes of codes per row).
+//
+// LDS row = four 16-byte units; unit u of row r sits at u ^ ((r >> 2) & 3) so
+// that the 16 rows one MFMA operand fetch reads hit disjoint banks.  A
+// direct load writes 64 consecutive 16-byte slots (one per lane), so each
+// lane fetches whichever global unit belongs in its slot.
+//
+// Step s: wait until this wave's loads of stage s have landed, barrier (all
+// waves' stage-s data visible, all waves done with stage s-1), issue the
+// loads of stage s+2 into the buffer stage s-1 used, then run stage s's
+// MFMAs.  The three stage buffers are distinct LDS variables so that the
+// compiler's wait for an in-flight LDS load only blocks reads of its target.
 // ============================================================================
-constexpr int kKS = 128;          // K elements per stage
+constexpr int kKS = 128;            // K elements per stage
 constexpr int kRowBytes = kKS / 2;  // 64 B of codes per row per stage
 
-template <int BM, int BN>
+template <int BM, int BN, int NW>
 struct StageLayout {
     static constexpr int W_CODES = 0;
     static constexpr int XB_CODES = W_CODES + BN * kRowBytes;
@@ -61,9 +85,33 @@ struct StageLayout {
     static constexpr int XB_SC = W_SC + BN * 4;
     static constexpr int XR_SC = XB_SC + BM * 4;
     static constexpr int BYTES = XR_SC + BM * 4;
+    // direct-load instructions per wave per stage (scale groups of 64 rows
+    // are spread over the waves; surplus waves repeat a group)
+    static constexpr int W_LD = BN / 16 / NW;
+    static constexpr int X_LD = BM / 16 / NW;
+    static constexpr int PER_STAGE = W_LD + 2 * X_LD + 3;
+    static_assert(BN % (16 * NW) == 0 && BM % (16 * NW) == 0, "tile rows per wave");
 };
 
+// Three LDS stage buffers sized for the largest tile (256 x 256).
+constexpr int kStageBytesMax = StageLayout<256, 256, 4>::BYTES;
+__shared__ __align__(16) uint8_t g_stage0[kStageBytesMax];
+__shared__ __align__(16) uint8_t g_stage1[kStageBytesMax];
+__shared__ __align__(16) uint8_t g_stage2[kStageBytesMax];
+
+template <int B>
+__device__ __forceinline__ uint8_t *stage_buf() {
+    return B == 0 ? g_stage0 : (B == 1 ? g_stage1 : g_stage2);
+}
+
 __device__ __forceinline__ int swz_unit(int row, int unit) { return unit ^ ((row >> 2) & 3); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 struct TileRows {
     int64_t m0;      // first output row of the tile
@@ -71,16 +119,10 @@ struct TileRows {
     int64_t expert;
 };
 
-// Map blockIdx.y to (expert, row range).  Dense: one expert.  Grouped: the
-// tiles of expert e cover rows offsets[e]..offsets[e+1]-1 in BM-row steps.
+// Grouped tiles: the tiles of expert e cover rows offsets[e]..offsets[e+1]-1
+// in BM-row steps.
 template <int BM>
-__device__ __forceinline__ bool tile_rows(const LinearArgs &a, int64_t tile, TileRows &tr) {
-    if (a.offsets == nullptr) {
-        tr.m0 = tile * BM;
-        tr.m_end = a.rows;
-        tr.expert = 0;
-        return tr.m0 < a.rows;
-    }
+__device__ __forceinline__ bool grouped_tile_rows(const LinearArgs &a, int64_t tile, TileRows &tr) {
     int64_t acc = 0;
     for (int64_t e = 0; e < a.E; e++) {
         const int64_t lo = a.offsets[e], hi = a.offsets[e + 1];
@@ -96,159 +138,225 @@ __device__ __forceinline__ bool tile_rows(const LinearArgs &a, int64_t tile, Til
     return false;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_dual_gemm_mx(LinearArgs a) {
-    constexpr int NT = WAVES_M * WAVES_N * 64;
-    constexpr int FM = BM / WAVES_M / 16;  // token fragments per wave
-    constexpr int FN = BN / WAVES_N / 16;  // weight fragments per wave
-    using L = StageLayout<BM, BN>;
-    constexpr int W_UNITS = BN * 4 / NT;   // 16-byte code units per thread per stage
-    constexpr int X_UNITS = BM * 4 / NT;
-    static_assert(BN * 4 % NT == 0 && BM * 4 % NT == 0, "tile / thread mismatch");
-    static_assert(BN % NT == 0 || NT % BN == 0, "scale rows / thread mismatch");
+// Workgroups are dealt to the eight XCDs round-robin (id % 8).  Give each XCD
+// a contiguous run of the tile order (token tiles fastest), so the tiles one
+// XCD runs at the same time share weight and token rows in its own L2.
+__device__ __forceinline__ int64_t xcd_tile(int64_t wg, int64_t ntiles) {
+    const int64_t per_xcd = (ntiles + 7) / 8;
+    return (wg % 8) * per_xcd + wg / 8;
+}
 
-    extern __shared__ __align__(16) uint8_t smem[];
+// WGM x WGN waves: WGM along the token rows, WGN along the weight rows.
+template <int BM, int BN, int WGM, int WGN>
+struct DualGemmMx {
+    static constexpr int NW = WGM * WGN;
+    using L = StageLayout<BM, BN, NW>;
+    static constexpr int FM = BM / WGM / 32;  // 32-row token fragments per wave
+    static constexpr int FN = BN / WGN / 32;  // 32-row weight fragments per wave
 
-    TileRows tr;
-    if (!tile_rows<BM>(a, blockIdx.y, tr)) return;
-    const int64_t n0 = (int64_t)blockIdx.x * BN;
-    const int64_t K = a.K;
-    const int64_t kb = K / 2, ks = K / 32;  // code / scale bytes per row
-    const uint8_t *wc = a.w_codes + tr.expert * a.nout * kb;
-    const uint8_t *wsc = a.w_scales + tr.expert * a.nout * ks;
+    __amdgpu_buffer_rsrc_t rW, rWs, rXb, rXr, rXbs, rXrs;
+    uint32_t w_off[L::W_LD], x_off[L::X_LD];
+    uint32_t ws_off, xs_off;
+    int wave, lane;
+    int64_t last_step;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-
-    // ---- per-thread global sources (fixed across the K loop)
-    const uint8_t *w_src[W_UNITS];
-    const uint8_t *xb_src[X_UNITS], *xr_src[X_UNITS];
-    int w_lds[W_UNITS], x_lds[X_UNITS];
+    // Issue this wave's direct loads of stage `stage` into buffer B.
+    template <int B>
+    __device__ __forceinline__ void issue(int64_t stage) {
+        uint8_t *st = stage_buf<B>();
+        const int64_t stp = stage < last_step ? stage : last_step;
+        const uint32_t co = (uint32_t)stp * kRowBytes, so = (uint32_t)stp * 4;
 #pragma unroll
-    for (int i = 0; i < W_UNITS; i++) {
-        const int u = tid + i * NT, row = u >> 2, unit = u & 3;
-        const int64_t n = n0 + row;
-        w_src[i] = n < a.nout ? wc + n * kb + unit * 16 : nullptr;
-        w_lds[i] = row * kRowBytes + swz_unit(row, unit) * 16;
-    }
+        for (int j = 0; j < L::W_LD; j++)
+            lds_load16(rW, st + L::W_CODES + (wave * L::W_LD + j) * 1024, w_off[j] + co);
 #pragma unroll
-    for (int i = 0; i < X_UNITS; i++) {
-        const int u = tid + i * NT, row = u >> 2, unit = u & 3;
-        const int64_t m = tr.m0 + row;
-        if (m < tr.m_end) {
-            const int64_t src = a.row_index ? (int64_t)a.row_index[m] : m;
-            xb_src[i] = a.b_codes + src * kb + unit * 16;
-            xr_src[i] = a.r_codes + src * kb + unit * 16;
-        } else {
-            xb_src[i] = xr_src[i] = nullptr;
+        for (int j = 0; j < L::X_LD; j++) {
+            lds_load16(rXb, st + L::XB_CODES + (wave * L::X_LD + j) * 1024, x_off[j] + co);
+            lds_load16(rXr, st + L::XR_CODES + (wave * L::X_LD + j) * 1024, x_off[j] + co);
         }
-        x_lds[i] = row * kRowBytes + swz_unit(row, unit) * 16;
-    }
-    // scale dwords: thread t < BN loads weight row t, t < BM token row t
-    const uint8_t *ws_src = nullptr, *xbs_src = nullptr, *xrs_src = nullptr;
-    if (tid < BN && n0 + tid < a.nout) ws_src = wsc + (n0 + tid) * ks;
-    if (tid < BM && tr.m0 + tid < tr.m_end) {
-        const int64_t m = tr.m0 + tid;
-        const int64_t src = a.row_index ? (int64_t)a.row_index[m] : m;
-        xbs_src = a.b_scales + src * ks;
-        xrs_src = a.r_scales + src * ks;
+        // scale dwords: 64 rows per instruction; waves beyond the row count
+        // reload an earlier group (identical bytes to identical places)
+        lds_load4(rWs, st + L::W_SC + (wave % (BN / 64)) * 256, ws_off + so);
+        lds_load4(rXbs, st + L::XB_SC + (wave % (BM / 64)) * 256, xs_off + so);
+        lds_load4(rXrs, st + L::XR_SC + (wave % (BM / 64)) * 256, xs_off + so);
     }
 
-    uint4 w_reg[W_UNITS], xb_reg[X_UNITS], xr_reg[X_UNITS];
-    uint32_t ws_reg = 0x7F7F7F7Fu, xbs_reg = 0x7F7F7F7Fu, xrs_reg = 0x7F7F7F7Fu;
-    const uint4 zero4 = make_uint4(0, 0, 0, 0);
-
-    auto gload = [&](int64_t step) {
-        const int64_t co = step * kRowBytes;
-#pragma unroll
-        for (int i = 0; i < W_UNITS; i++)
-            w_reg[i] = w_src[i] ? *reinterpret_cast<const uint4 *>(w_src[i] + co) : zero4;
-#pragma unroll
-        for (int i = 0; i < X_UNITS; i++) {
-            xb_reg[i] = xb_src[i] ? *reinterpret_cast<const uint4 *>(xb_src[i] + co) : zero4;
-            xr_reg[i] = xr_src[i] ? *reinterpret_cast<const uint4 *>(xr_src[i] + co) : zero4;
-        }
-        const int64_t so = step * 4;
-        if (ws_src) ws_reg = *reinterpret_cast<const uint32_t *>(ws_src + so);
-        if (xbs_src) xbs_reg = *reinterpret_cast<const uint32_t *>(xbs_src + so);
-        if (xrs_src) xrs_reg = *reinterpret_cast<const uint32_t *>(xrs_src + so);
-    };
-    auto lstore = [&](uint8_t *st) {
-#pragma unroll
-        for (int i = 0; i < W_UNITS; i++) *reinterpret_cast<uint4 *>(st + L::W_CODES + w_lds[i]) = w_reg[i];
-#pragma unroll
-        for (int i = 0; i < X_UNITS; i++) {
-            *reinterpret_cast<uint4 *>(st + L::XB_CODES + x_lds[i]) = xb_reg[i];
-            *reinterpret_cast<uint4 *>(st + L::XR_CODES + x_lds[i]) = xr_reg[i];
-        }
-        if (tid < BN) *reinterpret_cast<uint32_t *>(st + L::W_SC + tid * 4) = ws_reg;
-        if (tid < BM) {
-            *reinterpret_cast<uint32_t *>(st + L::XB_SC + tid * 4) = xbs_reg;
-            *reinterpret_cast<uint32_t *>(st + L::XR_SC + tid * 4) = xrs_reg;
-        }
-    };
-
-    v4f acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-    const int frow = lane & 15, fq = lane >> 4;
-    const int64_t nsteps = K / kKS;
-
-    gload(0);
-    lstore(smem);
-    __syncthreads();
-
-    for (int64_t s = 0; s < nsteps; s++) {
-        uint8_t *cur = smem + (s & 1) * L::BYTES;
-        if (s + 1 < nsteps) gload(s + 1);
-
-        v4i wf[FN];
-        int wsf[FN];
+    // Stage = two 64-wide K sub-steps; in sub-step t lane (row l%32, q = l/32)
+    // reads unit 2t+q of its row (block 2t+q of the stage).  Each row's four
+    // stage scales are read once as a dword and shifted by 8q, so byte 2t
+    // holds block 2t+q and the MFMA selects it with opsel = 2t.  The token
+    // fragments are double-buffered in registers: the next fragment's LDS
+    // reads are in flight while the current fragment's MFMAs run.
+    template <int B>
+    __device__ __forceinline__ void compute(v16f (&acc)[FM][FN], int wm, int wn) {
+        const uint8_t *cur = stage_buf<B>();
+        const int frow = lane & 31, fq = lane >> 5;
+        int wsc[FN], xbsc[FM], xrsc[FM];
 #pragma unroll
         for (int j = 0; j < FN; j++) {
-            const int row = wn * (FN * 16) + j * 16 + frow;
-            wf[j] = *reinterpret_cast<const v4i *>(cur + L::W_CODES + row * kRowBytes + swz_unit(row, fq) * 16);
-            wsf[j] = cur[L::W_SC + row * 4 + fq];
+            const int row = wn * (FN * 32) + j * 32 + frow;
+            wsc[j] = (int)(*reinterpret_cast<const uint32_t *>(cur + L::W_SC + row * 4) >> (8 * fq));
         }
 #pragma unroll
         for (int i = 0; i < FM; i++) {
-            const int row = wm * (FM * 16) + i * 16 + frow;
-            const int off = row * kRowBytes + swz_unit(row, fq) * 16;
-            const v4i xb = *reinterpret_cast<const v4i *>(cur + L::XB_CODES + off);
-            const v4i xr = *reinterpret_cast<const v4i *>(cur + L::XR_CODES + off);
-            const int xbs = cur[L::XB_SC + row * 4 + fq];
-            const int xrs = cur[L::XR_SC + row * 4 + fq];
-#pragma unroll
-            for (int j = 0; j < FN; j++) acc[i][j] = mfma_fp4(wf[j], xb, acc[i][j], wsf[j], xbs);
-#pragma unroll
-            for (int j = 0; j < FN; j++) acc[i][j] = mfma_fp4(wf[j], xr, acc[i][j], wsf[j], xrs);
+            const int row = wm * (FM * 32) + i * 32 + frow;
+            xbsc[i] = (int)(*reinterpret_cast<const uint32_t *>(cur + L::XB_SC + row * 4) >> (8 * fq));
+            xrsc[i] = (int)(*reinterpret_cast<const uint32_t *>(cur + L::XR_SC + row * 4) >> (8 * fq));
         }
-        if (s + 1 < nsteps) lstore(smem + ((s + 1) & 1) * L::BYTES);
-        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            const int unit = 2 * t + fq;
+            v4i wf[FN];
+#pragma unroll
+            for (int j = 0; j < FN; j++) {
+                const int row = wn * (FN * 32) + j * 32 + frow;
+                wf[j] = *reinterpret_cast<const v4i *>(cur + L::W_CODES + row * kRowBytes + swz_unit(row, unit) * 16);
+            }
+            v4i xb[2], xr[2];
+            {
+                const int row = wm * (FM * 32) + frow;
+                const int off = row * kRowBytes + swz_unit(row, unit) * 16;
+                xb[0] = *reinterpret_cast<const v4i *>(cur + L::XB_CODES + off);
+                xr[0] = *reinterpret_cast<const v4i *>(cur + L::XR_CODES + off);
+            }
+#pragma unroll
+            for (int i = 0; i < FM; i++) {
+                if (i + 1 < FM) {
+                    const int row = wm * (FM * 32) + (i + 1) * 32 + frow;
+                    const int off = row * kRowBytes + swz_unit(row, unit) * 16;
+                    xb[(i + 1) & 1] = *reinterpret_cast<const v4i *>(cur + L::XB_CODES + off);
+                    xr[(i + 1) & 1] = *reinterpret_cast<const v4i *>(cur + L::XR_CODES + off);
+                }
+                if (t == 0) {
+#pragma unroll
+                    for (int j = 0; j < FN; j++) acc[i][j] = mfma32_fp4<0>(wf[j], xb[i & 1], acc[i][j], wsc[j], xbsc[i]);
+#pragma unroll
+                    for (int j = 0; j < FN; j++) acc[i][j] = mfma32_fp4<0>(wf[j], xr[i & 1], acc[i][j], wsc[j], xrsc[i]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < FN; j++) acc[i][j] = mfma32_fp4<2>(wf[j], xb[i & 1], acc[i][j], wsc[j], xbsc[i]);
+#pragma unroll
+                    for (int j = 0; j < FN; j++) acc[i][j] = mfma32_fp4<2>(wf[j], xr[i & 1], acc[i][j], wsc[j], xrsc[i]);
+                }
+            }
+        }
     }
 
-    // ---- epilogue: lane holds Y[m][n..n+3]
+    // One pipeline step on buffer B (stage s); loads stage s+2 into (B+2)%3.
+    template <int B>
+    __device__ __forceinline__ void step(int64_t s, v16f (&acc)[FM][FN], int wm, int wn) {
+        wait_vmcnt<L::PER_STAGE>();   // stage s landed (stage s+1 may still fly)
+        __builtin_amdgcn_s_barrier();
+        this->template issue<(B + 2) % 3>(s + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        this->template compute<B>(acc, wm, wn);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+};
+
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
+void k_dual_gemm_mx(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
+    using G = DualGemmMx<BM, BN, WGM, WGN>;
+    using L = typename G::L;
+    constexpr int FM = G::FM, FN = G::FN;
+    static_assert(FM >= 1 && FN >= 1, "tile too small for 32x32 fragments");
+
+    TileRows tr;
+    int64_t ntile;
+    if (a.offsets == nullptr) {
+        const int64_t t = xcd_tile(blockIdx.x, n_ntiles * n_mtiles);
+        if (t >= n_ntiles * n_mtiles) return;
+        const int64_t mt = t % n_mtiles;
+        ntile = t / n_mtiles;
+        tr.m0 = mt * BM;
+        tr.m_end = a.rows;
+        tr.expert = 0;
+    } else {
+        ntile = blockIdx.x % n_ntiles;
+        if (!grouped_tile_rows<BM>(a, blockIdx.x / n_ntiles, tr)) return;
+    }
+    const int64_t n0 = ntile * BN;
+    const int64_t K = a.K;
+    const uint32_t kb = (uint32_t)(K / 2), ks = (uint32_t)(K / 32);
+    const uint32_t nout = (uint32_t)a.nout;
+
+    G g;
+    g.rW = make_rsrc(a.w_codes + tr.expert * a.nout * kb, nout * kb);
+    g.rWs = make_rsrc(a.w_scales + tr.expert * a.nout * ks, nout * ks);
+    g.rXb = make_rsrc(a.b_codes, (uint32_t)a.T * kb);
+    g.rXr = make_rsrc(a.r_codes, (uint32_t)a.T * kb);
+    g.rXbs = make_rsrc(a.b_scales, (uint32_t)a.T * ks);
+    g.rXrs = make_rsrc(a.r_scales, (uint32_t)a.T * ks);
+    const int tid = threadIdx.x;
+    g.lane = tid & 63;
+    g.wave = tid >> 6;
+    const int wm = g.wave / WGN, wn = g.wave % WGN;
+    g.last_step = K / kKS - 1;
+
+    // source offsets of the 16-byte slots this lane fills (fixed over K)
+#pragma unroll
+    for (int j = 0; j < L::W_LD; j++) {
+        const int row = (g.wave * L::W_LD + j) * 16 + (g.lane >> 2);
+        const int unit = swz_unit(row, g.lane & 3);
+        const int64_t n = n0 + row;
+        g.w_off[j] = n < a.nout ? (uint32_t)n * kb + unit * 16 : kOutOfRange;
+    }
+#pragma unroll
+    for (int j = 0; j < L::X_LD; j++) {
+        const int row = (g.wave * L::X_LD + j) * 16 + (g.lane >> 2);
+        const int unit = swz_unit(row, g.lane & 3);
+        const int64_t m = tr.m0 + row;
+        const int64_t src = m < tr.m_end ? (a.row_index ? (int64_t)a.row_index[m] : m) : -1;
+        g.x_off[j] = src >= 0 ? (uint32_t)src * kb + unit * 16 : kOutOfRange;
+    }
+    {
+        const int64_t n = n0 + (g.wave % (BN / 64)) * 64 + g.lane;
+        g.ws_off = n < a.nout ? (uint32_t)n * ks : kOutOfRange;
+        const int64_t m = tr.m0 + (g.wave % (BM / 64)) * 64 + g.lane;
+        const int64_t src = m < tr.m_end ? (a.row_index ? (int64_t)a.row_index[m] : m) : -1;
+        g.xs_off = src >= 0 ? (uint32_t)src * ks : kOutOfRange;
+    }
+
+    v16f acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+    const int64_t nsteps = K / kKS;
+    g.template issue<0>(0);
+    g.template issue<1>(1);
+    for (int64_t s = 0; s < nsteps; s += 3) {
+        g.template step<0>(s, acc, wm, wn);
+        if (s + 1 < nsteps) g.template step<1>(s + 1, acc, wm, wn);
+        if (s + 2 < nsteps) g.template step<2>(s + 2, acc, wm, wn);
+    }
+    wait_vmcnt<0>();  // drain the clamped tail loads before the workgroup exits
+
+    // ---- epilogue: accumulator group g of fragment (i, j) is Y[m][n..n+3]
+    const int frow = g.lane & 31, fq = g.lane >> 5;
 #pragma unroll
     for (int i = 0; i < FM; i++) {
-        const int64_t m = tr.m0 + wm * (FM * 16) + i * 16 + frow;
+        const int64_t m = tr.m0 + wm * (FM * 32) + i * 32 + frow;
         if (m >= tr.m_end) continue;
         float *yrow = a.y + m * a.ldy;
 #pragma unroll
         for (int j = 0; j < FN; j++) {
-            const int64_t n = n0 + wn * (FN * 16) + j * 16 + fq * 4;
-            const v4f v = acc[i][j];
-            if (a.y_vec && n + 3 < a.nout) {
-                *reinterpret_cast<v4f *>(yrow + n) = v;
-            } else {
-                if (n < a.nout) yrow[n] = v.x;
-                if (n + 1 < a.nout) yrow[n + 1] = v.y;
-                if (n + 2 < a.nout) yrow[n + 2] = v.z;
-                if (n + 3 < a.nout) yrow[n + 3] = v.w;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int64_t n = n0 + wn * (FN * 32) + j * 32 + 8 * q + 4 * fq;
+                const v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                if (a.y_vec && n + 3 < a.nout) {
+                    *reinterpret_cast<v4f *>(yrow + n) = v;
+                } else {
+                    if (n < a.nout) yrow[n] = v.x;
+                    if (n + 1 < a.nout) yrow[n + 1] = v.y;
+                    if (n + 2 < a.nout) yrow[n + 2] = v.z;
+                    if (n + 3 < a.nout) yrow[n + 3] = v.w;
+                }
             }
         }
     }
@@ -270,17 +378,21 @@ struct Chunk64 {
     uint32_t sc;
 };
 
-__device__ __forceinline__ void load_chunk(const uint8_t *codes_row, const uint8_t *sc_row, int64_t c,
-                                           int q, int64_t K, bool valid, Chunk64 &o) {
+// 64 code bytes and one scale dword of chunk c for the lane's row; rows or
+// K quarters that do not exist read as zeros (zero codes contribute nothing
+// whatever the scale).
+__device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                           uint32_t code_row, uint32_t sc_row, int64_t c, int q,
+                                           int64_t K, Chunk64 &o) {
     const int64_t k0 = c * kChunkK + q * 128;
-    if (valid && k0 < K) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(codes_row + k0 / 2);
-        o.u[0] = p[0]; o.u[1] = p[1]; o.u[2] = p[2]; o.u[3] = p[3];
-        o.sc = *reinterpret_cast<const uint32_t *>(sc_row + k0 / 32);
-    } else {
-        o.u[0] = o.u[1] = o.u[2] = o.u[3] = make_uint4(0, 0, 0, 0);
-        o.sc = 0x7F7F7F7Fu;
-    }
+    const bool in = k0 < K;
+    const uint32_t co = in ? code_row + (uint32_t)(k0 / 2) : kOutOfRange;
+    const uint32_t so = in ? sc_row + (uint32_t)(k0 / 32) : kOutOfRange;
+    o.u[0] = bload128(rc, co);
+    o.u[1] = bload128(rc, co + 16);
+    o.u[2] = bload128(rc, co + 32);
+    o.u[3] = bload128(rc, co + 48);
+    o.sc = bload32(rs, so);
 }
 
 __device__ __forceinline__ v4i as_v4i(uint4 u) { return v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w}; }
@@ -297,20 +409,22 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_dual_gemm_mx_small(LinearA
     const int64_t c_begin = blockIdx.y * chunks_per_split;
     const int64_t c_end = min(nch, c_begin + chunks_per_split);
 
+    const auto rW = make_rsrc(a.w_codes, (uint32_t)(a.nout * kb));
+    const auto rWs = make_rsrc(a.w_scales, (uint32_t)(a.nout * ks));
+    const auto rXb = make_rsrc(a.b_codes, (uint32_t)(a.T * kb));
+    const auto rXr = make_rsrc(a.r_codes, (uint32_t)(a.T * kb));
+    const auto rXbs = make_rsrc(a.b_scales, (uint32_t)(a.T * ks));
+    const auto rXrs = make_rsrc(a.r_scales, (uint32_t)(a.T * ks));
     const bool wvalid = n0 + r < a.nout;
-    const uint8_t *wrow = a.w_codes + (n0 + r) * kb;
-    const uint8_t *wsrow = a.w_scales + (n0 + r) * ks;
-    const uint8_t *xb_row[FM], *xr_row[FM], *xbs_row[FM], *xrs_row[FM];
-    bool xvalid[FM];
+    const uint32_t wrow = wvalid ? (uint32_t)((n0 + r) * kb) : kOutOfRange;
+    const uint32_t wsrow = wvalid ? (uint32_t)((n0 + r) * ks) : kOutOfRange;
+    uint32_t x_row[FM], xs_row[FM];
 #pragma unroll
     for (int f = 0; f < FM; f++) {
         const int64_t m = f * 16 + r;
-        xvalid[f] = m < a.rows;
-        const int64_t src = xvalid[f] ? (a.row_index ? (int64_t)a.row_index[m] : m) : 0;
-        xb_row[f] = a.b_codes + src * kb;
-        xr_row[f] = a.r_codes + src * kb;
-        xbs_row[f] = a.b_scales + src * ks;
-        xrs_row[f] = a.r_scales + src * ks;
+        const int64_t src = m < a.rows ? (a.row_index ? (int64_t)a.row_index[m] : m) : -1;
+        x_row[f] = src >= 0 ? (uint32_t)(src * kb) : kOutOfRange;
+        xs_row[f] = src >= 0 ? (uint32_t)(src * ks) : kOutOfRange;
     }
 
     v4f acc[FM];
@@ -319,11 +433,11 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_dual_gemm_mx_small(LinearA
 
     for (int64_t c = c_begin; c < c_end; c++) {
         Chunk64 w, xb[FM], xr[FM];
-        load_chunk(wrow, wsrow, c, q, K, wvalid, w);
+        load_chunk(rW, rWs, wrow, wsrow, c, q, K, w);
 #pragma unroll
         for (int f = 0; f < FM; f++) {
-            load_chunk(xb_row[f], xbs_row[f], c, q, K, xvalid[f], xb[f]);
-            load_chunk(xr_row[f], xrs_row[f], c, q, K, xvalid[f], xr[f]);
+            load_chunk(rXb, rXbs, x_row[f], xs_row[f], c, q, K, xb[f]);
+            load_chunk(rXr, rXrs, x_row[f], xs_row[f], c, q, K, xr[f]);
         }
 #pragma unroll
         for (int f = 0; f < FM; f++) {
@@ -366,22 +480,19 @@ __global__ void k_zero_rows(float *y, int64_t rows, int64_t cols, int64_t ldy) {
 // ============================================================================
 // launcher
 // ============================================================================
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WGM, int WGN>
 static hipError_t launch_prefill(const LinearArgs &a, hipStream_t st) {
-    using L = StageLayout<BM, BN>;
-    const size_t lds = 2 * (size_t)L::BYTES;
-    static bool attr_set = false;  // idempotent; benign if two threads race to set it
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_dual_gemm_mx<BM, BN, WM, WN>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
+    const int64_t n_ntiles = (a.nout + BN - 1) / BN;
+    int64_t blocks;
+    int64_t n_mtiles = 0;
+    if (a.offsets) {
+        blocks = n_ntiles * ((a.rows + BM - 1) / BM + a.E);  // upper bound; extra blocks exit
+    } else {
+        n_mtiles = (a.rows + BM - 1) / BM;
+        blocks = ((n_ntiles * n_mtiles + 7) / 8) * 8;
     }
-    int64_t mtiles;
-    if (a.offsets) mtiles = (a.rows + BM - 1) / BM + a.E;  // upper bound; extra blocks exit
-    else mtiles = (a.rows + BM - 1) / BM;
-    const dim3 grid((unsigned)((a.nout + BN - 1) / BN), (unsigned)mtiles);
-    hipLaunchKernelGGL((k_dual_gemm_mx<BM, BN, WM, WN>), grid, dim3(WM * WN * 64), lds, st, a);
+    hipLaunchKernelGGL((k_dual_gemm_mx<BM, BN, WGM, WGN>), dim3((unsigned)blocks), dim3(WGM * WGN * 64), 0, st, a,
+                       n_ntiles, n_mtiles);
     return hipGetLastError();
 }
 
@@ -406,6 +517,23 @@ static hipError_t launch_small(const LinearArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device id).
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Dense tile shape: one workgroup fills a CU (LDS), so the time is about
+// rounds(tiles / CUs) x tile size, with smaller tiles paying for their lower
+// operand reuse (relative cost per output element below, from measurement
+// of the three shapes on MI355X).
 hipError_t launch_linear_mx(const LinearArgs &a, hipStream_t st) {
     if (a.offsets == nullptr && a.rows <= 64) {
         if (a.rows <= 16) return launch_small<1>(a, st);
@@ -414,7 +542,21 @@ hipError_t launch_linear_mx(const LinearArgs &a, hipStream_t st) {
         return launch_small<4>(a, st);
     }
     if (a.offsets) return launch_prefill<128, 256, 2, 2>(a, st);
-    return launch_prefill<256, 256, 2, 2>(a, st);
+    const int64_t cus = device_cus();
+    struct Shape { int bm, bn; double cost; };
+    // relative cost per output element of each tile shape, measured on the
+    // MI355X for K = 4096..14336 (larger tiles reuse operands more)
+    const Shape shapes[3] = {{256, 256, 1.0}, {128, 256, 1.2}, {128, 128, 1.5}};
+    int best = 0;
+    double best_t = 0.0;
+    for (int i = 0; i < 3; i++) {
+        const int64_t tiles = ((a.rows + shapes[i].bm - 1) / shapes[i].bm) * ((a.nout + shapes[i].bn - 1) / shapes[i].bn);
+        const double t = (double)((tiles + cus - 1) / cus) * shapes[i].bm * shapes[i].bn * shapes[i].cost;
+        if (i == 0 || t < best_t) { best = i; best_t = t; }
+    }
+    if (best == 0) return launch_prefill<256, 256, 2, 2>(a, st);
+    if (best == 1) return launch_prefill<128, 256, 2, 2>(a, st);
+    return launch_prefill<128, 128, 2, 2>(a, st);
 }
 
 }  // namespace sharq

@@ -164,8 +164,8 @@ void k_dual_gemm_nv(LinearArgs a) {
             *reinterpret_cast<uint4 *>(st + L::XB_CODES + x_lds[i]) = xb_reg[i];
             *reinterpret_cast<uint4 *>(st + L::XR_CODES + x_lds[i]) = xr_reg[i];
         }
-        if (tid < BN) *reinterpret_cast<uint2 *>(st + L::W_SC + tid * kNvScRow) = ws_reg;
-        if (tid < BM) {
+        if (BN >= NT || tid < BN) *reinterpret_cast<uint2 *>(st + L::W_SC + tid * kNvScRow) = ws_reg;
+        if (BM >= NT || tid < BM) {
             *reinterpret_cast<uint2 *>(st + L::XB_SC + tid * kNvScRow) = xbs_reg;
             *reinterpret_cast<uint2 *>(st + L::XR_SC + tid * kNvScRow) = xrs_reg;
         }
@@ -185,7 +185,8 @@ void k_dual_gemm_nv(LinearArgs a) {
 
     for (int64_t s = 0; s < nsteps; s++) {
         uint8_t *cur = smem + (s & 1) * L::BYTES;
-        if (s + 1 < nsteps) gload(s + 1);
+        gload(s + 1 < nsteps ? s + 1 : s);  // see the MXFP4 kernel: one basic block per step
+        __builtin_amdgcn_sched_barrier(0);
 
         v8bf wd[FN][4];
 #pragma unroll
@@ -223,7 +224,8 @@ void k_dual_gemm_nv(LinearArgs a) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wd[j][t], xr, acc[i][j], 0, 0, 0);
             }
         }
-        if (s + 1 < nsteps) lstore(smem + ((s + 1) & 1) * L::BYTES);
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(smem + ((s + 1) & 1) * L::BYTES);
         __syncthreads();
     }
 

@@ -12,9 +12,12 @@
 // the four lanes of a DPP quad and an NVFP4 block (16) a lane pair.  The row
 // is read from HBM exactly once; everything else happens in registers.
 //
-//   MX + norm, K <= 8*512: the row stays in registers across the FP64 norm
-//                          reduction and the quantization pass;
-//   MX + norm, larger K:   the quantization pass re-reads the row (L2 hit);
+//   MX + norm, K <= 8192:  one row per workgroup of four waves; the row stays
+//                          in registers across the FP64 norm reduction (whose
+//                          per-wave partials meet in LDS) and the
+//                          quantization pass;
+//   MX + norm, larger K:   one wave per row, the quantization pass re-reads
+//                          the row (L2 hit);
 //   no norm:               tasks are (row, group of chunks), fully parallel;
 //   NVFP4:                 a pre-pass writes per-row norm statistics and
 //                          amax, a one-block kernel reduces the tensor scale,
@@ -27,7 +30,6 @@ namespace sharq {
 constexpr int kPrepWaves = 4;        // waves per workgroup
 constexpr int kChunk = 512;          // elements per wave-wide 128-bit load
 constexpr int kStreamChunks = 4;     // chunks per task when rows are split
-constexpr int kRegChunks = 8;        // register-resident row: K <= 4096
 
 struct RowStats {  // per-row statistics written by the NVFP4 pre-pass
     float r, mu, amax, pad;
@@ -85,31 +87,52 @@ __device__ __forceinline__ uint32_t select_m16(const float v[8], int n, int lane
     return keep;
 }
 
-template <int M>
-__device__ __forceinline__ uint32_t select8(const float v[8], int n, int lane) {
-    if constexpr (M == 16) return select_m16(v, n, lane);
-    else return select_in_lane<M>(v, n);
+// 2:4 (the workloads' pattern): element i is kept iff it beats at least two
+// of the three others.  The six magnitude comparisons (|a| >= |b| on floats,
+// which orders finite values, subnormals and +-0 exactly like the bit
+// patterns without sign) become lane masks, the majority logic runs on those
+// masks, and the kept values are selected straight from them.
+__device__ __forceinline__ void select_2of4(const float v[8], bool keep[8]) {
+#pragma unroll
+    for (int g = 0; g < 8; g += 4) {
+        const float a0 = fabsf(v[g]), a1 = fabsf(v[g + 1]), a2 = fabsf(v[g + 2]), a3 = fabsf(v[g + 3]);
+        const bool c01 = a0 >= a1, c02 = a0 >= a2, c03 = a0 >= a3;  // lower index wins ties
+        const bool c12 = a1 >= a2, c13 = a1 >= a3, c23 = a2 >= a3;
+        keep[g] = (c01 && c02) || (c03 && (c01 || c02));
+        keep[g + 1] = (!c01 && c12) || (c13 && (!c01 || c12));
+        keep[g + 2] = (!c02 && !c12) || (c23 && (!c02 || !c12));
+        keep[g + 3] = (!c03 && !c13) || (!c23 && (!c03 || !c13));
+    }
+}
+
+// FAST24: 1 = the 2:4 fast path, 0 = runtime N with M-wide groups.
+template <int M, int FAST24>
+__device__ __forceinline__ void select8(const float v[8], int n, int lane, bool keep[8]) {
+    if constexpr (FAST24) {
+        select_2of4(v, keep);
+    } else {
+        uint32_t k;
+        if constexpr (M == 16) k = select_m16(v, n, lane);
+        else k = select_in_lane<M>(v, n);
+#pragma unroll
+        for (int i = 0; i < 8; i++) keep[i] = (k >> i) & 1u;
+    }
 }
 
 // ---------------------------------------------------------------- block quantizers
 // MXFP4: 32-element block across a quad.  Writes packed codes of the lane's
-// eight elements, the dequantized values, and returns the E8M0 byte.
+// eight elements, the dequantized values (if DEQ), and returns the E8M0 byte.
+// The conversions take the block exponent as their scale operand, i.e. they
+// round v * 2^-E and decode to code * 2^E, both exactly.
+template <bool DEQ>
 __device__ __forceinline__ uint32_t quant_mx8(const float s[8], uint32_t &codes, float deq[8]) {
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(s[i]));
-    m = fmaxf(m, dpp_f32<kDppQuadXor1>(m));
-    m = fmaxf(m, dpp_f32<kDppQuadXor2>(m));
-    const int E = mx_shared_exp(m);
-    const float inv = pow2_neg(E), sc = pow2(E);
-    uint32_t c = 0;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        float q;
-        c |= e2m1_encode(__fmul_rn(s[i], inv), q) << (4 * i);
-        deq[i] = __fmul_rn(q, sc);
-    }
-    codes = c;
+    const int E = mx_shared_exp(quad_max_nonneg(m));
+    const float scale = e8m0_operand(E);
+    codes = e2m1_cvt8(s, scale);
+    if constexpr (DEQ) e2m1_dec8(codes, scale, deq);
     return (uint32_t)(E + 127);
 }
 
@@ -119,17 +142,16 @@ __device__ __forceinline__ uint32_t quant_nv8(const float s[8], float G, float G
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(s[i]));
-    m = fmaxf(m, dpp_f32<kDppQuadXor1>(m));
+    m = pair_max_nonneg(m);
     const uint32_t sb = e4m3_encode_sat(__fdiv_rn(m, G6));
     const float D = __fmul_rn(e4m3_value(sb), G);
-    uint32_t c = 0;
+    float u[8], q[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        float q = 0.0f;
-        if (sb != 0u) c |= e2m1_encode(__fdiv_rn(s[i], D), q) << (4 * i);
-        deq[i] = __fmul_rn(q, D);
-    }
-    codes = c;
+    for (int i = 0; i < 8; i++) u[i] = sb != 0u ? __fdiv_rn(s[i], D) : 0.0f;
+    codes = e2m1_cvt8(u, 1.0f);
+    e2m1_dec8(codes, 1.0f, q);
+#pragma unroll
+    for (int i = 0; i < 8; i++) deq[i] = __fmul_rn(q[i], D);
     return sb;
 }
 
@@ -160,20 +182,25 @@ __device__ __forceinline__ void load_param8(const uint16_t *p, int64_t e0, float
 // ---------------------------------------------------------------- per-chunk body
 // Normalized values v of one lane -> mask byte, backbone and residual codes
 // and scales, stored at element offset e0 of row `row`.
-template <int FMT, int M>
+template <int FMT, int M, int FAST24>
 __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, int64_t e0, int lane,
                                                 const float v[8], float G, float G6) {
-    const uint32_t keep = select8<M>(v, a.n, lane);
+    bool kp[8];
+    select8<M, FAST24>(v, a.n, lane, kp);
     float S[8], dq[8], R[8];
+    uint32_t keep = 0;
 #pragma unroll
-    for (int i = 0; i < 8; i++) S[i] = (keep >> i) & 1u ? v[i] : 0.0f;
+    for (int i = 0; i < 8; i++) {
+        S[i] = kp[i] ? v[i] : 0.0f;
+        keep |= kp[i] ? (1u << i) : 0u;
+    }
     uint32_t bc, rc, bs, rs;
-    if constexpr (FMT == kFmtMx) bs = quant_mx8(S, bc, dq);
+    if constexpr (FMT == kFmtMx) bs = quant_mx8<true>(S, bc, dq);
     else bs = quant_nv8(S, G, G6, bc, dq);
 #pragma unroll
     for (int i = 0; i < 8; i++) R[i] = __fsub_rn(v[i], dq[i]);
     float unused[8];
-    if constexpr (FMT == kFmtMx) rs = quant_mx8(R, rc, unused);
+    if constexpr (FMT == kFmtMx) rs = quant_mx8<false>(R, rc, unused);
     else rs = quant_nv8(R, G, G6, rc, unused);
 
     const int64_t K = a.K;
@@ -188,35 +215,42 @@ __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, 
     }
 }
 
-// ---------------------------------------------------------------- MX, norm, row in registers
-template <bool BF16, int NORM, int M>
-__global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_reg(PrepArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
-    if (row >= a.T) return;
+// ---------------------------------------------------------------- MX, norm, row split over a workgroup
+// One row per workgroup of four waves; wave w owns chunks w, w+4, ... (at
+// most CPW of them, held in registers).  Each wave reduces its FP64 partial
+// sums, the four partials meet in LDS and every wave adds them in the same
+// fixed order, so all waves derive the same r (and mu).
+template <bool BF16, int NORM, int M, int FAST24, int CPW>
+__global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_split(PrepArgs a) {
+    __shared__ double part[2][kPrepWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row = blockIdx.x;
     const uint16_t *xr = a.x + row * a.ldx;
     const int64_t K = a.K;
-    const int nch = (int)((K + kChunk - 1) / kChunk);
 
-    uint4 raw[kRegChunks];
+    uint4 raw[CPW];
+    bool in[CPW];
 #pragma unroll
-    for (int c = 0; c < kRegChunks; c++) {
-        const int64_t e0 = (int64_t)(c * kWave + lane) * 8;
-        raw[c] = (c < nch && e0 < K) ? *reinterpret_cast<const uint4 *>(xr + e0) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < CPW; j++) {
+        const int64_t e0 = ((int64_t)(wave + kPrepWaves * j) * kWave + lane) * 8;
+        in[j] = e0 < K;
+        raw[j] = in[j] ? *reinterpret_cast<const uint4 *>(xr + e0) : make_uint4(0, 0, 0, 0);
     }
-    // FP64 statistics (each lane serial over its elements, then a wave tree)
-    double s1 = 0.0;
     float v[8];
+    double s1 = 0.0;
 #pragma unroll
-    for (int c = 0; c < kRegChunks; c++) {
-        unpack8<BF16>(raw[c], v);
+    for (int j = 0; j < CPW; j++) {
+        unpack8<BF16>(raw[j], v);
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            if constexpr (NORM == kNormRms) s1 += (double)v[i] * (double)v[i];
+            if constexpr (NORM == kNormRms) s1 = __fma_rn((double)v[i], (double)v[i], s1);  // x*x exact in double
             else s1 += (double)v[i];
         }
     }
     s1 = wave_sum_f64(s1);
+    if (lane == 0) part[0][wave] = s1;
+    __syncthreads();
+    s1 = ((part[0][0] + part[0][1]) + part[0][2]) + part[0][3];
     float r, mu = 0.0f;
     if constexpr (NORM == kNormRms) {
         r = (float)(1.0 / sqrt(s1 / (double)K + (double)a.eps));
@@ -224,37 +258,39 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_reg(PrepArgs a) 
         const double mud = s1 / (double)K;
         double s2 = 0.0;
 #pragma unroll
-        for (int c = 0; c < kRegChunks; c++) {
-            const int64_t e0 = (int64_t)(c * kWave + lane) * 8;
-            if (c < nch && e0 < K) {
-                unpack8<BF16>(raw[c], v);
+        for (int j = 0; j < CPW; j++) {
+            if (in[j]) {
+                unpack8<BF16>(raw[j], v);
 #pragma unroll
                 for (int i = 0; i < 8; i++) {
                     const double d = (double)v[i] - mud;
-                    s2 += d * d;
+                    s2 += d * d;  // d*d is rounded on its own, as in the definition
                 }
             }
         }
         s2 = wave_sum_f64(s2);
+        if (lane == 0) part[1][wave] = s2;
+        __syncthreads();
+        s2 = ((part[1][0] + part[1][1]) + part[1][2]) + part[1][3];
         mu = (float)mud;
         r = (float)(1.0 / sqrt(s2 / (double)K + (double)a.eps));
     }
 #pragma unroll
-    for (int c = 0; c < kRegChunks; c++) {
-        const int64_t e0 = (int64_t)(c * kWave + lane) * 8;
-        if (c < nch && e0 < K) {
+    for (int j = 0; j < CPW; j++) {
+        const int64_t e0 = ((int64_t)(wave + kPrepWaves * j) * kWave + lane) * 8;
+        if (in[j]) {
             float g[8], b[8];
             load_param8<BF16, true>(a.gamma, e0, g, 1.0f);
             load_param8<BF16, NORM == kNormLayer>(a.beta, e0, b, 0.0f);
-            unpack8<BF16>(raw[c], v);
+            unpack8<BF16>(raw[j], v);
             normalize8<NORM>(v, g, b, r, mu);
-            decompose_store<kFmtMx, M>(a, row, e0, lane, v, 1.0f, 6.0f);
+            decompose_store<kFmtMx, M, FAST24>(a, row, e0, lane, v, 1.0f, 6.0f);
         }
     }
 }
 
 // ---------------------------------------------------------------- MX, norm, two reads
-template <bool BF16, int NORM, int M>
+template <bool BF16, int NORM, int M, int FAST24>
 __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_2pass(PrepArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
@@ -267,7 +303,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_2pass(PrepArgs a
         unpack8<BF16>(*reinterpret_cast<const uint4 *>(xr + e0), v);
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            if constexpr (NORM == kNormRms) s1 += (double)v[i] * (double)v[i];
+            if constexpr (NORM == kNormRms) s1 = __fma_rn((double)v[i], (double)v[i], s1);  // x*x exact in double
             else s1 += (double)v[i];
         }
     }
@@ -283,7 +319,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_2pass(PrepArgs a
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const double d = (double)v[i] - mud;
-                s2 += d * d;
+                s2 += d * d;  // d*d is rounded on its own, as in the definition
             }
         }
         s2 = wave_sum_f64(s2);
@@ -296,14 +332,14 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_2pass(PrepArgs a
         load_param8<BF16, NORM == kNormLayer>(a.beta, e0, b, 0.0f);
         unpack8<BF16>(*reinterpret_cast<const uint4 *>(xr + e0), v);
         normalize8<NORM>(v, g, b, r, mu);
-        decompose_store<kFmtMx, M>(a, row, e0, lane, v, 1.0f, 6.0f);
+        decompose_store<kFmtMx, M, FAST24>(a, row, e0, lane, v, 1.0f, 6.0f);
     }
 }
 
 // ---------------------------------------------------------------- streaming tasks
 // Row-split tasks: (row, kStreamChunks chunks).  Normalization statistics
 // come from the NVFP4 pre-pass (stats != nullptr) or there is no norm.
-template <bool BF16, int NORM, int FMT, int M>
+template <bool BF16, int NORM, int FMT, int M, int FAST24>
 __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_stream(PrepArgs a, const RowStats *stats) {
     const int lane = threadIdx.x & 63;
     const int64_t K = a.K;
@@ -339,7 +375,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_stream(PrepArgs a, 
                 load_param8<BF16, NORM == kNormLayer>(a.beta, e0, b, 0.0f);
                 normalize8<NORM>(v, g, b, r, mu);
             }
-            decompose_store<FMT, M>(a, row, e0, lane, v, G, G6);
+            decompose_store<FMT, M, FAST24>(a, row, e0, lane, v, G, G6);
         }
     }
 }
@@ -361,7 +397,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_nv_rowstats(PrepArgs a, 
             unpack8<BF16>(*reinterpret_cast<const uint4 *>(xr + e0), v);
 #pragma unroll
             for (int i = 0; i < 8; i++) {
-                if constexpr (NORM == kNormRms) s1 += (double)v[i] * (double)v[i];
+                if constexpr (NORM == kNormRms) s1 = __fma_rn((double)v[i], (double)v[i], s1);  // x*x exact in double
                 else s1 += (double)v[i];
             }
         }
@@ -376,7 +412,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_nv_rowstats(PrepArgs a, 
 #pragma unroll
                 for (int i = 0; i < 8; i++) {
                     const double d = (double)v[i] - mud;
-                    s2 += d * d;
+                    s2 += d * d;  // d*d is rounded on its own, as in the definition
                 }
             }
             s2 = wave_sum_f64(s2);
@@ -421,16 +457,18 @@ __global__ __launch_bounds__(1024) void k_nv_tensor_scale(const RowStats *stats,
 __global__ void k_fill_f32(float *p, float v) { *p = v; }
 
 // ---------------------------------------------------------------- launcher
-template <bool BF16, int NORM, int FMT, int M>
+template <bool BF16, int NORM, int FMT, int M, int FAST24>
 static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
     const dim3 blk(kPrepWaves * kWave);
     const int64_t K = a.K;
     if constexpr (FMT == kFmtMx && NORM != kNormNone) {
         const dim3 grid((unsigned)((a.T + kPrepWaves - 1) / kPrepWaves));
-        if (K <= (int64_t)kChunk * kRegChunks)
-            hipLaunchKernelGGL((k_prep_mx_reg<BF16, NORM, M>), grid, blk, 0, st, a);
+        if (K <= (int64_t)kChunk * kPrepWaves * 2)
+            hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 2>), dim3((unsigned)a.T), blk, 0, st, a);
+        else if (K <= (int64_t)kChunk * kPrepWaves * 4)
+            hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 4>), dim3((unsigned)a.T), blk, 0, st, a);
         else
-            hipLaunchKernelGGL((k_prep_mx_2pass<BF16, NORM, M>), grid, blk, 0, st, a);
+            hipLaunchKernelGGL((k_prep_mx_2pass<BF16, NORM, M, FAST24>), grid, blk, 0, st, a);
         if (a.global_scale) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, a.global_scale, 1.0f);
         return hipGetLastError();
     }
@@ -446,18 +484,19 @@ static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
     const int64_t tasks = a.T * tasks_per_row;
     const dim3 grid((unsigned)((tasks + kPrepWaves - 1) / kPrepWaves));
     if constexpr (FMT == kFmtNv || NORM == kNormNone)
-        hipLaunchKernelGGL((k_prep_stream<BF16, NORM, FMT, M>), grid, blk, 0, st, a, stats);
+        hipLaunchKernelGGL((k_prep_stream<BF16, NORM, FMT, M, FAST24>), grid, blk, 0, st, a, stats);
     return hipGetLastError();
 }
 
 template <bool BF16, int NORM, int FMT>
 static hipError_t launch_prep_m(const PrepArgs &a, void *ws, hipStream_t st) {
+    if (a.m == 4 && a.n == 2) return launch_prep_t<BF16, NORM, FMT, 4, 1>(a, ws, st);
     switch (a.m) {
-        case 1: return launch_prep_t<BF16, NORM, FMT, 1>(a, ws, st);
-        case 2: return launch_prep_t<BF16, NORM, FMT, 2>(a, ws, st);
-        case 4: return launch_prep_t<BF16, NORM, FMT, 4>(a, ws, st);
-        case 8: return launch_prep_t<BF16, NORM, FMT, 8>(a, ws, st);
-        case 16: return launch_prep_t<BF16, NORM, FMT, 16>(a, ws, st);
+        case 1: return launch_prep_t<BF16, NORM, FMT, 1, 0>(a, ws, st);
+        case 2: return launch_prep_t<BF16, NORM, FMT, 2, 0>(a, ws, st);
+        case 4: return launch_prep_t<BF16, NORM, FMT, 4, 0>(a, ws, st);
+        case 8: return launch_prep_t<BF16, NORM, FMT, 8, 0>(a, ws, st);
+        case 16: return launch_prep_t<BF16, NORM, FMT, 16, 0>(a, ws, st);
     }
     return hipErrorInvalidValue;
 }

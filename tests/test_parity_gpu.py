@@ -192,6 +192,7 @@ LINEAR_CASES = [
     # (fmt, T, K, nout)
     (0, 16, 256, 256), (0, 300, 640, 272), (0, 513, 1024, 520), (0, 1, 512, 64), (0, 5, 768, 48),
     (0, 17, 1280, 100), (0, 64, 4096, 256), (0, 65, 384, 1000), (0, 2, 14336, 64),
+    (0, 2048, 256, 16384),  # large enough that 256x256 tiles are chosen
     (1, 16, 256, 256), (1, 300, 640, 272), (1, 1, 512, 64), (1, 70, 1024, 130), (1, 257, 3584, 256),
 ]
 

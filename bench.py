@@ -106,10 +106,9 @@ def cpu_baseline(layers, sample_rows=32):
         t0 = time.perf_counter()
         p = oracle.prepare(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.n, wl.m, wl.fmt)
         t1 = time.perf_counter()
-        wq = L.w[0]
-        wc, ws = wq.codes[0].cpu().numpy(), wq.scales[0].cpu().numpy()
+        ow = oracle_weight(L)  # offline on both sides: not timed
         t2 = time.perf_counter()
-        dw = oracle.dequant(wc, ws, lin.k, wl.fmt, 1.0)
+        dw = ow.deq(0)
         _ = p.deq_backbone() @ dw.T + p.deq_residual() @ dw.T
         t3 = time.perf_counter()
         t_prep += t1 - t0
@@ -127,6 +126,19 @@ def cpu_baseline(layers, sample_rows=32):
     }
 
 
+_ORACLE_W = {}
+
+
+def oracle_weight(L):
+    """The oracle's own RTN payload of the layer's weight (host, cached)."""
+    import oracle
+    import synth
+    key = (L.wl.name, L.lin.name)
+    if key not in _ORACLE_W:
+        _ORACLE_W[key] = oracle.quantize_weight(synth.weight(L.wl, L.lin), L.wl.dtype, L.wl.fmt)
+    return _ORACLE_W[key]
+
+
 def error_report(sq, torch, layers, sample_rows=32):
     """Relative Frobenius error of the layer output vs an unquantized reference
     (normalized activation times the bf16 weight, in float64), for SharQ on
@@ -141,8 +153,7 @@ def error_report(sq, torch, layers, sample_rows=32):
         xh = oracle.normalize(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps).astype(np.float64)
         wf = synth.bits_to_f32(synth.weight(wl, lin)[0], wl.dtype).astype(np.float64)
         ref = xh @ wf.T
-        wq = L.w[0]
-        dw = oracle.dequant(wq.codes[0].cpu().numpy(), wq.scales[0].cpu().numpy(), lin.k, wl.fmt, 1.0)
+        dw = oracle_weight(L).deq(0)
         ysh = L.y[0][:sample_rows].double().cpu().numpy()
         rtn = oracle.prepare(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.m, wl.m, wl.fmt)
         yrtn = rtn.deq_backbone() @ dw.T

@@ -33,6 +33,17 @@
  *   - The N:M mask keeps, in every group of M consecutive elements along K,
  *     the N elements of largest magnitude; equal magnitudes favour the lower
  *     index.  Mask bitmap: bit k%8 of byte k/8 of the row.
+ *   - K-tiled layout of every FP4 code and scale array ("rows" = T for
+ *     prepared activations, nout for one expert's weights): K is cut into
+ *     tiles of 128 elements, the last one w = K - 128*floor(K/128) wide when
+ *     K is not a multiple of 128.  Tile t is stored after tiles 0..t-1 and
+ *     holds all rows back to back, each row with the tile's codes (w/2 bytes,
+ *     element k in the low nibble when k is even) or scales (w/B bytes):
+ *       byte of element k of row r = floor(k/128)*rows*(128/P)
+ *                                    + r*(w_t/P) + (k mod 128)/P,
+ *     P = 2 for codes, P = B (32 MX, 16 NV) for scales, w_t the width of
+ *     k's tile.  Total size rows*K/P, the same as row-major.  One K step of
+ *     the products then reads one contiguous run per array.
  */
 #ifndef SHARQ_H
 #define SHARQ_H
@@ -44,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 1
+#define SHARQ_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define SHARQ_API __attribute__((visibility("default")))
@@ -101,16 +112,16 @@ SHARQ_API size_t sharq_prepare_workspace_size(int64_t T, int64_t K, int32_t fmt)
  *   eps          added to the mean square / variance
  *   n, m         N:M mask, 0 <= n <= m, m in {1,2,4,8,16}, K % m == 0
  *   fmt          SHARQ_MXFP4 (K % 32 == 0) or SHARQ_NVFP4 (K % 16 == 0)
- *   mask         [T][K/8] bitmap or NULL (not written)
- *   b_codes      [T][K/2] backbone E2M1 codes, 4-byte aligned
- *   b_scales     [T][K/B] backbone block scales (E8M0 or E4M3 bytes)
- *   r_codes      [T][K/2] residual codes, 4-byte aligned
- *   r_scales     [T][K/B] residual block scales
+ *   mask         [T][K/8] row-major bitmap or NULL (not written)
+ *   b_codes      T*K/2 bytes, backbone E2M1 codes, K-tiled, 4-byte aligned
+ *   b_scales     T*K/B bytes, backbone block scales (E8M0 or E4M3), K-tiled
+ *   r_codes      T*K/2 bytes, residual codes, K-tiled, 4-byte aligned
+ *   r_scales     T*K/B bytes, residual block scales, K-tiled
  *   global_scale one device float: NVFP4 tensor scale (written); MXFP4: may
  *                be NULL, otherwise 1.0f is written
  *   workspace    sharq_prepare_workspace_size() bytes (NVFP4 only)
- * All outputs are dense row-major arrays owned by the caller.  T == 0 is a
- * valid no-op.
+ * All outputs are dense arrays owned by the caller.  T == 0 is a valid
+ * no-op.
  */
 SHARQ_API sharq_status sharq_prepare(const void *x, int32_t x_dtype, int64_t T, int64_t K, int64_t ldx,
                            int32_t norm, const void *gamma, const void *beta, float eps,
@@ -129,8 +140,9 @@ SHARQ_API size_t sharq_quantize_weight_workspace_size(int64_t experts, int64_t n
  *
  *   w            [experts][nout][K] F16 or BF16 (PyTorch Linear layout,
  *                Y = X W^T), contiguous, 16-byte aligned
- *   codes        [experts][nout][K/2] E2M1 codes
- *   scales       [experts][nout][K/B] block scales
+ *   codes        experts * nout*K/2 bytes: per expert (expert-major) the
+ *                nout x K E2M1 codes, K-tiled with rows = nout
+ *   scales       experts * nout*K/B bytes, per expert K-tiled likewise
  *   global_scale [experts] device floats: NVFP4 per-expert tensor scale
  *                amax/2688 (written); MXFP4: may be NULL, else 1.0f written
  *   workspace    sharq_quantize_weight_workspace_size() bytes
@@ -158,7 +170,7 @@ SHARQ_API size_t sharq_linear_workspace_size(int64_t rows, int64_t K, int64_t no
  * instruction).
  *
  *   b_codes, b_scales, r_codes, r_scales  prepared activations, T rows,
- *                as written by sharq_prepare (dense row-major)
+ *                as written by sharq_prepare (K-tiled)
  *   x_global_scale  device float (NVFP4), NULL for MXFP4
  *   T, K         prepared rows and reduction length (K % 128 == 0); each
  *                operand (T*K/2 code bytes, one expert's nout*K/2) < 2 GiB

@@ -89,12 +89,13 @@ def block_size(fmt: int) -> int:
 
 @dataclass
 class Prepared:
-    """Output of the fused preparation operator (dense row-major, on the GPU)."""
-    b_codes: torch.Tensor     # uint8 [T, K/2]
-    b_scales: torch.Tensor    # uint8 [T, K/B]
-    r_codes: torch.Tensor     # uint8 [T, K/2]
-    r_scales: torch.Tensor    # uint8 [T, K/B]
-    mask: Optional[torch.Tensor]  # uint8 [T, K/8] bitmap
+    """Output of the fused preparation operator (on the GPU).  Codes and
+    scales are K-tiled flat byte arrays (see layout.ktile_to_rows)."""
+    b_codes: torch.Tensor     # uint8 [T*K/2]
+    b_scales: torch.Tensor    # uint8 [T*K/B]
+    r_codes: torch.Tensor     # uint8 [T*K/2]
+    r_scales: torch.Tensor    # uint8 [T*K/B]
+    mask: Optional[torch.Tensor]  # uint8 [T, K/8] row-major bitmap
     global_scale: Optional[torch.Tensor]  # float32 [1] (NVFP4)
     T: int
     K: int
@@ -103,9 +104,10 @@ class Prepared:
 
 @dataclass
 class QWeight:
-    """One FP4 weight payload read by both paths."""
-    codes: torch.Tensor       # uint8 [E, nout, K/2]
-    scales: torch.Tensor      # uint8 [E, nout, K/B]
+    """One FP4 weight payload read by both paths; per expert, K-tiled with
+    nout rows."""
+    codes: torch.Tensor       # uint8 [E, nout*K/2]
+    scales: torch.Tensor      # uint8 [E, nout*K/B]
     global_scale: Optional[torch.Tensor]  # float32 [E] (NVFP4)
     E: int
     nout: int
@@ -117,8 +119,8 @@ def alloc_prepared(T: int, K: int, fmt: int, device, with_mask: bool = True) -> 
     B = block_size(fmt)
     u8 = dict(dtype=torch.uint8, device=device)
     return Prepared(
-        b_codes=torch.empty((T, K // 2), **u8), b_scales=torch.empty((T, K // B), **u8),
-        r_codes=torch.empty((T, K // 2), **u8), r_scales=torch.empty((T, K // B), **u8),
+        b_codes=torch.empty(T * K // 2, **u8), b_scales=torch.empty(T * K // B, **u8),
+        r_codes=torch.empty(T * K // 2, **u8), r_scales=torch.empty(T * K // B, **u8),
         mask=torch.empty((T, K // 8), **u8) if with_mask else None,
         global_scale=torch.empty(1, dtype=torch.float32, device=device) if fmt == NVFP4 else None,
         T=T, K=K, fmt=fmt)
@@ -152,7 +154,7 @@ def quantize_weight(w: torch.Tensor, fmt: int = MXFP4) -> QWeight:
     E, nout, K = w.shape
     B = block_size(fmt)
     u8 = dict(dtype=torch.uint8, device=w.device)
-    q = QWeight(codes=torch.empty((E, nout, K // 2), **u8), scales=torch.empty((E, nout, K // B), **u8),
+    q = QWeight(codes=torch.empty((E, nout * K // 2), **u8), scales=torch.empty((E, nout * K // B), **u8),
                 global_scale=torch.empty(E, dtype=torch.float32, device=w.device) if fmt == NVFP4 else None,
                 E=E, nout=nout, K=K, fmt=fmt)
     ws = _workspace(lib().sharq_quantize_weight_workspace_size(E, nout, K, fmt), w.device)

@@ -60,12 +60,14 @@ __device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t o
 }
 
 // Direct buffer -> LDS loads: lane i's bytes land at lds + i*size (lds is
-// wave-uniform); out-of-range lanes write zeros.
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
+// wave-uniform); out-of-range lanes write zeros.  The byte offset is the
+// per-lane voff plus the wave-uniform soff; callers keep voff + soff below
+// 2^32 (an out-of-range lane has voff = 2^31 and soff < 2^31).
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff, uint32_t soff = 0) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
 }
-__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t off) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, off, 0, 0, 0);
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff, uint32_t soff = 0) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voff, soff, 0, 0);
 }
 
 // ---------------------------------------------------------------- lane exchange

@@ -58,20 +58,32 @@ __device__ __forceinline__ v4f mfma_fp4_sel(v4i a, v4i b, v4f c, int sa, int sb)
 }
 
 // ============================================================================
-// Prefill: LDS-tiled, three-stage pipeline fed by direct global->LDS buffer
+// Prefill: LDS-tiled, three-buffer pipeline fed by direct global->LDS buffer
 // loads (no register staging).  Block tile BM token rows x BN weight rows,
-// four waves in a 2x2 grid, K step 128 (64 bytes of codes per row).
+// WGM x WGN waves, K stage 128 (64 bytes of codes per row) = two 64-wide
+// sub-steps of 32x32x64 MFMAs.
 //
-// LDS row = four 16-byte units; unit u of row r sits at u ^ ((r >> 2) & 3) so
-// that the 16 rows one MFMA operand fetch reads hit disjoint banks.  A
-// direct load writes 64 consecutive 16-byte slots (one per lane), so each
-// lane fetches whichever global unit belongs in its slot.
+// A stage is one K tile of the K-tiled operand layout, so each array's stage
+// is one contiguous run of rows x 64 bytes in HBM.  LDS row = four 16-byte
+// units; unit u of row r sits at u ^ ((r >> 2) & 3) so that the rows one
+// MFMA operand fetch reads spread over all banks.  A direct load writes 64
+// consecutive 16-byte slots (one per lane), so each lane fetches whichever
+// global unit belongs in its slot.
 //
-// Step s: wait until this wave's loads of stage s have landed, barrier (all
-// waves' stage-s data visible, all waves done with stage s-1), issue the
-// loads of stage s+2 into the buffer stage s-1 used, then run stage s's
-// MFMAs.  The three stage buffers are distinct LDS variables so that the
-// compiler's wait for an in-flight LDS load only blocks reads of its target.
+// Step s (stage s in buffer s % 3), every wave:
+//   1. MFMAs of sub-step 0 (fragments read during step s-1), with the LDS
+//      reads of stage s's sub-step-1 fragments threaded between them;
+//   2. wait until its own LDS reads are done and its own loads of stage s+1
+//      have landed, then barrier: every wave is past its reads of stage s
+//      and all of stage s+1 is in LDS;
+//   3. MFMAs of sub-step 1, with the direct loads of stage s+3 into buffer
+//      s % 3 and the LDS reads of stage s+1's scales and sub-step-0
+//      fragments threaded between them.
+// A stage's global loads thus have two steps to land, every LDS read has
+// the rest of a sub-step to complete, and no wave holds its matrix unit idle
+// behind a burst of memory instructions.  The three buffers are distinct LDS
+// variables so that the compiler's own wait before an LDS read only covers
+// the loads into that buffer.
 // ============================================================================
 constexpr int kKS = 128;            // K elements per stage
 constexpr int kRowBytes = kKS / 2;  // 64 B of codes per row per stage
@@ -106,11 +118,12 @@ __device__ __forceinline__ uint8_t *stage_buf() {
 
 __device__ __forceinline__ int swz_unit(int row, int unit) { return unit ^ ((row >> 2) & 3); }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
+// s_waitcnt on the vector-memory counter (at most N outstanding) and, with
+// LGKM0, on the LDS counter (none outstanding); gfx9 encoding.
+template <int N, bool LGKM0 = false>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | ((LGKM0 ? 0 : 15) << 8));
 }
 
 struct TileRows {
@@ -154,103 +167,184 @@ struct DualGemmMx {
     static constexpr int FM = BM / WGM / 32;  // 32-row token fragments per wave
     static constexpr int FN = BN / WGN / 32;  // 32-row weight fragments per wave
 
+    // Operand fragments of one 64-wide sub-step, and the four stage scales
+    // of every fragment row (byte b = block b of the stage).
+    struct Frags {
+        v4i w[FN], xb[FM], xr[FM];
+    };
+    struct Scales {
+        uint32_t w[FN], xb[FM], xr[FM];
+    };
+
     __amdgpu_buffer_rsrc_t rW, rWs, rXb, rXr, rXbs, rXrs;
     uint32_t w_off[L::W_LD], x_off[L::X_LD];
     uint32_t ws_off, xs_off;
-    int wave, lane;
+    int wave;  // wave-uniform
+    int lane, wm, wn;
     int64_t last_step;
+    uint32_t tw, tx;  // rows of the weight / token arrays: the K-tile stride
 
-    // Issue this wave's direct loads of stage `stage` into buffer B.
+    // One of this wave's PER_STAGE direct loads of stage `stage` into buffer
+    // B (stages past the end reload the last one, so every step issues the
+    // same number of loads).
     template <int B>
-    __device__ __forceinline__ void issue(int64_t stage) {
+    __device__ __forceinline__ void issue_one(int idx, int64_t stage) {
         uint8_t *st = stage_buf<B>();
         const int64_t stp = stage < last_step ? stage : last_step;
-        const uint32_t co = (uint32_t)stp * kRowBytes, so = (uint32_t)stp * 4;
-#pragma unroll
-        for (int j = 0; j < L::W_LD; j++)
-            lds_load16(rW, st + L::W_CODES + (wave * L::W_LD + j) * 1024, w_off[j] + co);
-#pragma unroll
-        for (int j = 0; j < L::X_LD; j++) {
-            lds_load16(rXb, st + L::XB_CODES + (wave * L::X_LD + j) * 1024, x_off[j] + co);
-            lds_load16(rXr, st + L::XR_CODES + (wave * L::X_LD + j) * 1024, x_off[j] + co);
+        const uint32_t cw = (uint32_t)stp * tw * kRowBytes, cx = (uint32_t)stp * tx * kRowBytes;
+        const uint32_t sw_ = (uint32_t)stp * tw * 4, sx = (uint32_t)stp * tx * 4;
+        if (idx < L::W_LD) {
+            lds_load16(rW, st + L::W_CODES + (wave * L::W_LD + idx) * 1024, w_off[idx], cw);
+        } else if (idx < L::W_LD + 2 * L::X_LD) {
+            const int j = (idx - L::W_LD) >> 1;
+            if (((idx - L::W_LD) & 1) == 0)
+                lds_load16(rXb, st + L::XB_CODES + (wave * L::X_LD + j) * 1024, x_off[j], cx);
+            else
+                lds_load16(rXr, st + L::XR_CODES + (wave * L::X_LD + j) * 1024, x_off[j], cx);
+        } else if (idx == L::W_LD + 2 * L::X_LD) {
+            // scale dwords: 64 rows per instruction; waves beyond the row
+            // count reload an earlier group (identical bytes, same place)
+            lds_load4(rWs, st + L::W_SC + (wave % (BN / 64)) * 256, ws_off, sw_);
+        } else if (idx == L::W_LD + 2 * L::X_LD + 1) {
+            lds_load4(rXbs, st + L::XB_SC + (wave % (BM / 64)) * 256, xs_off, sx);
+        } else {
+            lds_load4(rXrs, st + L::XR_SC + (wave % (BM / 64)) * 256, xs_off, sx);
         }
-        // scale dwords: 64 rows per instruction; waves beyond the row count
-        // reload an earlier group (identical bytes to identical places)
-        lds_load4(rWs, st + L::W_SC + (wave % (BN / 64)) * 256, ws_off + so);
-        lds_load4(rXbs, st + L::XB_SC + (wave % (BM / 64)) * 256, xs_off + so);
-        lds_load4(rXrs, st + L::XR_SC + (wave % (BM / 64)) * 256, xs_off + so);
     }
 
-    // Stage = two 64-wide K sub-steps; in sub-step t lane (row l%32, q = l/32)
-    // reads unit 2t+q of its row (block 2t+q of the stage).  Each row's four
-    // stage scales are read once as a dword and shifted by 8q, so byte 2t
-    // holds block 2t+q and the MFMA selects it with opsel = 2t.  The token
-    // fragments are double-buffered in registers: the next fragment's LDS
-    // reads are in flight while the current fragment's MFMAs run.
     template <int B>
-    __device__ __forceinline__ void compute(v16f (&acc)[FM][FN], int wm, int wn) {
-        const uint8_t *cur = stage_buf<B>();
-        const int frow = lane & 31, fq = lane >> 5;
-        int wsc[FN], xbsc[FM], xrsc[FM];
+    __device__ __forceinline__ void issue(int64_t stage) {
 #pragma unroll
-        for (int j = 0; j < FN; j++) {
-            const int row = wn * (FN * 32) + j * 32 + frow;
-            wsc[j] = (int)(*reinterpret_cast<const uint32_t *>(cur + L::W_SC + row * 4) >> (8 * fq));
-        }
-#pragma unroll
-        for (int i = 0; i < FM; i++) {
-            const int row = wm * (FM * 32) + i * 32 + frow;
-            xbsc[i] = (int)(*reinterpret_cast<const uint32_t *>(cur + L::XB_SC + row * 4) >> (8 * fq));
-            xrsc[i] = (int)(*reinterpret_cast<const uint32_t *>(cur + L::XR_SC + row * 4) >> (8 * fq));
-        }
+        for (int idx = 0; idx < L::PER_STAGE; idx++) issue_one<B>(idx, stage);
+    }
+
+    // LDS reads.  Sub-step T of the stage in buffer B: lane (row l%32,
+    // q = l/32) reads unit 2T+q of its row, i.e. block 2T+q of the stage.
+    // Read r of a stage's first half: the scale dwords (FN weight rows, FM
+    // backbone, FM residual), then the sub-step-0 fragments in the same order.
+    static constexpr int NREAD_FRAGS = FN + 2 * FM;
+    static constexpr int NREAD_NEXT = 2 * NREAD_FRAGS;
+
+    // Per-lane LDS byte offsets of the reads.  In sub-step T lane l feeds
+    // row wn*FN*32 + l%32 (weights) or wm*FM*32 + l%32 (tokens) and block
+    // 2q + T of the stage, q = l/32 (both operands use the same block, so the
+    // two sub-steps cover the stage's four blocks).  Its scales are the
+    // 16-bit pair of blocks 2q, 2q+1 of the row: byte T is sub-step T's, so
+    // opsel T selects it without any shifting.  Fragment j / i adds 32 rows
+    // (2048 code bytes, 128 scale bytes); 32-row steps keep the swizzle.
+    int rd_w[2], rd_x[2], rd_ws, rd_xs;
+
+    __device__ __forceinline__ void init_reads() {
+        const int frow = lane & 31, q = lane >> 5;
 #pragma unroll
         for (int t = 0; t < 2; t++) {
-            const int unit = 2 * t + fq;
-            v4i wf[FN];
-#pragma unroll
-            for (int j = 0; j < FN; j++) {
-                const int row = wn * (FN * 32) + j * 32 + frow;
-                wf[j] = *reinterpret_cast<const v4i *>(cur + L::W_CODES + row * kRowBytes + swz_unit(row, unit) * 16);
-            }
-            v4i xb[2], xr[2];
-            {
-                const int row = wm * (FM * 32) + frow;
-                const int off = row * kRowBytes + swz_unit(row, unit) * 16;
-                xb[0] = *reinterpret_cast<const v4i *>(cur + L::XB_CODES + off);
-                xr[0] = *reinterpret_cast<const v4i *>(cur + L::XR_CODES + off);
-            }
-#pragma unroll
-            for (int i = 0; i < FM; i++) {
-                if (i + 1 < FM) {
-                    const int row = wm * (FM * 32) + (i + 1) * 32 + frow;
-                    const int off = row * kRowBytes + swz_unit(row, unit) * 16;
-                    xb[(i + 1) & 1] = *reinterpret_cast<const v4i *>(cur + L::XB_CODES + off);
-                    xr[(i + 1) & 1] = *reinterpret_cast<const v4i *>(cur + L::XR_CODES + off);
-                }
-                if (t == 0) {
-#pragma unroll
-                    for (int j = 0; j < FN; j++) acc[i][j] = mfma32_fp4<0>(wf[j], xb[i & 1], acc[i][j], wsc[j], xbsc[i]);
-#pragma unroll
-                    for (int j = 0; j < FN; j++) acc[i][j] = mfma32_fp4<0>(wf[j], xr[i & 1], acc[i][j], wsc[j], xrsc[i]);
-                } else {
-#pragma unroll
-                    for (int j = 0; j < FN; j++) acc[i][j] = mfma32_fp4<2>(wf[j], xb[i & 1], acc[i][j], wsc[j], xbsc[i]);
-#pragma unroll
-                    for (int j = 0; j < FN; j++) acc[i][j] = mfma32_fp4<2>(wf[j], xr[i & 1], acc[i][j], wsc[j], xrsc[i]);
-                }
-            }
+            const int sw = swz_unit(frow, 2 * q + t) * 16;
+            rd_w[t] = (wn * (FN * 32) + frow) * kRowBytes + sw;
+            rd_x[t] = (wm * (FM * 32) + frow) * kRowBytes + sw;
+        }
+        rd_ws = (wn * (FN * 32) + frow) * 4 + 2 * q;
+        rd_xs = (wm * (FM * 32) + frow) * 4 + 2 * q;
+    }
+
+    template <int B, int T>
+    __device__ __forceinline__ void read_frag(int r, Frags &f) const {
+        const uint8_t *cur = stage_buf<B>();
+        if (r < FN) {
+            f.w[r] = *reinterpret_cast<const v4i *>(cur + (rd_w[T] + (L::W_CODES + r * 32 * kRowBytes)));
+        } else {
+            const int i = (r - FN) >> 1;
+            if (((r - FN) & 1) == 0)
+                f.xb[i] = *reinterpret_cast<const v4i *>(cur + (rd_x[T] + (L::XB_CODES + i * 32 * kRowBytes)));
+            else
+                f.xr[i] = *reinterpret_cast<const v4i *>(cur + (rd_x[T] + (L::XR_CODES + i * 32 * kRowBytes)));
         }
     }
 
-    // One pipeline step on buffer B (stage s); loads stage s+2 into (B+2)%3.
     template <int B>
-    __device__ __forceinline__ void step(int64_t s, v16f (&acc)[FM][FN], int wm, int wn) {
-        wait_vmcnt<L::PER_STAGE>();   // stage s landed (stage s+1 may still fly)
+    __device__ __forceinline__ void read_scale(int r, Scales &s) const {
+        const uint8_t *cur = stage_buf<B>();
+        if (r < FN) {
+            s.w[r] = *reinterpret_cast<const uint16_t *>(cur + (rd_ws + (L::W_SC + r * 128)));
+        } else {
+            const int i = (r - FN) >> 1;
+            if (((r - FN) & 1) == 0)
+                s.xb[i] = *reinterpret_cast<const uint16_t *>(cur + (rd_xs + (L::XB_SC + i * 128)));
+            else
+                s.xr[i] = *reinterpret_cast<const uint16_t *>(cur + (rd_xs + (L::XR_SC + i * 128)));
+        }
+    }
+
+    // Read r of the next stage's first half, in the order the sub-step-0
+    // MFMAs need them: each weight fragment's scale and codes, then per token
+    // fragment the backbone and residual scales and codes.
+    template <int B>
+    __device__ __forceinline__ void read_next(int r, Frags &f, Scales &s) const {
+        if (r < 2 * FN) {
+            if ((r & 1) == 0)
+                read_scale<B>(r >> 1, s);
+            else
+                read_frag<B, 0>(r >> 1, f);
+        } else {
+            const int i = (r - 2 * FN) >> 2, k = (r - 2 * FN) & 3;
+            if (k < 2)
+                read_scale<B>(FN + 2 * i + k, s);
+            else
+                read_frag<B, 0>(FN + 2 * i + (k - 2), f);
+        }
+    }
+
+    // MFMAs of sub-step T, in the order (token fragment i, backbone then
+    // residual, weight fragment j); so per accumulator: backbone then
+    // residual, sub-step 0 then 1.
+    //
+    // Other work is threaded between the MFMAs, one piece after each, in
+    // program order (scheduling barriers keep it there): MODE 0 reads the
+    // sub-step-1 fragments of buffer BR; MODE 1 reads the scales and
+    // sub-step-0 fragments of buffer BR and, in the later slots, issues the
+    // direct loads of stage `stage` into buffer BL.  A wave thus never stalls
+    // behind a burst of memory instructions while its matrix unit idles.
+    template <int T, int MODE, int BL, int BR>
+    __device__ __forceinline__ void mma(v16f (&acc)[FM][FN], const Frags &f, const Scales &s, int64_t stage,
+                                        Frags &fo, Scales &so) {
+        constexpr int NM = 2 * FM * FN;
+        constexpr int NOTHER = MODE == 0 ? NREAD_FRAGS : NREAD_NEXT;
+        constexpr int NLOAD = MODE == 0 ? 0 : L::PER_STAGE;
+        constexpr int NSLOT = NM > NOTHER ? (NM > NLOAD ? NM : NLOAD) : (NOTHER > NLOAD ? NOTHER : NLOAD);
+#pragma unroll
+        for (int k = 0; k < NSLOT; k++) {
+            const int i = k / (2 * FN), p = (k / FN) & 1, j = k % FN;
+            if (k < NM) {
+                if (p == 0)
+                    acc[i][j] = mfma32_fp4<T>(f.w[j], f.xb[i], acc[i][j], (int)s.w[j], (int)s.xb[i]);
+                else
+                    acc[i][j] = mfma32_fp4<T>(f.w[j], f.xr[i], acc[i][j], (int)s.w[j], (int)s.xr[i]);
+            }
+            constexpr int LOAD0 = NM > NLOAD ? NM - NLOAD - 1 : 0;  // loads go in the later slots
+            if (k >= LOAD0 && k - LOAD0 < NLOAD) this->template issue_one<BL>(k - LOAD0, stage);
+            if (k < NOTHER) {
+                if (MODE == 0)
+                    read_frag<BR, 1>(k, fo);
+                else
+                    read_next<BR>(k, fo, so);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // Step s on buffer B.  On entry f0/sc hold stage s's sub-step-0
+    // fragments and scales; on exit, stage s+1's.
+    template <int B>
+    __device__ __forceinline__ void step(int64_t s, v16f (&acc)[FM][FN], Frags &f0, Scales &sc) {
+        Frags f1;
+        Scales unused;
+        __builtin_amdgcn_sched_barrier(0);
+        this->template mma<0, 0, B, B>(acc, f0, sc, 0, f1, unused);
+        wait_vmcnt<L::PER_STAGE, true>();  // own reads of stage s done, stage s+1 landed
         __builtin_amdgcn_s_barrier();
-        this->template issue<(B + 2) % 3>(s + 2);
         __builtin_amdgcn_sched_barrier(0);
-        this->template compute<B>(acc, wm, wn);
-        __builtin_amdgcn_sched_barrier(0);
+        Scales sn;
+        this->template mma<1, 1, B, (B + 1) % 3>(acc, f1, sc, s + 3, f0, sn);
+        sc = sn;
     }
 };
 
@@ -290,9 +384,13 @@ void k_dual_gemm_mx(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
     g.rXrs = make_rsrc(a.r_scales, (uint32_t)a.T * ks);
     const int tid = threadIdx.x;
     g.lane = tid & 63;
-    g.wave = tid >> 6;
-    const int wm = g.wave / WGN, wn = g.wave % WGN;
+    g.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    g.wm = g.wave / WGN;
+    g.wn = g.wave % WGN;
     g.last_step = K / kKS - 1;
+    g.tw = nout;
+    g.tx = (uint32_t)a.T;
+    g.init_reads();
 
     // source offsets of the 16-byte slots this lane fills (fixed over K)
 #pragma unroll
@@ -300,7 +398,7 @@ void k_dual_gemm_mx(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
         const int row = (g.wave * L::W_LD + j) * 16 + (g.lane >> 2);
         const int unit = swz_unit(row, g.lane & 3);
         const int64_t n = n0 + row;
-        g.w_off[j] = n < a.nout ? (uint32_t)n * kb + unit * 16 : kOutOfRange;
+        g.w_off[j] = n < a.nout ? (uint32_t)n * kRowBytes + unit * 16 : kOutOfRange;
     }
 #pragma unroll
     for (int j = 0; j < L::X_LD; j++) {
@@ -308,14 +406,14 @@ void k_dual_gemm_mx(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
         const int unit = swz_unit(row, g.lane & 3);
         const int64_t m = tr.m0 + row;
         const int64_t src = m < tr.m_end ? (a.row_index ? (int64_t)a.row_index[m] : m) : -1;
-        g.x_off[j] = src >= 0 ? (uint32_t)src * kb + unit * 16 : kOutOfRange;
+        g.x_off[j] = src >= 0 ? (uint32_t)src * kRowBytes + unit * 16 : kOutOfRange;
     }
     {
         const int64_t n = n0 + (g.wave % (BN / 64)) * 64 + g.lane;
-        g.ws_off = n < a.nout ? (uint32_t)n * ks : kOutOfRange;
+        g.ws_off = n < a.nout ? (uint32_t)n * 4 : kOutOfRange;
         const int64_t m = tr.m0 + (g.wave % (BM / 64)) * 64 + g.lane;
         const int64_t src = m < tr.m_end ? (a.row_index ? (int64_t)a.row_index[m] : m) : -1;
-        g.xs_off = src >= 0 ? (uint32_t)src * ks : kOutOfRange;
+        g.xs_off = src >= 0 ? (uint32_t)src * 4 : kOutOfRange;
     }
 
     v16f acc[FM][FN];
@@ -327,17 +425,28 @@ void k_dual_gemm_mx(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
     const int64_t nsteps = K / kKS;
+    typename G::Frags f0;
+    typename G::Scales sc;
     g.template issue<0>(0);
     g.template issue<1>(1);
-    for (int64_t s = 0; s < nsteps; s += 3) {
-        g.template step<0>(s, acc, wm, wn);
-        if (s + 1 < nsteps) g.template step<1>(s + 1, acc, wm, wn);
-        if (s + 2 < nsteps) g.template step<2>(s + 2, acc, wm, wn);
+    g.template issue<2>(2);
+    wait_vmcnt<2 * L::PER_STAGE>();  // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int r = 0; r < G::NREAD_NEXT; r++) g.template read_next<0>(r, f0, sc);
+    int64_t s = 0;
+    for (; s + 3 <= nsteps; s += 3) {
+        g.template step<0>(s, acc, f0, sc);
+        g.template step<1>(s + 1, acc, f0, sc);
+        g.template step<2>(s + 2, acc, f0, sc);
     }
-    wait_vmcnt<0>();  // drain the clamped tail loads before the workgroup exits
+    if (s < nsteps) g.template step<0>(s, acc, f0, sc);
+    if (s + 1 < nsteps) g.template step<1>(s + 1, acc, f0, sc);
+    wait_vmcnt<0, true>();  // drain the tail loads before the workgroup exits
 
-    // ---- epilogue: accumulator group g of fragment (i, j) is Y[m][n..n+3]
+    // ---- epilogue: accumulator group q of fragment (i, j) is Y[m][n..n+3]
     const int frow = g.lane & 31, fq = g.lane >> 5;
+    const int wm = g.wm, wn = g.wn;
 #pragma unroll
     for (int i = 0; i < FM; i++) {
         const int64_t m = tr.m0 + wm * (FM * 32) + i * 32 + frow;
@@ -364,11 +473,12 @@ void k_dual_gemm_mx(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
 
 // ============================================================================
 // Decode / small-T: no LDS.  Each wave owns 16 weight rows and a range of
-// 512-element K chunks; lane (r = l%16, q = l/16) streams 64 contiguous code
-// bytes and one scale dword of weight row r per chunk, so quarter q feeds
-// blocks 4q..4q+3 and MFMA j (opsel j) uses block 4q+j.  Token rows come the
-// same way (they are few and stay in L2).  With several K splits the partial
-// sums meet in Y through FP32 atomic adds (Y zeroed first).
+// 512-element K chunks; lane (r = l%16, q = l/16) streams the 64 code bytes
+// and the scale dword of weight row r in K tile 4c+q of chunk c, so quarter q
+// feeds blocks 4q..4q+3 and MFMA j (opsel j) uses block 4q+j.  In the K-tiled
+// layout the 16 rows of one quarter are one contiguous kilobyte.  Token rows
+// come the same way (they are few and stay in L2).  With several K splits the
+// partial sums meet in Y through FP32 atomic adds (Y zeroed first).
 // ============================================================================
 constexpr int kSmallWaves = 4;
 constexpr int kChunkK = 512;
@@ -378,16 +488,17 @@ struct Chunk64 {
     uint32_t sc;
 };
 
-// 64 code bytes and one scale dword of chunk c for the lane's row; rows or
-// K quarters that do not exist read as zeros (zero codes contribute nothing
-// whatever the scale).
+// 64 code bytes and one scale dword of K tile 4c+q for the lane's row
+// (code_row = row * 64, sc_row = row * 4, or kOutOfRange; `rows` rows per
+// tile); rows or tiles that do not exist read as zeros (zero codes
+// contribute nothing whatever the scale).
 __device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
-                                           uint32_t code_row, uint32_t sc_row, int64_t c, int q,
-                                           int64_t K, Chunk64 &o) {
-    const int64_t k0 = c * kChunkK + q * 128;
-    const bool in = k0 < K;
-    const uint32_t co = in ? code_row + (uint32_t)(k0 / 2) : kOutOfRange;
-    const uint32_t so = in ? sc_row + (uint32_t)(k0 / 32) : kOutOfRange;
+                                           uint32_t code_row, uint32_t sc_row, uint32_t rows, int64_t c,
+                                           int q, int64_t K, Chunk64 &o) {
+    const int64_t tile = c * (kChunkK / kTileK) + q;
+    const bool in = tile * kTileK < K;
+    const uint32_t co = in ? code_row + (uint32_t)tile * rows * (kTileK / 2) : kOutOfRange;
+    const uint32_t so = in ? sc_row + (uint32_t)tile * rows * (kTileK / 32) : kOutOfRange;
     o.u[0] = bload128(rc, co);
     o.u[1] = bload128(rc, co + 16);
     o.u[2] = bload128(rc, co + 32);
@@ -416,15 +527,15 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_dual_gemm_mx_small(LinearA
     const auto rXbs = make_rsrc(a.b_scales, (uint32_t)(a.T * ks));
     const auto rXrs = make_rsrc(a.r_scales, (uint32_t)(a.T * ks));
     const bool wvalid = n0 + r < a.nout;
-    const uint32_t wrow = wvalid ? (uint32_t)((n0 + r) * kb) : kOutOfRange;
-    const uint32_t wsrow = wvalid ? (uint32_t)((n0 + r) * ks) : kOutOfRange;
+    const uint32_t wrow = wvalid ? (uint32_t)((n0 + r) * (kTileK / 2)) : kOutOfRange;
+    const uint32_t wsrow = wvalid ? (uint32_t)((n0 + r) * (kTileK / 32)) : kOutOfRange;
     uint32_t x_row[FM], xs_row[FM];
 #pragma unroll
     for (int f = 0; f < FM; f++) {
         const int64_t m = f * 16 + r;
         const int64_t src = m < a.rows ? (a.row_index ? (int64_t)a.row_index[m] : m) : -1;
-        x_row[f] = src >= 0 ? (uint32_t)(src * kb) : kOutOfRange;
-        xs_row[f] = src >= 0 ? (uint32_t)(src * ks) : kOutOfRange;
+        x_row[f] = src >= 0 ? (uint32_t)(src * (kTileK / 2)) : kOutOfRange;
+        xs_row[f] = src >= 0 ? (uint32_t)(src * (kTileK / 32)) : kOutOfRange;
     }
 
     v4f acc[FM];
@@ -433,11 +544,11 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_dual_gemm_mx_small(LinearA
 
     for (int64_t c = c_begin; c < c_end; c++) {
         Chunk64 w, xb[FM], xr[FM];
-        load_chunk(rW, rWs, wrow, wsrow, c, q, K, w);
+        load_chunk(rW, rWs, wrow, wsrow, (uint32_t)a.nout, c, q, K, w);
 #pragma unroll
         for (int f = 0; f < FM; f++) {
-            load_chunk(rXb, rXbs, x_row[f], xs_row[f], c, q, K, xb[f]);
-            load_chunk(rXr, rXrs, x_row[f], xs_row[f], c, q, K, xr[f]);
+            load_chunk(rXb, rXbs, x_row[f], xs_row[f], (uint32_t)a.T, c, q, K, xb[f]);
+            load_chunk(rXr, rXrs, x_row[f], xs_row[f], (uint32_t)a.T, c, q, K, xr[f]);
         }
 #pragma unroll
         for (int f = 0; f < FM; f++) {
@@ -554,7 +665,7 @@ hipError_t launch_linear_mx(const LinearArgs &a, hipStream_t st) {
         const double t = (double)((tiles + cus - 1) / cus) * shapes[i].bm * shapes[i].bn * shapes[i].cost;
         if (i == 0 || t < best_t) { best = i; best_t = t; }
     }
-    if (best == 0) return launch_prefill<256, 256, 2, 2>(a, st);
+    if (best == 0) return launch_prefill<256, 256, 4, 2>(a, st);
     if (best == 1) return launch_prefill<128, 256, 2, 2>(a, st);
     return launch_prefill<128, 128, 2, 2>(a, st);
 }

@@ -103,6 +103,9 @@ void k_dual_gemm_nv(LinearArgs a) {
     const uint8_t *wc = a.w_codes + expert * a.nout * kb;
     const uint8_t *wsc = a.w_scales + expert * a.nout * ks;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // K-tiled operands: a stage is one tile of rows x 64 code bytes and
+    // rows x 8 scale bytes; the tile stride is the array's row count
+    const int64_t tw = a.nout, tx = a.T;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
     const uint8_t *w_src[W_UNITS];
@@ -112,7 +115,7 @@ void k_dual_gemm_nv(LinearArgs a) {
     for (int i = 0; i < W_UNITS; i++) {
         const int u = tid + i * NT, row = u >> 2, unit = u & 3;
         const int64_t n = n0 + row;
-        w_src[i] = n < a.nout ? wc + n * kb + unit * 16 : nullptr;
+        w_src[i] = n < a.nout ? wc + n * kNvRow + unit * 16 : nullptr;
         w_lds[i] = row * kNvRow + nv_swz(row, unit) * 16;
     }
 #pragma unroll
@@ -121,8 +124,8 @@ void k_dual_gemm_nv(LinearArgs a) {
         const int64_t m = m0 + row;
         if (m < m_end) {
             const int64_t src = a.row_index ? (int64_t)a.row_index[m] : m;
-            xb_src[i] = a.b_codes + src * kb + unit * 16;
-            xr_src[i] = a.r_codes + src * kb + unit * 16;
+            xb_src[i] = a.b_codes + src * kNvRow + unit * 16;
+            xr_src[i] = a.r_codes + src * kNvRow + unit * 16;
         } else {
             xb_src[i] = xr_src[i] = nullptr;
         }
@@ -130,31 +133,31 @@ void k_dual_gemm_nv(LinearArgs a) {
     }
     // scales: 8 bytes per row per stage; thread t handles row t (if present)
     const uint8_t *ws_src = nullptr, *xbs_src = nullptr, *xrs_src = nullptr;
-    if (tid < BN && n0 + tid < a.nout) ws_src = wsc + (n0 + tid) * ks;
+    if (tid < BN && n0 + tid < a.nout) ws_src = wsc + (n0 + tid) * kNvScRow;
     if (tid < BM && m0 + tid < m_end) {
         const int64_t m = m0 + tid;
         const int64_t src = a.row_index ? (int64_t)a.row_index[m] : m;
-        xbs_src = a.b_scales + src * ks;
-        xrs_src = a.r_scales + src * ks;
+        xbs_src = a.b_scales + src * kNvScRow;
+        xrs_src = a.r_scales + src * kNvScRow;
     }
     uint4 w_reg[W_UNITS], xb_reg[X_UNITS], xr_reg[X_UNITS];
     uint2 ws_reg = make_uint2(0, 0), xbs_reg = make_uint2(0, 0), xrs_reg = make_uint2(0, 0);
     const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
     auto gload = [&](int64_t step) {
-        const int64_t co = step * kNvRow;
+        const int64_t cw = step * tw * kNvRow, cx = step * tx * kNvRow;
 #pragma unroll
         for (int i = 0; i < W_UNITS; i++)
-            w_reg[i] = w_src[i] ? *reinterpret_cast<const uint4 *>(w_src[i] + co) : zero4;
+            w_reg[i] = w_src[i] ? *reinterpret_cast<const uint4 *>(w_src[i] + cw) : zero4;
 #pragma unroll
         for (int i = 0; i < X_UNITS; i++) {
-            xb_reg[i] = xb_src[i] ? *reinterpret_cast<const uint4 *>(xb_src[i] + co) : zero4;
-            xr_reg[i] = xr_src[i] ? *reinterpret_cast<const uint4 *>(xr_src[i] + co) : zero4;
+            xb_reg[i] = xb_src[i] ? *reinterpret_cast<const uint4 *>(xb_src[i] + cx) : zero4;
+            xr_reg[i] = xr_src[i] ? *reinterpret_cast<const uint4 *>(xr_src[i] + cx) : zero4;
         }
-        const int64_t so = step * kNvScRow;
-        if (ws_src) ws_reg = *reinterpret_cast<const uint2 *>(ws_src + so);
-        if (xbs_src) xbs_reg = *reinterpret_cast<const uint2 *>(xbs_src + so);
-        if (xrs_src) xrs_reg = *reinterpret_cast<const uint2 *>(xrs_src + so);
+        const int64_t sw = step * tw * kNvScRow, sx = step * tx * kNvScRow;
+        if (ws_src) ws_reg = *reinterpret_cast<const uint2 *>(ws_src + sw);
+        if (xbs_src) xbs_reg = *reinterpret_cast<const uint2 *>(xbs_src + sx);
+        if (xrs_src) xrs_reg = *reinterpret_cast<const uint2 *>(xrs_src + sx);
     };
     auto lstore = [&](uint8_t *st) {
 #pragma unroll

@@ -10,6 +10,21 @@ namespace sharq {
 enum { kNormNone = 0, kNormRms = 1, kNormLayer = 2 };
 enum { kFmtMx = 0, kFmtNv = 1 };
 
+// K-tiled layout of every FP4 code and scale array (activations and
+// weights): K is cut into tiles of 128 elements (the last one may be
+// shorter); tile t stores all `rows` rows back to back, each row holding the
+// tile's codes (w/2 bytes for a tile of width w) or scales (w/B bytes).  One
+// K step of the products thus reads one contiguous run per array instead of
+// a short piece of every row.  `per` is elements per byte: 2 for codes, the
+// block size B for scales; K is a multiple of B.
+constexpr int kTileK = 128;
+
+__host__ __device__ inline int64_t ktile_offset(int64_t row, int64_t e, int64_t rows, int64_t K, int per) {
+    const int64_t t = e / kTileK;
+    const int64_t w = K - t * kTileK < kTileK ? K - t * kTileK : kTileK;
+    return t * rows * (kTileK / per) + row * (w / per) + (e - t * kTileK) / per;
+}
+
 struct PrepArgs {
     const uint16_t *x;
     int64_t T, K, ldx;

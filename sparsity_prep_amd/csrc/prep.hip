@@ -205,13 +205,15 @@ __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, 
 
     const int64_t K = a.K;
     if (a.mask) a.mask[row * (K / 8) + e0 / 8] = (uint8_t)keep;
-    *reinterpret_cast<uint32_t *>(a.b_codes + row * (K / 2) + e0 / 2) = bc;
-    *reinterpret_cast<uint32_t *>(a.r_codes + row * (K / 2) + e0 / 2) = rc;
+    const int64_t co = ktile_offset(row, e0, a.T, K, 2);
+    *reinterpret_cast<uint32_t *>(a.b_codes + co) = bc;
+    *reinterpret_cast<uint32_t *>(a.r_codes + co) = rc;
     constexpr int LPB = FMT == kFmtMx ? 4 : 2;  // lanes per scale block
     constexpr int B = FMT == kFmtMx ? 32 : 16;
     if ((lane % LPB) == 0) {
-        a.b_scales[row * (K / B) + e0 / B] = (uint8_t)bs;
-        a.r_scales[row * (K / B) + e0 / B] = (uint8_t)rs;
+        const int64_t so = ktile_offset(row, e0, a.T, K, B);
+        a.b_scales[so] = (uint8_t)bs;
+        a.r_scales[so] = (uint8_t)rs;
     }
 }
 

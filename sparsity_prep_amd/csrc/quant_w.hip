@@ -68,8 +68,10 @@ __global__ __launch_bounds__(kQWaves * kWave) void k_quant_w(QuantWArgs a) {
             unpack8<BF16>(*reinterpret_cast<const uint4 *>(a.w + row * K + e0), v);
             uint32_t codes;
             const uint32_t sb = quant_block8<FMT>(v, G, G6, codes);
-            *reinterpret_cast<uint32_t *>(a.codes + row * (K / 2) + e0 / 2) = codes;
-            if ((lane % LPB) == 0) a.scales[row * (K / B) + e0 / B] = (uint8_t)sb;
+            // expert-major; each expert's [nout x K] payload is K-tiled
+            const int64_t ex = row / a.nout, n = row - ex * a.nout;
+            *reinterpret_cast<uint32_t *>(a.codes + ex * a.nout * (K / 2) + ktile_offset(n, e0, a.nout, K, 2)) = codes;
+            if ((lane % LPB) == 0) a.scales[ex * a.nout * (K / B) + ktile_offset(n, e0, a.nout, K, B)] = (uint8_t)sb;
         }
     }
 }

@@ -13,6 +13,7 @@ import numpy as np
 import torch
 
 import oracle
+from sparsity_prep_amd.layout import ktile_to_rows
 
 BUDGET = 1e-5
 MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
@@ -103,9 +104,22 @@ def compare_prepared(gpu: dict, ora: oracle.Prepared, n: int, m: int, what: str 
 
 
 def prepared_to_host(p) -> dict:
-    return {"mask": None if p.mask is None else host(p.mask), "b_codes": host(p.b_codes),
-            "b_scales": host(p.b_scales), "r_codes": host(p.r_codes), "r_scales": host(p.r_scales),
+    """Prepared tensors on the host, codes and scales in row-major form."""
+    B = 32 if p.fmt == oracle.FMT_MXFP4 else 16
+    T, K = p.T, p.K
+    return {"mask": None if p.mask is None else host(p.mask),
+            "b_codes": ktile_to_rows(host(p.b_codes), T, K, 2), "b_scales": ktile_to_rows(host(p.b_scales), T, K, B),
+            "r_codes": ktile_to_rows(host(p.r_codes), T, K, 2), "r_scales": ktile_to_rows(host(p.r_scales), T, K, B),
             "G": None if p.global_scale is None else float(host(p.global_scale)[0])}
+
+
+def weight_to_host(q):
+    """Weight payload on the host: row-major codes [E, nout, K/2], scales [E, nout, K/B]."""
+    B = 32 if q.fmt == oracle.FMT_MXFP4 else 16
+    c, s = host(q.codes), host(q.scales)
+    codes = np.stack([ktile_to_rows(c[e], q.nout, q.K, 2) for e in range(q.E)])
+    scales = np.stack([ktile_to_rows(s[e], q.nout, q.K, B) for e in range(q.E)])
+    return codes, scales
 
 
 def rel_fro(y: np.ndarray, ref: np.ndarray) -> float:

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.sharq_abi_version() == 1
+    assert L.sharq_abi_version() == 2
     for code in range(9):
         assert L.sharq_status_string(code)
     assert L.sharq_status_string(99) == b"unknown status"

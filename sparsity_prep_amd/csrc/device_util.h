@@ -70,6 +70,15 @@ __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void *lds, u
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voff, soff, 0, 0);
 }
 
+// ---------------------------------------------------------------- XCD-aware grids
+// Workgroups are dealt to the eight XCDs round-robin (id % 8).  Block b of a
+// grid of nb blocks (nb a multiple of 8) -> logical block index such that
+// every XCD runs one contiguous range of logical blocks.  Neighbouring rows,
+// which share cache lines of the K-tiled outputs, then go through one L2.
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nb) { return (b % 8) * (nb / 8) + b / 8; }
+
+__host__ __device__ inline int64_t round_up8(int64_t n) { return (n + 7) / 8 * 8; }
+
 // ---------------------------------------------------------------- lane exchange
 // DPP quad permutations: lane i of every group of four reads lane perm[i].
 constexpr int kDppQuadXor1 = 0xB1;  // [1,0,3,2]

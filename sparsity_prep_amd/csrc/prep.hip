@@ -226,7 +226,8 @@ template <bool BF16, int NORM, int M, int FAST24, int CPW>
 __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_split(PrepArgs a) {
     __shared__ double part[2][kPrepWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t row = blockIdx.x;
+    const int64_t row = xcd_block(blockIdx.x, gridDim.x);
+    if (row >= a.T) return;
     const uint16_t *xr = a.x + row * a.ldx;
     const int64_t K = a.K;
 
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_split(PrepArgs a
 template <bool BF16, int NORM, int M, int FAST24>
 __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_2pass(PrepArgs a) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
+    const int64_t row = xcd_block(blockIdx.x, gridDim.x) * kPrepWaves + (threadIdx.x >> 6);
     if (row >= a.T) return;
     const uint16_t *xr = a.x + row * a.ldx;
     const int64_t K = a.K;
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_stream(PrepArgs a, 
     const int lane = threadIdx.x & 63;
     const int64_t K = a.K;
     const int64_t tasks_per_row = (K + (int64_t)kChunk * kStreamChunks - 1) / ((int64_t)kChunk * kStreamChunks);
-    const int64_t task = (int64_t)blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
+    const int64_t task = xcd_block(blockIdx.x, gridDim.x) * kPrepWaves + (threadIdx.x >> 6);
     const int64_t row = task / tasks_per_row;
     if (row >= a.T) return;
     const int64_t c0 = (task - row * tasks_per_row) * kStreamChunks;
@@ -464,11 +465,12 @@ static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
     const dim3 blk(kPrepWaves * kWave);
     const int64_t K = a.K;
     if constexpr (FMT == kFmtMx && NORM != kNormNone) {
-        const dim3 grid((unsigned)((a.T + kPrepWaves - 1) / kPrepWaves));
+        const dim3 grid((unsigned)round_up8((a.T + kPrepWaves - 1) / kPrepWaves));
+        const dim3 rows((unsigned)round_up8(a.T));
         if (K <= (int64_t)kChunk * kPrepWaves * 2)
-            hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 2>), dim3((unsigned)a.T), blk, 0, st, a);
+            hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 2>), rows, blk, 0, st, a);
         else if (K <= (int64_t)kChunk * kPrepWaves * 4)
-            hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 4>), dim3((unsigned)a.T), blk, 0, st, a);
+            hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 4>), rows, blk, 0, st, a);
         else
             hipLaunchKernelGGL((k_prep_mx_2pass<BF16, NORM, M, FAST24>), grid, blk, 0, st, a);
         if (a.global_scale) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, a.global_scale, 1.0f);
@@ -484,7 +486,7 @@ static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
     }
     const int64_t tasks_per_row = (K + (int64_t)kChunk * kStreamChunks - 1) / ((int64_t)kChunk * kStreamChunks);
     const int64_t tasks = a.T * tasks_per_row;
-    const dim3 grid((unsigned)((tasks + kPrepWaves - 1) / kPrepWaves));
+    const dim3 grid((unsigned)round_up8((tasks + kPrepWaves - 1) / kPrepWaves));
     if constexpr (FMT == kFmtNv || NORM == kNormNone)
         hipLaunchKernelGGL((k_prep_stream<BF16, NORM, FMT, M, FAST24>), grid, blk, 0, st, a, stats);
     return hipGetLastError();

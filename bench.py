@@ -1,34 +1,39 @@
 """Benchmark of the SharQ hot path on one MI355X.
 
-One step = the whole hot path over one batch: for each linear layer of a
+One step = the whole hot path over one batch: for each linear layer of the
+workload, the fused preparation (norm, 2:4 mask, FP4 backbone, residual, FP4
+residual) followed by the dual-path FP4 product.  The default workload is a
 Llama-3.1-8B-shaped prefill layer (2048 tokens; qkv 4096->6144 and gate_up
-4096->28672 with RMSNorm, down 14336->4096 without norm), the fused
-preparation (norm, 2:4 mask, MXFP4 backbone, residual, MXFP4 residual)
-followed by the dual-path MXFP4 product.  Inputs are seeded synthetic
-tensors of that shape, resident in HBM before the timed region; several
-copies of every input and weight are rotated so that the 256 MB Infinity
-Cache cannot serve a step from the previous one.
+4096->28672 with RMSNorm, down 14336->4096 without norm) in MXFP4.  Inputs
+are seeded synthetic tensors of the models' shapes, resident in HBM before
+the timed region; several copies of every input and weight are rotated so
+that the 256 MB Infinity Cache cannot serve a step from the previous one.
 
 Prints one JSON line: whole-step dual-product throughput (algorithmic
 TFLOP/s, 2*T*Nout*K*(1+N/M) per linear), prep GB/s, the roofline of the
 dominant kernel (the dual product) measured with HIP events on the launch
-stream, and the CPU oracle timed on a bounded sample on the host.
+stream, the CPU oracle timed on a bounded sample on the host, and the
+operator-level error of SharQ next to plain FP4 round-to-nearest.
 
-    python bench.py [--gpus 1] [--steps 30] [--warmup 5] [--workload llama|decode1|decode8|decode64|qwen|moe]
+    python bench.py [--gpus 1] [--steps 30] [--warmup 5]
+                    [--workload llama|decode1|decode8|decode64|qwen|moe]
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import platform
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+SAMPLE_ROWS = 32                # rows per linear in the CPU baseline and the error report
 
 
 def parse():
@@ -44,9 +49,13 @@ def parse():
     return ap.parse_args()
 
 
+def block_of(fmt):
+    return 32 if fmt == 0 else 16
+
+
 def prep_bytes(T, K, fmt):
     """Algorithmic bytes of one prep: read X (bf16) once, write codes, scales and mask."""
-    per_row = 2 * K + K + (K // 16 if fmt == 0 else K // 8) + K // 8
+    per_row = 2 * K + K + 2 * K // block_of(fmt) + K // 8
     return T * per_row
 
 
@@ -55,27 +64,53 @@ def gemm_flops(rows, K, nout, n, m):
     return 2.0 * rows * nout * K * (1.0 + n / m)
 
 
-class Layer:
-    """One linear of the workload with its device buffers (rotated copies)."""
+def weight_bytes(E, nout, K, fmt):
+    """FP4 weight payload (codes and block scales), read once per product."""
+    return E * nout * K * (0.5 + 1.0 / block_of(fmt))
 
-    def __init__(self, sq, torch, wl, lin, tokens, rotate, synth, dev):
-        import synth as _s
-        self.lin, self.tokens, self.wl = lin, tokens, wl
-        x = _s.activation(wl, lin, tokens)
+
+class Layer:
+    """One linear of the workload with its device buffers (rotated copies).
+
+    prep_tokens rows are prepared; the product writes `rows` output rows
+    (more than prep_tokens when a grouped product gathers rows of an MoE
+    expert batch through row_index)."""
+
+    def __init__(self, sq, torch, synth, wl, lin, prep_tokens, rotate, dev, route=None, gather=False):
+        self.lin, self.wl = lin, wl
+        self.prep_tokens = prep_tokens
+        x = synth.activation(wl, lin, prep_tokens)
         xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
         self.x = [xt] + [xt.clone() for _ in range(rotate - 1)]
+        self.x_host = x
         self.g = None
         if lin.norm:
-            self.g = torch.from_numpy(_s.gamma(wl, lin).view(np.int16)).view(torch.bfloat16).to(dev)
-        w = torch.from_numpy(_s.weight(wl, lin).view(np.int16)).view(torch.bfloat16).to(dev)
+            self.g = torch.from_numpy(synth.gamma(wl, lin).view(np.int16)).view(torch.bfloat16).to(dev)
+        w_bits = synth.weight(wl, lin)
+        w = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
         q = sq.quantize_weight(w, fmt=wl.fmt)
         del w
         self.w = [q] + [sq.QWeight(q.codes.clone(), q.scales.clone(),
                                    None if q.global_scale is None else q.global_scale.clone(),
                                    q.E, q.nout, q.K, q.fmt) for _ in range(rotate - 1)]
-        self.prep = [sq.alloc_prepared(tokens, lin.k, wl.fmt, dev) for _ in range(rotate)]
-        self.y = [torch.empty((tokens, lin.nout), dtype=torch.float32, device=dev) for _ in range(rotate)]
-        self.x_host = x
+        self.E = q.E
+        self.offs = self.ridx = None
+        self.rows = prep_tokens
+        S = min(SAMPLE_ROWS, prep_tokens)
+        self.sample_tokens = np.arange(S)          # host rows of x feeding the sampled outputs
+        self.sample_experts = np.zeros(S, np.int64)
+        if route is not None:
+            self.offs = torch.from_numpy(route.offsets).to(dev)
+            self.rows = int(route.offsets[-1])
+            if gather:
+                self.ridx = torch.from_numpy(route.row_index).to(dev)
+                self.sample_tokens = route.row_index[:S].astype(np.int64)
+            self.sample_experts = route.expert_of_row[:S].astype(np.int64)
+        experts = sorted(set(self.sample_experts.tolist()) | {0})
+        self.w_host = {e: w_bits[e] for e in experts}  # weight rows the host-side reports need
+        del w_bits
+        self.prep = [sq.alloc_prepared(prep_tokens, lin.k, wl.fmt, dev) for _ in range(rotate)]
+        self.y = [torch.empty((self.rows, lin.nout), dtype=torch.float32, device=dev) for _ in range(rotate)]
 
     def run(self, sq, i, ev=None):
         r = i % len(self.x)
@@ -85,82 +120,151 @@ class Layer:
                    fmt=self.wl.fmt, out=self.prep[r])
         if ev is not None:
             ev[1].record()
-        sq.linear(self.prep[r], self.w[r], out=self.y[r])
+        sq.linear(self.prep[r], self.w[r], group_offsets=self.offs, row_index=self.ridx, rows=self.rows,
+                  out=self.y[r])
         if ev is not None:
             ev[2].record()
-
-
-def cpu_baseline(layers, sample_rows=32):
-    """The oracle (C prep + float64 numpy product) on a bounded sample: the
-    first `sample_rows` tokens of every linear of the step."""
-    import oracle
-    import synth
-    from threadpoolctl import threadpool_info
-    t_prep = t_gemm = 0.0
-    flops = 0.0
-    pbytes = 0
-    for L in layers:
-        wl, lin = L.wl, L.lin
-        x = L.x_host[:sample_rows]
-        g = synth.gamma(wl, lin) if lin.norm else None
-        t0 = time.perf_counter()
-        p = oracle.prepare(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.n, wl.m, wl.fmt)
-        t1 = time.perf_counter()
-        ow = oracle_weight(L)  # offline on both sides: not timed
-        t2 = time.perf_counter()
-        dw = ow.deq(0)
-        _ = p.deq_backbone() @ dw.T + p.deq_residual() @ dw.T
-        t3 = time.perf_counter()
-        t_prep += t1 - t0
-        t_gemm += t3 - t2
-        flops += gemm_flops(x.shape[0], lin.k, lin.nout, wl.n, wl.m)
-        pbytes += prep_bytes(x.shape[0], lin.k, wl.fmt)
-    blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    total = t_prep + t_gemm
-    return {
-        "value": flops / total / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-        "sample": f"first {sample_rows} tokens of qkv, gate_up and down (full weights); prep in "
-                  f"single-threaded C ({pbytes / t_prep / 1e9:.3f} GB/s), product in float64 numpy "
-                  f"({flops / t_gemm / 1e9:.2f} GFLOP/s on {blas_threads} BLAS threads)",
-        "seconds": total, "prep_GBps": pbytes / t_prep / 1e9, "gemm_GFLOPs": flops / t_gemm / 1e9,
-    }
 
 
 _ORACLE_W = {}
 
 
-def oracle_weight(L):
-    """The oracle's own RTN payload of the layer's weight (host, cached)."""
+def oracle_weight(L, e):
+    """The oracle's own RTN payload of expert e of the layer's weight (host, cached)."""
     import oracle
-    import synth
-    key = (L.wl.name, L.lin.name)
+    key = (L.wl.name, L.lin.name, e)
     if key not in _ORACLE_W:
-        _ORACLE_W[key] = oracle.quantize_weight(synth.weight(L.wl, L.lin), L.wl.dtype, L.wl.fmt)
+        _ORACLE_W[key] = oracle.quantize_weight(L.w_host[e], L.wl.dtype, L.wl.fmt)
     return _ORACLE_W[key]
 
 
-def error_report(sq, torch, layers, sample_rows=32):
-    """Relative Frobenius error of the layer output vs an unquantized reference
-    (normalized activation times the bf16 weight, in float64), for SharQ on
-    the GPU and for plain MXFP4 round-to-nearest (N = M, no residual)."""
+def host_info():
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count()
+    model = platform.processor()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    from threadpoolctl import threadpool_info
+    blas = [f"{d.get('internal_api')} {d.get('version')} ({d.get('num_threads')} threads)"
+            for d in threadpool_info() if d.get("user_api") == "blas"]
+    return {"cpus_usable": ncpu, "cpu_model": model, "blas": blas}
+
+
+def cpu_baseline(layers):
+    """The oracle (C prep + float64 numpy product) on a bounded sample: the
+    first SAMPLE_ROWS tokens of every linear of the step (MoE: against expert
+    0).  The prep also runs on all usable cores (rows split over threads that
+    each call the same single-threaded oracle)."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info
+    t_prep = t_gemm = t_prep_all = 0.0
+    flops = 0.0
+    pbytes = pbytes_all = 0
+    cores = host_info()["cpus_usable"]
+    for L in layers:
+        wl, lin = L.wl, L.lin
+        S = min(SAMPLE_ROWS, L.prep_tokens)
+        x = L.x_host[:S]
+        g = synth.gamma(wl, lin) if lin.norm else None
+        dw = oracle_weight(L, 0).deq(0)  # offline on both sides: not timed
+        t0 = time.perf_counter()
+        p = oracle.prepare(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.n, wl.m, wl.fmt)
+        t1 = time.perf_counter()
+        _ = p.deq_backbone() @ dw.T + p.deq_residual() @ dw.T
+        t2 = time.perf_counter()
+        t_prep += t1 - t0
+        t_gemm += t2 - t1
+        flops += gemm_flops(S, lin.k, lin.nout, wl.n, wl.m)
+        pbytes += prep_bytes(S, lin.k, wl.fmt)
+        # all cores: S rows per thread
+        n_all = min(S * cores, L.prep_tokens)
+        chunks = [c for c in np.array_split(np.arange(n_all), cores) if c.size]
+        t3 = time.perf_counter()
+        with ThreadPoolExecutor(len(chunks)) as ex:
+            list(ex.map(lambda r: oracle.prepare(L.x_host, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.n,
+                                                 wl.m, wl.fmt, rows=r), chunks))
+        t_prep_all += time.perf_counter() - t3
+        pbytes_all += prep_bytes(n_all, lin.k, wl.fmt)
+    blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    total = t_prep + t_gemm
+    return {
+        "value": flops / total / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+        "sample": f"first {SAMPLE_ROWS} tokens of every linear (full weights); prep in single-threaded C "
+                  f"({pbytes / t_prep / 1e9:.3f} GB/s), product in float64 numpy "
+                  f"({flops / t_gemm / 1e9:.2f} GFLOP/s on {blas_threads} BLAS threads)",
+        "seconds": total, "prep_GBps_1thread": pbytes / t_prep / 1e9,
+        "prep_GBps_all_cores": pbytes_all / t_prep_all / 1e9, "gemm_GFLOPs": flops / t_gemm / 1e9,
+        "host": host_info(),
+    }
+
+
+def error_report(layers):
+    """Relative Frobenius error of sampled output rows against an unquantized
+    reference (the FP32 normalized activation times the bf16 weight, in
+    float64): SharQ on the GPU, SharQ in the oracle, plain FP4 round to
+    nearest (N = M, no residual), the N = M ablation (residual kept, no
+    mask), and SharQ's activation side alone (unquantized weight)."""
     import oracle
     import synth
     out = {}
     for L in layers:
         wl, lin = L.wl, L.lin
-        x = L.x_host[:sample_rows]
+        S = L.sample_tokens.size
+        x = L.x_host[L.sample_tokens]
         g = synth.gamma(wl, lin) if lin.norm else None
         xh = oracle.normalize(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps).astype(np.float64)
-        wf = synth.bits_to_f32(synth.weight(wl, lin)[0], wl.dtype).astype(np.float64)
-        ref = xh @ wf.T
-        dw = oracle_weight(L).deq(0)
-        ysh = L.y[0][:sample_rows].double().cpu().numpy()
+        sh = oracle.prepare(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.n, wl.m, wl.fmt)
         rtn = oracle.prepare(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.m, wl.m, wl.fmt)
-        yrtn = rtn.deq_backbone() @ dw.T
-        e_sh = float(np.linalg.norm(ysh - ref) / np.linalg.norm(ref))
-        e_rtn = float(np.linalg.norm(yrtn - ref) / np.linalg.norm(ref))
-        out[lin.name] = {"sharq_gpu": e_sh, "mxfp4_rtn": e_rtn, "gap_closed": 1.0 - e_sh / e_rtn}
+        xs = sh.deq_backbone() + sh.deq_residual()
+        xa = rtn.deq_backbone() + rtn.deq_residual()
+        ref = np.zeros((S, lin.nout))
+        y = {k: np.zeros((S, lin.nout)) for k in ("sharq_oracle", "rtn", "nm_ablation", "activation_only")}
+        for e in sorted(set(L.sample_experts.tolist())):
+            sel = np.nonzero(L.sample_experts == e)[0]
+            wf = synth.bits_to_f32(L.w_host[e], wl.dtype).astype(np.float64)
+            dw = oracle_weight(L, e).deq(0)
+            ref[sel] = xh[sel] @ wf.T
+            y["sharq_oracle"][sel] = xs[sel] @ dw.T
+            y["rtn"][sel] = rtn.deq_backbone()[sel] @ dw.T
+            y["nm_ablation"][sel] = xa[sel] @ dw.T
+            y["activation_only"][sel] = xs[sel] @ wf.T
+        ysh = L.y[0][:S].double().cpu().numpy()
+        den = np.linalg.norm(ref)
+        e = {"sharq_gpu": float(np.linalg.norm(ysh - ref) / den)}
+        e.update({k: float(np.linalg.norm(v - ref) / den) for k, v in y.items()})
+        e["gap_closed"] = 1.0 - e["sharq_gpu"] / e["rtn"]
+        out[lin.name] = e
     return out
+
+
+def build_layers(args, sq, torch, synth, dev):
+    if args.workload == "llama":
+        wl = synth.WORKLOADS[1]
+        return wl, [Layer(sq, torch, synth, wl, lin, wl.tokens, args.rotate, dev) for lin in wl.linears]
+    if args.workload.startswith("decode"):
+        wl, tokens = synth.WORKLOADS[2], int(args.workload[len("decode"):])
+        return wl, [Layer(sq, torch, synth, wl, lin, tokens, args.rotate, dev) for lin in wl.linears]
+    if args.workload == "qwen":
+        wl = synth.WORKLOADS[3]
+        return wl, [Layer(sq, torch, synth, wl, lin, wl.tokens, args.rotate, dev) for lin in wl.linears]
+    if args.workload == "moe":
+        wl = synth.WORKLOADS[4]
+        route = synth.moe_routing(wl)
+        rows = int(route.offsets[-1])
+        # gate_up: prep the unique tokens, the product gathers each expert's rows;
+        # down: prep the expert-sorted rows themselves
+        return wl, [Layer(sq, torch, synth, wl, wl.linears[0], wl.tokens, args.rotate, dev, route, gather=True),
+                    Layer(sq, torch, synth, wl, wl.linears[1], rows, args.rotate, dev, route)]
+    raise SystemExit(f"unknown workload {args.workload}")
 
 
 def main():
@@ -178,15 +282,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sq.lib()
-    if args.workload == "llama":
-        wl, tokens = synth.WORKLOADS[1], synth.WORKLOADS[1].tokens
-    elif args.workload.startswith("decode"):
-        wl, tokens = synth.WORKLOADS[2], int(args.workload[len("decode"):])
-    elif args.workload == "qwen":
-        wl, tokens = synth.WORKLOADS[3], synth.WORKLOADS[3].tokens
-    else:
-        raise SystemExit(f"unknown workload {args.workload}")
-    layers = [Layer(sq, torch, wl, lin, tokens, args.rotate, synth, dev) for lin in wl.linears]
+    wl, layers = build_layers(args, sq, torch, synth, dev)
     torch.cuda.synchronize()
 
     if args.copy_calibration:
@@ -220,12 +316,14 @@ def main():
             e = evs[s][li]
             prep_ms[li] += e[0].elapsed_time(e[1]) / args.steps
             gemm_ms[li] += e[1].elapsed_time(e[2]) / args.steps
-    flops = [gemm_flops(tokens, L.lin.k, L.lin.nout, wl.n, wl.m) for L in layers]
-    pbytes = [prep_bytes(tokens, L.lin.k, wl.fmt) for L in layers]
+    flops = [gemm_flops(L.rows, L.lin.k, L.lin.nout, wl.n, wl.m) for L in layers]
+    pbytes = [prep_bytes(L.prep_tokens, L.lin.k, wl.fmt) for L in layers]
+    wbytes = [weight_bytes(L.E, L.lin.nout, L.lin.k, wl.fmt) for L in layers]
     gemm_tflops = sum(flops) / (sum(gemm_ms) * 1e-3) / 1e12
     prep_gbps = sum(pbytes) / (sum(prep_ms) * 1e-3) / 1e9
     value = sum(flops) / (ms_step * 1e-3) / 1e12
-    peak = MXFP4_PEAK_TFLOPS if wl.fmt == 0 else BF16_PEAK_TFLOPS
+    nv = wl.fmt != 0
+    tokens = layers[0].prep_tokens
 
     result = {
         "metric": "prep GB/s + dual-GEMM TFLOP/s, % of HBM / MXFP4 MFMA peak, 1 MI355X",
@@ -238,31 +336,35 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4-e2m1 (mxfp4) x fp4 -> fp32" if wl.fmt == 0 else "fp4-e2m1 (nvfp4) -> bf16 mfma -> fp32",
-        "data": "synthetic (seeded; Llama-3.1-8B-shaped activations with outlier channels, N(0,0.02) weights)",
+        "dtype": "fp4-e2m1 (nvfp4) -> bf16 mfma -> fp32" if nv else "fp4-e2m1 (mxfp4) x fp4 -> fp32",
+        "data": "synthetic (seeded; model-shaped activations with outlier channels, N(0,0.02) weights)",
         "config": {"workload": f"{wl.name}" + ("" if tokens == wl.tokens else f"_T{tokens}"),
                    "tokens": tokens, "linears": {L.lin.name: [L.lin.k, L.lin.nout] for L in layers},
-                   "mask": f"{wl.n}:{wl.m}", "format": "MXFP4" if wl.fmt == 0 else "NVFP4",
+                   "mask": f"{wl.n}:{wl.m}", "format": "NVFP4" if nv else "MXFP4",
                    "rotated_copies": args.rotate},
         "prep_GBps": round(prep_gbps, 1),
         "prep_frac_hbm": round(prep_gbps / HBM_PEAK_GBPS, 4),
         "gemm_TFLOPs": round(gemm_tflops, 1),
-        "gemm_frac_peak": round(gemm_tflops / peak, 4),
-        "per_linear": {L.lin.name: {"prep_us": round(prep_ms[i] * 1e3, 2), "gemm_us": round(gemm_ms[i] * 1e3, 2),
+        "gemm_frac_peak": round(gemm_tflops / MXFP4_PEAK_TFLOPS, 4),
+        "per_linear": {L.lin.name: {"rows": L.rows, "prep_us": round(prep_ms[i] * 1e3, 2),
+                                    "gemm_us": round(gemm_ms[i] * 1e3, 2),
                                     "prep_GBps": round(pbytes[i] / (prep_ms[i] * 1e-3) / 1e9, 1),
-                                    "gemm_TFLOPs": round(flops[i] / (gemm_ms[i] * 1e-3) / 1e12, 1)}
+                                    "gemm_TFLOPs": round(flops[i] / (gemm_ms[i] * 1e-3) / 1e12, 1),
+                                    "weight_stream_GBps": round(wbytes[i] / (gemm_ms[i] * 1e-3) / 1e9, 1)}
                        for i, L in enumerate(layers)},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / peak, 4), "traffic": None,
-                     "kernel": "k_dual_gemm_mx (dual-path product)",
-                     "per_launch": "algorithmic 2*T*Nout*K*(1+N/M) flops / HIP-event launch time, "
-                                   "summed over the three linears"},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": MXFP4_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / MXFP4_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "k_dual_gemm<NVFP4> (dual-path product, bf16 MFMA)" if nv else "k_dual_gemm<MXFP4> (dual-path product)",
+                     "per_launch": "algorithmic 2*rows*Nout*K*(1+N/M) flops / HIP-event launch time, "
+                                   "summed over the linears"},
         "roofline_prep": {"bound": "hbm", "achieved": round(prep_gbps, 1), "peak": HBM_PEAK_GBPS,
                           "unit": "GB/s", "frac": round(prep_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
     }
+    if nv:
+        result["roofline"]["frac_of_bf16_peak"] = round(gemm_tflops / BF16_PEAK_TFLOPS, 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layers)
-        result["error_report"] = error_report(sq, torch, layers)
+        result["error_report"] = error_report(layers)
     print(json.dumps(result), flush=True)
 
 

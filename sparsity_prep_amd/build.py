@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libsharq.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "prep.hip", "quant_w.hip", "gemm_mx.hip", "gemm_nv.hip"]
+SOURCES = ["api.cpp", "prep.hip", "quant_w.hip", "gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -1,24 +1,31 @@
-// Dual-path MXFP4 linear layer for gfx950.
+// Dual-path FP4 linear layer for gfx950 (MXFP4 and NVFP4) and its dispatcher.
 //
-// Source: SharQ: Bridging Activation Sparsity and FP4 Quantization for LLM Inference, Abstract.  The backbone product (sparse
-// path) and the residual product (dense path, which restores what masking
-// dropped and what backbone rounding lost) read one FP4 weight payload.
+// Source: SharQ: Bridging Activation Sparsity and FP4 Quantization for LLM
+// Inference, Abstract.  The backbone product (sparse path) and the residual
+// product (dense path, which restores what masking dropped and what backbone
+// rounding lost) read one FP4 weight payload.
 //
-// Y[m][n] = sum_k (Qb[m][k] + Qr[m][k]) * W[n][k], evaluated as two
-// block-scaled FP4 matrix products into one FP32 accumulator: every weight
-// fragment is read from LDS once and feeds the backbone MFMA and the
-// residual MFMA (v_mfma_scale_f32_16x16x128_f8f6f4 with E2M1 operands and
-// per-lane E8M0 scales).  The backbone is multiplied densely on its
-// zero-filled form: gfx950's sparse matrix instructions (smfmac) take fp8,
-// bf8, f16 or bf16 operands without block scales, so none holds MXFP4.
+// Y[m][n] = sum_k (Qb[m][k] + Qr[m][k]) * W[n][k], evaluated as two matrix
+// products into one FP32 accumulator: every weight fragment is read from LDS
+// once and feeds the backbone MFMA and the residual MFMA.  The backbone is
+// multiplied densely on its zero-filled form: gfx950's sparse matrix
+// instructions (smfmac) take fp8, bf8, f16 or bf16 operands without block
+// scales, so none holds MXFP4.
+//
+//   MXFP4: v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands and per-lane
+//          E8M0 scales (16x16x128 in the small-T kernel).
+//   NVFP4: an E2M1 code times an E4M3 scale needs up to 6 significant bits,
+//          which no FP4/FP6/FP8 operand holds and a power-of-two block scale
+//          cannot express; bf16 holds it exactly.  The fragments are
+//          dequantized in registers (hardware FP4 conversion with the scale's
+//          power of two, one FP32 multiply by its mantissa) and multiplied
+//          with v_mfma_f32_32x32x16_bf16; the two tensor scales (activation
+//          and weight) are applied to the FP32 accumulator in the epilogue.
 //
 // Operand mapping: the weight fragment is the A operand, the activation
 // fragment the B operand, so every group of four accumulator values is four
 // consecutive output columns of one token row and leaves as one 128-bit
-// store.  Each lane feeds 16 bytes of codes (one 32-element block of one
-// row) and that block's scale byte.  The prefill kernel uses the 32x32x64
-// shape, the small-T kernel the 16x16x128 shape (lane l: row l%16, block
-// l/16).
+// store.  Each lane feeds 16 bytes of codes (32 elements of one row).
 #include "device_util.h"
 #include "kernels.h"
 
@@ -28,14 +35,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kCbszFp4 = 4;  // MFMA operand format code for E2M1
-
-__device__ __forceinline__ v4f mfma_fp4(v4i a, v4i b, v4f c, int sa, int sb) {
-    const v8i a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
-    const v8i b8 = {b.x, b.y, b.z, b.w, 0, 0, 0, 0};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, kCbszFp4, kCbszFp4, 0, sa, 0, sb);
-}
 
 // 32x32x64 block-scaled FP4 MFMA: lane l feeds row l%32 and the 32-element
 // block l/32 of the 64-wide K step; lane l, accumulator r holds
@@ -49,6 +51,7 @@ __device__ __forceinline__ v16f mfma32_fp4(v4i a, v4i b, v16f c, int sa, int sb)
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, kCbszFp4, kCbszFp4, OPSEL, sa, OPSEL, sb);
 }
 
+// 16x16x128 block-scaled FP4 MFMA (lane l: row l%16, block l/16).
 template <int OPSEL>
 __device__ __forceinline__ v4f mfma_fp4_sel(v4i a, v4i b, v4f c, int sa, int sb) {
     const v8i a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
@@ -57,18 +60,44 @@ __device__ __forceinline__ v4f mfma_fp4_sel(v4i a, v4i b, v4f c, int sa, int sb)
                                                            OPSEL, sb);
 }
 
+// 32 E2M1 codes (16 bytes, element e in nibble e) whose two halves carry the
+// E4M3 scales in bytes 0 and 1 of sc2 -> 32 bf16 values, in four groups of
+// eight (group t = elements 8t..8t+7).  A scale s = 2^e * mant is applied as
+// the hardware conversion's power of two followed by an exact FP32 multiply
+// by mant; code * s has at most 6 significant bits, so the bf16 truncation of
+// the product is exact.
+__device__ __forceinline__ void nv_dequant32(v4i c, uint32_t sc2, v8bf out[4]) {
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const uint32_t sb = __float_as_uint(e4m3_value((sc2 >> (8 * h)) & 0xFFu));
+        const float p2 = __uint_as_float(sb & 0xFF800000u);
+        const float mant = __uint_as_float((sb & 0x007FFFFFu) | 0x3F800000u);
+#pragma unroll
+        for (int w = 0; w < 2; w++) {
+            float q[8];
+            e2m1_dec8((uint32_t)c[2 * h + w], p2, q);
+            uint32_t pk[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                pk[i] = __builtin_amdgcn_perm(__float_as_uint(__fmul_rn(q[2 * i + 1], mant)),
+                                              __float_as_uint(__fmul_rn(q[2 * i], mant)), 0x07060302u);
+            out[2 * h + w] = __builtin_bit_cast(v8bf, (v4i){(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]});
+        }
+    }
+}
+
 // ============================================================================
 // Prefill: LDS-tiled, three-buffer pipeline fed by direct global->LDS buffer
 // loads (no register staging).  Block tile BM token rows x BN weight rows,
-// WGM x WGN waves, K stage 128 (64 bytes of codes per row) = two 64-wide
-// sub-steps of 32x32x64 MFMAs.
+// WGM x WGN waves, K stage 128 = two 64-wide sub-steps.
 //
 // A stage is one K tile of the K-tiled operand layout, so each array's stage
-// is one contiguous run of rows x 64 bytes in HBM.  LDS row = four 16-byte
-// units; unit u of row r sits at u ^ ((r >> 2) & 3) so that the rows one
-// MFMA operand fetch reads spread over all banks.  A direct load writes 64
-// consecutive 16-byte slots (one per lane), so each lane fetches whichever
-// global unit belongs in its slot.
+// is one contiguous run of rows x 64 code bytes (rows x SB scale bytes,
+// SB = 4 for MXFP4, 8 for NVFP4) in HBM.  LDS row = four 16-byte units; unit
+// u of row r sits at u ^ ((r >> 2) & 3) so that the rows one MFMA operand
+// fetch reads spread over all banks.  A direct load writes 64 consecutive
+// slots (one per lane), so each lane fetches whichever global bytes belong
+// in its slot.
 //
 // Step s (stage s in buffer s % 3), every wave:
 //   1. MFMAs of sub-step 0 (fragments read during step s-1), with the LDS
@@ -84,29 +113,40 @@ __device__ __forceinline__ v4f mfma_fp4_sel(v4i a, v4i b, v4f c, int sa, int sb)
 // behind a burst of memory instructions.  The three buffers are distinct LDS
 // variables so that the compiler's own wait before an LDS read only covers
 // the loads into that buffer.
+//
+// In sub-step T lane l feeds row l%32 of its fragment and the 32 elements of
+// unit 2q + T, q = l/32 (both operands use the same unit, so the two
+// sub-steps cover the stage's 128 elements).
 // ============================================================================
 constexpr int kKS = 128;            // K elements per stage
 constexpr int kRowBytes = kKS / 2;  // 64 B of codes per row per stage
 
-template <int BM, int BN, int NW>
+template <int FMT, int BM, int BN, int NW>
 struct StageLayout {
+    static constexpr int SB = FMT == kFmtMx ? 4 : 8;  // scale bytes per row per stage
     static constexpr int W_CODES = 0;
     static constexpr int XB_CODES = W_CODES + BN * kRowBytes;
     static constexpr int XR_CODES = XB_CODES + BM * kRowBytes;
     static constexpr int W_SC = XR_CODES + BM * kRowBytes;
-    static constexpr int XB_SC = W_SC + BN * 4;
-    static constexpr int XR_SC = XB_SC + BM * 4;
-    static constexpr int BYTES = XR_SC + BM * 4;
-    // direct-load instructions per wave per stage (scale groups of 64 rows
-    // are spread over the waves; surplus waves repeat a group)
+    static constexpr int XB_SC = W_SC + BN * SB;
+    static constexpr int XR_SC = XB_SC + BM * SB;
+    static constexpr int BYTES = XR_SC + BM * SB;
+    // direct-load instructions per wave per stage: 16-byte code slots, 16
+    // rows per instruction; 4-byte scale slots, RPI rows per instruction,
+    // spread over the waves (surplus waves repeat an earlier instruction:
+    // identical bytes to identical places)
     static constexpr int W_LD = BN / 16 / NW;
     static constexpr int X_LD = BM / 16 / NW;
-    static constexpr int PER_STAGE = W_LD + 2 * X_LD + 3;
+    static constexpr int RPI = 64 * 4 / SB;
+    static constexpr int SC_W = BN / RPI, SC_X = BM / RPI, SC_TOT = SC_W + 2 * SC_X;
+    static constexpr int SC_LD = (SC_TOT + NW - 1) / NW;
+    static constexpr int PER_STAGE = W_LD + 2 * X_LD + SC_LD;
     static_assert(BN % (16 * NW) == 0 && BM % (16 * NW) == 0, "tile rows per wave");
+    static_assert(BN % RPI == 0 && BM % RPI == 0, "scale rows per instruction");
 };
 
-// Three LDS stage buffers sized for the largest tile (256 x 256).
-constexpr int kStageBytesMax = StageLayout<256, 256, 4>::BYTES;
+// Three LDS stage buffers sized for the largest tile (MXFP4, 256 x 256).
+constexpr int kStageBytesMax = StageLayout<kFmtMx, 256, 256, 4>::BYTES;
 __shared__ __align__(16) uint8_t g_stage0[kStageBytesMax];
 __shared__ __align__(16) uint8_t g_stage1[kStageBytesMax];
 __shared__ __align__(16) uint8_t g_stage2[kStageBytesMax];
@@ -160,15 +200,16 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t wg, int64_t ntiles) {
 }
 
 // WGM x WGN waves: WGM along the token rows, WGN along the weight rows.
-template <int BM, int BN, int WGM, int WGN>
-struct DualGemmMx {
+template <int FMT, int BM, int BN, int WGM, int WGN>
+struct DualGemm {
     static constexpr int NW = WGM * WGN;
-    using L = StageLayout<BM, BN, NW>;
+    using L = StageLayout<FMT, BM, BN, NW>;
     static constexpr int FM = BM / WGM / 32;  // 32-row token fragments per wave
     static constexpr int FN = BN / WGN / 32;  // 32-row weight fragments per wave
 
-    // Operand fragments of one 64-wide sub-step, and the four stage scales
-    // of every fragment row (byte b = block b of the stage).
+    // Operand fragments of one 64-wide sub-step, and the 16-bit scale pair
+    // of every fragment row: MXFP4, blocks 2q and 2q+1 (byte T for sub-step
+    // T, selected by opsel); NVFP4, the two 16-element blocks of unit 2q+T.
     struct Frags {
         v4i w[FN], xb[FM], xr[FM];
     };
@@ -177,12 +218,20 @@ struct DualGemmMx {
     };
 
     __amdgpu_buffer_rsrc_t rW, rWs, rXb, rXr, rXbs, rXrs;
-    uint32_t w_off[L::W_LD], x_off[L::X_LD];
-    uint32_t ws_off, xs_off;
+    uint32_t w_off[L::W_LD], x_off[L::X_LD], s_off[L::SC_LD];
+    // scale load k of this wave: resource, LDS offset in the stage, rows of
+    // its array (wave-uniform, fixed at set-up so the K loop has no branches)
+    __amdgpu_buffer_rsrc_t s_rsrc[L::SC_LD];
+    int s_lds[L::SC_LD];
+    uint32_t s_rows[L::SC_LD];
     int wave;  // wave-uniform
     int lane, wm, wn;
     int64_t last_step;
     uint32_t tw, tx;  // rows of the weight / token arrays: the K-tile stride
+
+    // Scale-load instruction k of this wave: global index (wave + k*NW) mod
+    // SC_TOT over [W chunks | XB chunks | XR chunks].
+    static __device__ __forceinline__ int sc_index(int wave, int k) { return (wave + k * NW) % L::SC_TOT; }
 
     // One of this wave's PER_STAGE direct loads of stage `stage` into buffer
     // B (stages past the end reload the last one, so every step issues the
@@ -191,24 +240,19 @@ struct DualGemmMx {
     __device__ __forceinline__ void issue_one(int idx, int64_t stage) {
         uint8_t *st = stage_buf<B>();
         const int64_t stp = stage < last_step ? stage : last_step;
-        const uint32_t cw = (uint32_t)stp * tw * kRowBytes, cx = (uint32_t)stp * tx * kRowBytes;
-        const uint32_t sw_ = (uint32_t)stp * tw * 4, sx = (uint32_t)stp * tx * 4;
         if (idx < L::W_LD) {
-            lds_load16(rW, st + L::W_CODES + (wave * L::W_LD + idx) * 1024, w_off[idx], cw);
+            lds_load16(rW, st + L::W_CODES + (wave * L::W_LD + idx) * 1024, w_off[idx],
+                       (uint32_t)stp * tw * kRowBytes);
         } else if (idx < L::W_LD + 2 * L::X_LD) {
             const int j = (idx - L::W_LD) >> 1;
+            const uint32_t cx = (uint32_t)stp * tx * kRowBytes;
             if (((idx - L::W_LD) & 1) == 0)
                 lds_load16(rXb, st + L::XB_CODES + (wave * L::X_LD + j) * 1024, x_off[j], cx);
             else
                 lds_load16(rXr, st + L::XR_CODES + (wave * L::X_LD + j) * 1024, x_off[j], cx);
-        } else if (idx == L::W_LD + 2 * L::X_LD) {
-            // scale dwords: 64 rows per instruction; waves beyond the row
-            // count reload an earlier group (identical bytes, same place)
-            lds_load4(rWs, st + L::W_SC + (wave % (BN / 64)) * 256, ws_off, sw_);
-        } else if (idx == L::W_LD + 2 * L::X_LD + 1) {
-            lds_load4(rXbs, st + L::XB_SC + (wave % (BM / 64)) * 256, xs_off, sx);
         } else {
-            lds_load4(rXrs, st + L::XR_SC + (wave % (BM / 64)) * 256, xs_off, sx);
+            const int k = idx - L::W_LD - 2 * L::X_LD;
+            lds_load4(s_rsrc[k], st + s_lds[k], s_off[k], (uint32_t)stp * s_rows[k] * L::SB);
         }
     }
 
@@ -218,21 +262,10 @@ struct DualGemmMx {
         for (int idx = 0; idx < L::PER_STAGE; idx++) issue_one<B>(idx, stage);
     }
 
-    // LDS reads.  Sub-step T of the stage in buffer B: lane (row l%32,
-    // q = l/32) reads unit 2T+q of its row, i.e. block 2T+q of the stage.
-    // Read r of a stage's first half: the scale dwords (FN weight rows, FM
-    // backbone, FM residual), then the sub-step-0 fragments in the same order.
-    static constexpr int NREAD_FRAGS = FN + 2 * FM;
-    static constexpr int NREAD_NEXT = 2 * NREAD_FRAGS;
-
-    // Per-lane LDS byte offsets of the reads.  In sub-step T lane l feeds
-    // row wn*FN*32 + l%32 (weights) or wm*FM*32 + l%32 (tokens) and block
-    // 2q + T of the stage, q = l/32 (both operands use the same block, so the
-    // two sub-steps cover the stage's four blocks).  Its scales are the
-    // 16-bit pair of blocks 2q, 2q+1 of the row: byte T is sub-step T's, so
-    // opsel T selects it without any shifting.  Fragment j / i adds 32 rows
-    // (2048 code bytes, 128 scale bytes); 32-row steps keep the swizzle.
-    int rd_w[2], rd_x[2], rd_ws, rd_xs;
+    // Per-lane LDS byte offsets of the reads (row wn*FN*32 + l%32 for
+    // weights, wm*FM*32 + l%32 for tokens; fragment j / i adds 32 rows, which
+    // keeps the swizzle).
+    int rd_w[2], rd_x[2], rd_ws[2], rd_xs[2];
 
     __device__ __forceinline__ void init_reads() {
         const int frow = lane & 31, q = lane >> 5;
@@ -241,10 +274,14 @@ struct DualGemmMx {
             const int sw = swz_unit(frow, 2 * q + t) * 16;
             rd_w[t] = (wn * (FN * 32) + frow) * kRowBytes + sw;
             rd_x[t] = (wm * (FM * 32) + frow) * kRowBytes + sw;
+            const int sc = FMT == kFmtMx ? 2 * q : 2 * (2 * q + t);
+            rd_ws[t] = (wn * (FN * 32) + frow) * L::SB + sc;
+            rd_xs[t] = (wm * (FM * 32) + frow) * L::SB + sc;
         }
-        rd_ws = (wn * (FN * 32) + frow) * 4 + 2 * q;
-        rd_xs = (wm * (FM * 32) + frow) * 4 + 2 * q;
     }
+
+    static constexpr int NREAD_FRAGS = FN + 2 * FM;
+    static constexpr int NREAD_NEXT = 2 * NREAD_FRAGS;
 
     template <int B, int T>
     __device__ __forceinline__ void read_frag(int r, Frags &f) const {
@@ -260,37 +297,46 @@ struct DualGemmMx {
         }
     }
 
-    template <int B>
+    template <int B, int T>
     __device__ __forceinline__ void read_scale(int r, Scales &s) const {
         const uint8_t *cur = stage_buf<B>();
         if (r < FN) {
-            s.w[r] = *reinterpret_cast<const uint16_t *>(cur + (rd_ws + (L::W_SC + r * 128)));
+            s.w[r] = *reinterpret_cast<const uint16_t *>(cur + (rd_ws[T] + (L::W_SC + r * 32 * L::SB)));
         } else {
             const int i = (r - FN) >> 1;
             if (((r - FN) & 1) == 0)
-                s.xb[i] = *reinterpret_cast<const uint16_t *>(cur + (rd_xs + (L::XB_SC + i * 128)));
+                s.xb[i] = *reinterpret_cast<const uint16_t *>(cur + (rd_xs[T] + (L::XB_SC + i * 32 * L::SB)));
             else
-                s.xr[i] = *reinterpret_cast<const uint16_t *>(cur + (rd_xs + (L::XR_SC + i * 128)));
+                s.xr[i] = *reinterpret_cast<const uint16_t *>(cur + (rd_xs[T] + (L::XR_SC + i * 32 * L::SB)));
         }
     }
 
     // Read r of the next stage's first half, in the order the sub-step-0
     // MFMAs need them: each weight fragment's scale and codes, then per token
-    // fragment the backbone and residual scales and codes.
+    // fragment the backbone and residual scales and codes.  NVFP4 reads the
+    // sub-step-1 scales with the sub-step-1 fragments.
     template <int B>
     __device__ __forceinline__ void read_next(int r, Frags &f, Scales &s) const {
         if (r < 2 * FN) {
             if ((r & 1) == 0)
-                read_scale<B>(r >> 1, s);
+                read_scale<B, 0>(r >> 1, s);
             else
                 read_frag<B, 0>(r >> 1, f);
         } else {
             const int i = (r - 2 * FN) >> 2, k = (r - 2 * FN) & 3;
             if (k < 2)
-                read_scale<B>(FN + 2 * i + k, s);
+                read_scale<B, 0>(FN + 2 * i + k, s);
             else
                 read_frag<B, 0>(FN + 2 * i + (k - 2), f);
         }
+    }
+
+    template <int B>
+    __device__ __forceinline__ void read_sub1(int r, Frags &f, Scales &s) const {
+        if (FMT == kFmtMx || r < NREAD_FRAGS)
+            read_frag<B, 1>(r, f);
+        else
+            read_scale<B, 1>(r - NREAD_FRAGS, s);
     }
 
     // MFMAs of sub-step T, in the order (token fragment i, backbone then
@@ -299,35 +345,76 @@ struct DualGemmMx {
     //
     // Other work is threaded between the MFMAs, one piece after each, in
     // program order (scheduling barriers keep it there): MODE 0 reads the
-    // sub-step-1 fragments of buffer BR; MODE 1 reads the scales and
-    // sub-step-0 fragments of buffer BR and, in the later slots, issues the
-    // direct loads of stage `stage` into buffer BL.  A wave thus never stalls
-    // behind a burst of memory instructions while its matrix unit idles.
+    // sub-step-1 fragments (NVFP4: and scales) of buffer BR; MODE 1 reads the
+    // scales and sub-step-0 fragments of buffer BR and, in the later slots,
+    // issues the direct loads of stage `stage` into buffer BL.  A wave thus
+    // never stalls behind a burst of memory instructions while its matrix
+    // unit idles.
     template <int T, int MODE, int BL, int BR>
     __device__ __forceinline__ void mma(v16f (&acc)[FM][FN], const Frags &f, const Scales &s, int64_t stage,
                                         Frags &fo, Scales &so) {
-        constexpr int NM = 2 * FM * FN;
-        constexpr int NOTHER = MODE == 0 ? NREAD_FRAGS : NREAD_NEXT;
-        constexpr int NLOAD = MODE == 0 ? 0 : L::PER_STAGE;
-        constexpr int NSLOT = NM > NOTHER ? (NM > NLOAD ? NM : NLOAD) : (NOTHER > NLOAD ? NOTHER : NLOAD);
+        if constexpr (FMT == kFmtMx) {
+            constexpr int NM = 2 * FM * FN;
+            constexpr int NOTHER = MODE == 0 ? NREAD_FRAGS : NREAD_NEXT;
+            constexpr int NLOAD = MODE == 0 ? 0 : L::PER_STAGE;
+            constexpr int NSLOT = NM > NOTHER ? (NM > NLOAD ? NM : NLOAD) : (NOTHER > NLOAD ? NOTHER : NLOAD);
 #pragma unroll
-        for (int k = 0; k < NSLOT; k++) {
-            const int i = k / (2 * FN), p = (k / FN) & 1, j = k % FN;
-            if (k < NM) {
-                if (p == 0)
-                    acc[i][j] = mfma32_fp4<T>(f.w[j], f.xb[i], acc[i][j], (int)s.w[j], (int)s.xb[i]);
-                else
-                    acc[i][j] = mfma32_fp4<T>(f.w[j], f.xr[i], acc[i][j], (int)s.w[j], (int)s.xr[i]);
+            for (int k = 0; k < NSLOT; k++) {
+                const int i = k / (2 * FN), p = (k / FN) & 1, j = k % FN;
+                if (k < NM) {
+                    if (p == 0)
+                        acc[i][j] = mfma32_fp4<T>(f.w[j], f.xb[i], acc[i][j], (int)s.w[j], (int)s.xb[i]);
+                    else
+                        acc[i][j] = mfma32_fp4<T>(f.w[j], f.xr[i], acc[i][j], (int)s.w[j], (int)s.xr[i]);
+                }
+                constexpr int LOAD0 = NM > NLOAD ? NM - NLOAD - 1 : 0;  // loads go in the later slots
+                if (k >= LOAD0 && k - LOAD0 < NLOAD) this->template issue_one<BL>(k - LOAD0, stage);
+                if (k < NOTHER) {
+                    if (MODE == 0)
+                        read_sub1<BR>(k, fo, so);
+                    else
+                        read_next<BR>(k, fo, so);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            constexpr int LOAD0 = NM > NLOAD ? NM - NLOAD - 1 : 0;  // loads go in the later slots
-            if (k >= LOAD0 && k - LOAD0 < NLOAD) this->template issue_one<BL>(k - LOAD0, stage);
-            if (k < NOTHER) {
-                if (MODE == 0)
-                    read_frag<BR, 1>(k, fo);
-                else
-                    read_next<BR>(k, fo, so);
+        } else {
+            // NVFP4: dequantize each fragment once per sub-step, four bf16
+            // MFMAs per fragment pair; side work spread over the token
+            // fragments.
+            constexpr int NOTHER = MODE == 0 ? 2 * NREAD_FRAGS : NREAD_NEXT;
+            constexpr int NLOAD = MODE == 0 ? 0 : L::PER_STAGE;
+            constexpr int PER_I_OTHER = (NOTHER + FM - 1) / FM;
+            constexpr int PER_I_LOAD = (NLOAD + FM - 1) / FM;
+            v8bf wd[FN][4];
+#pragma unroll
+            for (int j = 0; j < FN; j++) nv_dequant32(f.w[j], s.w[j], wd[j]);
+#pragma unroll
+            for (int i = 0; i < FM; i++) {
+                v8bf xb[4], xr[4];
+                nv_dequant32(f.xb[i], s.xb[i], xb);
+                nv_dequant32(f.xr[i], s.xr[i], xr);
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+#pragma unroll
+                    for (int t = 0; t < 4; t++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wd[j][t], xb[t], acc[i][j], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+#pragma unroll
+                    for (int t = 0; t < 4; t++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wd[j][t], xr[t], acc[i][j], 0, 0, 0);
+#pragma unroll
+                for (int k = i * PER_I_LOAD; k < (i + 1) * PER_I_LOAD && k < NLOAD; k++)
+                    this->template issue_one<BL>(k, stage);
+#pragma unroll
+                for (int k = i * PER_I_OTHER; k < (i + 1) * PER_I_OTHER && k < NOTHER; k++) {
+                    if (MODE == 0)
+                        read_sub1<BR>(k, fo, so);
+                    else
+                        read_next<BR>(k, fo, so);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -336,25 +423,26 @@ struct DualGemmMx {
     template <int B>
     __device__ __forceinline__ void step(int64_t s, v16f (&acc)[FM][FN], Frags &f0, Scales &sc) {
         Frags f1;
-        Scales unused;
+        Scales s1;  // NVFP4: sub-step-1 scales (MXFP4 uses sc for both sub-steps)
         __builtin_amdgcn_sched_barrier(0);
-        this->template mma<0, 0, B, B>(acc, f0, sc, 0, f1, unused);
+        this->template mma<0, 0, B, B>(acc, f0, sc, 0, f1, s1);
         wait_vmcnt<L::PER_STAGE, true>();  // own reads of stage s done, stage s+1 landed
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         Scales sn;
-        this->template mma<1, 1, B, (B + 1) % 3>(acc, f1, sc, s + 3, f0, sn);
+        this->template mma<1, 1, B, (B + 1) % 3>(acc, f1, FMT == kFmtMx ? sc : s1, s + 3, f0, sn);
         sc = sn;
     }
 };
 
-template <int BM, int BN, int WGM, int WGN>
+template <int FMT, int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
-void k_dual_gemm_mx(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
-    using G = DualGemmMx<BM, BN, WGM, WGN>;
+void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
+    using G = DualGemm<FMT, BM, BN, WGM, WGN>;
     using L = typename G::L;
     constexpr int FM = G::FM, FN = G::FN;
     static_assert(FM >= 1 && FN >= 1, "tile too small for 32x32 fragments");
+    static_assert(L::BYTES <= kStageBytesMax, "stage does not fit its LDS buffer");
 
     TileRows tr;
     int64_t ntile;
@@ -372,7 +460,8 @@ void k_dual_gemm_mx(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
     }
     const int64_t n0 = ntile * BN;
     const int64_t K = a.K;
-    const uint32_t kb = (uint32_t)(K / 2), ks = (uint32_t)(K / 32);
+    constexpr int SB = L::SB;
+    const uint32_t kb = (uint32_t)(K / 2), ks = (uint32_t)(K / kKS) * SB;  // per row: code / scale bytes
     const uint32_t nout = (uint32_t)a.nout;
 
     G g;
@@ -392,7 +481,7 @@ void k_dual_gemm_mx(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
     g.tx = (uint32_t)a.T;
     g.init_reads();
 
-    // source offsets of the 16-byte slots this lane fills (fixed over K)
+    // source offsets of the slots this lane fills (fixed over K)
 #pragma unroll
     for (int j = 0; j < L::W_LD; j++) {
         const int row = (g.wave * L::W_LD + j) * 16 + (g.lane >> 2);
@@ -408,12 +497,28 @@ void k_dual_gemm_mx(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
         const int64_t src = m < tr.m_end ? (a.row_index ? (int64_t)a.row_index[m] : m) : -1;
         g.x_off[j] = src >= 0 ? (uint32_t)src * kRowBytes + unit * 16 : kOutOfRange;
     }
-    {
-        const int64_t n = n0 + (g.wave % (BN / 64)) * 64 + g.lane;
-        g.ws_off = n < a.nout ? (uint32_t)n * 4 : kOutOfRange;
-        const int64_t m = tr.m0 + (g.wave % (BM / 64)) * 64 + g.lane;
-        const int64_t src = m < tr.m_end ? (a.row_index ? (int64_t)a.row_index[m] : m) : -1;
-        g.xs_off = src >= 0 ? (uint32_t)src * 4 : kOutOfRange;
+    // scale slots: 4 bytes per lane, SB/4 lanes per row
+#pragma unroll
+    for (int k = 0; k < L::SC_LD; k++) {
+        const int gi = G::sc_index(g.wave, k);
+        const int lpr = SB / 4;
+        const int part = (g.lane % lpr) * 4;
+        if (gi < L::SC_W) {
+            const int64_t n = n0 + gi * L::RPI + g.lane / lpr;
+            g.s_off[k] = n < a.nout ? (uint32_t)n * SB + part : kOutOfRange;
+            g.s_rsrc[k] = g.rWs;
+            g.s_lds[k] = L::W_SC + gi * 256;
+            g.s_rows[k] = nout;
+        } else {
+            const int c = (gi - L::SC_W) % L::SC_X;
+            const int64_t m = tr.m0 + c * L::RPI + g.lane / lpr;
+            const int64_t src = m < tr.m_end ? (a.row_index ? (int64_t)a.row_index[m] : m) : -1;
+            g.s_off[k] = src >= 0 ? (uint32_t)src * SB + part : kOutOfRange;
+            const bool resid = gi >= L::SC_W + L::SC_X;
+            g.s_rsrc[k] = resid ? g.rXrs : g.rXbs;
+            g.s_lds[k] = (resid ? L::XR_SC : L::XB_SC) + c * 256;
+            g.s_rows[k] = (uint32_t)a.T;
+        }
     }
 
     v16f acc[FM][FN];
@@ -444,7 +549,10 @@ void k_dual_gemm_mx(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
     if (s + 1 < nsteps) g.template step<1>(s + 1, acc, f0, sc);
     wait_vmcnt<0, true>();  // drain the tail loads before the workgroup exits
 
-    // ---- epilogue: accumulator group q of fragment (i, j) is Y[m][n..n+3]
+    // ---- epilogue: accumulator group q of fragment (i, j) is Y[m][n..n+3];
+    // NVFP4 applies the two tensor scales here
+    float alpha = 1.0f;
+    if constexpr (FMT == kFmtNv) alpha = __fmul_rn(*a.x_gscale, a.w_gscale[tr.expert]);
     const int frow = g.lane & 31, fq = g.lane >> 5;
     const int wm = g.wm, wn = g.wn;
 #pragma unroll
@@ -457,7 +565,9 @@ void k_dual_gemm_mx(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const int64_t n = n0 + wn * (FN * 32) + j * 32 + 8 * q + 4 * fq;
-                const v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                if constexpr (FMT == kFmtNv) v = v4f{__fmul_rn(v.x, alpha), __fmul_rn(v.y, alpha),
+                                                     __fmul_rn(v.z, alpha), __fmul_rn(v.w, alpha)};
                 if (a.y_vec && n + 3 < a.nout) {
                     *reinterpret_cast<v4f *>(yrow + n) = v;
                 } else {
@@ -591,7 +701,7 @@ __global__ void k_zero_rows(float *y, int64_t rows, int64_t cols, int64_t ldy) {
 // ============================================================================
 // launcher
 // ============================================================================
-template <int BM, int BN, int WGM, int WGN>
+template <int FMT, int BM, int BN, int WGM, int WGN>
 static hipError_t launch_prefill(const LinearArgs &a, hipStream_t st) {
     const int64_t n_ntiles = (a.nout + BN - 1) / BN;
     int64_t blocks;
@@ -602,7 +712,7 @@ static hipError_t launch_prefill(const LinearArgs &a, hipStream_t st) {
         n_mtiles = (a.rows + BM - 1) / BM;
         blocks = ((n_ntiles * n_mtiles + 7) / 8) * 8;
     }
-    hipLaunchKernelGGL((k_dual_gemm_mx<BM, BN, WGM, WGN>), dim3((unsigned)blocks), dim3(WGM * WGN * 64), 0, st, a,
+    hipLaunchKernelGGL((k_dual_gemm<FMT, BM, BN, WGM, WGN>), dim3((unsigned)blocks), dim3(WGM * WGN * 64), 0, st, a,
                        n_ntiles, n_mtiles);
     return hipGetLastError();
 }
@@ -645,14 +755,14 @@ static int device_cus() {
 // rounds(tiles / CUs) x tile size, with smaller tiles paying for their lower
 // operand reuse (relative cost per output element below, from measurement
 // of the three shapes on MI355X).
-hipError_t launch_linear_mx(const LinearArgs &a, hipStream_t st) {
+static hipError_t launch_linear_mx(const LinearArgs &a, hipStream_t st) {
     if (a.offsets == nullptr && a.rows <= 64) {
         if (a.rows <= 16) return launch_small<1>(a, st);
         if (a.rows <= 32) return launch_small<2>(a, st);
         if (a.rows <= 48) return launch_small<3>(a, st);
         return launch_small<4>(a, st);
     }
-    if (a.offsets) return launch_prefill<128, 256, 2, 2>(a, st);
+    if (a.offsets) return launch_prefill<kFmtMx, 128, 256, 2, 2>(a, st);
     const int64_t cus = device_cus();
     struct Shape { int bm, bn; double cost; };
     // relative cost per output element of each tile shape, measured on the
@@ -665,9 +775,21 @@ hipError_t launch_linear_mx(const LinearArgs &a, hipStream_t st) {
         const double t = (double)((tiles + cus - 1) / cus) * shapes[i].bm * shapes[i].bn * shapes[i].cost;
         if (i == 0 || t < best_t) { best = i; best_t = t; }
     }
-    if (best == 0) return launch_prefill<256, 256, 4, 2>(a, st);
-    if (best == 1) return launch_prefill<128, 256, 2, 2>(a, st);
-    return launch_prefill<128, 128, 2, 2>(a, st);
+    if (best == 0) return launch_prefill<kFmtMx, 256, 256, 4, 2>(a, st);
+    if (best == 1) return launch_prefill<kFmtMx, 128, 256, 2, 2>(a, st);
+    return launch_prefill<kFmtMx, 128, 128, 2, 2>(a, st);
+}
+
+hipError_t launch_linear(const LinearArgs &a, void *ws, size_t ws_bytes, hipStream_t st) {
+    (void)ws;
+    (void)ws_bytes;
+    if (a.fmt == kFmtMx) return launch_linear_mx(a, st);
+    return launch_prefill<kFmtNv, 128, 256, 2, 2>(a, st);
+}
+
+size_t linear_workspace_bytes(int64_t rows, int64_t K, int64_t nout, int64_t E, int fmt) {
+    (void)rows; (void)K; (void)nout; (void)E; (void)fmt;
+    return 0;
 }
 
 }  // namespace sharq

@@ -89,6 +89,7 @@ sharq_status sharq_prepare(const void *x, int32_t x_dtype, int64_t T, int64_t K,
     a.r_codes = r_codes;
     a.r_scales = r_scales;
     a.global_scale = global_scale;
+    a.off32 = K % 128 == 0 && T * (K / 2) < ((int64_t)1 << 32);
     return hip_status(launch_prepare(a, workspace, static_cast<hipStream_t>(stream)));
 }
 

@@ -92,6 +92,12 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
+// Same permutation with bound_ctrl set (every quad source lane exists, so the
+// result is identical); this form folds into the consuming VALU instruction.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32_bc(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -143,8 +149,10 @@ __device__ __forceinline__ uint32_t e2m1_cvt8(const float u[8], float scale) {
     p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, u[2], u[3], scale, 1);
     p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, u[4], u[5], scale, 2);
     p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, u[6], u[7], scale, 3);
-    const uint32_t zero_mag = ~(p | (p >> 1) | (p >> 2)) & 0x11111111u;
-    return p & ~(zero_mag << 3);
+    // adding 7 to each nibble's 3-bit magnitude carries into its sign
+    // position exactly when the magnitude is non-zero
+    const uint32_t nz = (p & 0x77777777u) + 0x77777777u;
+    return p & (nz | 0x77777777u);
 }
 
 typedef float sharq_v2f __attribute__((ext_vector_type(2)));
@@ -170,25 +178,24 @@ __device__ __forceinline__ int floor_log2_f32(float a) {
 }
 
 // OCP MX shared exponent for E2M1 elements: floor(log2 amax) - 2, or -127
-// for amax == 0 (never below -127; at most 125 for finite floats).
-// Branch-free: amax == 0 lands on the subnormal formula (-150 - 2), which
-// the clamp maps to -127.
+// for amax == 0 (never below -127; at most 125 for finite floats).  The
+// frexp exponent of a finite a > 0 (subnormals included) is floor(log2 a)+1.
 __device__ __forceinline__ int mx_shared_exp(float amax) {
-    const int e = floor_log2_f32(amax) - 2;
-    return e < -127 ? -127 : e;
+    const int e = __builtin_amdgcn_frexp_expf(amax) - 3;
+    return amax == 0.0f ? -127 : (e < -127 ? -127 : e);
 }
 
 // Max over the four lanes of a quad (MX block) / a lane pair (NVFP4 block)
 // of a non-negative float, done on the bit pattern (same order as the value).
 __device__ __forceinline__ float quad_max_nonneg(float m) {
     uint32_t b = __float_as_uint(m);
-    b = max(b, dpp_u32<kDppQuadXor1>(b));
-    b = max(b, dpp_u32<kDppQuadXor2>(b));
+    b = max(b, dpp_u32_bc<kDppQuadXor1>(b));
+    b = max(b, dpp_u32_bc<kDppQuadXor2>(b));
     return __uint_as_float(b);
 }
 __device__ __forceinline__ float pair_max_nonneg(float m) {
     uint32_t b = __float_as_uint(m);
-    b = max(b, dpp_u32<kDppQuadXor1>(b));
+    b = max(b, dpp_u32_bc<kDppQuadXor1>(b));
     return __uint_as_float(b);
 }
 

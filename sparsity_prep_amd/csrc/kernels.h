@@ -19,10 +19,14 @@ enum { kFmtMx = 0, kFmtNv = 1 };
 // block size B for scales; K is a multiple of B.
 constexpr int kTileK = 128;
 
-__host__ __device__ inline int64_t ktile_offset(int64_t row, int64_t e, int64_t rows, int64_t K, int per) {
-    const int64_t t = e / kTileK;
-    const int64_t w = K - t * kTileK < kTileK ? K - t * kTileK : kTileK;
-    return t * rows * (kTileK / per) + row * (w / per) + (e - t * kTileK) / per;
+template <int PER>
+__host__ __device__ inline int64_t ktile_offset(int64_t row, int64_t e, int64_t rows, int64_t K) {
+    static_assert(PER == 2 || PER == 16 || PER == 32, "codes or block scales");
+    const uint64_t t = (uint64_t)e / kTileK;
+    const uint64_t rem = (uint64_t)K - t * kTileK;
+    const uint64_t w = rem < (uint64_t)kTileK ? rem : (uint64_t)kTileK;
+    return (int64_t)(t * (uint64_t)rows * (kTileK / PER) + (uint64_t)row * (w / PER) +
+                     ((uint64_t)e % kTileK) / PER);
 }
 
 struct PrepArgs {
@@ -34,6 +38,7 @@ struct PrepArgs {
     bool bf16;
     uint8_t *mask, *b_codes, *b_scales, *r_codes, *r_scales;
     float *global_scale;
+    bool off32;  // K % 128 == 0 and T*K/2 < 2^32: 32-bit K-tiled offsets
 };
 
 hipError_t launch_prepare(const PrepArgs &a, void *ws, hipStream_t st);

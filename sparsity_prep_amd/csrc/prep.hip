@@ -30,6 +30,8 @@ namespace sharq {
 constexpr int kPrepWaves = 4;        // waves per workgroup
 constexpr int kChunk = 512;          // elements per wave-wide 128-bit load
 constexpr int kStreamChunks = 4;     // chunks per task when rows are split
+constexpr int64_t kPrepRowsGrid = 512;    // row workgroups that fill the GPU (two per CU)
+constexpr int64_t kPrepWavesGrid = 4096;  // streaming waves that fill the GPU (four per SIMD)
 
 struct RowStats {  // per-row statistics written by the NVFP4 pre-pass
     float r, mu, amax, pad;
@@ -90,26 +92,35 @@ __device__ __forceinline__ uint32_t select_m16(const float v[8], int n, int lane
 // 2:4 (the workloads' pattern): element i is kept iff it beats at least two
 // of the three others.  The six magnitude comparisons (|a| >= |b| on floats,
 // which orders finite values, subnormals and +-0 exactly like the bit
-// patterns without sign) become lane masks, the majority logic runs on those
-// masks, and the kept values are selected straight from them.
-__device__ __forceinline__ void select_2of4(const float v[8], bool keep[8]) {
+// patterns without sign) are taken as wave-wide lane masks (ballot), the
+// majority logic runs on those masks in scalar registers, and each lane reads
+// its keep flags back as lane masks (inverse ballot) to select the kept
+// values, so no per-lane 0/1 values are materialized.  Inactive lanes
+// contribute 0 bits and never read theirs.
+__device__ __forceinline__ void select_2of4(const float v[8], uint64_t km[8]) {
 #pragma unroll
     for (int g = 0; g < 8; g += 4) {
         const float a0 = fabsf(v[g]), a1 = fabsf(v[g + 1]), a2 = fabsf(v[g + 2]), a3 = fabsf(v[g + 3]);
-        const bool c01 = a0 >= a1, c02 = a0 >= a2, c03 = a0 >= a3;  // lower index wins ties
-        const bool c12 = a1 >= a2, c13 = a1 >= a3, c23 = a2 >= a3;
-        keep[g] = (c01 && c02) || (c03 && (c01 || c02));
-        keep[g + 1] = (!c01 && c12) || (c13 && (!c01 || c12));
-        keep[g + 2] = (!c02 && !c12) || (c23 && (!c02 || !c12));
-        keep[g + 3] = (!c03 && !c13) || (!c23 && (!c03 || !c13));
+        // lower index wins ties
+        const uint64_t c01 = __builtin_amdgcn_ballot_w64(a0 >= a1), c02 = __builtin_amdgcn_ballot_w64(a0 >= a2);
+        const uint64_t c03 = __builtin_amdgcn_ballot_w64(a0 >= a3), c12 = __builtin_amdgcn_ballot_w64(a1 >= a2);
+        const uint64_t c13 = __builtin_amdgcn_ballot_w64(a1 >= a3), c23 = __builtin_amdgcn_ballot_w64(a2 >= a3);
+        km[g] = (c01 & c02) | (c01 & c03) | (c02 & c03);
+        km[g + 1] = (~c01 & c12) | (~c01 & c13) | (c12 & c13);
+        km[g + 2] = (~c02 & ~c12) | (~c02 & c23) | (~c12 & c23);
+        km[g + 3] = (~c03 & ~c13) | (~c03 & ~c23) | (~c13 & ~c23);
     }
 }
 
-// FAST24: 1 = the 2:4 fast path, 0 = runtime N with M-wide groups.
+// FAST24: 1 = the 2:4 fast path, 0 = runtime N with M-wide groups.  keep[i]
+// is element i's flag (as a lane predicate).
 template <int M, int FAST24>
 __device__ __forceinline__ void select8(const float v[8], int n, int lane, bool keep[8]) {
     if constexpr (FAST24) {
-        select_2of4(v, keep);
+        uint64_t km[8];
+        select_2of4(v, km);
+#pragma unroll
+        for (int i = 0; i < 8; i++) keep[i] = __builtin_amdgcn_inverse_ballot_w64(km[i]);
     } else {
         uint32_t k;
         if constexpr (M == 16) k = select_m16(v, n, lane);
@@ -179,6 +190,15 @@ __device__ __forceinline__ void load_param8(const uint16_t *p, int64_t e0, float
     }
 }
 
+// Raw 128-bit word of a per-column parameter (gamma, beta), loaded early so
+// its latency overlaps the row's own loads; absent parameters read as the
+// bit pattern of dflt in every element.
+template <bool HAS>
+__device__ __forceinline__ uint4 param_raw(const uint16_t *p, int64_t e0, uint32_t dflt_pair) {
+    if (HAS && p != nullptr) return *reinterpret_cast<const uint4 *>(p + e0);
+    return make_uint4(dflt_pair, dflt_pair, dflt_pair, dflt_pair);
+}
+
 // ---------------------------------------------------------------- per-chunk body
 // Normalized values v of one lane -> mask byte, backbone and residual codes
 // and scales, stored at element offset e0 of row `row`.
@@ -204,91 +224,126 @@ __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, 
     else rs = quant_nv8(R, G, G6, rc, unused);
 
     const int64_t K = a.K;
-    if (a.mask) a.mask[row * (K / 8) + e0 / 8] = (uint8_t)keep;
-    const int64_t co = ktile_offset(row, e0, a.T, K, 2);
-    *reinterpret_cast<uint32_t *>(a.b_codes + co) = bc;
-    *reinterpret_cast<uint32_t *>(a.r_codes + co) = rc;
     constexpr int LPB = FMT == kFmtMx ? 4 : 2;  // lanes per scale block
     constexpr int B = FMT == kFmtMx ? 32 : 16;
-    if ((lane % LPB) == 0) {
-        const int64_t so = ktile_offset(row, e0, a.T, K, B);
-        a.b_scales[so] = (uint8_t)bs;
-        a.r_scales[so] = (uint8_t)rs;
+    // `row` is wave-uniform, so every row base below is a scalar address and
+    // the per-lane part stays a 32-bit offset
+    const uint32_t e = (uint32_t)e0;  // e0 < K < 2^31
+    if (a.mask) (a.mask + row * (K / 8))[e >> 3] = (uint8_t)keep;
+    if (a.off32) {  // K % 128 == 0 and each array < 4 GiB: tile t at t*T*(row bytes)
+        const uint32_t t = e / kTileK, w = e % kTileK;
+        const uint32_t co = t * (uint32_t)(a.T * (kTileK / 2)) + w / 2;
+        const uint32_t so = t * (uint32_t)(a.T * (kTileK / B)) + w / B;
+        *reinterpret_cast<uint32_t *>(a.b_codes + row * (kTileK / 2) + co) = bc;
+        *reinterpret_cast<uint32_t *>(a.r_codes + row * (kTileK / 2) + co) = rc;
+        if ((lane % LPB) == 0) {
+            (a.b_scales + row * (kTileK / B))[so] = (uint8_t)bs;
+            (a.r_scales + row * (kTileK / B))[so] = (uint8_t)rs;
+        }
+    } else {
+        const int64_t co = ktile_offset<2>(row, e0, a.T, K);
+        const int64_t so = ktile_offset<B>(row, e0, a.T, K);
+        *reinterpret_cast<uint32_t *>(a.b_codes + co) = bc;
+        *reinterpret_cast<uint32_t *>(a.r_codes + co) = rc;
+        if ((lane % LPB) == 0) {
+            a.b_scales[so] = (uint8_t)bs;
+            a.r_scales[so] = (uint8_t)rs;
+        }
     }
 }
 
 // ---------------------------------------------------------------- MX, norm, row split over a workgroup
-// One row per workgroup of four waves; wave w owns chunks w, w+4, ... (at
-// most CPW of them, held in registers).  Each wave reduces its FP64 partial
-// sums, the four partials meet in LDS and every wave adds them in the same
-// fixed order, so all waves derive the same r (and mu).
+// A workgroup of four waves handles `rpw` consecutive rows, one at a time;
+// wave w owns chunks w, w+4, ... of a row (at most CPW of them, held in
+// registers).  The next row's words are loaded before the current row is
+// reduced and quantized, so its latency hides behind the current row's
+// arithmetic.  Each wave reduces its FP64 partial sums, the four partials
+// meet in LDS (two slots, alternating by row) and every wave adds them in
+// the same fixed order, so all waves derive the same r (and mu).  gamma and
+// beta are loaded once per workgroup.
 template <bool BF16, int NORM, int M, int FAST24, int CPW>
-__global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_split(PrepArgs a) {
-    __shared__ double part[2][kPrepWaves];
+__global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_split(PrepArgs a, int64_t rpw) {
+    __shared__ double part[2][2][kPrepWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t row = xcd_block(blockIdx.x, gridDim.x);
-    if (row >= a.T) return;
-    const uint16_t *xr = a.x + row * a.ldx;
+    const int64_t row0 = xcd_block(blockIdx.x, gridDim.x) * rpw;
+    const int64_t row_end = row0 + rpw < a.T ? row0 + rpw : a.T;
+    if (row0 >= row_end) return;
     const int64_t K = a.K;
 
-    uint4 raw[CPW];
     bool in[CPW];
+    uint4 graw[CPW], braw[CPW], raw[CPW];
+    constexpr uint32_t kOnePair = BF16 ? 0x3F803F80u : 0x3C003C00u;  // 1.0, 1.0
 #pragma unroll
     for (int j = 0; j < CPW; j++) {
         const int64_t e0 = ((int64_t)(wave + kPrepWaves * j) * kWave + lane) * 8;
         in[j] = e0 < K;
-        raw[j] = in[j] ? *reinterpret_cast<const uint4 *>(xr + e0) : make_uint4(0, 0, 0, 0);
+        raw[j] = in[j] ? *reinterpret_cast<const uint4 *>(a.x + row0 * a.ldx + e0) : make_uint4(0, 0, 0, 0);
+        graw[j] = in[j] ? param_raw<true>(a.gamma, e0, kOnePair) : make_uint4(0, 0, 0, 0);
+        braw[j] = in[j] ? param_raw<NORM == kNormLayer>(a.beta, e0, 0u) : make_uint4(0, 0, 0, 0);
     }
-    float v[8];
-    double s1 = 0.0;
-#pragma unroll
-    for (int j = 0; j < CPW; j++) {
-        unpack8<BF16>(raw[j], v);
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            if constexpr (NORM == kNormRms) s1 = __fma_rn((double)v[i], (double)v[i], s1);  // x*x exact in double
-            else s1 += (double)v[i];
-        }
-    }
-    s1 = wave_sum_f64(s1);
-    if (lane == 0) part[0][wave] = s1;
-    __syncthreads();
-    s1 = ((part[0][0] + part[0][1]) + part[0][2]) + part[0][3];
-    float r, mu = 0.0f;
-    if constexpr (NORM == kNormRms) {
-        r = (float)(1.0 / sqrt(s1 / (double)K + (double)a.eps));
-    } else {
-        const double mud = s1 / (double)K;
-        double s2 = 0.0;
+    for (int64_t row = row0; row < row_end; row++) {
+        const int slot = (int)(row & 1);
+        uint4 nraw[CPW];
+        const bool more = row + 1 < row_end;
 #pragma unroll
         for (int j = 0; j < CPW; j++) {
-            if (in[j]) {
-                unpack8<BF16>(raw[j], v);
+            const int64_t e0 = ((int64_t)(wave + kPrepWaves * j) * kWave + lane) * 8;
+            nraw[j] = (more && in[j]) ? *reinterpret_cast<const uint4 *>(a.x + (row + 1) * a.ldx + e0)
+                                      : make_uint4(0, 0, 0, 0);
+        }
+        float v[8];
+        double s1 = 0.0;
 #pragma unroll
-                for (int i = 0; i < 8; i++) {
-                    const double d = (double)v[i] - mud;
-                    s2 += d * d;  // d*d is rounded on its own, as in the definition
-                }
+        for (int j = 0; j < CPW; j++) {
+            unpack8<BF16>(raw[j], v);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                if constexpr (NORM == kNormRms) s1 = __fma_rn((double)v[i], (double)v[i], s1);  // x*x exact in double
+                else s1 += (double)v[i];
             }
         }
-        s2 = wave_sum_f64(s2);
-        if (lane == 0) part[1][wave] = s2;
+        s1 = wave_sum_f64(s1);
+        if (lane == 0) part[slot][0][wave] = s1;
         __syncthreads();
-        s2 = ((part[1][0] + part[1][1]) + part[1][2]) + part[1][3];
-        mu = (float)mud;
-        r = (float)(1.0 / sqrt(s2 / (double)K + (double)a.eps));
-    }
+        s1 = ((part[slot][0][0] + part[slot][0][1]) + part[slot][0][2]) + part[slot][0][3];
+        float r, mu = 0.0f;
+        if constexpr (NORM == kNormRms) {
+            r = (float)(1.0 / sqrt(s1 / (double)K + (double)a.eps));
+        } else {
+            const double mud = s1 / (double)K;
+            double s2 = 0.0;
 #pragma unroll
-    for (int j = 0; j < CPW; j++) {
-        const int64_t e0 = ((int64_t)(wave + kPrepWaves * j) * kWave + lane) * 8;
-        if (in[j]) {
-            float g[8], b[8];
-            load_param8<BF16, true>(a.gamma, e0, g, 1.0f);
-            load_param8<BF16, NORM == kNormLayer>(a.beta, e0, b, 0.0f);
-            unpack8<BF16>(raw[j], v);
-            normalize8<NORM>(v, g, b, r, mu);
-            decompose_store<kFmtMx, M, FAST24>(a, row, e0, lane, v, 1.0f, 6.0f);
+            for (int j = 0; j < CPW; j++) {
+                if (in[j]) {
+                    unpack8<BF16>(raw[j], v);
+#pragma unroll
+                    for (int i = 0; i < 8; i++) {
+                        const double d = (double)v[i] - mud;
+                        s2 += d * d;  // d*d is rounded on its own, as in the definition
+                    }
+                }
+            }
+            s2 = wave_sum_f64(s2);
+            if (lane == 0) part[slot][1][wave] = s2;
+            __syncthreads();
+            s2 = ((part[slot][1][0] + part[slot][1][1]) + part[slot][1][2]) + part[slot][1][3];
+            mu = (float)mud;
+            r = (float)(1.0 / sqrt(s2 / (double)K + (double)a.eps));
         }
+#pragma unroll
+        for (int j = 0; j < CPW; j++) {
+            const int64_t e0 = ((int64_t)(wave + kPrepWaves * j) * kWave + lane) * 8;
+            if (in[j]) {
+                float g[8], b[8];
+                unpack8<BF16>(graw[j], g);
+                unpack8<BF16>(braw[j], b);
+                unpack8<BF16>(raw[j], v);
+                normalize8<NORM>(v, g, b, r, mu);
+                decompose_store<kFmtMx, M, FAST24>(a, row, e0, lane, v, 1.0f, 6.0f);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < CPW; j++) raw[j] = nraw[j];
     }
 }
 
@@ -296,7 +351,8 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_split(PrepArgs a
 template <bool BF16, int NORM, int M, int FAST24>
 __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_2pass(PrepArgs a) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = xcd_block(blockIdx.x, gridDim.x) * kPrepWaves + (threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t row = xcd_block(blockIdx.x, gridDim.x) * kPrepWaves + wave;
     if (row >= a.T) return;
     const uint16_t *xr = a.x + row * a.ldx;
     const int64_t K = a.K;
@@ -341,44 +397,80 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_2pass(PrepArgs a
 
 // ---------------------------------------------------------------- streaming tasks
 // Row-split tasks: (row, kStreamChunks chunks).  Normalization statistics
-// come from the NVFP4 pre-pass (stats != nullptr) or there is no norm.
+// come from the NVFP4 pre-pass (stats != nullptr) or there is no norm.  Each
+// wave handles `tpw` consecutive tasks and loads the next task's words before
+// it quantizes the current one.
+template <bool BF16, int NORM>
+__device__ __forceinline__ void stream_load(const PrepArgs &a, int64_t task, int64_t tpr, int lane,
+                                            uint4 raw[kStreamChunks], uint4 graw[kStreamChunks],
+                                            uint4 braw[kStreamChunks]) {
+    constexpr uint32_t kOnePair = BF16 ? 0x3F803F80u : 0x3C003C00u;  // 1.0, 1.0
+    const int64_t row = task / tpr;
+    const int64_t c0 = (task - row * tpr) * kStreamChunks;
+    const uint16_t *xr = a.x + row * a.ldx;
+#pragma unroll
+    for (int c = 0; c < kStreamChunks; c++) {
+        const int64_t e0 = ((c0 + c) * kWave + lane) * 8;
+        raw[c] = e0 < a.K ? *reinterpret_cast<const uint4 *>(xr + e0) : make_uint4(0, 0, 0, 0);
+        if constexpr (NORM != kNormNone) {
+            graw[c] = e0 < a.K ? param_raw<true>(a.gamma, e0, kOnePair) : make_uint4(0, 0, 0, 0);
+            braw[c] = e0 < a.K ? param_raw<NORM == kNormLayer>(a.beta, e0, 0u) : make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
 template <bool BF16, int NORM, int FMT, int M, int FAST24>
-__global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_stream(PrepArgs a, const RowStats *stats) {
+__global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_stream(PrepArgs a, const RowStats *stats,
+                                                                    int64_t tpw) {
     const int lane = threadIdx.x & 63;
     const int64_t K = a.K;
-    const int64_t tasks_per_row = (K + (int64_t)kChunk * kStreamChunks - 1) / ((int64_t)kChunk * kStreamChunks);
-    const int64_t task = xcd_block(blockIdx.x, gridDim.x) * kPrepWaves + (threadIdx.x >> 6);
-    const int64_t row = task / tasks_per_row;
-    if (row >= a.T) return;
-    const int64_t c0 = (task - row * tasks_per_row) * kStreamChunks;
-    const uint16_t *xr = a.x + row * a.ldx;
-    float r = 1.0f, mu = 0.0f, G = 1.0f, G6 = 6.0f;
-    if constexpr (NORM != kNormNone) {
-        r = stats[row].r;
-        mu = stats[row].mu;
-    }
+    const int64_t tpr = (K + (int64_t)kChunk * kStreamChunks - 1) / ((int64_t)kChunk * kStreamChunks);
+    const int64_t ntasks = a.T * tpr;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t0 = (xcd_block(blockIdx.x, gridDim.x) * kPrepWaves + wave) * tpw;
+    const int64_t t_end = t0 + tpw < ntasks ? t0 + tpw : ntasks;
+    if (t0 >= t_end) return;
+    float G = 1.0f, G6 = 6.0f;
     if constexpr (FMT == kFmtNv) {
         G = *a.global_scale;
         G6 = __fmul_rn(6.0f, G);
     }
-    uint4 raw[kStreamChunks];
+    uint4 raw[kStreamChunks], graw[kStreamChunks], braw[kStreamChunks];
+    stream_load<BF16, NORM>(a, t0, tpr, lane, raw, graw, braw);
+    for (int64_t task = t0; task < t_end; task++) {
+        uint4 nraw[kStreamChunks], ngraw[kStreamChunks], nbraw[kStreamChunks];
+        const bool more = task + 1 < t_end;
+        if (more) stream_load<BF16, NORM>(a, task + 1, tpr, lane, nraw, ngraw, nbraw);
+        const int64_t row = task / tpr;
+        const int64_t c0 = (task - row * tpr) * kStreamChunks;
+        float r = 1.0f, mu = 0.0f;
+        if constexpr (NORM != kNormNone) {
+            r = stats[row].r;
+            mu = stats[row].mu;
+        }
 #pragma unroll
-    for (int c = 0; c < kStreamChunks; c++) {
-        const int64_t e0 = ((c0 + c) * kWave + lane) * 8;
-        raw[c] = e0 < K ? *reinterpret_cast<const uint4 *>(xr + e0) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int c = 0; c < kStreamChunks; c++) {
-        const int64_t e0 = ((c0 + c) * kWave + lane) * 8;
-        if (e0 < K) {
-            float v[8], g[8], b[8];
-            unpack8<BF16>(raw[c], v);
-            if constexpr (NORM != kNormNone) {
-                load_param8<BF16, true>(a.gamma, e0, g, 1.0f);
-                load_param8<BF16, NORM == kNormLayer>(a.beta, e0, b, 0.0f);
-                normalize8<NORM>(v, g, b, r, mu);
+        for (int c = 0; c < kStreamChunks; c++) {
+            const int64_t e0 = ((c0 + c) * kWave + lane) * 8;
+            if (e0 < K) {
+                float v[8];
+                unpack8<BF16>(raw[c], v);
+                if constexpr (NORM != kNormNone) {
+                    float g[8], b[8];
+                    unpack8<BF16>(graw[c], g);
+                    unpack8<BF16>(braw[c], b);
+                    normalize8<NORM>(v, g, b, r, mu);
+                }
+                decompose_store<FMT, M, FAST24>(a, row, e0, lane, v, G, G6);
             }
-            decompose_store<FMT, M, FAST24>(a, row, e0, lane, v, G, G6);
+        }
+        if (!more) break;
+#pragma unroll
+        for (int c = 0; c < kStreamChunks; c++) {
+            raw[c] = nraw[c];
+            if constexpr (NORM != kNormNone) {
+                graw[c] = ngraw[c];
+                braw[c] = nbraw[c];
+            }
         }
     }
 }
@@ -466,11 +558,13 @@ static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
     const int64_t K = a.K;
     if constexpr (FMT == kFmtMx && NORM != kNormNone) {
         const dim3 grid((unsigned)round_up8((a.T + kPrepWaves - 1) / kPrepWaves));
-        const dim3 rows((unsigned)round_up8(a.T));
+        // rows per workgroup: about two workgroups per CU once T allows it
+        const int64_t rpw = a.T >= 4 * kPrepRowsGrid ? 4 : (a.T >= 2 * kPrepRowsGrid ? 2 : 1);
+        const dim3 rows((unsigned)round_up8((a.T + rpw - 1) / rpw));
         if (K <= (int64_t)kChunk * kPrepWaves * 2)
-            hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 2>), rows, blk, 0, st, a);
+            hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 2>), rows, blk, 0, st, a, rpw);
         else if (K <= (int64_t)kChunk * kPrepWaves * 4)
-            hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 4>), rows, blk, 0, st, a);
+            hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 4>), rows, blk, 0, st, a, rpw);
         else
             hipLaunchKernelGGL((k_prep_mx_2pass<BF16, NORM, M, FAST24>), grid, blk, 0, st, a);
         if (a.global_scale) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, a.global_scale, 1.0f);
@@ -486,9 +580,12 @@ static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
     }
     const int64_t tasks_per_row = (K + (int64_t)kChunk * kStreamChunks - 1) / ((int64_t)kChunk * kStreamChunks);
     const int64_t tasks = a.T * tasks_per_row;
-    const dim3 grid((unsigned)round_up8((tasks + kPrepWaves - 1) / kPrepWaves));
+    // tasks per wave: enough waves for about four per SIMD, each looping
+    const int64_t tpw = tasks >= 4 * kPrepWavesGrid ? 4 : (tasks >= 2 * kPrepWavesGrid ? 2 : 1);
+    const int64_t waves = (tasks + tpw - 1) / tpw;
+    const dim3 grid((unsigned)round_up8((waves + kPrepWaves - 1) / kPrepWaves));
     if constexpr (FMT == kFmtNv || NORM == kNormNone)
-        hipLaunchKernelGGL((k_prep_stream<BF16, NORM, FMT, M, FAST24>), grid, blk, 0, st, a, stats);
+        hipLaunchKernelGGL((k_prep_stream<BF16, NORM, FMT, M, FAST24>), grid, blk, 0, st, a, stats, tpw);
     return hipGetLastError();
 }
 

@@ -70,8 +70,8 @@ __global__ __launch_bounds__(kQWaves * kWave) void k_quant_w(QuantWArgs a) {
             const uint32_t sb = quant_block8<FMT>(v, G, G6, codes);
             // expert-major; each expert's [nout x K] payload is K-tiled
             const int64_t ex = row / a.nout, n = row - ex * a.nout;
-            *reinterpret_cast<uint32_t *>(a.codes + ex * a.nout * (K / 2) + ktile_offset(n, e0, a.nout, K, 2)) = codes;
-            if ((lane % LPB) == 0) a.scales[ex * a.nout * (K / B) + ktile_offset(n, e0, a.nout, K, B)] = (uint8_t)sb;
+            *reinterpret_cast<uint32_t *>(a.codes + ex * a.nout * (K / 2) + ktile_offset<2>(n, e0, a.nout, K)) = codes;
+            if ((lane % LPB) == 0) a.scales[ex * a.nout * (K / B) + ktile_offset<B>(n, e0, a.nout, K)] = (uint8_t)sb;
         }
     }
 }

@@ -67,6 +67,12 @@ def lib():
         L.or_normalize.argtypes = [p, i32, i64, i64, i64, i32, p, p, i32, f32, p]
         L.or_prepare.argtypes = [p, i32, i64, i64, i64, i32, p, p, i32, f32, i32, i32, i32,
                                  p, i64, p, p, p, p, p, p, p, p, p]
+        L.or_prepare_swiglu.argtypes = [p, i64, i64, i64, i32, i32, i32, p, i64, p, p, p, p, p, p,
+                                        p, p, p]
+        L.or_exp32.argtypes = [f32]
+        L.or_exp32.restype = f32
+        L.or_silu32.argtypes = [f32]
+        L.or_silu32.restype = f32
         L.or_e2m1_encode_n.argtypes = [p, i64, p]
         L.or_e2m1_encode_n.restype = None
         L.or_e4m3_encode_n.argtypes = [p, i64, p]
@@ -74,7 +80,7 @@ def lib():
         L.or_quantize_weight.argtypes = [p, i32, i64, i64, i64, i64, i32, p, p, p]
         L.or_dequant.argtypes = [p, p, i64, i64, i32, f32, p]
         L.or_quantize_rows.argtypes = [p, i32, i64, i64, i32, f32, p, p]
-        for fn in (L.or_normalize, L.or_prepare, L.or_quantize_weight, L.or_dequant,
+        for fn in (L.or_normalize, L.or_prepare, L.or_prepare_swiglu, L.or_quantize_weight, L.or_dequant,
                    L.or_quantize_rows):
             fn.restype = i32
         _lib = L
@@ -187,6 +193,35 @@ def prepare(x: np.ndarray, dtype: str, K: int, norm: int, gamma: Optional[np.nda
                           _ptr(out.xhat), _ptr(out.deqb), _ptr(out.resid))
     _check(rc, "prepare")
     return out
+
+
+def prepare_swiglu(gu: np.ndarray, K: int, n: int, m: int, fmt: int,
+                   rows: Optional[np.ndarray] = None, trace: bool = False) -> Prepared:
+    """Prepare SiLU(gate) * up from float32 rows [gate (K) | up (K) | ...]
+    (the gate/up product's output), with no normalization."""
+    gu = np.ascontiguousarray(gu, dtype=np.float32)
+    T, ld = gu.shape
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nr = T if r is None else r.size
+    out = Prepared(nr, K, fmt)
+    if trace:
+        out.xhat = np.zeros((nr, K), np.float32)
+        out.deqb = np.zeros((nr, K), np.float32)
+        out.resid = np.zeros((nr, K), np.float32)
+    rc = lib().or_prepare_swiglu(_ptr(gu), T, K, ld, n, m, fmt, _ptr(r), nr, _ptr(out.mask),
+                                 _ptr(out.b_codes), _ptr(out.b_scales), _ptr(out.r_codes),
+                                 _ptr(out.r_scales), _ptr(out.gscale), _ptr(out.xhat), _ptr(out.deqb),
+                                 _ptr(out.resid))
+    _check(rc, "prepare_swiglu")
+    return out
+
+
+def exp32(y: float) -> float:
+    return float(lib().or_exp32(float(y)))
+
+
+def silu32(g: float) -> float:
+    return float(lib().or_silu32(float(g)))
 
 
 def normalize(x: np.ndarray, dtype: str, K: int, norm: int, gamma, beta, eps: float) -> np.ndarray:

@@ -299,6 +299,66 @@ static int check_shape(int64_t K, int N, int M, int fmt)
     return OR_OK;
 }
 
+/* One prepared row i from its normalized values xh[K]: mask, backbone
+ * S = mask ? xh : +0 quantized, residual R = xh - deq(Q(S)) quantized
+ * (scratch S, dq, R, keep are K long; traces nullable). */
+static void decompose_row(const float *xh, int64_t K, int N, int M, int fmt, float G, int64_t i,
+                          float *S, float *dq, float *R, uint8_t *keep, uint8_t *mask,
+                          uint8_t *b_codes, uint8_t *b_scales, uint8_t *r_codes, uint8_t *r_scales,
+                          float *xhat_out, float *deqb_out, float *resid_out)
+{
+    int B = fmt == OR_FMT_MXFP4 ? 32 : 16;
+    /* mask and backbone */
+    for (int64_t g0 = 0; g0 < K; g0 += M) or_select_group(xh + g0, M, N, keep + g0);
+    for (int64_t k = 0; k < K; k++) S[k] = keep[k] ? xh[k] : 0.0f;
+    if (mask) {
+        uint8_t *mrow = mask + i * (K / 8);
+        for (int64_t j = 0; j < K / 8; j++) mrow[j] = 0;
+        for (int64_t k = 0; k < K; k++)
+            if (keep[k]) mrow[k / 8] |= (uint8_t)(1u << (k % 8));
+    }
+    quantize_row(S, K, fmt, G, b_codes + i * (K / 2), b_scales + i * (K / B), dq);
+    /* residual against the dequantized backbone */
+    for (int64_t k = 0; k < K; k++) R[k] = xh[k] - dq[k];
+    if (xhat_out) memcpy(xhat_out + i * K, xh, sizeof(float) * K);
+    if (deqb_out) memcpy(deqb_out + i * K, dq, sizeof(float) * K);
+    if (resid_out) memcpy(resid_out + i * K, R, sizeof(float) * K);
+    quantize_row(R, K, fmt, G, r_codes + i * (K / 2), r_scales + i * (K / B), NULL);
+}
+
+/* ------------------------------------------------------------------ */
+/* SiLU(gate) * up (the activation feeding a down projection)          */
+/* ------------------------------------------------------------------ */
+
+/* e^y in float, as a fixed sequence of correctly rounded float operations
+ * (so any IEEE implementation of the same steps gives the same bits):
+ * Cody-Waite reduction y = n ln2 + r with n = rint(y log2 e) and ln2 split
+ * into a 15-bit head and a tail, e^r by its degree-6 Taylor polynomial in
+ * Horner form, then scaling by 2^n.  Defined as 0 below -87 (so results are
+ * never subnormal) and +inf above 88.  About 2 ulp from the true e^y. */
+float or_exp32(float y)
+{
+    if (!(y <= 88.0f)) return INFINITY;
+    if (y < -87.0f) return 0.0f;
+    float n = nearbyintf(y * 1.44269504f);
+    float r = (y - n * 0.693145752f) - n * 1.42860677e-6f;
+    float p = 0.00138888889f;          /* 1/720 */
+    p = p * r + 0.00833333333f;        /* 1/120 */
+    p = p * r + 0.0416666667f;         /* 1/24 */
+    p = p * r + 0.166666667f;          /* 1/6 */
+    p = p * r + 0.5f;
+    p = p * r + 1.0f;
+    p = p * r + 1.0f;
+    return ldexpf(p, (int)n);
+}
+
+/* SiLU(g) = g / (1 + e^-g), each step rounded to float. */
+float or_silu32(float g)
+{
+    float d = 1.0f + or_exp32(-g);
+    return g / d;
+}
+
 /* ------------------------------------------------------------------ */
 /* public entry points                                                 */
 /* ------------------------------------------------------------------ */
@@ -341,7 +401,6 @@ int or_prepare(const void *x, int xdt, int64_t T, int64_t K, int64_t ldx, int no
                float *xhat_out, float *deqb_out, float *resid_out)
 {
     if (check_shape(K, N, M, fmt) != OR_OK || T < 0 || ldx < K) return OR_EINVAL;
-    int B = fmt == OR_FMT_MXFP4 ? 32 : 16;
     float *row = malloc(sizeof(float) * K), *xh = malloc(sizeof(float) * K),
           *g = malloc(sizeof(float) * K), *bt = malloc(sizeof(float) * K),
           *S = malloc(sizeof(float) * K), *dq = malloc(sizeof(float) * K),
@@ -373,22 +432,8 @@ int or_prepare(const void *x, int xdt, int64_t T, int64_t K, int64_t ldx, int no
         if (t < 0 || t >= T) { rc = OR_EINVAL; goto out; }
         for (int64_t k = 0; k < K; k++) row[k] = load_elem(x, xdt, t * ldx + k);
         normalize_row(row, K, norm, g, beta ? bt : NULL, eps, xh);
-        /* mask and backbone */
-        for (int64_t g0 = 0; g0 < K; g0 += M) or_select_group(xh + g0, M, N, keep + g0);
-        for (int64_t k = 0; k < K; k++) S[k] = keep[k] ? xh[k] : 0.0f;
-        if (mask) {
-            uint8_t *mrow = mask + i * (K / 8);
-            memset(mrow, 0, K / 8);
-            for (int64_t k = 0; k < K; k++)
-                if (keep[k]) mrow[k / 8] |= (uint8_t)(1u << (k % 8));
-        }
-        quantize_row(S, K, fmt, G, b_codes + i * (K / 2), b_scales + i * (K / B), dq);
-        /* residual against the dequantized backbone */
-        for (int64_t k = 0; k < K; k++) R[k] = xh[k] - dq[k];
-        if (xhat_out) memcpy(xhat_out + i * K, xh, sizeof(float) * K);
-        if (deqb_out) memcpy(deqb_out + i * K, dq, sizeof(float) * K);
-        if (resid_out) memcpy(resid_out + i * K, R, sizeof(float) * K);
-        quantize_row(R, K, fmt, G, r_codes + i * (K / 2), r_scales + i * (K / B), NULL);
+        decompose_row(xh, K, N, M, fmt, G, i, S, dq, R, keep, mask, b_codes, b_scales, r_codes,
+                      r_scales, xhat_out, deqb_out, resid_out);
     }
 out:
     free(row); free(xh); free(g); free(bt); free(S); free(dq); free(R); free(keep);
@@ -465,4 +510,47 @@ int or_dequant(const uint8_t *codes, const uint8_t *scales, int64_t nrows, int64
             out[r * K + k] = v;
         }
     return OR_OK;
+}
+
+/*
+ * Prepare the input of a down projection straight from the gate/up product:
+ * row t of GU (row stride ld floats) holds the gate in columns [0, K) and
+ * the up projection in [K, 2K); the activation is
+ *   xhat[k] = fl32(SiLU(gate[k]) * up[k])   (no normalization)
+ * and the rest is exactly or_prepare's (mask, backbone, residual, NVFP4
+ * tensor scale over all T rows).  Same outputs and traces as or_prepare.
+ */
+int or_prepare_swiglu(const float *gu, int64_t T, int64_t K, int64_t ld, int N, int M, int fmt,
+                      const int64_t *rows, int64_t nrows, uint8_t *mask, uint8_t *b_codes,
+                      uint8_t *b_scales, uint8_t *r_codes, uint8_t *r_scales, float *gscale,
+                      float *xhat_out, float *deqb_out, float *resid_out)
+{
+    if (check_shape(K, N, M, fmt) != OR_OK || T < 0 || ld < 2 * K) return OR_EINVAL;
+    float *xh = malloc(sizeof(float) * K), *S = malloc(sizeof(float) * K),
+          *dq = malloc(sizeof(float) * K), *R = malloc(sizeof(float) * K);
+    uint8_t *keep = malloc(K);
+    int rc = OR_OK;
+    if (!xh || !S || !dq || !R || !keep) { rc = OR_ENOMEM; goto out; }
+    float G = 1.0f;
+    if (fmt == OR_FMT_NVFP4) {
+        float amax = 0.0f;
+        for (int64_t t = 0; t < T; t++)
+            for (int64_t k = 0; k < K; k++) {
+                float v = or_silu32(gu[t * ld + k]) * gu[t * ld + K + k];
+                if (fabsf(v) > amax) amax = fabsf(v);
+            }
+        G = or_nv_global_scale(amax);
+    }
+    if (gscale) *gscale = G;
+    int64_t nr = rows ? nrows : T;
+    for (int64_t i = 0; i < nr; i++) {
+        int64_t t = rows ? rows[i] : i;
+        if (t < 0 || t >= T) { rc = OR_EINVAL; goto out; }
+        for (int64_t k = 0; k < K; k++) xh[k] = or_silu32(gu[t * ld + k]) * gu[t * ld + K + k];
+        decompose_row(xh, K, N, M, fmt, G, i, S, dq, R, keep, mask, b_codes, b_scales, r_codes,
+                      r_scales, xhat_out, deqb_out, resid_out);
+    }
+out:
+    free(xh); free(S); free(dq); free(R); free(keep);
+    return rc;
 }

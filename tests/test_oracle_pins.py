@@ -454,3 +454,63 @@ def test_grouped_linear_matches_per_expert():
                 getattr(sub, key)[:] = getattr(p, key)[ridx[r]]
             sub.gscale[:] = p.gscale
             assert np.array_equal(y[r], oracle.linear(sub, wq, expert=e)[0])
+
+
+# ---------------------------------------------------------------- SiLU(gate) * up
+# The down projection's input is SiLU(gate) * up; its fused preparation is
+# defined with a float exponential built from fixed IEEE steps (so the GPU and
+# the oracle can reproduce it bit for bit).  Pins: the mathematics of exp and
+# SiLU within a few ulp, and the column convention of the gate/up rows.
+
+def _ulp(v: float) -> float:
+    return float(np.spacing(np.float32(abs(v)))) if v != 0 else float(np.finfo(np.float32).smallest_subnormal)
+
+
+def test_exp32_against_the_exponential():
+    ys = np.concatenate([np.linspace(-87.0, 88.0, 20001, dtype=np.float32),
+                         np.array([0.0, 1e-30, -1e-30, 0.5, -0.5, 1.0, -1.0, 20.0, -20.0], np.float32)])
+    for y in ys:
+        got, ref = oracle.exp32(float(y)), math.exp(float(y))
+        assert abs(got - ref) <= 4 * _ulp(ref), (float(y), got, ref)
+    assert oracle.exp32(0.0) == 1.0
+    assert oracle.exp32(-87.5) == 0.0 and math.isinf(oracle.exp32(88.5))
+
+
+def test_silu32_against_its_definition():
+    for g in np.linspace(-40.0, 40.0, 8001, dtype=np.float32):
+        got, ref = oracle.silu32(float(g)), float(g) / (1.0 + math.exp(-float(g)))
+        assert abs(got - ref) <= 4 * _ulp(ref) + 1e-37, (float(g), got, ref)
+    assert oracle.silu32(0.0) == 0.0
+    assert oracle.silu32(100.0) == 100.0                       # e^-100 is below the range: exactly g
+    assert oracle.silu32(-100.0) == 0.0 and math.copysign(1.0, oracle.silu32(-100.0)) < 0  # g / inf = -0
+
+
+@pytest.mark.parametrize("fmt", [oracle.FMT_MXFP4, oracle.FMT_NVFP4])
+def test_prepare_swiglu_is_prepare_of_the_product(fmt):
+    rng = np.random.default_rng(5 + fmt)
+    T, K, ld = 6, 256, 2 * 256 + 32
+    gu = (rng.standard_normal((T, ld)) * 3.0).astype(np.float32)
+    gu[:, 7] *= 20.0
+    x = np.empty((T, K), np.float32)
+    for t in range(T):
+        for k in range(K):
+            x[t, k] = np.float32(oracle.silu32(float(gu[t, k]))) * gu[t, K + k]
+    a = oracle.prepare_swiglu(gu, K, 2, 4, fmt, trace=True)
+    b = oracle.prepare(x, "f32", K, oracle.NORM_NONE, None, None, 0.0, 2, 4, fmt)
+    assert np.array_equal(a.xhat.view(np.uint32), x.view(np.uint32))
+    for key in ("mask", "b_codes", "b_scales", "r_codes", "r_scales", "gscale"):
+        assert np.array_equal(getattr(a, key), getattr(b, key)), key
+
+
+def test_prepare_swiglu_column_convention():
+    """gate = 100 gives SiLU = 100 exactly, gate = 0 gives 0: the activation
+    is 100*up and 0*up; swapping gate and up would change both."""
+    K = 64
+    up = np.linspace(-3.0, 3.0, K, dtype=np.float32)
+    gu = np.zeros((2, 2 * K), np.float32)
+    gu[0, :K] = 100.0
+    gu[0, K:] = up
+    gu[1, K:] = up
+    a = oracle.prepare_swiglu(gu, K, 2, 4, oracle.FMT_MXFP4, trace=True)
+    assert np.array_equal(a.xhat[0], np.float32(100.0) * up)
+    assert np.array_equal(a.xhat[1].view(np.uint32), (np.float32(0.0) * up).view(np.uint32))

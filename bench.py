@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--workload", default="llama")
     ap.add_argument("--rotate", type=int, default=3, help="copies of every input rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the fused SiLU(gate)*up prep and the bf16 / fp8 GEMM comparisons")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter calibration)")
     return ap.parse_args()
@@ -246,6 +248,86 @@ def error_report(layers):
     return out
 
 
+def _event_ms(torch, fn, reps=20):
+    """Mean time of fn() over reps launches on the current stream (HIP events)."""
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def swiglu_report(sq, torch, wl, layers):
+    """The down projection's prep from the gate/up product's float32 output:
+    fused (SiLU(gate)*up computed inside the prep kernel) against an unfused
+    chain (torch SiLU*up to a bf16 tensor, then the bf16 prep)."""
+    gu_layer = next((L for L in layers if L.lin.name == "gate_up"), None)
+    down = next((L for L in layers if L.lin.name == "down"), None)
+    if gu_layer is None or down is None or gu_layer.rows != down.prep_tokens:
+        return None
+    Ys = gu_layer.y                     # rotated copies, so the Infinity Cache cannot hold the input
+    T, K = Ys[0].shape[0], Ys[0].shape[1] // 2
+    out = sq.alloc_prepared(T, K, wl.fmt, Ys[0].device)
+    it = [0]
+
+    def nxt():
+        it[0] += 1
+        return Ys[it[0] % len(Ys)]
+
+    fused = _event_ms(torch, lambda: sq.prepare_swiglu(nxt(), K, n=wl.n, m=wl.m, fmt=wl.fmt, out=out))
+    act = torch.empty((T, K), dtype=torch.bfloat16, device=Ys[0].device)
+
+    def unfused_chain():
+        Y = nxt()
+        act.copy_(torch.nn.functional.silu(Y[:, :K]) * Y[:, K:])
+        sq.prepare(act, norm=0, n=wl.n, m=wl.m, fmt=wl.fmt, out=out)
+
+    chain = _event_ms(torch, unfused_chain)
+    B = block_of(wl.fmt)
+    algo = T * (8 * K + K + 2 * K // B + K // 8)   # read gate and up (f32), write the prepared tensors
+    return {"rows": T, "K": K, "fused_us": round(fused * 1e3, 2), "fused_GBps": round(algo / (fused * 1e-3) / 1e9, 1),
+            "unfused_torch_silu_bf16_then_prep_us": round(chain * 1e3, 2),
+            "speedup": round(chain / fused, 3),
+            "bytes_note": "fused algorithmic bytes = read 2K f32 + write codes, scales, mask"}
+
+
+def gemm_baselines(torch, synth, wl, layers, sharq_ms):
+    """The same linears as plain bf16 GEMMs (torch.matmul, hipBLASLt) and as
+    per-tensor-scaled FP8 e4m3 GEMMs (torch._scaled_mm), activation
+    quantization not included; times next to SharQ's prep + product."""
+    if wl.experts > 1:
+        return None
+    res = {}
+    tot = {"bf16": 0.0, "fp8": 0.0}
+    for L in layers:
+        w = torch.from_numpy(np.ascontiguousarray(L.w_host[0]).view(np.int16)).view(torch.bfloat16).to(L.x[0].device)
+        x = L.x[0]
+        bf = _event_ms(torch, lambda: torch.matmul(x, w.t()))
+        r = {"bf16_us": round(bf * 1e3, 2)}
+        tot["bf16"] += bf
+        try:
+            f8 = torch.float8_e4m3fn
+            xq, wq = x.to(f8), w.to(f8)
+            one = torch.ones((), dtype=torch.float32, device=x.device)
+            fp8 = _event_ms(torch, lambda: torch._scaled_mm(xq, wq.t(), scale_a=one, scale_b=one,
+                                                            out_dtype=torch.bfloat16))
+            r["fp8_us"] = round(fp8 * 1e3, 2)
+            tot["fp8"] += fp8
+        except Exception as e:  # no FP8 GEMM in this torch build
+            r["fp8_error"] = str(e)[:120]
+            tot["fp8"] = None
+        res[L.lin.name] = r
+        del w
+    res["total_us"] = {"sharq_prep_plus_product": round(sharq_ms * 1e3, 2),
+                       "bf16_gemm": round(tot["bf16"] * 1e3, 2),
+                       "fp8_gemm": None if tot["fp8"] is None else round(tot["fp8"] * 1e3, 2)}
+    return res
+
+
 def build_layers(args, sq, torch, synth, dev):
     if args.workload == "llama":
         wl = synth.WORKLOADS[1]
@@ -362,6 +444,9 @@ def main():
     }
     if nv:
         result["roofline"]["frac_of_bf16_peak"] = round(gemm_tflops / BF16_PEAK_TFLOPS, 4)
+    if not args.no_extras:
+        result["swiglu_prep"] = swiglu_report(sq, torch, wl, layers)
+        result["gemm_baselines"] = gemm_baselines(torch, synth, wl, layers, sum(prep_ms) + sum(gemm_ms))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layers)
         result["error_report"] = error_report(layers)

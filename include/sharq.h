@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 2
+#define SHARQ_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define SHARQ_API __attribute__((visibility("default")))
@@ -129,6 +129,32 @@ SHARQ_API sharq_status sharq_prepare(const void *x, int32_t x_dtype, int64_t T, 
                            uint8_t *b_scales, uint8_t *r_codes, uint8_t *r_scales,
                            float *global_scale, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/*
+ * sharq_prepare_swiglu -- the same fused preparation for the input of a
+ * down projection, computed straight from the gate/up product's FP32 output
+ * instead of a stored bf16 activation (SharQ: Bridging Activation Sparsity
+ * and FP4 Quantization for LLM Inference, Abstract: the fused preparation
+ * absorbs the element-wise work around the linear layer; the down input of a
+ * SwiGLU MLP is SiLU(gate) * up).  Per row t, for k < K:
+ *   xhat[k] = fl32(SiLU(gate[k]) * up[k]),  SiLU(g) = fl32(g / fl32(1 + e^-g))
+ * with e^y a fixed sequence of correctly rounded float operations: Cody-Waite
+ * reduction y = n*ln2 + r (n = rint(fl32(y*1.44269504)), ln2 split as
+ * 0.693145752 + 1.42860677e-6), the degree-6 Taylor polynomial of e^r in
+ * Horner form, times 2^n; 0 for y < -87, +inf for y > 88.  No
+ * normalization; mask, backbone, residual and NVFP4 tensor scale exactly as
+ * sharq_prepare.
+ *
+ *   gate_up      [T][ld] FP32, gate in columns [0, K), up in [K, 2K);
+ *                16-byte aligned, ld >= 2K, ld*4 % 16 == 0
+ *   other arguments and outputs as sharq_prepare (workspace:
+ *   sharq_prepare_workspace_size())
+ */
+SHARQ_API sharq_status sharq_prepare_swiglu(const float *gate_up, int64_t T, int64_t K, int64_t ld,
+                                  int32_t n, int32_t m, int32_t fmt, uint8_t *mask,
+                                  uint8_t *b_codes, uint8_t *b_scales, uint8_t *r_codes,
+                                  uint8_t *r_scales, float *global_scale, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace sharq_quantize_weight needs. */
 SHARQ_API size_t sharq_quantize_weight_workspace_size(int64_t experts, int64_t nout, int64_t K, int32_t fmt);

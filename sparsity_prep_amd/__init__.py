@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.sharq_prepare.argtypes = [p, i32, i64, i64, i64, i32, p, p, f32, i32, i32, i32,
                                     p, p, p, p, p, p, p, sz, p]
         L.sharq_prepare.restype = ctypes.c_int
+        L.sharq_prepare_swiglu.argtypes = [p, i64, i64, i64, i32, i32, i32, p, p, p, p, p, p, p, sz, p]
+        L.sharq_prepare_swiglu.restype = ctypes.c_int
         L.sharq_quantize_weight_workspace_size.argtypes = [i64, i64, i64, i32]
         L.sharq_quantize_weight_workspace_size.restype = sz
         L.sharq_quantize_weight.argtypes = [p, i32, i64, i64, i64, i32, p, p, p, p, sz, p]
@@ -142,6 +144,25 @@ def prepare(x: torch.Tensor, norm: int = NORM_RMS, gamma: Optional[torch.Tensor]
         _ptr(out.r_scales), _ptr(out.global_scale), _ptr(ws), 0 if ws is None else ws.numel(),
         _stream(x.device))
     _check(st, "sharq_prepare")
+    return out
+
+
+def prepare_swiglu(gate_up: torch.Tensor, K: int, n: int = 2, m: int = 4, fmt: int = MXFP4,
+                   with_mask: bool = True, out: Optional[Prepared] = None) -> Prepared:
+    """Fused SiLU(gate) * up -> N:M mask -> FP4 backbone -> residual -> FP4
+    residual, from float32 rows [gate (K) | up (K) | ...] (the gate/up
+    product's output)."""
+    if gate_up.dim() != 2 or gate_up.dtype != torch.float32 or gate_up.stride(1) != 1:
+        raise SharqError("gate_up must be a 2-D row-major float32 tensor")
+    T = gate_up.shape[0]
+    if out is None:
+        out = alloc_prepared(T, K, fmt, gate_up.device, with_mask)
+    ws = _workspace(lib().sharq_prepare_workspace_size(T, K, fmt), gate_up.device)
+    st = lib().sharq_prepare_swiglu(
+        _ptr(gate_up), T, K, gate_up.stride(0), n, m, fmt, _ptr(out.mask), _ptr(out.b_codes),
+        _ptr(out.b_scales), _ptr(out.r_codes), _ptr(out.r_scales), _ptr(out.global_scale), _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(gate_up.device))
+    _check(st, "sharq_prepare_swiglu")
     return out
 
 

@@ -70,7 +70,7 @@ sharq_status sharq_prepare(const void *x, int32_t x_dtype, int64_t T, int64_t K,
     if (need > 0 && (!workspace || workspace_bytes < need)) return SHARQ_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace, 16)) return SHARQ_ERR_ALIGN;
 
-    PrepArgs a;
+    PrepArgs a{};
     a.x = static_cast<const uint16_t *>(x);
     a.T = T;
     a.K = K;
@@ -91,6 +91,43 @@ sharq_status sharq_prepare(const void *x, int32_t x_dtype, int64_t T, int64_t K,
     a.global_scale = global_scale;
     a.off32 = K % 128 == 0 && T * (K / 2) < ((int64_t)1 << 32);
     return hip_status(launch_prepare(a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+sharq_status sharq_prepare_swiglu(const float *gate_up, int64_t T, int64_t K, int64_t ld, int32_t n, int32_t m,
+                                  int32_t fmt, uint8_t *mask, uint8_t *b_codes, uint8_t *b_scales,
+                                  uint8_t *r_codes, uint8_t *r_scales, float *global_scale, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    if (!valid_fmt(fmt)) return SHARQ_ERR_UNSUPPORTED;
+    if (T < 0 || K <= 0 || ld < 2 * K || K % block_of(fmt) != 0) return SHARQ_ERR_SHAPE;
+    if (m != 1 && m != 2 && m != 4 && m != 8 && m != 16) return SHARQ_ERR_NM;
+    if (n < 0 || n > m || K % m != 0) return SHARQ_ERR_NM;
+    if (T == 0) return SHARQ_OK;
+    if (!gate_up || !b_codes || !b_scales || !r_codes || !r_scales) return SHARQ_ERR_NULL;
+    if (fmt == SHARQ_NVFP4 && !global_scale) return SHARQ_ERR_NULL;
+    if (!aligned(gate_up, 16) || (ld * 4) % 16 != 0) return SHARQ_ERR_ALIGN;
+    if (!aligned(b_codes, 4) || !aligned(r_codes, 4)) return SHARQ_ERR_ALIGN;
+    if (global_scale && !aligned(global_scale, 4)) return SHARQ_ERR_ALIGN;
+    const size_t need = prepare_workspace_bytes(T, fmt);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return SHARQ_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 16)) return SHARQ_ERR_ALIGN;
+
+    PrepArgs a{};
+    a.T = T;
+    a.K = K;
+    a.n = n;
+    a.m = m;
+    a.norm = SHARQ_NORM_NONE;
+    a.fmt = fmt;
+    a.mask = mask;
+    a.b_codes = b_codes;
+    a.b_scales = b_scales;
+    a.r_codes = r_codes;
+    a.r_scales = r_scales;
+    a.global_scale = global_scale;
+    a.off32 = K % 128 == 0 && T * (K / 2) < ((int64_t)1 << 32);
+    a.gu = gate_up;
+    a.ldgu = ld;
+    return hip_status(launch_prepare_swiglu(a, workspace, static_cast<hipStream_t>(stream)));
 }
 
 size_t sharq_quantize_weight_workspace_size(int64_t experts, int64_t nout, int64_t K, int32_t fmt) {

@@ -39,9 +39,14 @@ struct PrepArgs {
     uint8_t *mask, *b_codes, *b_scales, *r_codes, *r_scales;
     float *global_scale;
     bool off32;  // K % 128 == 0 and T*K/2 < 2^32: 32-bit K-tiled offsets
+    // SiLU(gate)*up source (sharq_prepare_swiglu): rows of gu with stride ldgu
+    // floats, gate in [0, K), up in [K, 2K); x is unused then
+    const float *gu;
+    int64_t ldgu;
 };
 
 hipError_t launch_prepare(const PrepArgs &a, void *ws, hipStream_t st);
+hipError_t launch_prepare_swiglu(const PrepArgs &a, void *ws, hipStream_t st);
 size_t prepare_workspace_bytes(int64_t T, int fmt);
 
 struct QuantWArgs {

@@ -475,6 +475,90 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_stream(PrepArgs a, 
     }
 }
 
+// ---------------------------------------------------------------- SiLU(gate) * up source
+// The activation of a down projection computed from the gate/up product's
+// float rows: x = fl32(SiLU(gate) * up), SiLU(g) = g / (1 + e^-g), with e^y
+// evaluated by fixed correctly rounded float steps: Cody-Waite reduction
+// y = n ln2 + r (n = rint(y log2 e), ln2 as a 15-bit head plus a tail), the
+// degree-6 Taylor polynomial of e^r in Horner form, scaling by 2^n; 0 below
+// -87 (never subnormal), +inf above 88.
+__device__ __forceinline__ float exp32_fixed(float y) {
+    if (!(y <= 88.0f)) return __builtin_inff();
+    if (y < -87.0f) return 0.0f;
+    const float n = __builtin_rintf(__fmul_rn(y, 1.44269504f));
+    const float r = __fsub_rn(__fsub_rn(y, __fmul_rn(n, 0.693145752f)), __fmul_rn(n, 1.42860677e-6f));
+    float p = 0.00138888889f;                      // 1/720
+    p = __fadd_rn(__fmul_rn(p, r), 0.00833333333f);  // 1/120
+    p = __fadd_rn(__fmul_rn(p, r), 0.0416666667f);   // 1/24
+    p = __fadd_rn(__fmul_rn(p, r), 0.166666667f);    // 1/6
+    p = __fadd_rn(__fmul_rn(p, r), 0.5f);
+    p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+    p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+    return __builtin_ldexpf(p, (int)n);
+}
+
+__device__ __forceinline__ float silu_times(float g, float u) {
+    const float d = __fadd_rn(1.0f, exp32_fixed(-g));
+    return __fmul_rn(__fdiv_rn(g, d), u);
+}
+
+// Eight activations at element e0 of a row from its gate and up words.
+__device__ __forceinline__ void swiglu8(const float *row, int64_t K, int64_t e0, float v[8]) {
+    const float4 g0 = *reinterpret_cast<const float4 *>(row + e0);
+    const float4 g1 = *reinterpret_cast<const float4 *>(row + e0 + 4);
+    const float4 u0 = *reinterpret_cast<const float4 *>(row + K + e0);
+    const float4 u1 = *reinterpret_cast<const float4 *>(row + K + e0 + 4);
+    v[0] = silu_times(g0.x, u0.x); v[1] = silu_times(g0.y, u0.y);
+    v[2] = silu_times(g0.z, u0.z); v[3] = silu_times(g0.w, u0.w);
+    v[4] = silu_times(g1.x, u1.x); v[5] = silu_times(g1.y, u1.y);
+    v[6] = silu_times(g1.z, u1.z); v[7] = silu_times(g1.w, u1.w);
+}
+
+// (row, kStreamChunks chunks) tasks, one per wave.
+template <int FMT, int M, int FAST24>
+__global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_swiglu(PrepArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t K = a.K;
+    const int64_t tpr = (K + (int64_t)kChunk * kStreamChunks - 1) / ((int64_t)kChunk * kStreamChunks);
+    const int64_t task = xcd_block(blockIdx.x, gridDim.x) * kPrepWaves + wave;
+    const int64_t row = task / tpr;
+    if (row >= a.T) return;
+    const int64_t c0 = (task - row * tpr) * kStreamChunks;
+    const float *gr = a.gu + row * a.ldgu;
+    float G = 1.0f, G6 = 6.0f;
+    if constexpr (FMT == kFmtNv) {
+        G = *a.global_scale;
+        G6 = __fmul_rn(6.0f, G);
+    }
+#pragma unroll
+    for (int c = 0; c < kStreamChunks; c++) {
+        const int64_t e0 = ((c0 + c) * kWave + lane) * 8;
+        if (e0 < K) {
+            float v[8];
+            swiglu8(gr, K, e0, v);
+            decompose_store<FMT, M, FAST24>(a, row, e0, lane, v, G, G6);
+        }
+    }
+}
+
+// NVFP4: per-row amax of the activation (stats[row].amax; r = 1, mu = 0).
+__global__ __launch_bounds__(kPrepWaves * kWave) void k_swiglu_rowstats(PrepArgs a, RowStats *stats) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kPrepWaves + (threadIdx.x >> 6);
+    if (row >= a.T) return;
+    const float *gr = a.gu + row * a.ldgu;
+    float m = 0.0f, v[8];
+    for (int64_t e0 = (int64_t)lane * 8; e0 < a.K; e0 += kChunk) {
+        swiglu8(gr, a.K, e0, v);
+#pragma unroll
+        for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    if (lane == 0) stats[row] = RowStats{1.0f, 0.0f, m, 0.0f};
+}
+
 // ---------------------------------------------------------------- NVFP4 pre-pass
 // Per row: norm statistics and amax of the normalized row.
 template <bool BF16, int NORM>
@@ -616,6 +700,42 @@ static hipError_t launch_prep_n(const PrepArgs &a, void *ws, hipStream_t st) {
         case kNormLayer: return launch_prep_f<BF16, kNormLayer>(a, ws, st);
     }
     return hipErrorInvalidValue;
+}
+
+template <int FMT, int M, int FAST24>
+static hipError_t launch_swiglu_t(const PrepArgs &a, void *ws, hipStream_t st) {
+    const dim3 blk(kPrepWaves * kWave);
+    if constexpr (FMT == kFmtNv) {
+        RowStats *stats = reinterpret_cast<RowStats *>(ws);
+        hipLaunchKernelGGL(k_swiglu_rowstats, dim3((unsigned)((a.T + kPrepWaves - 1) / kPrepWaves)), blk, 0, st, a,
+                           stats);
+        hipLaunchKernelGGL(k_nv_tensor_scale, dim3(1), dim3(1024), 0, st, stats, a.T, a.global_scale);
+    } else if (a.global_scale) {
+        hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, a.global_scale, 1.0f);
+    }
+    const int64_t tpr = (a.K + (int64_t)kChunk * kStreamChunks - 1) / ((int64_t)kChunk * kStreamChunks);
+    const int64_t tasks = a.T * tpr;
+    const dim3 grid((unsigned)round_up8((tasks + kPrepWaves - 1) / kPrepWaves));
+    hipLaunchKernelGGL((k_prep_swiglu<FMT, M, FAST24>), grid, blk, 0, st, a);
+    return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_swiglu_m(const PrepArgs &a, void *ws, hipStream_t st) {
+    if (a.m == 4 && a.n == 2) return launch_swiglu_t<FMT, 4, 1>(a, ws, st);
+    switch (a.m) {
+        case 1: return launch_swiglu_t<FMT, 1, 0>(a, ws, st);
+        case 2: return launch_swiglu_t<FMT, 2, 0>(a, ws, st);
+        case 4: return launch_swiglu_t<FMT, 4, 0>(a, ws, st);
+        case 8: return launch_swiglu_t<FMT, 8, 0>(a, ws, st);
+        case 16: return launch_swiglu_t<FMT, 16, 0>(a, ws, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prepare_swiglu(const PrepArgs &a, void *ws, hipStream_t st) {
+    if (a.T == 0) return hipSuccess;
+    return a.fmt == kFmtMx ? launch_swiglu_m<kFmtMx>(a, ws, st) : launch_swiglu_m<kFmtNv>(a, ws, st);
 }
 
 hipError_t launch_prepare(const PrepArgs &a, void *ws, hipStream_t st) {

@@ -229,3 +229,18 @@ def uniform_bits_f32(n: int, seed: int = 0) -> np.ndarray:
     exp = (u >> np.uint32(23)) & np.uint32(0xFF)
     u = np.where(exp == 0xFF, u & np.uint32(0x807FFFFF), u)
     return u.view(np.float32)
+
+
+def small_gate_up(k: int, tokens: int, ld: Optional[int] = None, seed: int = 0, outliers: int = 4,
+                  mult: float = 20.0, tag: int = 0) -> np.ndarray:
+    """Float32 rows [gate (k) | up (k) | padding] shaped like a gate/up
+    product's output: N(0, 3^2) gates, N(0, 1) ups, a few up channels scaled
+    up as outliers."""
+    ld = 2 * k if ld is None else ld
+    rng = _rng(seed, 5000 + tag, k, tokens)
+    gu = rng.standard_normal((tokens, ld), dtype=np.float32)
+    gu[:, :k] *= np.float32(3.0)
+    if outliers:
+        ch = rng.choice(k, size=min(outliers, k), replace=False)
+        gu[:, k + ch] *= np.float32(mult)
+    return gu

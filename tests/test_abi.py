@@ -34,7 +34,7 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     names = declared_symbols()
-    for n in ("sharq_prepare", "sharq_linear", "sharq_quantize_weight"):
+    for n in ("sharq_prepare", "sharq_prepare_swiglu", "sharq_linear", "sharq_quantize_weight"):
         assert n in names
 
 
@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.sharq_abi_version() == 2
+    assert L.sharq_abi_version() == 3
     for code in range(9):
         assert L.sharq_status_string(code)
     assert L.sharq_status_string(99) == b"unknown status"
@@ -83,6 +83,29 @@ def test_prepare_validation(L):
     assert prep(L, fmt=NV, G=FAKE) == WORKSPACE
     assert prep(L, fmt=NV, G=FAKE, ws=FAKE, wsb=1) == WORKSPACE
     assert prep(L, T=0, x=None) == OK              # empty tensor is a no-op, no HIP call
+
+
+def swiglu(L, gu=FAKE, T=4, K=256, ld=None, n=2, m=4, fmt=MX, bc=FAKE, G=None, ws=None, wsb=0):
+    return L.sharq_prepare_swiglu(gu, T, K, 2 * K if ld is None else ld, n, m, fmt, FAKE, bc, FAKE, FAKE,
+                                  FAKE, G, ws, wsb, None)
+
+
+def test_prepare_swiglu_validation(L):
+    L.sharq_prepare_swiglu.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32] + \
+                                      [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p]
+    assert swiglu(L, fmt=4) == UNSUPPORTED
+    assert swiglu(L, ld=300) == SHAPE              # ld < 2K
+    assert swiglu(L, K=100) == SHAPE
+    assert swiglu(L, T=-1) == SHAPE
+    assert swiglu(L, n=5) == NM
+    assert swiglu(L, gu=None) == NULL
+    assert swiglu(L, bc=None) == NULL
+    assert swiglu(L, gu=MISALIGNED) == ALIGN
+    assert swiglu(L, ld=2 * 256 + 2) == ALIGN      # rows not 16-byte aligned
+    assert swiglu(L, fmt=NV) == NULL
+    assert swiglu(L, fmt=NV, G=FAKE) == WORKSPACE
+    assert swiglu(L, T=0, gu=None) == OK
 
 
 def test_quantize_weight_validation(L):

@@ -144,6 +144,53 @@ def test_prep_strided_rows():
     compare_prepared(prepared_to_host(p), o, 2, 4, "strided")
 
 
+# ---------------------------------------------------------------- fused SiLU(gate) * up prep
+
+SWIGLU_CASES = [
+    # (fmt, n, m, T, K, ld)
+    (0, 2, 4, 5, 256, 512),
+    (0, 2, 4, 37, 2560 + 32, 2 * (2560 + 32) + 64),
+    (0, 1, 4, 3, 4096, 8192),
+    (0, 4, 8, 9, 1024, 2048),
+    (0, 2, 4, 2, 14336, 28672),
+    (1, 2, 4, 9, 256, 512),
+    (1, 2, 4, 33, 2048 + 16, 2 * (2048 + 16)),
+    (1, 8, 16, 4, 3584, 7168 + 4),
+    (1, 2, 4, 3, 18944, 37888),
+]
+
+
+@pytest.mark.parametrize("case", SWIGLU_CASES, ids=lambda c: "fmt%d-%d:%d-T%d-K%d-ld%d" % c)
+def test_prep_swiglu(case):
+    fmt, n, m, T, K, ld = case
+    tag = SWIGLU_CASES.index(case)
+    gu = synth.small_gate_up(K, T, ld, tag=tag)
+    p = sq().prepare_swiglu(torch.from_numpy(gu).cuda(), K, n=n, m=m, fmt=fmt)
+    torch.cuda.synchronize()
+    gh = prepared_to_host(p)
+    o = oracle.prepare_swiglu(gu, K, n, m, fmt, trace=True)
+    stats = compare_prepared(gh, o, n, m, str(case))
+    assert stats["mismatched"] == 0, stats
+    if fmt == oracle.FMT_NVFP4:
+        assert gh["G"] == float(o.gscale[0])
+
+
+def test_prep_swiglu_column_slice():
+    """The gate/up block may be a column slice of a wider output buffer."""
+    K, T = 512, 6
+    gu = synth.small_gate_up(K, T, 2 * K + 128, tag=99)
+    d = torch.from_numpy(gu).cuda()[:, 64:64 + 2 * K]
+    p = sq().prepare_swiglu(d, K, n=2, m=4, fmt=0)
+    torch.cuda.synchronize()
+    o = oracle.prepare_swiglu(np.ascontiguousarray(gu[:, 64:64 + 2 * K]), K, 2, 4, 0, trace=True)
+    assert compare_prepared(prepared_to_host(p), o, 2, 4, "slice")["mismatched"] == 0
+
+
+def test_prep_swiglu_zero_rows_is_noop():
+    p = sq().prepare_swiglu(torch.zeros((0, 512), dtype=torch.float32, device="cuda"), 256, fmt=1)
+    assert p.b_codes.numel() == 0
+
+
 # ---------------------------------------------------------------- weight quantization
 
 @pytest.mark.parametrize("fmt", [0, 1])

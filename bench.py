@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--workload", default="llama")
     ap.add_argument("--rotate", type=int, default=3, help="copies of every input rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
+                    help="time the step as one captured HIP graph (auto: for decode batches, where "
+                         "host launch overhead would otherwise dominate)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the fused SiLU(gate)*up prep and the bf16 / fp8 GEMM comparisons")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -113,6 +116,16 @@ class Layer:
         del w_bits
         self.prep = [sq.alloc_prepared(prep_tokens, lin.k, wl.fmt, dev) for _ in range(rotate)]
         self.y = [torch.empty((self.rows, lin.nout), dtype=torch.float32, device=dev) for _ in range(rotate)]
+
+    def run_prep(self, sq, i):
+        r = i % len(self.x)
+        sq.prepare(self.x[r], norm=self.lin.norm, gamma=self.g, eps=self.wl.eps, n=self.wl.n, m=self.wl.m,
+                   fmt=self.wl.fmt, out=self.prep[r])
+
+    def run_gemm(self, sq, i):
+        r = i % len(self.x)
+        sq.linear(self.prep[r], self.w[r], group_offsets=self.offs, row_index=self.ridx, rows=self.rows,
+                  out=self.y[r])
 
     def run(self, sq, i, ev=None):
         r = i % len(self.x)
@@ -380,24 +393,65 @@ def main():
             L.run(sq, i)
     torch.cuda.synchronize()
 
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers]
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        for li, L in enumerate(layers):
-            L.run(sq, s, evs[s][li])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    use_graph = args.graph == "on" or (args.graph == "auto" and layers[0].prep_tokens <= 64)
+    if use_graph:
+        # one graph per rotated copy, each holding the whole step; per-phase
+        # graphs give the kernel times (events around back-to-back replays)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(2):
+                for L in layers:
+                    L.run(sq, i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        step_graphs, phase_graphs = [], []
+        for r in range(args.rotate):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for L in layers:
+                    L.run(sq, r)
+            step_graphs.append(g)
+        for L in layers:
+            gp, gg = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gp):
+                L.run_prep(sq, 0)
+            with torch.cuda.graph(gg):
+                L.run_gemm(sq, 0)
+            phase_graphs.append((gp, gg))
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            step_graphs[i % args.rotate].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            step_graphs[s % args.rotate].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_step = (t1 - t0) * 1e3 / args.steps
+        prep_ms, gemm_ms = [], []
+        for gp, gg in phase_graphs:
+            prep_ms.append(_event_ms(torch, gp.replay, reps=args.steps))
+            gemm_ms.append(_event_ms(torch, gg.replay, reps=args.steps))
+    else:
+        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            for li, L in enumerate(layers):
+                L.run(sq, s, evs[s][li])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_step = (t1 - t0) * 1e3 / args.steps
 
-    prep_ms = [0.0] * len(layers)
-    gemm_ms = [0.0] * len(layers)
-    for s in range(args.steps):
-        for li in range(len(layers)):
-            e = evs[s][li]
-            prep_ms[li] += e[0].elapsed_time(e[1]) / args.steps
-            gemm_ms[li] += e[1].elapsed_time(e[2]) / args.steps
+        prep_ms = [0.0] * len(layers)
+        gemm_ms = [0.0] * len(layers)
+        for s in range(args.steps):
+            for li in range(len(layers)):
+                e = evs[s][li]
+                prep_ms[li] += e[0].elapsed_time(e[1]) / args.steps
+                gemm_ms[li] += e[1].elapsed_time(e[2]) / args.steps
     flops = [gemm_flops(L.rows, L.lin.k, L.lin.nout, wl.n, wl.m) for L in layers]
     pbytes = [prep_bytes(L.prep_tokens, L.lin.k, wl.fmt) for L in layers]
     wbytes = [weight_bytes(L.E, L.lin.nout, L.lin.k, wl.fmt) for L in layers]
@@ -423,7 +477,8 @@ def main():
         "config": {"workload": f"{wl.name}" + ("" if tokens == wl.tokens else f"_T{tokens}"),
                    "tokens": tokens, "linears": {L.lin.name: [L.lin.k, L.lin.nout] for L in layers},
                    "mask": f"{wl.n}:{wl.m}", "format": "NVFP4" if nv else "MXFP4",
-                   "rotated_copies": args.rotate},
+                   "rotated_copies": args.rotate,
+                   "launch": "one HIP graph per step" if use_graph else "eager launches"},
         "prep_GBps": round(prep_gbps, 1),
         "prep_frac_hbm": round(prep_gbps / HBM_PEAK_GBPS, 4),
         "gemm_TFLOPs": round(gemm_tflops, 1),

@@ -145,15 +145,17 @@ struct StageLayout {
     static_assert(BN % RPI == 0 && BM % RPI == 0, "scale rows per instruction");
 };
 
-// Three LDS stage buffers sized for the largest tile (MXFP4, 256 x 256).
-constexpr int kStageBytesMax = StageLayout<kFmtMx, 256, 256, 4>::BYTES;
-__shared__ __align__(16) uint8_t g_stage0[kStageBytesMax];
-__shared__ __align__(16) uint8_t g_stage1[kStageBytesMax];
-__shared__ __align__(16) uint8_t g_stage2[kStageBytesMax];
+// LDS stage buffers, sized per tile shape (so smaller tiles leave room for
+// a second workgroup on the CU); an unused third buffer is never referenced
+// and takes no LDS.
+constexpr int kLdsBytes = 160 * 1024;
+template <int BYTES> __shared__ __align__(16) uint8_t g_stage0[BYTES];
+template <int BYTES> __shared__ __align__(16) uint8_t g_stage1[BYTES];
+template <int BYTES> __shared__ __align__(16) uint8_t g_stage2[BYTES];
 
-template <int B>
+template <int B, int BYTES>
 __device__ __forceinline__ uint8_t *stage_buf() {
-    return B == 0 ? g_stage0 : (B == 1 ? g_stage1 : g_stage2);
+    return B == 0 ? g_stage0<BYTES> : (B == 1 ? g_stage1<BYTES> : g_stage2<BYTES>);
 }
 
 __device__ __forceinline__ int swz_unit(int row, int unit) { return unit ^ ((row >> 2) & 3); }
@@ -199,9 +201,17 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t wg, int64_t ntiles) {
     return (wg % 8) * per_xcd + wg / 8;
 }
 
-// WGM x WGN waves: WGM along the token rows, WGN along the weight rows.
-template <int FMT, int BM, int BN, int WGM, int WGN>
+// WGM x WGN waves: WGM along the token rows, WGN along the weight rows; NS
+// LDS stages (2 or 3).
+// LSPLIT (three stages only): the last LSPLIT of a stage's direct loads are
+// issued one sub-step later than the rest, so the loads of all waves spread
+// over a whole step instead of bunching in one sub-step.
+// RPS LDS reads are issued per MFMA slot, so a sub-step's reads are all in
+// flight early and have landed before the next sub-step needs them.
+template <int FMT, int BM, int BN, int WGM, int WGN, int NS, int LSPLIT = 0, int RPS = 1>
 struct DualGemm {
+    static_assert(NS == 2 || NS == 3, "two or three stages");
+    static_assert(LSPLIT == 0 || NS == 3, "split loads need a third stage");
     static constexpr int NW = WGM * WGN;
     using L = StageLayout<FMT, BM, BN, NW>;
     static constexpr int FM = BM / WGM / 32;  // 32-row token fragments per wave
@@ -238,7 +248,7 @@ struct DualGemm {
     // same number of loads).
     template <int B>
     __device__ __forceinline__ void issue_one(int idx, int64_t stage) {
-        uint8_t *st = stage_buf<B>();
+        uint8_t *st = stage_buf<B, L::BYTES>();
         const int64_t stp = stage < last_step ? stage : last_step;
         if (idx < L::W_LD) {
             lds_load16(rW, st + L::W_CODES + (wave * L::W_LD + idx) * 1024, w_off[idx],
@@ -285,7 +295,7 @@ struct DualGemm {
 
     template <int B, int T>
     __device__ __forceinline__ void read_frag(int r, Frags &f) const {
-        const uint8_t *cur = stage_buf<B>();
+        const uint8_t *cur = stage_buf<B, L::BYTES>();
         if (r < FN) {
             f.w[r] = *reinterpret_cast<const v4i *>(cur + (rd_w[T] + (L::W_CODES + r * 32 * kRowBytes)));
         } else {
@@ -299,7 +309,7 @@ struct DualGemm {
 
     template <int B, int T>
     __device__ __forceinline__ void read_scale(int r, Scales &s) const {
-        const uint8_t *cur = stage_buf<B>();
+        const uint8_t *cur = stage_buf<B, L::BYTES>();
         if (r < FN) {
             s.w[r] = *reinterpret_cast<const uint16_t *>(cur + (rd_ws[T] + (L::W_SC + r * 32 * L::SB)));
         } else {
@@ -356,8 +366,11 @@ struct DualGemm {
         if constexpr (FMT == kFmtMx) {
             constexpr int NM = 2 * FM * FN;
             constexpr int NOTHER = MODE == 0 ? NREAD_FRAGS : NREAD_NEXT;
-            constexpr int NLOAD = MODE == 0 ? 0 : L::PER_STAGE;
-            constexpr int NSLOT = NM > NOTHER ? (NM > NLOAD ? NM : NLOAD) : (NOTHER > NLOAD ? NOTHER : NLOAD);
+            // direct loads of this sub-step: indices [LLO, LLO + NLOAD)
+            constexpr int NLOAD = MODE == 0 ? LSPLIT : L::PER_STAGE - LSPLIT;
+            constexpr int LLO = MODE == 0 ? L::PER_STAGE - LSPLIT : 0;
+            constexpr int NRSLOT = (NOTHER + RPS - 1) / RPS;
+            constexpr int NSLOT = NM > NRSLOT ? (NM > NLOAD ? NM : NLOAD) : (NRSLOT > NLOAD ? NRSLOT : NLOAD);
 #pragma unroll
             for (int k = 0; k < NSLOT; k++) {
                 const int i = k / (2 * FN), p = (k / FN) & 1, j = k % FN;
@@ -367,13 +380,23 @@ struct DualGemm {
                     else
                         acc[i][j] = mfma32_fp4<T>(f.w[j], f.xr[i], acc[i][j], (int)s.w[j], (int)s.xr[i]);
                 }
-                constexpr int LOAD0 = NM > NLOAD ? NM - NLOAD - 1 : 0;  // loads go in the later slots
-                if (k >= LOAD0 && k - LOAD0 < NLOAD) this->template issue_one<BL>(k - LOAD0, stage);
-                if (k < NOTHER) {
-                    if (MODE == 0)
-                        read_sub1<BR>(k, fo, so);
-                    else
-                        read_next<BR>(k, fo, so);
+                if constexpr (LSPLIT == 0) {
+                    constexpr int LOAD0 = NM > NLOAD ? NM - NLOAD - 1 : 0;  // loads go in the later slots
+                    if (k >= LOAD0 && k - LOAD0 < NLOAD) this->template issue_one<BL>(k - LOAD0, stage);
+                } else {
+#pragma unroll
+                    for (int l = 0; l < NLOAD; l++)  // spread evenly over the slots
+                        if (((2 * l + 1) * NSLOT) / (2 * NLOAD) == k) this->template issue_one<BL>(LLO + l, stage);
+                }
+#pragma unroll
+                for (int q = 0; q < RPS; q++) {
+                    const int r = k * RPS + q;
+                    if (r < NOTHER) {
+                        if (MODE == 0)
+                            read_sub1<BR>(r, fo, so);
+                        else
+                            read_next<BR>(r, fo, so);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -382,7 +405,8 @@ struct DualGemm {
             // MFMAs per fragment pair; side work spread over the token
             // fragments.
             constexpr int NOTHER = MODE == 0 ? 2 * NREAD_FRAGS : NREAD_NEXT;
-            constexpr int NLOAD = MODE == 0 ? 0 : L::PER_STAGE;
+            constexpr int NLOAD = MODE == 0 ? LSPLIT : L::PER_STAGE - LSPLIT;
+            constexpr int LLO = MODE == 0 ? L::PER_STAGE - LSPLIT : 0;
             constexpr int PER_I_OTHER = (NOTHER + FM - 1) / FM;
             constexpr int PER_I_LOAD = (NLOAD + FM - 1) / FM;
             v8bf wd[FN][4];
@@ -405,7 +429,7 @@ struct DualGemm {
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wd[j][t], xr[t], acc[i][j], 0, 0, 0);
 #pragma unroll
                 for (int k = i * PER_I_LOAD; k < (i + 1) * PER_I_LOAD && k < NLOAD; k++)
-                    this->template issue_one<BL>(k, stage);
+                    this->template issue_one<BL>(LLO + k, stage);
 #pragma unroll
                 for (int k = i * PER_I_OTHER; k < (i + 1) * PER_I_OTHER && k < NOTHER; k++) {
                     if (MODE == 0)
@@ -425,24 +449,28 @@ struct DualGemm {
         Frags f1;
         Scales s1;  // NVFP4: sub-step-1 scales (MXFP4 uses sc for both sub-steps)
         __builtin_amdgcn_sched_barrier(0);
-        this->template mma<0, 0, B, B>(acc, f0, sc, 0, f1, s1);
-        wait_vmcnt<L::PER_STAGE, true>();  // own reads of stage s done, stage s+1 landed
+        // sub-step 0 issues the late loads of stage s+2 (buffer (B+2)%3, read
+        // last in step s-1, so free since that step's barrier)
+        this->template mma<0, 0, NS == 3 ? (B + 2) % 3 : B, B>(acc, f0, sc, s + 2, f1, s1);
+        wait_vmcnt<(NS - 2) * L::PER_STAGE, true>();  // own reads of stage s done, stage s+1 landed
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         Scales sn;
-        this->template mma<1, 1, B, (B + 1) % 3>(acc, f1, FMT == kFmtMx ? sc : s1, s + 3, f0, sn);
+        this->template mma<1, 1, B, (B + 1) % NS>(acc, f1, FMT == kFmtMx ? sc : s1, s + NS, f0, sn);
         sc = sn;
     }
 };
 
-template <int FMT, int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
-void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
-    using G = DualGemm<FMT, BM, BN, WGM, WGN>;
+// OCC workgroups share a CU (LDS and registers are sized for that).
+template <int FMT, int BM, int BN, int WGM, int WGN, int NS, int OCC, int LSPLIT, int RPS>
+__global__ __launch_bounds__(WGM * WGN * 64)
+__attribute__((amdgpu_waves_per_eu(OCC * WGM * WGN / 4, OCC * WGM * WGN / 4)))
+void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles, int64_t n_begin) {
+    using G = DualGemm<FMT, BM, BN, WGM, WGN, NS, LSPLIT, RPS>;
     using L = typename G::L;
     constexpr int FM = G::FM, FN = G::FN;
     static_assert(FM >= 1 && FN >= 1, "tile too small for 32x32 fragments");
-    static_assert(L::BYTES <= kStageBytesMax, "stage does not fit its LDS buffer");
+    static_assert(L::BYTES * NS * OCC <= kLdsBytes, "stages do not fit the CU's LDS");
 
     TileRows tr;
     int64_t ntile;
@@ -458,7 +486,7 @@ void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
         ntile = blockIdx.x % n_ntiles;
         if (!grouped_tile_rows<BM>(a, blockIdx.x / n_ntiles, tr)) return;
     }
-    const int64_t n0 = ntile * BN;
+    const int64_t n0 = n_begin + ntile * BN;
     const int64_t K = a.K;
     constexpr int SB = L::SB;
     const uint32_t kb = (uint32_t)(K / 2), ks = (uint32_t)(K / kKS) * SB;  // per row: code / scale bytes
@@ -534,19 +562,22 @@ void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles) {
     typename G::Scales sc;
     g.template issue<0>(0);
     g.template issue<1>(1);
-    g.template issue<2>(2);
-    wait_vmcnt<2 * L::PER_STAGE>();  // stage 0 landed
+    if constexpr (NS == 3) {  // stage 2 less its late loads (issued in step 0)
+#pragma unroll
+        for (int idx = 0; idx < L::PER_STAGE - LSPLIT; idx++) g.template issue_one<2>(idx, 2);
+    }
+    wait_vmcnt<(NS - 1) * L::PER_STAGE - LSPLIT>();  // stage 0 landed
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int r = 0; r < G::NREAD_NEXT; r++) g.template read_next<0>(r, f0, sc);
     int64_t s = 0;
-    for (; s + 3 <= nsteps; s += 3) {
+    for (; s + NS <= nsteps; s += NS) {
         g.template step<0>(s, acc, f0, sc);
         g.template step<1>(s + 1, acc, f0, sc);
-        g.template step<2>(s + 2, acc, f0, sc);
+        if constexpr (NS == 3) g.template step<2>(s + 2, acc, f0, sc);
     }
     if (s < nsteps) g.template step<0>(s, acc, f0, sc);
-    if (s + 1 < nsteps) g.template step<1>(s + 1, acc, f0, sc);
+    if (NS == 3 && s + 1 < nsteps) g.template step<1>(s + 1, acc, f0, sc);
     wait_vmcnt<0, true>();  // drain the tail loads before the workgroup exits
 
     // ---- epilogue: accumulator group q of fragment (i, j) is Y[m][n..n+3];
@@ -701,9 +732,11 @@ __global__ void k_zero_rows(float *y, int64_t rows, int64_t cols, int64_t ldy) {
 // ============================================================================
 // launcher
 // ============================================================================
-template <int FMT, int BM, int BN, int WGM, int WGN>
-static hipError_t launch_prefill(const LinearArgs &a, hipStream_t st) {
-    const int64_t n_ntiles = (a.nout + BN - 1) / BN;
+// Output columns [n_begin, n_end) of the product (all of them by default).
+template <int FMT, int BM, int BN, int WGM, int WGN, int NS = 3, int OCC = 1, int LSPLIT = 0, int RPS = 1>
+static hipError_t launch_prefill(const LinearArgs &a, hipStream_t st, int64_t n_begin = 0, int64_t n_end = -1) {
+    if (n_end < 0) n_end = a.nout;
+    const int64_t n_ntiles = (n_end - n_begin + BN - 1) / BN;
     int64_t blocks;
     int64_t n_mtiles = 0;
     if (a.offsets) {
@@ -712,8 +745,9 @@ static hipError_t launch_prefill(const LinearArgs &a, hipStream_t st) {
         n_mtiles = (a.rows + BM - 1) / BM;
         blocks = ((n_ntiles * n_mtiles + 7) / 8) * 8;
     }
-    hipLaunchKernelGGL((k_dual_gemm<FMT, BM, BN, WGM, WGN>), dim3((unsigned)blocks), dim3(WGM * WGN * 64), 0, st, a,
-                       n_ntiles, n_mtiles);
+    hipLaunchKernelGGL((k_dual_gemm<FMT, BM, BN, WGM, WGN, NS, OCC, LSPLIT, RPS>), dim3((unsigned)blocks),
+                       dim3(WGM * WGN * 64), 0,
+                       st, a, n_ntiles, n_mtiles, n_begin);
     return hipGetLastError();
 }
 
@@ -751,10 +785,46 @@ static int device_cus() {
     return cus[dev];
 }
 
-// Dense tile shape: one workgroup fills a CU (LDS), so the time is about
-// rounds(tiles / CUs) x tile size, with smaller tiles paying for their lower
-// operand reuse (relative cost per output element below, from measurement
-// of the three shapes on MI355X).
+// Dense MXFP4 tile shapes: 256x256 (8 waves), 128x256 and 128x128 (4 waves).
+// One workgroup fills a CU (LDS), so a launch takes about rounds(tiles / CUs)
+// times the tile time, with smaller tiles paying for their lower operand
+// reuse (relative cost per output element, measured on MI355X for
+// K = 4096..14336).
+struct TileShape {
+    int bm, bn;
+    double cost;
+};
+constexpr TileShape kMxShapes[3] = {{256, 256, 1.0}, {128, 256, 1.2}, {128, 128, 1.5}};
+
+static double shape_time(int s, int64_t rows, int64_t cols, int64_t cus) {
+    const TileShape &t = kMxShapes[s];
+    const int64_t tiles = ((rows + t.bm - 1) / t.bm) * ((cols + t.bn - 1) / t.bn);
+    return (double)((tiles + cus - 1) / cus) * t.bm * t.bn * t.cost;
+}
+
+static int best_shape(int64_t rows, int64_t cols, int64_t cus, double *t_best) {
+    int best = 0;
+    for (int s = 0; s < 3; s++) {
+        const double t = shape_time(s, rows, cols, cus);
+        if (s == 0 || t < *t_best) {
+            best = s;
+            *t_best = t;
+        }
+    }
+    return best;
+}
+
+static hipError_t launch_mx_shape(int s, const LinearArgs &a, hipStream_t st, int64_t n_begin, int64_t n_end) {
+    // split loads over two sub-steps, two LDS reads per MFMA slot
+    if (s == 0) return launch_prefill<kFmtMx, 256, 256, 4, 2, 3, 1, 4, 2>(a, st, n_begin, n_end);
+    if (s == 1) return launch_prefill<kFmtMx, 128, 256, 2, 2, 3, 1, 4, 2>(a, st, n_begin, n_end);
+    return launch_prefill<kFmtMx, 128, 128, 2, 2>(a, st, n_begin, n_end);
+}
+
+// A product whose 256x256 tiles fill some rounds of the CUs and leave a
+// partial last round runs as two launches over column ranges: full rounds
+// of 256x256 tiles, then the remaining columns in the shape that fits them
+// best, instead of a last round that leaves CUs idle.
 static hipError_t launch_linear_mx(const LinearArgs &a, hipStream_t st) {
     if (a.offsets == nullptr && a.rows <= 64) {
         if (a.rows <= 16) return launch_small<1>(a, st);
@@ -762,29 +832,31 @@ static hipError_t launch_linear_mx(const LinearArgs &a, hipStream_t st) {
         if (a.rows <= 48) return launch_small<3>(a, st);
         return launch_small<4>(a, st);
     }
-    if (a.offsets) return launch_prefill<kFmtMx, 128, 256, 2, 2>(a, st);
+    if (a.offsets) return launch_prefill<kFmtMx, 128, 256, 2, 2, 3, 1, 4, 2>(a, st);
     const int64_t cus = device_cus();
-    struct Shape { int bm, bn; double cost; };
-    // relative cost per output element of each tile shape, measured on the
-    // MI355X for K = 4096..14336 (larger tiles reuse operands more)
-    const Shape shapes[3] = {{256, 256, 1.0}, {128, 256, 1.2}, {128, 128, 1.5}};
-    int best = 0;
-    double best_t = 0.0;
-    for (int i = 0; i < 3; i++) {
-        const int64_t tiles = ((a.rows + shapes[i].bm - 1) / shapes[i].bm) * ((a.nout + shapes[i].bn - 1) / shapes[i].bn);
-        const double t = (double)((tiles + cus - 1) / cus) * shapes[i].bm * shapes[i].bn * shapes[i].cost;
-        if (i == 0 || t < best_t) { best = i; best_t = t; }
+    double t_one = 0.0;
+    const int one = best_shape(a.rows, a.nout, cus, &t_one);
+    const int64_t mt = (a.rows + 255) / 256;
+    const int64_t full_rounds = (mt * ((a.nout + 255) / 256)) / cus;
+    const int64_t n_split = (full_rounds * cus / mt) * 256;
+    if (full_rounds >= 1 && n_split > 0 && n_split < a.nout) {
+        double t_rem = 0.0;
+        const int rem = best_shape(a.rows, a.nout - n_split, cus, &t_rem);
+        const double t_main = (double)((mt * (n_split / 256) + cus - 1) / cus) * 256 * 256;
+        if (t_main + t_rem < 0.97 * t_one) {  // a second launch costs a little
+            const hipError_t e = launch_mx_shape(0, a, st, 0, n_split);
+            if (e != hipSuccess) return e;
+            return launch_mx_shape(rem, a, st, n_split, a.nout);
+        }
     }
-    if (best == 0) return launch_prefill<kFmtMx, 256, 256, 4, 2>(a, st);
-    if (best == 1) return launch_prefill<kFmtMx, 128, 256, 2, 2>(a, st);
-    return launch_prefill<kFmtMx, 128, 128, 2, 2>(a, st);
+    return launch_mx_shape(one, a, st, 0, a.nout);
 }
 
 hipError_t launch_linear(const LinearArgs &a, void *ws, size_t ws_bytes, hipStream_t st) {
     (void)ws;
     (void)ws_bytes;
     if (a.fmt == kFmtMx) return launch_linear_mx(a, st);
-    return launch_prefill<kFmtNv, 128, 256, 2, 2>(a, st);
+    return launch_prefill<kFmtNv, 128, 256, 2, 2, 3, 1, 4, 1>(a, st);
 }
 
 size_t linear_workspace_bytes(int64_t rows, int64_t K, int64_t nout, int64_t E, int fmt) {

@@ -300,6 +300,50 @@ def test_determinism():
     assert np.array_equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("fmt,T", [(0, 8), (1, 8), (0, 300)], ids=["mx-decode8", "nv-decode8", "mx-T300"])
+def test_graph_replay_matches_eager(fmt, T):
+    """The whole path (prep + product) captured in one HIP graph: every replay,
+    with eager work and synchronizations between replays, reproduces the
+    eager result (prepared tensors bit-exact; the product to float rounding,
+    as the small-batch kernel sums K splits with atomics)."""
+    K, nout = 2048, 384
+    w = synth.small_weight(nout, K, tag=31 + fmt)
+    qw = sq().quantize_weight(dev16(w, "bf16"), fmt=fmt)
+    x = dev16(synth.small_case(K, T, "bf16", tag=32 + fmt), "bf16")
+    g = dev16(synth.small_gamma(K, "bf16", tag=33), "bf16")
+    out = sq().alloc_prepared(T, K, fmt, x.device)
+    y = torch.empty((T, nout), dtype=torch.float32, device="cuda")
+
+    def step():
+        sq().prepare(x, norm=1, gamma=g, eps=1e-5, n=2, m=4, fmt=fmt, out=out)
+        sq().linear(out, qw, out=y)
+
+    step()
+    torch.cuda.synchronize()
+    ref_p, ref_y = prepared_to_host(out), host(y)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        y.fill_(float("nan"))
+        out.b_codes.zero_()
+        out.r_scales.fill_(7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = prepared_to_host(out)
+        for key in ("mask", "b_codes", "b_scales", "r_codes", "r_scales", "G"):
+            assert np.array_equal(got[key], ref_p[key]), (rep, key)
+        assert rel_fro(host(y), ref_y) <= 1e-6, rep
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 # ---------------------------------------------------------------- full-size workloads
 
 def _weight_sample_check(wl, lin, qw, w_bits, nrows=128, seed=0):

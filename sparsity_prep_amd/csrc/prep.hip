@@ -30,8 +30,7 @@ namespace sharq {
 constexpr int kPrepWaves = 4;        // waves per workgroup
 constexpr int kChunk = 512;          // elements per wave-wide 128-bit load
 constexpr int kStreamChunks = 4;     // chunks per task when rows are split
-constexpr int64_t kPrepRowsGrid = 512;    // row workgroups that fill the GPU (two per CU)
-constexpr int64_t kPrepWavesGrid = 4096;  // streaming waves that fill the GPU (four per SIMD)
+constexpr int64_t kPrepRowsGrid = 1024;   // row workgroups that fill the GPU (four per CU)
 
 struct RowStats {  // per-row statistics written by the NVFP4 pre-pass
     float r, mu, amax, pad;
@@ -665,7 +664,10 @@ static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
     const int64_t tasks_per_row = (K + (int64_t)kChunk * kStreamChunks - 1) / ((int64_t)kChunk * kStreamChunks);
     const int64_t tasks = a.T * tasks_per_row;
     // tasks per wave: enough waves for about four per SIMD, each looping
-    const int64_t tpw = tasks >= 4 * kPrepWavesGrid ? 4 : (tasks >= 2 * kPrepWavesGrid ? 2 : 1);
+    // one task per wave: measured fastest on MI355X for every shape tried
+    // (more resident waves hide the load latency better than the in-wave
+    // prefetch of a next task)
+    const int64_t tpw = 1;
     const int64_t waves = (tasks + tpw - 1) / tpw;
     const dim3 grid((unsigned)round_up8((waves + kPrepWaves - 1) / kPrepWaves));
     if constexpr (FMT == kFmtNv || NORM == kNormNone)

@@ -33,6 +33,10 @@ import numpy as np
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+# 32x32x64 block-scaled FP4 MFMA issued back to back from registers with
+# random operands (no memory traffic), measured on MI355X: the chip lowers its
+# clock under that load (about 1.5 GHz against 2.4 GHz with constant operands)
+MFMA_RANDOM_FP4_TFLOPS = 6250.0
 SAMPLE_ROWS = 32                # rows per linear in the CPU baseline and the error report
 
 
@@ -341,6 +345,25 @@ def gemm_baselines(torch, synth, wl, layers, sharq_ms):
     return res
 
 
+def measured_traffic(name):
+    """HBM-side bytes per step of a kernel family from the committed counter
+    summary under profiles/ (FETCH_SIZE / WRITE_SIZE scaled by a plain copy),
+    or None when the kernel sources changed after the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", name)
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        h = hashlib.sha256()
+        for src in t["sources"]:
+            with open(os.path.join(root, src), "rb") as f:
+                h.update(f.read())
+    except (OSError, ValueError, KeyError):
+        return None
+    return t if h.hexdigest() == t["source_sha256"] else None
+
+
 def build_layers(args, sq, torch, synth, dev):
     if args.workload == "llama":
         wl = synth.WORKLOADS[1]
@@ -499,6 +522,15 @@ def main():
     }
     if nv:
         result["roofline"]["frac_of_bf16_peak"] = round(gemm_tflops / BF16_PEAK_TFLOPS, 4)
+    if wl.name == "llama3.1-8b_prefill_T2048_mxfp4" and tokens == wl.tokens:
+        for key, fname in (("roofline", "k_dual_gemm_mxfp4_llama3.1-8b_prefill_T2048.traffic.json"),
+                           ("roofline_prep", "k_prep_mxfp4_llama3.1-8b_prefill_T2048.traffic.json")):
+            t = measured_traffic(fname)
+            if t is not None:
+                result[key]["traffic"] = t["bytes_per_step"]
+                result[key]["traffic_unit"] = "bytes per step (all launches of the kernel in one step)"
+                result[key]["algorithmic_bytes_per_step"] = t["algorithmic_bytes_per_step"]
+    result["roofline"]["mfma_ceiling_random_fp4_TFLOPs"] = MFMA_RANDOM_FP4_TFLOPS
     if not args.no_extras:
         result["swiglu_prep"] = swiglu_report(sq, torch, wl, layers)
         result["gemm_baselines"] = gemm_baselines(torch, synth, wl, layers, sum(prep_ms) + sum(gemm_ms))

@@ -178,17 +178,40 @@ struct TileRows {
 // in BM-row steps.
 template <int BM>
 __device__ __forceinline__ bool grouped_tile_rows(const LinearArgs &a, int64_t tile, TileRows &tr) {
+    // Every wave finds the expert whose tile range holds `tile` on its own:
+    // lane l takes expert base + l, the wave's inclusive prefix sum of the
+    // experts' tile counts places each range, and one ballot picks the
+    // lane whose range contains the tile (64 experts per pass).
+    const int lane = threadIdx.x & 63;
     int64_t acc = 0;
-    for (int64_t e = 0; e < a.E; e++) {
-        const int64_t lo = a.offsets[e], hi = a.offsets[e + 1];
-        const int64_t nt = (hi - lo + BM - 1) / BM;
-        if (tile < acc + nt) {
-            tr.m0 = lo + (tile - acc) * BM;
-            tr.m_end = hi;
-            tr.expert = e;
+    for (int64_t base = 0; base < a.E; base += 64) {
+        const int64_t e = base + lane;
+        int32_t lo = 0, hi = 0, nt = 0;
+        if (e < a.E) {
+            lo = a.offsets[e];
+            hi = a.offsets[e + 1];
+            nt = (hi - lo + BM - 1) / BM;
+        }
+        int32_t incl = nt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t up = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += up;
+        }
+        const int64_t first = acc + (incl - nt);
+        const uint64_t hit = __ballot(e < a.E && tile >= first && tile < first + nt);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            // wave-uniform values, kept in scalar registers
+            const int32_t lo_l = __builtin_amdgcn_readfirstlane(__shfl(lo, l, 64));
+            const int32_t hi_l = __builtin_amdgcn_readfirstlane(__shfl(hi, l, 64));
+            const int32_t first_l = __builtin_amdgcn_readfirstlane(__shfl((int32_t)(incl - nt), l, 64));
+            tr.m0 = lo_l + (tile - acc - first_l) * BM;
+            tr.m_end = hi_l;
+            tr.expert = base + l;
             return true;
         }
-        acc += nt;
+        acc += __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
     }
     return false;
 }

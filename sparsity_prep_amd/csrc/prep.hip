@@ -29,7 +29,7 @@ namespace sharq {
 
 constexpr int kPrepWaves = 4;        // waves per workgroup
 constexpr int kChunk = 512;          // elements per wave-wide 128-bit load
-constexpr int kStreamChunks = 4;     // chunks per task when rows are split
+constexpr int kStreamChunks = 2;     // chunks per task when rows are split (measured: 2 beats 4 and 8)
 constexpr int64_t kPrepRowsGrid = 1024;   // row workgroups that fill the GPU (four per CU)
 
 struct RowStats {  // per-row statistics written by the NVFP4 pre-pass
@@ -201,8 +201,28 @@ __device__ __forceinline__ uint4 param_raw(const uint16_t *p, int64_t e0, uint32
 // ---------------------------------------------------------------- per-chunk body
 // Normalized values v of one lane -> mask byte, backbone and residual codes
 // and scales, stored at element offset e0 of row `row`.
+// Per-lane constant parts of the K-tiled offsets of a wave-wide chunk (512
+// elements, chunk index ch along K, which starts on a K-tile boundary): lane
+// l writes K tile 4ch + l/16, elements (l%16)*8 .. +7 of it.  With these the
+// byte offset of the lane's codes (scales) in the 32-bit path is
+// ch * T * 256 (ch * T * 512/B) + row * 64 (row * 128/B) + co (so), a
+// scalar base plus this constant.
+struct LaneOff {
+    uint32_t co, so;
+};
+
+template <int FMT>
+__device__ __forceinline__ LaneOff lane_offsets(const PrepArgs &a, int lane) {
+    constexpr uint32_t B = FMT == kFmtMx ? 32 : 16;
+    const uint32_t q = (uint32_t)lane >> 4, w = ((uint32_t)lane & 15u) * 8u;
+    return {q * (uint32_t)(a.T * (kTileK / 2)) + w / 2, q * (uint32_t)(a.T * (kTileK / B)) + w / B};
+}
+
+// Decompose eight consecutive normalized values (elements 8*lane .. +7 of
+// chunk ch of `row`; row and ch wave-uniform) and store their share of the
+// mask, codes and scales.
 template <int FMT, int M, int FAST24>
-__device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, int64_t e0, int lane,
+__device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, int64_t ch, int lane, LaneOff lo,
                                                 const float v[8], float G, float G6) {
     bool kp[8];
     select8<M, FAST24>(v, a.n, lane, kp);
@@ -225,21 +245,18 @@ __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, 
     const int64_t K = a.K;
     constexpr int LPB = FMT == kFmtMx ? 4 : 2;  // lanes per scale block
     constexpr int B = FMT == kFmtMx ? 32 : 16;
-    // `row` is wave-uniform, so every row base below is a scalar address and
-    // the per-lane part stays a 32-bit offset
-    const uint32_t e = (uint32_t)e0;  // e0 < K < 2^31
-    if (a.mask) (a.mask + row * (K / 8))[e >> 3] = (uint8_t)keep;
-    if (a.off32) {  // K % 128 == 0 and each array < 4 GiB: tile t at t*T*(row bytes)
-        const uint32_t t = e / kTileK, w = e % kTileK;
-        const uint32_t co = t * (uint32_t)(a.T * (kTileK / 2)) + w / 2;
-        const uint32_t so = t * (uint32_t)(a.T * (kTileK / B)) + w / B;
-        *reinterpret_cast<uint32_t *>(a.b_codes + row * (kTileK / 2) + co) = bc;
-        *reinterpret_cast<uint32_t *>(a.r_codes + row * (kTileK / 2) + co) = rc;
+    if (a.mask) (a.mask + row * (K / 8) + ch * (kChunk / 8))[lane] = (uint8_t)keep;
+    if (a.off32) {  // K % 128 == 0 and each array < 4 GiB
+        const uint32_t cb = (uint32_t)ch * (uint32_t)(a.T * (kChunk / 2));
+        const uint32_t sb = (uint32_t)ch * (uint32_t)(a.T * (kChunk / B));
+        *reinterpret_cast<uint32_t *>(a.b_codes + row * (kTileK / 2) + cb + lo.co) = bc;
+        *reinterpret_cast<uint32_t *>(a.r_codes + row * (kTileK / 2) + cb + lo.co) = rc;
         if ((lane % LPB) == 0) {
-            (a.b_scales + row * (kTileK / B))[so] = (uint8_t)bs;
-            (a.r_scales + row * (kTileK / B))[so] = (uint8_t)rs;
+            (a.b_scales + row * (kTileK / B) + sb)[lo.so] = (uint8_t)bs;
+            (a.r_scales + row * (kTileK / B) + sb)[lo.so] = (uint8_t)rs;
         }
     } else {
+        const int64_t e0 = ch * kChunk + lane * 8;
         const int64_t co = ktile_offset<2>(row, e0, a.T, K);
         const int64_t so = ktile_offset<B>(row, e0, a.T, K);
         *reinterpret_cast<uint32_t *>(a.b_codes + co) = bc;
@@ -263,7 +280,9 @@ __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, 
 template <bool BF16, int NORM, int M, int FAST24, int CPW>
 __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_split(PrepArgs a, int64_t rpw) {
     __shared__ double part[2][2][kPrepWaves];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const LaneOff lo = lane_offsets<kFmtMx>(a, lane);
     const int64_t row0 = xcd_block(blockIdx.x, gridDim.x) * rpw;
     const int64_t row_end = row0 + rpw < a.T ? row0 + rpw : a.T;
     if (row0 >= row_end) return;
@@ -331,14 +350,13 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_split(PrepArgs a
         }
 #pragma unroll
         for (int j = 0; j < CPW; j++) {
-            const int64_t e0 = ((int64_t)(wave + kPrepWaves * j) * kWave + lane) * 8;
             if (in[j]) {
                 float g[8], b[8];
                 unpack8<BF16>(graw[j], g);
                 unpack8<BF16>(braw[j], b);
                 unpack8<BF16>(raw[j], v);
                 normalize8<NORM>(v, g, b, r, mu);
-                decompose_store<kFmtMx, M, FAST24>(a, row, e0, lane, v, 1.0f, 6.0f);
+                decompose_store<kFmtMx, M, FAST24>(a, row, wave + kPrepWaves * j, lane, lo, v, 1.0f, 6.0f);
             }
         }
 #pragma unroll
@@ -384,21 +402,24 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_2pass(PrepArgs a
         mu = (float)mud;
         r = (float)(1.0 / sqrt(s2 / (double)K + (double)a.eps));
     }
-    for (int64_t e0 = (int64_t)lane * 8; e0 < K; e0 += kChunk) {
-        float g[8], b[8];
-        load_param8<BF16, true>(a.gamma, e0, g, 1.0f);
-        load_param8<BF16, NORM == kNormLayer>(a.beta, e0, b, 0.0f);
-        unpack8<BF16>(*reinterpret_cast<const uint4 *>(xr + e0), v);
-        normalize8<NORM>(v, g, b, r, mu);
-        decompose_store<kFmtMx, M, FAST24>(a, row, e0, lane, v, 1.0f, 6.0f);
+    const LaneOff lo = lane_offsets<kFmtMx>(a, lane);
+    for (int64_t ch = 0; ch * kChunk < K; ch++) {
+        const int64_t e0 = ch * kChunk + lane * 8;
+        if (e0 < K) {
+            float g[8], b[8];
+            load_param8<BF16, true>(a.gamma, e0, g, 1.0f);
+            load_param8<BF16, NORM == kNormLayer>(a.beta, e0, b, 0.0f);
+            unpack8<BF16>(*reinterpret_cast<const uint4 *>(xr + e0), v);
+            normalize8<NORM>(v, g, b, r, mu);
+            decompose_store<kFmtMx, M, FAST24>(a, row, ch, lane, lo, v, 1.0f, 6.0f);
+        }
     }
 }
 
 // ---------------------------------------------------------------- streaming tasks
 // Row-split tasks: (row, kStreamChunks chunks).  Normalization statistics
-// come from the NVFP4 pre-pass (stats != nullptr) or there is no norm.  Each
-// wave handles `tpw` consecutive tasks and loads the next task's words before
-// it quantizes the current one.
+// come from the NVFP4 pre-pass (stats != nullptr) or there is no norm.  One
+// task per wave.
 template <bool BF16, int NORM>
 __device__ __forceinline__ void stream_load(const PrepArgs &a, int64_t task, int64_t tpr, int lane,
                                             uint4 raw[kStreamChunks], uint4 graw[kStreamChunks],
@@ -419,57 +440,40 @@ __device__ __forceinline__ void stream_load(const PrepArgs &a, int64_t task, int
 }
 
 template <bool BF16, int NORM, int FMT, int M, int FAST24>
-__global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_stream(PrepArgs a, const RowStats *stats,
-                                                                    int64_t tpw) {
+__global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_stream(PrepArgs a, const RowStats *stats) {
     const int lane = threadIdx.x & 63;
     const int64_t K = a.K;
     const int64_t tpr = (K + (int64_t)kChunk * kStreamChunks - 1) / ((int64_t)kChunk * kStreamChunks);
-    const int64_t ntasks = a.T * tpr;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t t0 = (xcd_block(blockIdx.x, gridDim.x) * kPrepWaves + wave) * tpw;
-    const int64_t t_end = t0 + tpw < ntasks ? t0 + tpw : ntasks;
-    if (t0 >= t_end) return;
+    const int64_t task = xcd_block(blockIdx.x, gridDim.x) * kPrepWaves + wave;
+    if (task >= a.T * tpr) return;
+    const LaneOff lo = lane_offsets<FMT>(a, lane);
     float G = 1.0f, G6 = 6.0f;
     if constexpr (FMT == kFmtNv) {
         G = *a.global_scale;
         G6 = __fmul_rn(6.0f, G);
     }
     uint4 raw[kStreamChunks], graw[kStreamChunks], braw[kStreamChunks];
-    stream_load<BF16, NORM>(a, t0, tpr, lane, raw, graw, braw);
-    for (int64_t task = t0; task < t_end; task++) {
-        uint4 nraw[kStreamChunks], ngraw[kStreamChunks], nbraw[kStreamChunks];
-        const bool more = task + 1 < t_end;
-        if (more) stream_load<BF16, NORM>(a, task + 1, tpr, lane, nraw, ngraw, nbraw);
-        const int64_t row = task / tpr;
-        const int64_t c0 = (task - row * tpr) * kStreamChunks;
-        float r = 1.0f, mu = 0.0f;
-        if constexpr (NORM != kNormNone) {
-            r = stats[row].r;
-            mu = stats[row].mu;
-        }
+    stream_load<BF16, NORM>(a, task, tpr, lane, raw, graw, braw);
+    const int64_t row = task / tpr;
+    const int64_t c0 = (task - row * tpr) * kStreamChunks;
+    float r = 1.0f, mu = 0.0f;
+    if constexpr (NORM != kNormNone) {
+        r = stats[row].r;
+        mu = stats[row].mu;
+    }
 #pragma unroll
-        for (int c = 0; c < kStreamChunks; c++) {
-            const int64_t e0 = ((c0 + c) * kWave + lane) * 8;
-            if (e0 < K) {
-                float v[8];
-                unpack8<BF16>(raw[c], v);
-                if constexpr (NORM != kNormNone) {
-                    float g[8], b[8];
-                    unpack8<BF16>(graw[c], g);
-                    unpack8<BF16>(braw[c], b);
-                    normalize8<NORM>(v, g, b, r, mu);
-                }
-                decompose_store<FMT, M, FAST24>(a, row, e0, lane, v, G, G6);
-            }
-        }
-        if (!more) break;
-#pragma unroll
-        for (int c = 0; c < kStreamChunks; c++) {
-            raw[c] = nraw[c];
+    for (int c = 0; c < kStreamChunks; c++) {
+        if ((c0 + c) * kChunk + lane * 8 < K) {
+            float v[8];
+            unpack8<BF16>(raw[c], v);
             if constexpr (NORM != kNormNone) {
-                graw[c] = ngraw[c];
-                braw[c] = nbraw[c];
+                float g[8], b[8];
+                unpack8<BF16>(graw[c], g);
+                unpack8<BF16>(braw[c], b);
+                normalize8<NORM>(v, g, b, r, mu);
             }
+            decompose_store<FMT, M, FAST24>(a, row, c0 + c, lane, lo, v, G, G6);
         }
     }
 }
@@ -525,6 +529,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_swiglu(PrepArgs a) 
     if (row >= a.T) return;
     const int64_t c0 = (task - row * tpr) * kStreamChunks;
     const float *gr = a.gu + row * a.ldgu;
+    const LaneOff lo = lane_offsets<FMT>(a, lane);
     float G = 1.0f, G6 = 6.0f;
     if constexpr (FMT == kFmtNv) {
         G = *a.global_scale;
@@ -532,11 +537,11 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_swiglu(PrepArgs a) 
     }
 #pragma unroll
     for (int c = 0; c < kStreamChunks; c++) {
-        const int64_t e0 = ((c0 + c) * kWave + lane) * 8;
+        const int64_t e0 = (c0 + c) * kChunk + lane * 8;
         if (e0 < K) {
             float v[8];
             swiglu8(gr, K, e0, v);
-            decompose_store<FMT, M, FAST24>(a, row, e0, lane, v, G, G6);
+            decompose_store<FMT, M, FAST24>(a, row, c0 + c, lane, lo, v, G, G6);
         }
     }
 }
@@ -665,13 +670,12 @@ static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
     const int64_t tasks = a.T * tasks_per_row;
     // tasks per wave: enough waves for about four per SIMD, each looping
     // one task per wave: measured fastest on MI355X for every shape tried
-    // (more resident waves hide the load latency better than the in-wave
+    // (more resident waves hide the load latency better than an in-wave
     // prefetch of a next task)
-    const int64_t tpw = 1;
-    const int64_t waves = (tasks + tpw - 1) / tpw;
+    const int64_t waves = tasks;
     const dim3 grid((unsigned)round_up8((waves + kPrepWaves - 1) / kPrepWaves));
     if constexpr (FMT == kFmtNv || NORM == kNormNone)
-        hipLaunchKernelGGL((k_prep_stream<BF16, NORM, FMT, M, FAST24>), grid, blk, 0, st, a, stats, tpw);
+        hipLaunchKernelGGL((k_prep_stream<BF16, NORM, FMT, M, FAST24>), grid, blk, 0, st, a, stats);
     return hipGetLastError();
 }
 

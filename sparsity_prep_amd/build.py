@@ -21,7 +21,6 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off",              # no FMA contraction: every rounding is explicit
-    "-munsafe-fp-atomics",            # hardware FP32 atomic add
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fvisibility=hidden",            # only the C ABI (SHARQ_API) is exported
     "-Wall", "-Wno-unused-function",

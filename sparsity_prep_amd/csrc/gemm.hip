@@ -636,15 +636,17 @@ void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles, int64_t n_beg
 }
 
 // ============================================================================
-// Decode / small-T: no LDS.  Each wave owns 16 weight rows and a range of
-// 512-element K chunks; lane (r = l%16, q = l/16) streams the 64 code bytes
+// Decode / small-T.  A workgroup of kSmallWaves waves owns 16 weight rows and
+// splits K between its waves (wave w takes the w-th contiguous share of the
+// 512-element K chunks); lane (r = l%16, q = l/16) streams the 64 code bytes
 // and the scale dword of weight row r in K tile 4c+q of chunk c, so quarter q
 // feeds blocks 4q..4q+3 and MFMA j (opsel j) uses block 4q+j.  In the K-tiled
 // layout the 16 rows of one quarter are one contiguous kilobyte.  Token rows
-// come the same way (they are few and stay in L2).  With several K splits the
-// partial sums meet in Y through FP32 atomic adds (Y zeroed first).
+// come the same way (they are few and stay in L2).  Each wave loads its next
+// weight chunk before it multiplies the current one; the waves' partial sums meet in
+// LDS and are added in wave order, so the result does not depend on timing.
 // ============================================================================
-constexpr int kSmallWaves = 4;
+constexpr int kSmallWaves = 8;
 constexpr int kChunkK = 512;
 
 struct Chunk64 {
@@ -673,83 +675,115 @@ __device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t rc, __amdgpu_b
 __device__ __forceinline__ v4i as_v4i(uint4 u) { return v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w}; }
 
 template <int FM>
-__global__ __launch_bounds__(kSmallWaves * 64) void k_dual_gemm_mx_small(LinearArgs a, int64_t chunks_per_split,
-                                                                          int atomic) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r = lane & 15, q = lane >> 4;
-    const int64_t n0 = ((int64_t)blockIdx.x * kSmallWaves + wave) * 16;
-    if (n0 >= a.nout) return;
+struct SmallGemm {
+    __amdgpu_buffer_rsrc_t rW, rWs, rXb, rXr, rXbs, rXrs;
+    uint32_t wrow, wsrow, x_row[FM], xs_row[FM];
+    uint32_t nout, T;
+    int q;
+    int64_t K;
+
+    __device__ __forceinline__ void load_w(int64_t c, Chunk64 &w) const {
+        load_chunk(rW, rWs, wrow, wsrow, nout, c, q, K, w);
+    }
+
+    // the token rows' chunk c (few rows, L2-resident) and the MFMAs with the
+    // weight chunk w
+    __device__ __forceinline__ void mma(int64_t c, const Chunk64 &w, v4f (&acc)[FM]) const {
+        Chunk64 xb[FM], xr[FM];
+#pragma unroll
+        for (int f = 0; f < FM; f++) {
+            load_chunk(rXb, rXbs, x_row[f], xs_row[f], T, c, q, K, xb[f]);
+            load_chunk(rXr, rXrs, x_row[f], xs_row[f], T, c, q, K, xr[f]);
+        }
+#pragma unroll
+        for (int f = 0; f < FM; f++) {
+            const Chunk64 &b = xb[f], &r = xr[f];
+            acc[f] = mfma_fp4_sel<0>(as_v4i(w.u[0]), as_v4i(b.u[0]), acc[f], (int)w.sc, (int)b.sc);
+            acc[f] = mfma_fp4_sel<0>(as_v4i(w.u[0]), as_v4i(r.u[0]), acc[f], (int)w.sc, (int)r.sc);
+            acc[f] = mfma_fp4_sel<1>(as_v4i(w.u[1]), as_v4i(b.u[1]), acc[f], (int)w.sc, (int)b.sc);
+            acc[f] = mfma_fp4_sel<1>(as_v4i(w.u[1]), as_v4i(r.u[1]), acc[f], (int)w.sc, (int)r.sc);
+            acc[f] = mfma_fp4_sel<2>(as_v4i(w.u[2]), as_v4i(b.u[2]), acc[f], (int)w.sc, (int)b.sc);
+            acc[f] = mfma_fp4_sel<2>(as_v4i(w.u[2]), as_v4i(r.u[2]), acc[f], (int)w.sc, (int)r.sc);
+            acc[f] = mfma_fp4_sel<3>(as_v4i(w.u[3]), as_v4i(b.u[3]), acc[f], (int)w.sc, (int)b.sc);
+            acc[f] = mfma_fp4_sel<3>(as_v4i(w.u[3]), as_v4i(r.u[3]), acc[f], (int)w.sc, (int)r.sc);
+        }
+    }
+};
+
+template <int FM>
+__global__ __launch_bounds__(kSmallWaves * 64) void k_dual_gemm_mx_small(LinearArgs a) {
+    __shared__ v4f part[kSmallWaves][FM][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
     const int64_t K = a.K, kb = K / 2, ks = K / 32;
     const int64_t nch = (K + kChunkK - 1) / kChunkK;
-    const int64_t c_begin = blockIdx.y * chunks_per_split;
-    const int64_t c_end = min(nch, c_begin + chunks_per_split);
+    const int64_t cpw = (nch + kSmallWaves - 1) / kSmallWaves;
+    const int64_t c0 = wave * cpw;
+    const int64_t c1 = c0 + cpw < nch ? c0 + cpw : nch;
 
-    const auto rW = make_rsrc(a.w_codes, (uint32_t)(a.nout * kb));
-    const auto rWs = make_rsrc(a.w_scales, (uint32_t)(a.nout * ks));
-    const auto rXb = make_rsrc(a.b_codes, (uint32_t)(a.T * kb));
-    const auto rXr = make_rsrc(a.r_codes, (uint32_t)(a.T * kb));
-    const auto rXbs = make_rsrc(a.b_scales, (uint32_t)(a.T * ks));
-    const auto rXrs = make_rsrc(a.r_scales, (uint32_t)(a.T * ks));
+    SmallGemm<FM> g;
+    g.rW = make_rsrc(a.w_codes, (uint32_t)(a.nout * kb));
+    g.rWs = make_rsrc(a.w_scales, (uint32_t)(a.nout * ks));
+    g.rXb = make_rsrc(a.b_codes, (uint32_t)(a.T * kb));
+    g.rXr = make_rsrc(a.r_codes, (uint32_t)(a.T * kb));
+    g.rXbs = make_rsrc(a.b_scales, (uint32_t)(a.T * ks));
+    g.rXrs = make_rsrc(a.r_scales, (uint32_t)(a.T * ks));
+    g.nout = (uint32_t)a.nout;
+    g.T = (uint32_t)a.T;
+    g.q = lane >> 4;
+    g.K = K;
     const bool wvalid = n0 + r < a.nout;
-    const uint32_t wrow = wvalid ? (uint32_t)((n0 + r) * (kTileK / 2)) : kOutOfRange;
-    const uint32_t wsrow = wvalid ? (uint32_t)((n0 + r) * (kTileK / 32)) : kOutOfRange;
-    uint32_t x_row[FM], xs_row[FM];
+    g.wrow = wvalid ? (uint32_t)((n0 + r) * (kTileK / 2)) : kOutOfRange;
+    g.wsrow = wvalid ? (uint32_t)((n0 + r) * (kTileK / 32)) : kOutOfRange;
 #pragma unroll
     for (int f = 0; f < FM; f++) {
         const int64_t m = f * 16 + r;
         const int64_t src = m < a.rows ? (a.row_index ? (int64_t)a.row_index[m] : m) : -1;
-        x_row[f] = src >= 0 ? (uint32_t)(src * (kTileK / 2)) : kOutOfRange;
-        xs_row[f] = src >= 0 ? (uint32_t)(src * (kTileK / 32)) : kOutOfRange;
+        g.x_row[f] = src >= 0 ? (uint32_t)(src * (kTileK / 2)) : kOutOfRange;
+        g.xs_row[f] = src >= 0 ? (uint32_t)(src * (kTileK / 32)) : kOutOfRange;
     }
 
     v4f acc[FM];
 #pragma unroll
     for (int f = 0; f < FM; f++) acc[f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-    for (int64_t c = c_begin; c < c_end; c++) {
-        Chunk64 w, xb[FM], xr[FM];
-        load_chunk(rW, rWs, wrow, wsrow, (uint32_t)a.nout, c, q, K, w);
-#pragma unroll
-        for (int f = 0; f < FM; f++) {
-            load_chunk(rXb, rXbs, x_row[f], xs_row[f], (uint32_t)a.T, c, q, K, xb[f]);
-            load_chunk(rXr, rXrs, x_row[f], xs_row[f], (uint32_t)a.T, c, q, K, xr[f]);
-        }
-#pragma unroll
-        for (int f = 0; f < FM; f++) {
-            acc[f] = mfma_fp4_sel<0>(as_v4i(w.u[0]), as_v4i(xb[f].u[0]), acc[f], (int)w.sc, (int)xb[f].sc);
-            acc[f] = mfma_fp4_sel<0>(as_v4i(w.u[0]), as_v4i(xr[f].u[0]), acc[f], (int)w.sc, (int)xr[f].sc);
-            acc[f] = mfma_fp4_sel<1>(as_v4i(w.u[1]), as_v4i(xb[f].u[1]), acc[f], (int)w.sc, (int)xb[f].sc);
-            acc[f] = mfma_fp4_sel<1>(as_v4i(w.u[1]), as_v4i(xr[f].u[1]), acc[f], (int)w.sc, (int)xr[f].sc);
-            acc[f] = mfma_fp4_sel<2>(as_v4i(w.u[2]), as_v4i(xb[f].u[2]), acc[f], (int)w.sc, (int)xb[f].sc);
-            acc[f] = mfma_fp4_sel<2>(as_v4i(w.u[2]), as_v4i(xr[f].u[2]), acc[f], (int)w.sc, (int)xr[f].sc);
-            acc[f] = mfma_fp4_sel<3>(as_v4i(w.u[3]), as_v4i(xb[f].u[3]), acc[f], (int)w.sc, (int)xb[f].sc);
-            acc[f] = mfma_fp4_sel<3>(as_v4i(w.u[3]), as_v4i(xr[f].u[3]), acc[f], (int)w.sc, (int)xr[f].sc);
-        }
+    // two weight chunks in flight: the next one loads while the current one
+    // multiplies
+    Chunk64 wa, wb;
+    if (c0 < c1) g.load_w(c0, wa);
+    for (int64_t c = c0; c < c1; c += 2) {
+        if (c + 1 < c1) g.load_w(c + 1, wb);
+        g.mma(c, wa, acc);
+        if (c + 2 < c1) g.load_w(c + 2, wa);
+        if (c + 1 < c1) g.mma(c + 1, wb, acc);
     }
+
+#pragma unroll
+    for (int f = 0; f < FM; f++) part[wave][f][lane] = acc[f];
+    __syncthreads();
+    if (wave != 0) return;
 #pragma unroll
     for (int f = 0; f < FM; f++) {
+        v4f s = part[0][f][lane];
+#pragma unroll
+        for (int w = 1; w < kSmallWaves; w++) {
+            const v4f p = part[w][f][lane];
+            s = v4f{__fadd_rn(s.x, p.x), __fadd_rn(s.y, p.y), __fadd_rn(s.z, p.z), __fadd_rn(s.w, p.w)};
+        }
         const int64_t m = f * 16 + r;
         if (m >= a.rows) continue;
         float *yrow = a.y + m * a.ldy;
-        const int64_t n = n0 + q * 4;
-        const float vals[4] = {acc[f].x, acc[f].y, acc[f].z, acc[f].w};
-        if (atomic) {
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                if (n + i < a.nout) atomicAdd(yrow + n + i, vals[i]);
-        } else if (a.y_vec && n + 3 < a.nout) {
-            *reinterpret_cast<v4f *>(yrow + n) = acc[f];
+        const int64_t n = n0 + (lane >> 4) * 4;
+        if (a.y_vec && n + 3 < a.nout) {
+            *reinterpret_cast<v4f *>(yrow + n) = s;
         } else {
+            const float vals[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
             for (int i = 0; i < 4; i++)
                 if (n + i < a.nout) yrow[n + i] = vals[i];
         }
     }
-}
-
-__global__ void k_zero_rows(float *y, int64_t rows, int64_t cols, int64_t ldy) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < rows * cols) y[(i / cols) * ldy + i % cols] = 0.0f;
 }
 
 // ============================================================================
@@ -776,22 +810,8 @@ static hipError_t launch_prefill(const LinearArgs &a, hipStream_t st, int64_t n_
 
 template <int FM>
 static hipError_t launch_small(const LinearArgs &a, hipStream_t st) {
-    const int64_t nwaves_n = (a.nout + 15) / 16;
-    const int64_t nch = (a.K + kChunkK - 1) / kChunkK;
-    // aim for ~8 waves per CU on 256 CUs
-    int64_t split = (2048 + nwaves_n - 1) / nwaves_n;
-    if (split > nch) split = nch;
-    if (split < 1) split = 1;
-    const int64_t cps = (nch + split - 1) / split;
-    split = (nch + cps - 1) / cps;
-    const int atomic = split > 1;
-    if (atomic) {
-        const int64_t n = a.rows * a.nout;
-        hipLaunchKernelGGL(k_zero_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.y, a.rows,
-                           a.nout, a.ldy);
-    }
-    const dim3 grid((unsigned)((nwaves_n + kSmallWaves - 1) / kSmallWaves), (unsigned)split);
-    hipLaunchKernelGGL((k_dual_gemm_mx_small<FM>), grid, dim3(kSmallWaves * 64), 0, st, a, cps, atomic);
+    hipLaunchKernelGGL((k_dual_gemm_mx_small<FM>), dim3((unsigned)((a.nout + 15) / 16)), dim3(kSmallWaves * 64), 0, st,
+                       a);
     return hipGetLastError();
 }
 

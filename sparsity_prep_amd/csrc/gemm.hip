@@ -135,13 +135,14 @@ struct StageLayout {
     // rows per instruction; 4-byte scale slots, RPI rows per instruction,
     // spread over the waves (surplus waves repeat an earlier instruction:
     // identical bytes to identical places)
-    static constexpr int W_LD = BN / 16 / NW;
-    static constexpr int X_LD = BM / 16 / NW;
+    static constexpr int W_NI = BN / 16, X_NI = BM / 16;  // 16-row code loads per array
+    static constexpr int W_LD = (W_NI + NW - 1) / NW;
+    static constexpr int X_LD = (X_NI + NW - 1) / NW;
     static constexpr int RPI = 64 * 4 / SB;
     static constexpr int SC_W = BN / RPI, SC_X = BM / RPI, SC_TOT = SC_W + 2 * SC_X;
     static constexpr int SC_LD = (SC_TOT + NW - 1) / NW;
     static constexpr int PER_STAGE = W_LD + 2 * X_LD + SC_LD;
-    static_assert(BN % (16 * NW) == 0 && BM % (16 * NW) == 0, "tile rows per wave");
+    static_assert(BN % 16 == 0 && BM % 16 == 0, "tile rows per load");
     static_assert(BN % RPI == 0 && BM % RPI == 0, "scale rows per instruction");
 };
 
@@ -252,6 +253,11 @@ struct DualGemm {
 
     __amdgpu_buffer_rsrc_t rW, rWs, rXb, rXr, rXbs, rXrs;
     uint32_t w_off[L::W_LD], x_off[L::X_LD], s_off[L::SC_LD];
+    // 16-row code load j of this wave: slot (wave * LD + j) mod the loads per
+    // array (when the waves do not divide the loads evenly, the surplus ones
+    // repeat a slot: identical bytes to identical places)
+    static __device__ __forceinline__ int w_slot(int wave, int j) { return (wave * L::W_LD + j) % L::W_NI; }
+    static __device__ __forceinline__ int x_slot(int wave, int j) { return (wave * L::X_LD + j) % L::X_NI; }
     // scale load k of this wave: resource, LDS offset in the stage, rows of
     // its array (wave-uniform, fixed at set-up so the K loop has no branches)
     __amdgpu_buffer_rsrc_t s_rsrc[L::SC_LD];
@@ -274,15 +280,15 @@ struct DualGemm {
         uint8_t *st = stage_buf<B, L::BYTES>();
         const int64_t stp = stage < last_step ? stage : last_step;
         if (idx < L::W_LD) {
-            lds_load16(rW, st + L::W_CODES + (wave * L::W_LD + idx) * 1024, w_off[idx],
+            lds_load16(rW, st + L::W_CODES + w_slot(wave, idx) * 1024, w_off[idx],
                        (uint32_t)stp * tw * kRowBytes);
         } else if (idx < L::W_LD + 2 * L::X_LD) {
             const int j = (idx - L::W_LD) >> 1;
             const uint32_t cx = (uint32_t)stp * tx * kRowBytes;
             if (((idx - L::W_LD) & 1) == 0)
-                lds_load16(rXb, st + L::XB_CODES + (wave * L::X_LD + j) * 1024, x_off[j], cx);
+                lds_load16(rXb, st + L::XB_CODES + x_slot(wave, j) * 1024, x_off[j], cx);
             else
-                lds_load16(rXr, st + L::XR_CODES + (wave * L::X_LD + j) * 1024, x_off[j], cx);
+                lds_load16(rXr, st + L::XR_CODES + x_slot(wave, j) * 1024, x_off[j], cx);
         } else {
             const int k = idx - L::W_LD - 2 * L::X_LD;
             lds_load4(s_rsrc[k], st + s_lds[k], s_off[k], (uint32_t)stp * s_rows[k] * L::SB);
@@ -535,14 +541,14 @@ void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles, int64_t n_beg
     // source offsets of the slots this lane fills (fixed over K)
 #pragma unroll
     for (int j = 0; j < L::W_LD; j++) {
-        const int row = (g.wave * L::W_LD + j) * 16 + (g.lane >> 2);
+        const int row = G::w_slot(g.wave, j) * 16 + (g.lane >> 2);
         const int unit = swz_unit(row, g.lane & 3);
         const int64_t n = n0 + row;
         g.w_off[j] = n < a.nout ? (uint32_t)n * kRowBytes + unit * 16 : kOutOfRange;
     }
 #pragma unroll
     for (int j = 0; j < L::X_LD; j++) {
-        const int row = (g.wave * L::X_LD + j) * 16 + (g.lane >> 2);
+        const int row = G::x_slot(g.wave, j) * 16 + (g.lane >> 2);
         const int unit = swz_unit(row, g.lane & 3);
         const int64_t m = tr.m0 + row;
         const int64_t src = m < tr.m_end ? (a.row_index ? (int64_t)a.row_index[m] : m) : -1;
@@ -828,7 +834,8 @@ static int device_cus() {
     return cus[dev];
 }
 
-// Dense MXFP4 tile shapes: 256x256 (8 waves), 128x256 and 128x128 (4 waves).
+// Dense MXFP4 tile shapes: 256x256 and 256x192 (8 waves), 128x256 and 128x128
+// (4 waves).
 // One workgroup fills a CU (LDS), so a launch takes about rounds(tiles / CUs)
 // times the tile time, with smaller tiles paying for their lower operand
 // reuse (relative cost per output element, measured on MI355X for
@@ -837,7 +844,8 @@ struct TileShape {
     int bm, bn;
     double cost;
 };
-constexpr TileShape kMxShapes[3] = {{256, 256, 1.0}, {128, 256, 1.2}, {128, 128, 1.5}};
+constexpr int kNumMxShapes = 4;
+constexpr TileShape kMxShapes[kNumMxShapes] = {{256, 256, 1.0}, {128, 256, 1.2}, {128, 128, 1.5}, {256, 192, 1.27}};
 
 static double shape_time(int s, int64_t rows, int64_t cols, int64_t cus) {
     const TileShape &t = kMxShapes[s];
@@ -847,7 +855,7 @@ static double shape_time(int s, int64_t rows, int64_t cols, int64_t cus) {
 
 static int best_shape(int64_t rows, int64_t cols, int64_t cus, double *t_best) {
     int best = 0;
-    for (int s = 0; s < 3; s++) {
+    for (int s = 0; s < kNumMxShapes; s++) {
         const double t = shape_time(s, rows, cols, cus);
         if (s == 0 || t < *t_best) {
             best = s;
@@ -861,6 +869,7 @@ static hipError_t launch_mx_shape(int s, const LinearArgs &a, hipStream_t st, in
     // split loads over two sub-steps, two LDS reads per MFMA slot
     if (s == 0) return launch_prefill<kFmtMx, 256, 256, 4, 2, 3, 1, 4, 2>(a, st, n_begin, n_end);
     if (s == 1) return launch_prefill<kFmtMx, 128, 256, 2, 2, 3, 1, 4, 2>(a, st, n_begin, n_end);
+    if (s == 3) return launch_prefill<kFmtMx, 256, 192, 4, 2, 3, 1, 4, 2>(a, st, n_begin, n_end);
     return launch_prefill<kFmtMx, 128, 128, 2, 2>(a, st, n_begin, n_end);
 }
 

@@ -243,6 +243,7 @@ LINEAR_CASES = [
     (0, 17, 1280, 100), (0, 64, 4096, 256), (0, 65, 384, 1000), (0, 2, 14336, 64),
     (0, 3, 8320, 40), (0, 48, 4480, 1000),  # small batch: 17 / 9 K chunks over the workgroup's 8 waves
     (0, 2048, 256, 16384),  # large enough that 256x256 tiles are chosen
+    (0, 1000, 384, 12200),  # 256x192 tiles (one full round), ragged rows and columns
     (1, 16, 256, 256), (1, 300, 640, 272), (1, 1, 512, 64), (1, 70, 1024, 130), (1, 257, 3584, 256),
 ]
 

@@ -212,7 +212,9 @@ SHARQ_API size_t sharq_linear_workspace_size(int64_t rows, int64_t K, int64_t no
  *   y            [rows][ldy] FP32, ldy >= nout, 4-byte aligned (128-bit
  *                stores are used when y is 16-byte aligned and ldy % 4 == 0)
  * Contents of group_offsets and row_index are trusted (device memory is not
- * read on the host); out-of-range values are undefined behaviour.
+ * read on the host); out-of-range values are undefined behaviour.  Every
+ * output element is summed in a fixed order (no atomics), so repeated calls
+ * on the same inputs give identical results.
  */
 SHARQ_API sharq_status sharq_linear(const uint8_t *b_codes, const uint8_t *b_scales, const uint8_t *r_codes,
                           const uint8_t *r_scales, const float *x_global_scale, int64_t T,

@@ -269,17 +269,17 @@ __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, 
 }
 
 // ---------------------------------------------------------------- MX, norm, row split over a workgroup
-// A workgroup of four waves handles `rpw` consecutive rows, one at a time;
-// wave w owns chunks w, w+4, ... of a row (at most CPW of them, held in
+// A workgroup of NWG waves handles `rpw` consecutive rows, one at a time;
+// wave w owns chunks w, w+NWG, ... of a row (at most CPW of them, held in
 // registers).  The next row's words are loaded before the current row is
 // reduced and quantized, so its latency hides behind the current row's
-// arithmetic.  Each wave reduces its FP64 partial sums, the four partials
+// arithmetic.  Each wave reduces its FP64 partial sums, the NWG partials
 // meet in LDS (two slots, alternating by row) and every wave adds them in
 // the same fixed order, so all waves derive the same r (and mu).  gamma and
 // beta are loaded once per workgroup.
-template <bool BF16, int NORM, int M, int FAST24, int CPW>
-__global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_split(PrepArgs a, int64_t rpw) {
-    __shared__ double part[2][2][kPrepWaves];
+template <bool BF16, int NORM, int M, int FAST24, int CPW, int NWG>
+__global__ __launch_bounds__(NWG * kWave) void k_prep_mx_split(PrepArgs a, int64_t rpw) {
+    __shared__ double part[2][2][NWG];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const LaneOff lo = lane_offsets<kFmtMx>(a, lane);
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_split(PrepArgs a
     constexpr uint32_t kOnePair = BF16 ? 0x3F803F80u : 0x3C003C00u;  // 1.0, 1.0
 #pragma unroll
     for (int j = 0; j < CPW; j++) {
-        const int64_t e0 = ((int64_t)(wave + kPrepWaves * j) * kWave + lane) * 8;
+        const int64_t e0 = ((int64_t)(wave + NWG * j) * kWave + lane) * 8;
         in[j] = e0 < K;
         raw[j] = in[j] ? *reinterpret_cast<const uint4 *>(a.x + row0 * a.ldx + e0) : make_uint4(0, 0, 0, 0);
         graw[j] = in[j] ? param_raw<true>(a.gamma, e0, kOnePair) : make_uint4(0, 0, 0, 0);
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_split(PrepArgs a
         const bool more = row + 1 < row_end;
 #pragma unroll
         for (int j = 0; j < CPW; j++) {
-            const int64_t e0 = ((int64_t)(wave + kPrepWaves * j) * kWave + lane) * 8;
+            const int64_t e0 = ((int64_t)(wave + NWG * j) * kWave + lane) * 8;
             nraw[j] = (more && in[j]) ? *reinterpret_cast<const uint4 *>(a.x + (row + 1) * a.ldx + e0)
                                       : make_uint4(0, 0, 0, 0);
         }
@@ -323,7 +323,9 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_split(PrepArgs a
         s1 = wave_sum_f64(s1);
         if (lane == 0) part[slot][0][wave] = s1;
         __syncthreads();
-        s1 = ((part[slot][0][0] + part[slot][0][1]) + part[slot][0][2]) + part[slot][0][3];
+        s1 = part[slot][0][0];
+#pragma unroll
+        for (int w = 1; w < NWG; w++) s1 += part[slot][0][w];
         float r, mu = 0.0f;
         if constexpr (NORM == kNormRms) {
             r = (float)(1.0 / sqrt(s1 / (double)K + (double)a.eps));
@@ -344,7 +346,9 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_split(PrepArgs a
             s2 = wave_sum_f64(s2);
             if (lane == 0) part[slot][1][wave] = s2;
             __syncthreads();
-            s2 = ((part[slot][1][0] + part[slot][1][1]) + part[slot][1][2]) + part[slot][1][3];
+            s2 = part[slot][1][0];
+#pragma unroll
+            for (int w = 1; w < NWG; w++) s2 += part[slot][1][w];
             mu = (float)mud;
             r = (float)(1.0 / sqrt(s2 / (double)K + (double)a.eps));
         }
@@ -356,7 +360,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_split(PrepArgs a
                 unpack8<BF16>(braw[j], b);
                 unpack8<BF16>(raw[j], v);
                 normalize8<NORM>(v, g, b, r, mu);
-                decompose_store<kFmtMx, M, FAST24>(a, row, wave + kPrepWaves * j, lane, lo, v, 1.0f, 6.0f);
+                decompose_store<kFmtMx, M, FAST24>(a, row, wave + NWG * j, lane, lo, v, 1.0f, 6.0f);
             }
         }
 #pragma unroll
@@ -649,10 +653,11 @@ static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
         // rows per workgroup: about two workgroups per CU once T allows it
         const int64_t rpw = a.T >= 4 * kPrepRowsGrid ? 4 : (a.T >= 2 * kPrepRowsGrid ? 2 : 1);
         const dim3 rows((unsigned)round_up8((a.T + rpw - 1) / rpw));
+        // four waves of two chunks beat eight waves of one at K = 4096 (MI355X)
         if (K <= (int64_t)kChunk * kPrepWaves * 2)
-            hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 2>), rows, blk, 0, st, a, rpw);
+            hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 2, kPrepWaves>), rows, blk, 0, st, a, rpw);
         else if (K <= (int64_t)kChunk * kPrepWaves * 4)
-            hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 4>), rows, blk, 0, st, a, rpw);
+            hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 4, kPrepWaves>), rows, blk, 0, st, a, rpw);
         else
             hipLaunchKernelGGL((k_prep_mx_2pass<BF16, NORM, M, FAST24>), grid, blk, 0, st, a);
         if (a.global_scale) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, a.global_scale, 1.0f);
@@ -668,7 +673,6 @@ static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
     }
     const int64_t tasks_per_row = (K + (int64_t)kChunk * kStreamChunks - 1) / ((int64_t)kChunk * kStreamChunks);
     const int64_t tasks = a.T * tasks_per_row;
-    // tasks per wave: enough waves for about four per SIMD, each looping
     // one task per wave: measured fastest on MI355X for every shape tried
     // (more resident waves hide the load latency better than an in-wave
     // prefetch of a next task)

@@ -12,11 +12,16 @@ that the 256 MB Infinity Cache cannot serve a step from the previous one.
 Prints one JSON line: whole-step dual-product throughput (algorithmic
 TFLOP/s, 2*T*Nout*K*(1+N/M) per linear), prep GB/s, the roofline of the
 dominant kernel (the dual product) measured with HIP events on the launch
-stream, the CPU oracle timed on a bounded sample on the host, and the
-operator-level error of SharQ next to plain FP4 round-to-nearest.
+stream (with its HBM-side traffic from the committed counter summary under
+profiles/ while the kernel sources match it), the CPU oracle timed on a
+bounded sample on the host, the operator-level error of SharQ next to plain
+FP4 round-to-nearest, the fused SiLU(gate)*up prep of the down projection
+next to the unfused chain, and the same linears as bf16 / FP8 GEMMs.
+Decode batches (64 tokens or fewer) are timed as one HIP graph per step.
 
     python bench.py [--gpus 1] [--steps 30] [--warmup 5]
                     [--workload llama|decode1|decode8|decode64|qwen|moe]
+                    [--graph auto|on|off] [--no-extras] [--no-cpu-baseline]
 """
 from __future__ import annotations
 

@@ -87,9 +87,10 @@ __device__ __forceinline__ void nv_dequant32(v4i c, uint32_t sc2, v8bf out[4]) {
 }
 
 // ============================================================================
-// Prefill: LDS-tiled, three-buffer pipeline fed by direct global->LDS buffer
-// loads (no register staging).  Block tile BM token rows x BN weight rows,
-// WGM x WGN waves, K stage 128 = two 64-wide sub-steps.
+// Prefill: LDS-tiled pipeline (three stage buffers in the shapes used; two
+// supported) fed by direct global->LDS buffer loads (no register staging).
+// Block tile BM token rows x BN weight rows, WGM x WGN waves, K stage 128 =
+// two 64-wide sub-steps.
 //
 // A stage is one K tile of the K-tiled operand layout, so each array's stage
 // is one contiguous run of rows x 64 code bytes (rows x SB scale bytes,
@@ -101,18 +102,21 @@ __device__ __forceinline__ void nv_dequant32(v4i c, uint32_t sc2, v8bf out[4]) {
 //
 // Step s (stage s in buffer s % 3), every wave:
 //   1. MFMAs of sub-step 0 (fragments read during step s-1), with the LDS
-//      reads of stage s's sub-step-1 fragments threaded between them;
+//      reads of stage s's sub-step-1 fragments and the last LSPLIT direct
+//      loads of stage s+2 (into buffer (s+2) % 3, free since step s-1's
+//      barrier) threaded between them;
 //   2. wait until its own LDS reads are done and its own loads of stage s+1
 //      have landed, then barrier: every wave is past its reads of stage s
 //      and all of stage s+1 is in LDS;
-//   3. MFMAs of sub-step 1, with the direct loads of stage s+3 into buffer
-//      s % 3 and the LDS reads of stage s+1's scales and sub-step-0
-//      fragments threaded between them.
-// A stage's global loads thus have two steps to land, every LDS read has
-// the rest of a sub-step to complete, and no wave holds its matrix unit idle
-// behind a burst of memory instructions.  The three buffers are distinct LDS
+//   3. MFMAs of sub-step 1, with the other direct loads of stage s+3 into
+//      buffer s % 3 and the LDS reads of stage s+1's scales and sub-step-0
+//      fragments threaded between them (RPS reads per MFMA).
+// A stage's global loads thus have 1.5 to 2 steps to land, every LDS read
+// has the rest of a sub-step to complete, and no wave holds its matrix unit
+// idle behind a burst of memory instructions.  The buffers are distinct LDS
 // variables so that the compiler's own wait before an LDS read only covers
-// the loads into that buffer.
+// the loads into that buffer.  With two stages (NS = 2) the loads of stage
+// s+2 all go into buffer s % 2 in step s and have one step to land.
 //
 // In sub-step T lane l feeds row l%32 of its fragment and the 32 elements of
 // unit 2q + T, q = l/32 (both operands use the same unit, so the two

@@ -197,6 +197,9 @@ def linear(prep: Prepared, wq: QWeight, group_offsets: Optional[torch.Tensor] = 
     dev = prep.b_codes.device
     if out is None:
         out = torch.empty((rows, wq.nout), dtype=torch.float32, device=dev)
+    elif (out.dim() != 2 or out.dtype != torch.float32 or out.shape[0] < rows or out.shape[1] != wq.nout
+          or out.stride(1) != 1):
+        raise SharqError("out must be a float32 [rows, nout] tensor with unit column stride")
     ws = _workspace(lib().sharq_linear_workspace_size(rows, wq.K, wq.nout, wq.E, wq.fmt), dev)
     st = lib().sharq_linear(
         _ptr(prep.b_codes), _ptr(prep.b_scales), _ptr(prep.r_codes), _ptr(prep.r_scales),

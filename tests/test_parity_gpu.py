@@ -244,6 +244,7 @@ LINEAR_CASES = [
     (0, 3, 8320, 40), (0, 48, 4480, 1000),  # small batch: 17 / 9 K chunks over the workgroup's 8 waves
     (0, 2048, 256, 16384),  # large enough that 256x256 tiles are chosen
     (0, 1000, 384, 12200),  # 256x192 tiles (one full round), ragged rows and columns
+    (0, 300, 128, 200), (0, 5, 128, 40), (1, 130, 128, 96),  # K = 128: a single stage / chunk
     (1, 16, 256, 256), (1, 300, 640, 272), (1, 1, 512, 64), (1, 70, 1024, 130), (1, 257, 3584, 256),
 ]
 
@@ -285,6 +286,48 @@ def test_linear_grouped(fmt):
     y2 = host(sq().linear(pg2, qw, group_offsets=torch.from_numpy(offsets).cuda(), rows=401))
     _, ref2 = ref_linear(pg2, qw, offsets=offsets)
     assert rel_fro(y2, ref2) <= TOL
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_linear_grouped_many_experts(fmt):
+    """More experts than one wave has lanes (the tile lookup takes two
+    passes), empty experts first, last and in between, gathered rows."""
+    K, nout, E, T = 256, 64, 80, 120
+    x = synth.small_case(K, T, "bf16", outliers=2, tag=41)
+    pg = gpu_prepare(x, "bf16", K, 0, None, None, 0.0, 2, 4, fmt)
+    w = synth.small_weight(nout, K, experts=E, tag=42)
+    qw = sq().quantize_weight(dev16(w, "bf16"), fmt=fmt)
+    rng = np.random.default_rng(43)
+    counts = rng.integers(0, 19, E)
+    counts[[0, 1, 37, 63, 64, E - 1]] = 0
+    counts[65] = 300  # one expert with several row tiles, right after the first pass
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    row_index = rng.integers(0, T, offsets[-1]).astype(np.int32)
+    y = host(sq().linear(pg, qw, group_offsets=torch.from_numpy(offsets).cuda(),
+                         row_index=torch.from_numpy(row_index).cuda(), rows=int(offsets[-1])))
+    _, ref = ref_linear(pg, qw, row_index=row_index, offsets=offsets)
+    assert rel_fro(y, ref) <= TOL
+
+
+@pytest.mark.parametrize("T", [300, 5], ids=["tiled", "small"])
+def test_linear_strided_unaligned_output(T):
+    """Y written into a column window of a wider buffer, 12 bytes past a
+    16-byte boundary (scalar stores); the columns around it stay untouched."""
+    K, nout = 512, 72
+    x = synth.small_case(K, T, "bf16", tag=51)
+    pg = gpu_prepare(x, "bf16", K, 0, None, None, 0.0, 2, 4, 0)
+    w = synth.small_weight(nout, K, tag=52)
+    qw = sq().quantize_weight(dev16(w, "bf16"), fmt=0)
+    buf = torch.full((T, nout + 13), float("nan"), dtype=torch.float32, device="cuda")
+    out = buf[:, 3:3 + nout]
+    sq().linear(pg, qw, out=out)
+    torch.cuda.synchronize()
+    full = host(buf)
+    _, ref = ref_linear(pg, qw)
+    assert rel_fro(full[:, 3:3 + nout], ref) <= TOL
+    assert np.isnan(full[:, :3]).all() and np.isnan(full[:, 3 + nout:]).all()
+    dense = host(sq().linear(pg, qw))
+    assert np.array_equal(full[:, 3:3 + nout], dense)
 
 
 def test_determinism():

@@ -16,11 +16,13 @@
 //          E8M0 scales (16x16x128 in the small-T kernel).
 //   NVFP4: an E2M1 code times an E4M3 scale needs up to 6 significant bits,
 //          which no FP4/FP6/FP8 operand holds and a power-of-two block scale
-//          cannot express; bf16 holds it exactly.  The fragments are
-//          dequantized in registers (hardware FP4 conversion with the scale's
-//          power of two, one FP32 multiply by its mantissa) and multiplied
-//          with v_mfma_f32_32x32x16_bf16; the two tensor scales (activation
-//          and weight) are applied to the FP32 accumulator in the epilogue.
+//          cannot express; f16 holds it exactly (as does bf16, but gfx950
+//          multiplies packed f16 and not packed bf16).  The fragments are
+//          dequantized in registers (hardware FP4 -> f16 conversion with the
+//          scale's power of two, one packed f16 multiply by its mantissa)
+//          and multiplied with v_mfma_f32_32x32x16_f16; the two tensor
+//          scales (activation and weight) are applied to the FP32
+//          accumulator in the epilogue.
 //
 // Operand mapping: the weight fragment is the A operand, the activation
 // fragment the B operand, so every group of four accumulator values is four
@@ -35,7 +37,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kCbszFp4 = 4;  // MFMA operand format code for E2M1
 
@@ -61,29 +64,58 @@ __device__ __forceinline__ v4f mfma_fp4_sel(v4i a, v4i b, v4f c, int sa, int sb)
 }
 
 // 32 E2M1 codes (16 bytes, element e in nibble e) whose two halves carry the
-// E4M3 scales in bytes 0 and 1 of sc2 -> 32 bf16 values, in four groups of
+// E4M3 scales in bytes 0 and 1 of sc2 -> 32 f16 values, in four groups of
 // eight (group t = elements 8t..8t+7).  A scale s = 2^e * mant is applied as
-// the hardware conversion's power of two followed by an exact FP32 multiply
-// by mant; code * s has at most 6 significant bits, so the bf16 truncation of
-// the product is exact.
-__device__ __forceinline__ void nv_dequant32(v4i c, uint32_t sc2, v8bf out[4]) {
+// the hardware conversion's power of two (FP4 -> f16 pairs) followed by a
+// packed f16 multiply by mant.  code * s has at most 6 significant bits and
+// a magnitude in [2^-10, 2880] (or is 0), so every step is exact in f16.
+__device__ __forceinline__ void nv_dequant32(v4i c, uint32_t sc2, v8h out[4]) {
 #pragma unroll
     for (int h = 0; h < 2; h++) {
         const uint32_t sb = __float_as_uint(e4m3_value((sc2 >> (8 * h)) & 0xFFu));
         const float p2 = __uint_as_float(sb & 0xFF800000u);
-        const float mant = __uint_as_float((sb & 0x007FFFFFu) | 0x3F800000u);
+        const _Float16 m = (_Float16)__uint_as_float((sb & 0x007FFFFFu) | 0x3F800000u);
+        const v2h mm = {m, m};
 #pragma unroll
         for (int w = 0; w < 2; w++) {
-            float q[8];
-            e2m1_dec8((uint32_t)c[2 * h + w], p2, q);
-            uint32_t pk[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                pk[i] = __builtin_amdgcn_perm(__float_as_uint(__fmul_rn(q[2 * i + 1], mant)),
-                                              __float_as_uint(__fmul_rn(q[2 * i], mant)), 0x07060302u);
-            out[2 * h + w] = __builtin_bit_cast(v8bf, (v4i){(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]});
+            const uint32_t word = (uint32_t)c[2 * h + w];
+            const v2h a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, p2, 0) * mm;
+            const v2h a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, p2, 1) * mm;
+            const v2h a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, p2, 2) * mm;
+            const v2h a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, p2, 3) * mm;
+            out[2 * h + w] = v8h{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
         }
     }
+}
+
+// The same, one group of eight at a time: the scale pair of a fragment
+// decoded once (power of two and f16 mantissa of each 16-element half), then
+// group t (elements 8t..8t+7, half t/2) on demand.
+struct NvScale {
+    float p2[2];
+    v2h mm[2];
+};
+
+__device__ __forceinline__ NvScale nv_scale(uint32_t sc2) {
+    NvScale o;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const uint32_t sb = __float_as_uint(e4m3_value((sc2 >> (8 * h)) & 0xFFu));
+        o.p2[h] = __uint_as_float(sb & 0xFF800000u);
+        const _Float16 m = (_Float16)__uint_as_float((sb & 0x007FFFFFu) | 0x3F800000u);
+        o.mm[h] = v2h{m, m};
+    }
+    return o;
+}
+
+template <int t>
+__device__ __forceinline__ v8h nv_group(v4i c, const NvScale &s) {
+    const uint32_t word = (uint32_t)c[t];
+    const v2h a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, s.p2[t / 2], 0) * s.mm[t / 2];
+    const v2h a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, s.p2[t / 2], 1) * s.mm[t / 2];
+    const v2h a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, s.p2[t / 2], 2) * s.mm[t / 2];
+    const v2h a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, s.p2[t / 2], 3) * s.mm[t / 2];
+    return v8h{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
 }
 
 // ============================================================================
@@ -434,7 +466,7 @@ struct DualGemm {
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
-            // NVFP4: dequantize each fragment once per sub-step, four bf16
+            // NVFP4: dequantize each fragment once per sub-step, four f16
             // MFMAs per fragment pair; side work spread over the token
             // fragments.
             constexpr int NOTHER = MODE == 0 ? 2 * NREAD_FRAGS : NREAD_NEXT;
@@ -442,24 +474,57 @@ struct DualGemm {
             constexpr int LLO = MODE == 0 ? L::PER_STAGE - LSPLIT : 0;
             constexpr int PER_I_OTHER = (NOTHER + FM - 1) / FM;
             constexpr int PER_I_LOAD = (NLOAD + FM - 1) / FM;
-            v8bf wd[FN][4];
+            // Software pipeline over groups of eight K elements: the scales
+            // are decoded first, then group t+1 of the weight fragments (on
+            // the first token fragment) and of the token fragments is
+            // dequantized while the MFMAs of group t run.  Consecutive MFMAs
+            // go to the FN different accumulators, so none waits on the
+            // previous one.
+            NvScale sw[FN], sxb[FM], sxr[FM];
 #pragma unroll
-            for (int j = 0; j < FN; j++) nv_dequant32(f.w[j], s.w[j], wd[j]);
+            for (int j = 0; j < FN; j++) sw[j] = nv_scale(s.w[j]);
 #pragma unroll
             for (int i = 0; i < FM; i++) {
-                v8bf xb[4], xr[4];
-                nv_dequant32(f.xb[i], s.xb[i], xb);
-                nv_dequant32(f.xr[i], s.xr[i], xr);
+                sxb[i] = nv_scale(s.xb[i]);
+                sxr[i] = nv_scale(s.xr[i]);
+            }
+            v8h wd[FN][4], xb[2][4], xr[2][4];
 #pragma unroll
-                for (int j = 0; j < FN; j++)
+            for (int j = 0; j < FN; j++) wd[j][0] = nv_group<0>(f.w[j], sw[j]);
+            xb[0][0] = nv_group<0>(f.xb[0], sxb[0]);
+            xr[0][0] = nv_group<0>(f.xr[0], sxr[0]);
 #pragma unroll
-                    for (int t = 0; t < 4; t++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wd[j][t], xb[t], acc[i][j], 0, 0, 0);
+            for (int i = 0; i < FM; i++) {
+                const int cb = i & 1;
 #pragma unroll
-                for (int j = 0; j < FN; j++)
+                for (int t = 0; t < 4; t++) {
+                    if (t + 1 < 4) {
+                        if (i == 0) {
 #pragma unroll
-                    for (int t = 0; t < 4; t++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wd[j][t], xr[t], acc[i][j], 0, 0, 0);
+                            for (int j = 0; j < FN; j++)
+                                wd[j][t + 1] = t == 0 ? nv_group<1>(f.w[j], sw[j])
+                                             : t == 1 ? nv_group<2>(f.w[j], sw[j]) : nv_group<3>(f.w[j], sw[j]);
+                        }
+                        xb[cb][t + 1] = t == 0 ? nv_group<1>(f.xb[i], sxb[i])
+                                      : t == 1 ? nv_group<2>(f.xb[i], sxb[i]) : nv_group<3>(f.xb[i], sxb[i]);
+                        xr[cb][t + 1] = t == 0 ? nv_group<1>(f.xr[i], sxr[i])
+                                      : t == 1 ? nv_group<2>(f.xr[i], sxr[i]) : nv_group<3>(f.xr[i], sxr[i]);
+                    } else if (i + 1 < FM) {
+                        xb[cb ^ 1][0] = nv_group<0>(f.xb[i + 1], sxb[i + 1]);
+                        xr[cb ^ 1][0] = nv_group<0>(f.xr[i + 1], sxr[i + 1]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < FN; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wd[j][t], xb[cb][t], acc[i][j], 0, 0, 0);
+#pragma unroll
+                    for (int j = 0; j < FN; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wd[j][t], xr[cb][t], acc[i][j], 0, 0, 0);
+#pragma unroll
+                    for (int k = 0; k < 2 * FN; k++) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                    }
+                }
 #pragma unroll
                 for (int k = i * PER_I_LOAD; k < (i + 1) * PER_I_LOAD && k < NLOAD; k++)
                     this->template issue_one<BL>(LLO + k, stage);
@@ -912,6 +977,12 @@ hipError_t launch_linear(const LinearArgs &a, void *ws, size_t ws_bytes, hipStre
     (void)ws;
     (void)ws_bytes;
     if (a.fmt == kFmtMx) return launch_linear_mx(a, st);
+    // NVFP4: 128x256 tiles; short-K products that fill only a few rounds run
+    // faster as 128x128 tiles with two workgroups per CU (measured on
+    // MI355X: the second workgroup's dequantization overlaps the first's MFMAs)
+    const int64_t tiles = ((a.rows + 127) / 128) * ((a.nout + 255) / 256);
+    if (a.offsets == nullptr && a.K <= 4096 && tiles <= 4 * device_cus())
+        return launch_prefill<kFmtNv, 128, 128, 2, 2, 2, 2, 0, 1>(a, st);
     return launch_prefill<kFmtNv, 128, 256, 2, 2, 3, 1, 4, 1>(a, st);
 }
 

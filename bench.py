@@ -37,7 +37,7 @@ import numpy as np
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
-BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+F16_PEAK_TFLOPS = 2500.0        # MI355X dense f16 / bf16 MFMA
 # 32x32x64 block-scaled FP4 MFMA issued back to back from registers with
 # random operands (no memory traffic), measured on MI355X: the chip lowers its
 # clock under that load (about 1.5 GHz against 2.4 GHz with constant operands)
@@ -500,7 +500,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4-e2m1 (nvfp4) -> bf16 mfma -> fp32" if nv else "fp4-e2m1 (mxfp4) x fp4 -> fp32",
+        "dtype": "fp4-e2m1 (nvfp4) -> f16 mfma -> fp32" if nv else "fp4-e2m1 (mxfp4) x fp4 -> fp32",
         "data": "synthetic (seeded; model-shaped activations with outlier channels, N(0,0.02) weights)",
         "config": {"workload": f"{wl.name}" + ("" if tokens == wl.tokens else f"_T{tokens}"),
                    "tokens": tokens, "linears": {L.lin.name: [L.lin.k, L.lin.nout] for L in layers},
@@ -519,14 +519,14 @@ def main():
                        for i, L in enumerate(layers)},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": MXFP4_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / MXFP4_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "k_dual_gemm<NVFP4> (dual-path product, bf16 MFMA)" if nv else "k_dual_gemm<MXFP4> (dual-path product)",
+                     "kernel": "k_dual_gemm<NVFP4> (dual-path product, f16 MFMA)" if nv else "k_dual_gemm<MXFP4> (dual-path product)",
                      "per_launch": "algorithmic 2*rows*Nout*K*(1+N/M) flops / HIP-event launch time, "
                                    "summed over the linears"},
         "roofline_prep": {"bound": "hbm", "achieved": round(prep_gbps, 1), "peak": HBM_PEAK_GBPS,
                           "unit": "GB/s", "frac": round(prep_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
     }
     if nv:
-        result["roofline"]["frac_of_bf16_peak"] = round(gemm_tflops / BF16_PEAK_TFLOPS, 4)
+        result["roofline"]["frac_of_f16_peak"] = round(gemm_tflops / F16_PEAK_TFLOPS, 4)
     if wl.name == "llama3.1-8b_prefill_T2048_mxfp4" and tokens == wl.tokens:
         for key, fname in (("roofline", "k_dual_gemm_mxfp4_llama3.1-8b_prefill_T2048.traffic.json"),
                            ("roofline_prep", "k_prep_mxfp4_llama3.1-8b_prefill_T2048.traffic.json")):

@@ -63,58 +63,43 @@ __device__ __forceinline__ v4f mfma_fp4_sel(v4i a, v4i b, v4f c, int sa, int sb)
                                                            OPSEL, sb);
 }
 
-// 32 E2M1 codes (16 bytes, element e in nibble e) whose two halves carry the
-// E4M3 scales in bytes 0 and 1 of sc2 -> 32 f16 values, in four groups of
-// eight (group t = elements 8t..8t+7).  A scale s = 2^e * mant is applied as
-// the hardware conversion's power of two (FP4 -> f16 pairs) followed by a
-// packed f16 multiply by mant.  code * s has at most 6 significant bits and
-// a magnitude in [2^-10, 2880] (or is 0), so every step is exact in f16.
-__device__ __forceinline__ void nv_dequant32(v4i c, uint32_t sc2, v8h out[4]) {
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-        const uint32_t sb = __float_as_uint(e4m3_value((sc2 >> (8 * h)) & 0xFFu));
-        const float p2 = __uint_as_float(sb & 0xFF800000u);
-        const _Float16 m = (_Float16)__uint_as_float((sb & 0x007FFFFFu) | 0x3F800000u);
-        const v2h mm = {m, m};
-#pragma unroll
-        for (int w = 0; w < 2; w++) {
-            const uint32_t word = (uint32_t)c[2 * h + w];
-            const v2h a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, p2, 0) * mm;
-            const v2h a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, p2, 1) * mm;
-            const v2h a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, p2, 2) * mm;
-            const v2h a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, p2, 3) * mm;
-            out[2 * h + w] = v8h{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
-        }
-    }
-}
+// NVFP4 fragment dequantization.  A lane's fragment is 32 E2M1 codes (16
+// bytes, element e in nibble e) whose two 16-element halves carry E4M3
+// scales in bytes 0 and 1 of its scale pair.  A scale s = 2^e * mant is
+// applied as the hardware conversion's power of two (FP4 -> f16 pairs)
+// followed by a packed f16 multiply by mant; code * s has at most 6
+// significant bits and a magnitude in [2^-10, 2880] (or is 0), so every step
+// is exact in f16.  The scale pair is decoded once (the hardware FP8, OCP
+// E4M3, conversion is exact, subnormal scales included): the power of two of
+// each half and both f16 mantissas in one register; then group t (elements
+// 8t..8t+7, half t/2) is converted on demand.
+typedef float v2f __attribute__((ext_vector_type(2)));
 
-// The same, one group of eight at a time: the scale pair of a fragment
-// decoded once (power of two and f16 mantissa of each 16-element half), then
-// group t (elements 8t..8t+7, half t/2) on demand.
 struct NvScale {
     float p2[2];
-    v2h mm[2];
+    v2h mp;
 };
 
 __device__ __forceinline__ NvScale nv_scale(uint32_t sc2) {
+    const v2f sv = __builtin_amdgcn_cvt_pk_f32_fp8((int)sc2, false);
     NvScale o;
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-        const uint32_t sb = __float_as_uint(e4m3_value((sc2 >> (8 * h)) & 0xFFu));
-        o.p2[h] = __uint_as_float(sb & 0xFF800000u);
-        const _Float16 m = (_Float16)__uint_as_float((sb & 0x007FFFFFu) | 0x3F800000u);
-        o.mm[h] = v2h{m, m};
-    }
+    const uint32_t b0 = __float_as_uint(sv.x), b1 = __float_as_uint(sv.y);
+    o.p2[0] = __uint_as_float(b0 & 0xFF800000u);
+    o.p2[1] = __uint_as_float(b1 & 0xFF800000u);
+    o.mp = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(__uint_as_float((b0 & 0x007FFFFFu) | 0x3F800000u),
+                                                               __uint_as_float((b1 & 0x007FFFFFu) | 0x3F800000u)));
     return o;
 }
 
 template <int t>
 __device__ __forceinline__ v8h nv_group(v4i c, const NvScale &s) {
     const uint32_t word = (uint32_t)c[t];
-    const v2h a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, s.p2[t / 2], 0) * s.mm[t / 2];
-    const v2h a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, s.p2[t / 2], 1) * s.mm[t / 2];
-    const v2h a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, s.p2[t / 2], 2) * s.mm[t / 2];
-    const v2h a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, s.p2[t / 2], 3) * s.mm[t / 2];
+    const _Float16 m = s.mp[t / 2];
+    const v2h mm = {m, m};
+    const v2h a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, s.p2[t / 2], 0) * mm;
+    const v2h a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, s.p2[t / 2], 1) * mm;
+    const v2h a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, s.p2[t / 2], 2) * mm;
+    const v2h a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, s.p2[t / 2], 3) * mm;
     return v8h{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
 }
 
@@ -977,12 +962,11 @@ hipError_t launch_linear(const LinearArgs &a, void *ws, size_t ws_bytes, hipStre
     (void)ws;
     (void)ws_bytes;
     if (a.fmt == kFmtMx) return launch_linear_mx(a, st);
-    // NVFP4: 128x256 tiles; short-K products that fill only a few rounds run
-    // faster as 128x128 tiles with two workgroups per CU (measured on
-    // MI355X: the second workgroup's dequantization overlaps the first's MFMAs)
-    const int64_t tiles = ((a.rows + 127) / 128) * ((a.nout + 255) / 256);
-    if (a.offsets == nullptr && a.K <= 4096 && tiles <= 4 * device_cus())
-        return launch_prefill<kFmtNv, 128, 128, 2, 2, 2, 2, 0, 1>(a, st);
+    // NVFP4: 128x256 tiles; products with K <= 4096 run faster as 128x128
+    // tiles with two workgroups per CU (measured on MI355X: one workgroup's
+    // dequantization overlaps the other's MFMAs, which the shorter K loop's
+    // per-tile overheads favour)
+    if (a.offsets == nullptr && a.K <= 4096) return launch_prefill<kFmtNv, 128, 128, 2, 2, 2, 2, 0, 1>(a, st);
     return launch_prefill<kFmtNv, 128, 256, 2, 2, 3, 1, 4, 1>(a, st);
 }
 

@@ -309,6 +309,32 @@ def test_linear_grouped_many_experts(fmt):
     assert rel_fro(y, ref) <= TOL
 
 
+@pytest.mark.parametrize("T", [4, 300], ids=["short", "tiled"])
+def test_nvfp4_every_block_scale(T):
+    """NVFP4 product where the 16-element blocks take every finite E4M3
+    block scale (subnormal ones included) and a one-hot weight picks one
+    element per block: every output is a single exact product, so the GPU
+    must match the oracle's decoding of the same codes and scales exactly."""
+    K, nout = 2048, 128
+    e4m3 = np.array([oracle.e4m3_decode(c) for c in range(127)], np.float64)
+    x = np.zeros((T, K), np.float32)
+    for t in range(T):
+        codes = 1 + (np.arange(K // 16) + 7 * t) % 126          # 1..126: all finite non-zero scales
+        x[t, ::16] = (6.0 * e4m3[codes]).astype(np.float32)      # block amax = 6 * scale, code 6
+        x[t, 16 * (t % (K // 16))] = 2688.0                        # tensor amax: G = 1
+    w = np.zeros((nout, K), np.float32)
+    w[np.arange(nout), 16 * np.arange(nout)] = 2688.0            # weight tensor scale 1, code 6 x 448
+    xb, wb = synth.to_bits(x, "bf16"), synth.to_bits(w, "bf16")
+    pg = gpu_prepare(xb, "bf16", K, 0, None, None, 0.0, 2, 4, 1)
+    assert float(host(pg.global_scale)[0]) == 1.0
+    qw = sq().quantize_weight(dev16(wb, "bf16"), fmt=1)
+    y = host(sq().linear(pg, qw))
+    _, ref = ref_linear(pg, qw)
+    assert np.array_equal(y, ref.astype(np.float32))
+    assert float(host(qw.global_scale)[0]) == 1.0
+    assert np.array_equal(y, x[:, ::16][:, :nout] * np.float32(2688.0))
+
+
 @pytest.mark.parametrize("T", [300, 5], ids=["tiled", "small"])
 def test_linear_strided_unaligned_output(T):
     """Y written into a column window of a wider buffer, 12 bytes past a

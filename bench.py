@@ -10,18 +10,20 @@ the timed region; several copies of every input and weight are rotated so
 that the 256 MB Infinity Cache cannot serve a step from the previous one.
 
 Prints one JSON line: whole-step dual-product throughput (algorithmic
-TFLOP/s, 2*T*Nout*K*(1+N/M) per linear), prep GB/s, the roofline of the
-dominant kernel (the dual product) measured with HIP events on the launch
-stream (with its HBM-side traffic from the committed counter summary under
-profiles/ while the kernel sources match it), the CPU oracle timed on a
-bounded sample on the host, the operator-level error of SharQ next to plain
-FP4 round-to-nearest, the fused SiLU(gate)*up prep of the down projection
-next to the unfused chain, and the same linears as bf16 / FP8 GEMMs.
-Decode batches (64 tokens or fewer) are timed as one HIP graph per step.
+TFLOP/s, 2*T*Nout*K*(1+N/M) per linear) with every timed step run as one
+captured HIP graph (--graph off: eager launches), prep GB/s, the roofline of
+the dominant kernel (the dual product) from per-launch times taken with HIP
+events on the launch stream (eager steps around every launch; for decode
+batches, graphs holding one phase over the rotated copies), with its
+HBM-side traffic from the committed counter summary under profiles/ while
+the kernel sources match it, the CPU oracle timed on a bounded sample on
+the host, the operator-level error of SharQ next to plain FP4
+round-to-nearest, the fused SiLU(gate)*up prep of the down projection next
+to the unfused chain, and the same linears as bf16 / FP8 GEMMs.
 
     python bench.py [--gpus 1] [--steps 30] [--warmup 5]
                     [--workload llama|decode1|decode8|decode64|qwen|moe]
-                    [--graph auto|on|off] [--no-extras] [--no-cpu-baseline]
+                    [--graph on|off] [--no-extras] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -51,11 +53,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama")
-    ap.add_argument("--rotate", type=int, default=3, help="copies of every input rotated across steps")
+    ap.add_argument("--rotate", type=int, default=None,
+                    help="copies of every input and weight rotated across steps (default: 3, and 8 for "
+                         "decode batches, so that the rotated set outgrows the 256 MB Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
-                    help="time the step as one captured HIP graph (auto: for decode batches, where "
-                         "host launch overhead would otherwise dominate)")
+    ap.add_argument("--graph", choices=["on", "off"], default="on",
+                    help="run every timed step as one captured HIP graph (off: eager launches "
+                         "from the host, with HIP events around every launch)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the fused SiLU(gate)*up prep and the bf16 / fp8 GEMM comparisons")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -283,6 +287,18 @@ def _event_ms(torch, fn, reps=20):
     return a.elapsed_time(b) / reps
 
 
+def _replay_ms(torch, graph):
+    """Time of one replay of a captured graph (HIP events, after one warm replay)."""
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
 def swiglu_report(sq, torch, wl, layers):
     """The down projection's prep from the gate/up product's float32 output:
     fused (SiLU(gate)*up computed inside the prep kernel) against an unfused
@@ -370,11 +386,15 @@ def measured_traffic(name):
 
 
 def build_layers(args, sq, torch, synth, dev):
+    if args.rotate is None and not args.workload.startswith("decode"):
+        args.rotate = 3
     if args.workload == "llama":
         wl = synth.WORKLOADS[1]
         return wl, [Layer(sq, torch, synth, wl, lin, wl.tokens, args.rotate, dev) for lin in wl.linears]
     if args.workload.startswith("decode"):
         wl, tokens = synth.WORKLOADS[2], int(args.workload[len("decode"):])
+        if args.rotate is None:
+            args.rotate = 8
         return wl, [Layer(sq, torch, synth, wl, lin, tokens, args.rotate, dev) for lin in wl.linears]
     if args.workload == "qwen":
         wl = synth.WORKLOADS[3]
@@ -421,10 +441,22 @@ def main():
             L.run(sq, i)
     torch.cuda.synchronize()
 
-    use_graph = args.graph == "on" or (args.graph == "auto" and layers[0].prep_tokens <= 64)
+    use_graph = args.graph == "on"
+    decode = layers[0].prep_tokens <= 64
+    prep_ms = [0.0] * len(layers)
+    gemm_ms = [0.0] * len(layers)
+
+    def eager_steps(evs):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            for li, L in enumerate(layers):
+                L.run(sq, s, None if evs is None else evs[s][li])
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
     if use_graph:
-        # one graph per rotated copy, each holding the whole step; per-phase
-        # graphs give the kernel times (events around back-to-back replays)
+        # one captured graph per rotated copy, holding the whole step
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -433,20 +465,13 @@ def main():
                     L.run(sq, i)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        step_graphs, phase_graphs = [], []
+        step_graphs = []
         for r in range(args.rotate):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for L in layers:
                     L.run(sq, r)
             step_graphs.append(g)
-        for L in layers:
-            gp, gg = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gp):
-                L.run_prep(sq, 0)
-            with torch.cuda.graph(gg):
-                L.run_gemm(sq, 0)
-            phase_graphs.append((gp, gg))
         torch.cuda.synchronize()
         for i in range(args.warmup):
             step_graphs[i % args.rotate].replay()
@@ -455,26 +480,30 @@ def main():
         for s in range(args.steps):
             step_graphs[s % args.rotate].replay()
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        ms_step = (t1 - t0) * 1e3 / args.steps
-        prep_ms, gemm_ms = [], []
-        for gp, gg in phase_graphs:
-            prep_ms.append(_event_ms(torch, gp.replay, reps=args.steps))
-            gemm_ms.append(_event_ms(torch, gg.replay, reps=args.steps))
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    if use_graph and decode:
+        # per-launch times of decode kernels (a few microseconds each, shorter
+        # than a host launch): one graph per phase holding that phase once per
+        # timed step over the rotated copies, timed with HIP events around a replay
+        for li, L in enumerate(layers):
+            gp, gg = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gp):
+                for i in range(args.steps):
+                    L.run_prep(sq, i)
+            with torch.cuda.graph(gg):
+                for i in range(args.steps):
+                    L.run_gemm(sq, i)
+            prep_ms[li] = _replay_ms(torch, gp) / args.steps
+            gemm_ms[li] = _replay_ms(torch, gg) / args.steps
     else:
+        # per-launch times from eager steps with HIP events around every launch
+        # (same order and cache state as the step; each interval also holds the
+        # gap after the preceding launch)
         evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers]
                for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for s in range(args.steps):
-            for li, L in enumerate(layers):
-                L.run(sq, s, evs[s][li])
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        ms_step = (t1 - t0) * 1e3 / args.steps
-
-        prep_ms = [0.0] * len(layers)
-        gemm_ms = [0.0] * len(layers)
+        t_eager = eager_steps(evs)
+        if not use_graph:
+            ms_step = t_eager * 1e3 / args.steps
         for s in range(args.steps):
             for li in range(len(layers)):
                 e = evs[s][li]
@@ -521,7 +550,9 @@ def main():
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / MXFP4_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "k_dual_gemm<NVFP4> (dual-path product, f16 MFMA)" if nv else "k_dual_gemm<MXFP4> (dual-path product)",
                      "per_launch": "algorithmic 2*rows*Nout*K*(1+N/M) flops / HIP-event launch time, "
-                                   "summed over the linears"},
+                                   "summed over the linears",
+                     "timing": ("graphs of one phase over the rotated copies, HIP events around a replay"
+                                if use_graph and decode else "eager steps, HIP events around every launch")},
         "roofline_prep": {"bound": "hbm", "achieved": round(prep_gbps, 1), "peak": HBM_PEAK_GBPS,
                           "unit": "GB/s", "frac": round(prep_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
     }

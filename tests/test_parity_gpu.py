@@ -371,24 +371,11 @@ def test_determinism():
     assert np.array_equal(outs[0][1], outs[1][1])
 
 
-@pytest.mark.parametrize("fmt,T", [(0, 8), (1, 8), (0, 300)], ids=["mx-decode8", "nv-decode8", "mx-T300"])
-def test_graph_replay_matches_eager(fmt, T):
-    """The whole path (prep + product) captured in one HIP graph: every replay,
-    with eager work and synchronizations between replays, reproduces the
-    eager result bit for bit (prepared tensors and the product: every sum
-    is taken in a fixed order)."""
-    K, nout = 2048, 384
-    w = synth.small_weight(nout, K, tag=31 + fmt)
-    qw = sq().quantize_weight(dev16(w, "bf16"), fmt=fmt)
-    x = dev16(synth.small_case(K, T, "bf16", tag=32 + fmt), "bf16")
-    g = dev16(synth.small_gamma(K, "bf16", tag=33), "bf16")
-    out = sq().alloc_prepared(T, K, fmt, x.device)
-    y = torch.empty((T, nout), dtype=torch.float32, device="cuda")
-
-    def step():
-        sq().prepare(x, norm=1, gamma=g, eps=1e-5, n=2, m=4, fmt=fmt, out=out)
-        sq().linear(out, qw, out=y)
-
+def _check_graph_replays(step, out, y):
+    """Run step eagerly, capture it in one HIP graph, then replay the graph
+    three times with eager work and synchronizations in between; every
+    replay must reproduce the eager prepared tensors and product bit for bit
+    (every sum is taken in a fixed order)."""
     step()
     torch.cuda.synchronize()
     ref_p, ref_y = prepared_to_host(out), host(y)
@@ -413,6 +400,49 @@ def test_graph_replay_matches_eager(fmt, T):
         assert np.array_equal(host(y), ref_y), rep
         step()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("fmt,T", [(0, 8), (1, 8), (0, 300), (1, 300)],
+                         ids=["mx-decode8", "nv-decode8", "mx-T300", "nv-T300"])
+def test_graph_replay_matches_eager(fmt, T):
+    """The whole path (normalized prep + product) captured in one HIP graph."""
+    K, nout = 2048, 384
+    w = synth.small_weight(nout, K, tag=31 + fmt)
+    qw = sq().quantize_weight(dev16(w, "bf16"), fmt=fmt)
+    x = dev16(synth.small_case(K, T, "bf16", tag=32 + fmt), "bf16")
+    g = dev16(synth.small_gamma(K, "bf16", tag=33), "bf16")
+    out = sq().alloc_prepared(T, K, fmt, x.device)
+    y = torch.empty((T, nout), dtype=torch.float32, device="cuda")
+
+    def step():
+        sq().prepare(x, norm=1, gamma=g, eps=1e-5, n=2, m=4, fmt=fmt, out=out)
+        sq().linear(out, qw, out=y)
+
+    _check_graph_replays(step, out, y)
+
+
+def test_graph_replay_grouped_matches_eager():
+    """A grouped expert product over gathered rows, after a prep without a
+    norm, captured in one HIP graph."""
+    K, nout, E, T = 768, 256, 6, 200
+    w = synth.small_weight(nout, K, experts=E, tag=34)
+    qw = sq().quantize_weight(dev16(w, "bf16"), fmt=0)
+    x = dev16(synth.small_case(K, T, "bf16", tag=35), "bf16")
+    rng = np.random.default_rng(36)
+    counts = rng.integers(0, 160, E)
+    counts[2] = 0
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(offsets[-1])
+    offs = torch.from_numpy(offsets).cuda()
+    ridx = torch.from_numpy(rng.integers(0, T, rows).astype(np.int32)).cuda()
+    out = sq().alloc_prepared(T, K, 0, x.device)
+    y = torch.empty((rows, nout), dtype=torch.float32, device="cuda")
+
+    def step():
+        sq().prepare(x, norm=0, n=2, m=4, fmt=0, out=out)
+        sq().linear(out, qw, group_offsets=offs, row_index=ridx, rows=rows, out=y)
+
+    _check_graph_replays(step, out, y)
 
 
 # ---------------------------------------------------------------- full-size workloads

@@ -121,7 +121,7 @@ SHARQ_API size_t sharq_prepare_workspace_size(int64_t T, int64_t K, int32_t fmt)
  *                be NULL, otherwise 1.0f is written
  *   workspace    sharq_prepare_workspace_size() bytes (NVFP4 only)
  * All outputs are dense arrays owned by the caller.  T == 0 is a valid
- * no-op.
+ * no-op; T must stay below 2^31 - 64 (SHARQ_ERR_SHAPE otherwise).
  */
 SHARQ_API sharq_status sharq_prepare(const void *x, int32_t x_dtype, int64_t T, int64_t K, int64_t ldx,
                            int32_t norm, const void *gamma, const void *beta, float eps,

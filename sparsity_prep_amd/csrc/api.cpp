@@ -14,6 +14,9 @@ namespace {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// the normalized MXFP4 prep launches one workgroup per row
+constexpr int64_t kMaxPrepRows = ((int64_t)1 << 31) - 64;
+
 int block_of(int32_t fmt) { return fmt == SHARQ_MXFP4 ? 32 : 16; }
 
 bool valid_fmt(int32_t fmt) { return fmt == SHARQ_MXFP4 || fmt == SHARQ_NVFP4; }
@@ -56,6 +59,7 @@ sharq_status sharq_prepare(const void *x, int32_t x_dtype, int64_t T, int64_t K,
     if (norm != SHARQ_NORM_NONE && norm != SHARQ_NORM_RMS && norm != SHARQ_NORM_LAYER)
         return SHARQ_ERR_UNSUPPORTED;
     if (T < 0 || K <= 0 || ldx < K || K % block_of(fmt) != 0) return SHARQ_ERR_SHAPE;
+    if (T >= kMaxPrepRows) return SHARQ_ERR_SHAPE;  // one workgroup per row must fit the grid
     if (m != 1 && m != 2 && m != 4 && m != 8 && m != 16) return SHARQ_ERR_NM;
     if (n < 0 || n > m || K % m != 0) return SHARQ_ERR_NM;
     if (T == 0) return SHARQ_OK;
@@ -99,6 +103,7 @@ sharq_status sharq_prepare_swiglu(const float *gate_up, int64_t T, int64_t K, in
                                   size_t workspace_bytes, void *stream) {
     if (!valid_fmt(fmt)) return SHARQ_ERR_UNSUPPORTED;
     if (T < 0 || K <= 0 || ld < 2 * K || K % block_of(fmt) != 0) return SHARQ_ERR_SHAPE;
+    if (T >= kMaxPrepRows) return SHARQ_ERR_SHAPE;
     if (m != 1 && m != 2 && m != 4 && m != 8 && m != 16) return SHARQ_ERR_NM;
     if (n < 0 || n > m || K % m != 0) return SHARQ_ERR_NM;
     if (T == 0) return SHARQ_OK;

@@ -70,6 +70,7 @@ def test_prepare_validation(L):
     assert prep(L, K=100) == SHAPE                # not a multiple of 32
     assert prep(L, K=256, ldx=128) == SHAPE
     assert prep(L, T=-1) == SHAPE
+    assert prep(L, T=2**31) == SHAPE               # rows beyond the one-workgroup-per-row grid
     assert prep(L, n=5, m=4) == NM
     assert prep(L, n=-1, m=4) == NM
     assert prep(L, n=2, m=3) == NM
@@ -98,6 +99,7 @@ def test_prepare_swiglu_validation(L):
     assert swiglu(L, ld=300) == SHAPE              # ld < 2K
     assert swiglu(L, K=100) == SHAPE
     assert swiglu(L, T=-1) == SHAPE
+    assert swiglu(L, T=2**31) == SHAPE
     assert swiglu(L, n=5) == NM
     assert swiglu(L, gu=None) == NULL
     assert swiglu(L, bc=None) == NULL

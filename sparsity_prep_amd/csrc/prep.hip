@@ -145,18 +145,28 @@ __device__ __forceinline__ uint32_t quant_mx8(const float s[8], uint32_t &codes,
     return (uint32_t)(E + 127);
 }
 
-// NVFP4: 16-element block across a lane pair, tensor scale G (G6 = fl32(6G)).
-__device__ __forceinline__ uint32_t quant_nv8(const float s[8], float G, float G6, uint32_t &codes,
+// NVFP4: 16-element block across a lane pair, tensor scale G, rG6 = the
+// double reciprocal of fl32(6G).  The two quotients the format defines,
+// fl32(amax / fl32(6G)) and fl32(v / D), are formed as float(double(x) * r)
+// with r the double reciprocal of the float divisor.  The quotient of two
+// floats is never closer than 2^-49 (relative) to a midpoint M between
+// adjacent floats: v = M*D would make the 24-bit significand of v a
+// multiple of M's odd 25-bit one, and otherwise v and M*D differ by at least
+// one unit of their common bit grid.  The double product is within 2^-52 of
+// the quotient, so both round to the same float.  A zero divisor gives the
+// same infinities and NaNs as the division.
+__device__ __forceinline__ uint32_t quant_nv8(const float s[8], float G, double rG6, uint32_t &codes,
                                               float deq[8]) {
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(s[i]));
     m = pair_max_nonneg(m);
-    const uint32_t sb = e4m3_encode_sat(__fdiv_rn(m, G6));
+    const uint32_t sb = e4m3_encode_sat((float)((double)m * rG6));
     const float D = __fmul_rn(e4m3_value(sb), G);
+    const double rD = 1.0 / (double)D;
     float u[8], q[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) u[i] = sb != 0u ? __fdiv_rn(s[i], D) : 0.0f;
+    for (int i = 0; i < 8; i++) u[i] = sb != 0u ? (float)((double)s[i] * rD) : 0.0f;
     codes = e2m1_cvt8(u, 1.0f);
     e2m1_dec8(codes, 1.0f, q);
 #pragma unroll
@@ -222,7 +232,7 @@ __device__ __forceinline__ LaneOff lane_offsets(const PrepArgs &a, int lane) {
 // mask, codes and scales.
 template <int FMT, int M, int FAST24>
 __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, int64_t ch, int lane, LaneOff lo,
-                                                const float v[8], float G, float G6) {
+                                                const float v[8], float G, double rG6) {
     bool kp[8];
     select8<M, FAST24>(v, a.n, lane, kp);
     float S[8], dq[8], R[8];
@@ -234,12 +244,12 @@ __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, 
     }
     uint32_t bc, rc, bs, rs;
     if constexpr (FMT == kFmtMx) bs = quant_mx8<true>(S, bc, dq);
-    else bs = quant_nv8(S, G, G6, bc, dq);
+    else bs = quant_nv8(S, G, rG6, bc, dq);
 #pragma unroll
     for (int i = 0; i < 8; i++) R[i] = __fsub_rn(v[i], dq[i]);
     float unused[8];
     if constexpr (FMT == kFmtMx) rs = quant_mx8<false>(R, rc, unused);
-    else rs = quant_nv8(R, G, G6, rc, unused);
+    else rs = quant_nv8(R, G, rG6, rc, unused);
 
     const int64_t K = a.K;
     constexpr int LPB = FMT == kFmtMx ? 4 : 2;  // lanes per scale block
@@ -352,7 +362,7 @@ __global__ __launch_bounds__(NWG * kWave) void k_prep_mx_row(PrepArgs a) {
             unpack8<BF16>(braw[j], b);
             unpack8<BF16>(raw[j], v);
             normalize8<NORM>(v, g, b, r, mu);
-            decompose_store<kFmtMx, M, FAST24>(a, row, wave + NWG * j, lane, lo, v, 1.0f, 6.0f);
+            decompose_store<kFmtMx, M, FAST24>(a, row, wave + NWG * j, lane, lo, v, 1.0f, 0.0);
         }
     }
 }
@@ -404,7 +414,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_2pass(PrepArgs a
             load_param8<BF16, NORM == kNormLayer>(a.beta, e0, b, 0.0f);
             unpack8<BF16>(*reinterpret_cast<const uint4 *>(xr + e0), v);
             normalize8<NORM>(v, g, b, r, mu);
-            decompose_store<kFmtMx, M, FAST24>(a, row, ch, lane, lo, v, 1.0f, 6.0f);
+            decompose_store<kFmtMx, M, FAST24>(a, row, ch, lane, lo, v, 1.0f, 0.0);
         }
     }
 }
@@ -441,10 +451,11 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_stream(PrepArgs a, 
     const int64_t task = xcd_block(blockIdx.x, gridDim.x) * kPrepWaves + wave;
     if (task >= a.T * tpr) return;
     const LaneOff lo = lane_offsets<FMT>(a, lane);
-    float G = 1.0f, G6 = 6.0f;
+    float G = 1.0f;
+    double rG6 = 0.0;  // 1 / fl32(6G), NVFP4 only
     if constexpr (FMT == kFmtNv) {
         G = *a.global_scale;
-        G6 = __fmul_rn(6.0f, G);
+        rG6 = 1.0 / (double)__fmul_rn(6.0f, G);
     }
     uint4 raw[kStreamChunks], graw[kStreamChunks], braw[kStreamChunks];
     stream_load<BF16, NORM>(a, task, tpr, lane, raw, graw, braw);
@@ -466,7 +477,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_stream(PrepArgs a, 
                 unpack8<BF16>(braw[c], b);
                 normalize8<NORM>(v, g, b, r, mu);
             }
-            decompose_store<FMT, M, FAST24>(a, row, c0 + c, lane, lo, v, G, G6);
+            decompose_store<FMT, M, FAST24>(a, row, c0 + c, lane, lo, v, G, rG6);
         }
     }
 }
@@ -523,10 +534,11 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_swiglu(PrepArgs a) 
     const int64_t c0 = (task - row * tpr) * kStreamChunks;
     const float *gr = a.gu + row * a.ldgu;
     const LaneOff lo = lane_offsets<FMT>(a, lane);
-    float G = 1.0f, G6 = 6.0f;
+    float G = 1.0f;
+    double rG6 = 0.0;  // 1 / fl32(6G), NVFP4 only
     if constexpr (FMT == kFmtNv) {
         G = *a.global_scale;
-        G6 = __fmul_rn(6.0f, G);
+        rG6 = 1.0 / (double)__fmul_rn(6.0f, G);
     }
 #pragma unroll
     for (int c = 0; c < kStreamChunks; c++) {
@@ -534,7 +546,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_swiglu(PrepArgs a) 
         if (e0 < K) {
             float v[8];
             swiglu8(gr, K, e0, v);
-            decompose_store<FMT, M, FAST24>(a, row, c0 + c, lane, lo, v, G, G6);
+            decompose_store<FMT, M, FAST24>(a, row, c0 + c, lane, lo, v, G, rG6);
         }
     }
 }
@@ -557,7 +569,103 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_swiglu_rowstats(PrepArgs
 }
 
 // ---------------------------------------------------------------- NVFP4 pre-pass
-// Per row: norm statistics and amax of the normalized row.
+// Per row: norm statistics and amax of the normalized row, one row per
+// workgroup of kPrepWaves waves with all of the row's words loaded at once
+// (wave w owns chunks w, w+kPrepWaves, ..., at most CPW of them); the FP64
+// partial sums and the partial maxima meet in LDS and are combined in a
+// fixed order.  Rows longer than kPrepWaves*CPW chunks use k_nv_rowstats.
+template <bool BF16, int NORM, int CPW>
+__global__ __launch_bounds__(kPrepWaves * kWave) void k_nv_rowstats_wg(PrepArgs a, RowStats *stats) {
+    __shared__ double part[2][kPrepWaves];
+    __shared__ float pmax[kPrepWaves];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t row = xcd_block(blockIdx.x, gridDim.x);
+    if (row >= a.T) return;
+    const int64_t K = a.K;
+    bool in[CPW];
+    uint4 raw[CPW];
+#pragma unroll
+    for (int j = 0; j < CPW; j++) {
+        const int64_t e0 = ((int64_t)(wave + kPrepWaves * j) * kWave + lane) * 8;
+        in[j] = e0 < K;
+        raw[j] = in[j] ? *reinterpret_cast<const uint4 *>(a.x + row * a.ldx + e0) : make_uint4(0, 0, 0, 0);
+    }
+    float v[8];
+    float r = 1.0f, mu = 0.0f;
+    if constexpr (NORM != kNormNone) {
+        double s1 = 0.0;
+#pragma unroll
+        for (int j = 0; j < CPW; j++) {
+            unpack8<BF16>(raw[j], v);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                if constexpr (NORM == kNormRms) s1 = __fma_rn((double)v[i], (double)v[i], s1);  // x*x exact in double
+                else s1 += (double)v[i];
+            }
+        }
+        s1 = wave_sum_f64(s1);
+        if (lane == 0) part[0][wave] = s1;
+        __syncthreads();
+        s1 = part[0][0];
+#pragma unroll
+        for (int w = 1; w < kPrepWaves; w++) s1 += part[0][w];
+        if constexpr (NORM == kNormRms) {
+            r = (float)(1.0 / sqrt(s1 / (double)K + (double)a.eps));
+        } else {
+            const double mud = s1 / (double)K;
+            double s2 = 0.0;
+#pragma unroll
+            for (int j = 0; j < CPW; j++) {
+                if (in[j]) {
+                    unpack8<BF16>(raw[j], v);
+#pragma unroll
+                    for (int i = 0; i < 8; i++) {
+                        const double d = (double)v[i] - mud;
+                        s2 += d * d;  // d*d is rounded on its own, as in the definition
+                    }
+                }
+            }
+            s2 = wave_sum_f64(s2);
+            if (lane == 0) part[1][wave] = s2;
+            __syncthreads();
+            s2 = part[1][0];
+#pragma unroll
+            for (int w = 1; w < kPrepWaves; w++) s2 += part[1][w];
+            mu = (float)mud;
+            r = (float)(1.0 / sqrt(s2 / (double)K + (double)a.eps));
+        }
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPW; j++) {
+        if (in[j]) {
+            const int64_t e0 = ((int64_t)(wave + kPrepWaves * j) * kWave + lane) * 8;
+            unpack8<BF16>(raw[j], v);
+            if constexpr (NORM != kNormNone) {
+                float g[8], b[8];
+                load_param8<BF16, true>(a.gamma, e0, g, 1.0f);
+                load_param8<BF16, NORM == kNormLayer>(a.beta, e0, b, 0.0f);
+                normalize8<NORM>(v, g, b, r, mu);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    if (lane == 0) pmax[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 1; w < kPrepWaves; w++) m = fmaxf(m, pmax[w]);
+        stats[row] = RowStats{r, mu, m, 0.0f};
+    }
+}
+
+// Per row: norm statistics and amax of the normalized row, one row per wave
+// looping over the row (any K; the row is read twice with a norm, three
+// times with LayerNorm, the later reads mostly from cache).
 template <bool BF16, int NORM>
 __global__ __launch_bounds__(kPrepWaves * kWave) void k_nv_rowstats(PrepArgs a, RowStats *stats) {
     const int lane = threadIdx.x & 63;
@@ -652,8 +760,29 @@ static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
     }
     RowStats *stats = reinterpret_cast<RowStats *>(ws);
     if constexpr (FMT == kFmtNv) {
-        const dim3 grid((unsigned)((a.T + kPrepWaves - 1) / kPrepWaves));
-        hipLaunchKernelGGL((k_nv_rowstats<BF16, NORM>), grid, blk, 0, st, a, stats);
+        // one row per workgroup while the row fits in registers (norm rows up
+        // to 8192 elements, rows without norm up to 32768)
+        const dim3 rows((unsigned)round_up8(a.T));
+        constexpr int64_t kWg = (int64_t)kChunk * kPrepWaves;
+        if (K <= kWg * 2)
+            hipLaunchKernelGGL((k_nv_rowstats_wg<BF16, NORM, 2>), rows, blk, 0, st, a, stats);
+        else if (K <= kWg * 4)
+            hipLaunchKernelGGL((k_nv_rowstats_wg<BF16, NORM, 4>), rows, blk, 0, st, a, stats);
+        else {
+            bool done = false;
+            if constexpr (NORM == kNormNone) {
+                if (K <= kWg * 8) {
+                    hipLaunchKernelGGL((k_nv_rowstats_wg<BF16, NORM, 8>), rows, blk, 0, st, a, stats);
+                    done = true;
+                } else if (K <= kWg * 16) {
+                    hipLaunchKernelGGL((k_nv_rowstats_wg<BF16, NORM, 16>), rows, blk, 0, st, a, stats);
+                    done = true;
+                }
+            }
+            if (!done)
+                hipLaunchKernelGGL((k_nv_rowstats<BF16, NORM>), dim3((unsigned)((a.T + kPrepWaves - 1) / kPrepWaves)),
+                                   blk, 0, st, a, stats);
+        }
         hipLaunchKernelGGL(k_nv_tensor_scale, dim3(1), dim3(1024), 0, st, stats, a.T, a.global_scale);
     } else if (a.global_scale) {
         hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, a.global_scale, 1.0f);

@@ -96,6 +96,12 @@ PREP_CASES = [
     (1, 1, "f16", 1, 2, 5, 3584),
     (1, 1, "bf16", 8, 16, 3, 4608),
     (1, 0, "bf16", 4, 4, 2, 48),
+    (0, 1, "bf16", 2, 4, 3, 8192 + 128),   # MXFP4 norm row beyond one workgroup's registers
+    (1, 2, "bf16", 2, 4, 3, 6144),         # NVFP4 statistics: four chunks per wave
+    (1, 1, "bf16", 2, 4, 3, 8192 + 512),   # NVFP4 norm statistics, looped row
+    (1, 0, "bf16", 2, 4, 5, 12288 + 16),   # NVFP4 amax, eight chunks per wave
+    (1, 0, "bf16", 2, 4, 4, 18944),        # NVFP4 amax, sixteen chunks per wave
+    (1, 0, "bf16", 2, 4, 2, 32768 + 256),  # NVFP4 amax, looped row
 ]
 
 

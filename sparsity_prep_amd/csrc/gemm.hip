@@ -931,13 +931,32 @@ static hipError_t launch_mx_shape(int s, const LinearArgs &a, hipStream_t st, in
 // partial last round runs as two launches over column ranges: full rounds
 // of 256x256 tiles, then the remaining columns in the shape that fits them
 // best, instead of a last round that leaves CUs idle.
+// Up to 64 rows: the small-batch kernel (weight rows split over many
+// workgroups, K over their waves; every workgroup re-reads the token rows)
+// or one row of 64x64 tiles with two workgroups per CU, whichever this
+// model of MI355X measurements says is faster: the small kernel streams the
+// weight at about 3.5 / 2.2 / 1.6 / 1.2 TB/s for 16 / 32 / 48 / 64 rows
+// after about 3 us; the tiles take about 0.31 us per 128-wide K step and
+// round of tiles, or stream the weight at 4.5 TB/s, after about 1 us.
+static hipError_t launch_linear_mx_few_rows(const LinearArgs &a, hipStream_t st) {
+    constexpr double kSmallTBps[4] = {3.5, 2.2, 1.6, 1.2};
+    const int fm = a.rows <= 16 ? 1 : a.rows <= 32 ? 2 : a.rows <= 48 ? 3 : 4;
+    const double w_mb = (double)a.nout * (double)a.K * (0.5 + 1.0 / 32.0) * 1e-6;
+    const double t_small = 3.0 + w_mb / kSmallTBps[fm - 1];
+    const int64_t tiles = (a.nout + 63) / 64;
+    const int64_t slots = 2 * device_cus();
+    const double rounds = (double)((tiles + slots - 1) / slots);
+    const double t_step = (double)(a.K / 128) * 0.31 * rounds, t_stream = w_mb / 4.5;
+    const double t_tiled = 1.0 + (t_step > t_stream ? t_step : t_stream);
+    if (t_tiled < t_small) return launch_prefill<kFmtMx, 64, 64, 2, 2, 3, 2>(a, st);
+    if (fm == 1) return launch_small<1>(a, st);
+    if (fm == 2) return launch_small<2>(a, st);
+    if (fm == 3) return launch_small<3>(a, st);
+    return launch_small<4>(a, st);
+}
+
 static hipError_t launch_linear_mx(const LinearArgs &a, hipStream_t st) {
-    if (a.offsets == nullptr && a.rows <= 64) {
-        if (a.rows <= 16) return launch_small<1>(a, st);
-        if (a.rows <= 32) return launch_small<2>(a, st);
-        if (a.rows <= 48) return launch_small<3>(a, st);
-        return launch_small<4>(a, st);
-    }
+    if (a.offsets == nullptr && a.rows <= 64) return launch_linear_mx_few_rows(a, st);
     if (a.offsets) return launch_prefill<kFmtMx, 128, 256, 2, 2, 3, 1, 4, 2>(a, st);
     const int64_t cus = device_cus();
     double t_one = 0.0;

@@ -12,9 +12,11 @@
 // the four lanes of a DPP quad and an NVFP4 block (16) a lane pair.  The row
 // is read from HBM exactly once; everything else happens in registers.
 //
-//   MX + norm, K <= 8192:  one row per workgroup of four waves; the row stays
-//                          in registers across the FP64 norm reduction (whose
-//                          per-wave partials meet in LDS) and the
+//   MX + norm, K <= 8192:  a workgroup of four waves per row (from 2048 rows
+//                          on, 2 or 4 consecutive rows per workgroup, the
+//                          next row loaded during the current one); the row
+//                          stays in registers across the FP64 norm reduction
+//                          (whose per-wave partials meet in LDS) and the
 //                          quantization pass;
 //   MX + norm, larger K:   one wave per row, the quantization pass re-reads
 //                          the row (L2 hit);
@@ -30,6 +32,7 @@ namespace sharq {
 constexpr int kPrepWaves = 4;        // waves per workgroup
 constexpr int kChunk = 512;          // elements per wave-wide 128-bit load
 constexpr int kStreamChunks = 2;     // chunks per task when rows are split (measured: 2 beats 4 and 8)
+constexpr int64_t kPrepRowsGrid = 1024;   // row workgroups that fill the GPU (four per CU)
 
 struct RowStats {  // per-row statistics written by the NVFP4 pre-pass
     float r, mu, amax, pad;
@@ -277,15 +280,114 @@ __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, 
     }
 }
 
+// ---------------------------------------------------------------- MX, norm, row split over a workgroup
+// A workgroup of NWG waves handles `rpw` consecutive rows, one at a time;
+// wave w owns chunks w, w+NWG, ... of a row (at most CPW of them, held in
+// registers).  The next row's words are loaded before the current row is
+// reduced and quantized, so its latency hides behind the current row's
+// arithmetic.  Each wave reduces its FP64 partial sums, the NWG partials
+// meet in LDS (two slots, alternating by row) and every wave adds them in
+// the same fixed order, so all waves derive the same r (and mu).  gamma and
+// beta are loaded once per workgroup.
+template <bool BF16, int NORM, int M, int FAST24, int CPW, int NWG>
+__global__ __launch_bounds__(NWG * kWave) void k_prep_mx_split(PrepArgs a, int64_t rpw) {
+    __shared__ double part[2][2][NWG];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const LaneOff lo = lane_offsets<kFmtMx>(a, lane);
+    const int64_t row0 = xcd_block(blockIdx.x, gridDim.x) * rpw;
+    const int64_t row_end = row0 + rpw < a.T ? row0 + rpw : a.T;
+    if (row0 >= row_end) return;
+    const int64_t K = a.K;
+
+    bool in[CPW];
+    uint4 graw[CPW], braw[CPW], raw[CPW];
+    constexpr uint32_t kOnePair = BF16 ? 0x3F803F80u : 0x3C003C00u;  // 1.0, 1.0
+#pragma unroll
+    for (int j = 0; j < CPW; j++) {
+        const int64_t e0 = ((int64_t)(wave + NWG * j) * kWave + lane) * 8;
+        in[j] = e0 < K;
+        raw[j] = in[j] ? *reinterpret_cast<const uint4 *>(a.x + row0 * a.ldx + e0) : make_uint4(0, 0, 0, 0);
+        graw[j] = in[j] ? param_raw<true>(a.gamma, e0, kOnePair) : make_uint4(0, 0, 0, 0);
+        braw[j] = in[j] ? param_raw<NORM == kNormLayer>(a.beta, e0, 0u) : make_uint4(0, 0, 0, 0);
+    }
+    for (int64_t row = row0; row < row_end; row++) {
+        const int slot = (int)(row & 1);
+        uint4 nraw[CPW];
+        const bool more = row + 1 < row_end;
+#pragma unroll
+        for (int j = 0; j < CPW; j++) {
+            const int64_t e0 = ((int64_t)(wave + NWG * j) * kWave + lane) * 8;
+            nraw[j] = (more && in[j]) ? *reinterpret_cast<const uint4 *>(a.x + (row + 1) * a.ldx + e0)
+                                      : make_uint4(0, 0, 0, 0);
+        }
+        float v[8];
+        double s1 = 0.0;
+#pragma unroll
+        for (int j = 0; j < CPW; j++) {
+            unpack8<BF16>(raw[j], v);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                if constexpr (NORM == kNormRms) s1 = __fma_rn((double)v[i], (double)v[i], s1);  // x*x exact in double
+                else s1 += (double)v[i];
+            }
+        }
+        s1 = wave_sum_f64(s1);
+        if (lane == 0) part[slot][0][wave] = s1;
+        __syncthreads();
+        s1 = part[slot][0][0];
+#pragma unroll
+        for (int w = 1; w < NWG; w++) s1 += part[slot][0][w];
+        float r, mu = 0.0f;
+        if constexpr (NORM == kNormRms) {
+            r = (float)(1.0 / sqrt(s1 / (double)K + (double)a.eps));
+        } else {
+            const double mud = s1 / (double)K;
+            double s2 = 0.0;
+#pragma unroll
+            for (int j = 0; j < CPW; j++) {
+                if (in[j]) {
+                    unpack8<BF16>(raw[j], v);
+#pragma unroll
+                    for (int i = 0; i < 8; i++) {
+                        const double d = (double)v[i] - mud;
+                        s2 += d * d;  // d*d is rounded on its own, as in the definition
+                    }
+                }
+            }
+            s2 = wave_sum_f64(s2);
+            if (lane == 0) part[slot][1][wave] = s2;
+            __syncthreads();
+            s2 = part[slot][1][0];
+#pragma unroll
+            for (int w = 1; w < NWG; w++) s2 += part[slot][1][w];
+            mu = (float)mud;
+            r = (float)(1.0 / sqrt(s2 / (double)K + (double)a.eps));
+        }
+#pragma unroll
+        for (int j = 0; j < CPW; j++) {
+            if (in[j]) {
+                float g[8], b[8];
+                unpack8<BF16>(graw[j], g);
+                unpack8<BF16>(braw[j], b);
+                unpack8<BF16>(raw[j], v);
+                normalize8<NORM>(v, g, b, r, mu);
+                decompose_store<kFmtMx, M, FAST24>(a, row, wave + NWG * j, lane, lo, v, 1.0f, 6.0f);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < CPW; j++) raw[j] = nraw[j];
+    }
+}
+
 // ---------------------------------------------------------------- MX, norm, one row per workgroup
 // A workgroup of NWG waves handles one row; wave w owns chunks w, w+NWG, ...
 // of it (at most CPW of them, held in registers from one batch of loads).
 // Each wave reduces its FP64 partial sums, the NWG partials meet in LDS and
 // every wave adds them in the same fixed order, so all waves derive the same
-// r (and mu).  Measured on MI355X against two and more rows per workgroup
-// (with the next row loaded during the current one, or all rows loaded at
-// once): one row per workgroup, many workgroups in flight, is as fast or
-// faster at every prefill shape and clearly faster at a few hundred rows.
+// r (and mu).  Used below kPrepRowsGrid * 2 rows, where it beats the split
+// kernel run with one row per workgroup (measured on MI355X: about 15% at
+// a few hundred rows).
 template <bool BF16, int NORM, int M, int FAST24, int CPW, int NWG>
 __global__ __launch_bounds__(NWG * kWave) void k_prep_mx_row(PrepArgs a) {
     __shared__ double part[2][NWG];
@@ -747,12 +849,22 @@ static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
     const int64_t K = a.K;
     if constexpr (FMT == kFmtMx && NORM != kNormNone) {
         const dim3 grid((unsigned)round_up8((a.T + kPrepWaves - 1) / kPrepWaves));
-        const dim3 rows((unsigned)round_up8(a.T));
+        // rows per workgroup: about two workgroups per CU once T allows it;
+        // below that one row per workgroup with all of its words loaded at once
+        const int64_t rpw = a.T >= 4 * kPrepRowsGrid ? 4 : (a.T >= 2 * kPrepRowsGrid ? 2 : 1);
+        const dim3 rows((unsigned)round_up8((a.T + rpw - 1) / rpw));
         // four waves of two chunks beat eight waves of one at K = 4096 (MI355X)
-        if (K <= (int64_t)kChunk * kPrepWaves * 2)
-            hipLaunchKernelGGL((k_prep_mx_row<BF16, NORM, M, FAST24, 2, kPrepWaves>), rows, blk, 0, st, a);
-        else if (K <= (int64_t)kChunk * kPrepWaves * 4)
-            hipLaunchKernelGGL((k_prep_mx_row<BF16, NORM, M, FAST24, 4, kPrepWaves>), rows, blk, 0, st, a);
+        if (K <= (int64_t)kChunk * kPrepWaves * 2) {
+            if (rpw > 1)
+                hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 2, kPrepWaves>), rows, blk, 0, st, a, rpw);
+            else
+                hipLaunchKernelGGL((k_prep_mx_row<BF16, NORM, M, FAST24, 2, kPrepWaves>), rows, blk, 0, st, a);
+        } else if (K <= (int64_t)kChunk * kPrepWaves * 4) {
+            if (rpw > 1)
+                hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 4, kPrepWaves>), rows, blk, 0, st, a, rpw);
+            else
+                hipLaunchKernelGGL((k_prep_mx_row<BF16, NORM, M, FAST24, 4, kPrepWaves>), rows, blk, 0, st, a);
+        }
         else
             hipLaunchKernelGGL((k_prep_mx_2pass<BF16, NORM, M, FAST24>), grid, blk, 0, st, a);
         if (a.global_scale) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, a.global_scale, 1.0f);

@@ -977,16 +977,29 @@ static hipError_t launch_linear_mx(const LinearArgs &a, hipStream_t st) {
     return launch_mx_shape(one, a, st, 0, a.nout);
 }
 
+// NVFP4 (f16 MFMA on fragments dequantized in registers): 128x128 tiles
+// with two workgroups per CU (one workgroup's dequantization overlaps the
+// other's MFMAs), or 256x256 tiles of four waves with 128x128 per wave
+// (each dequantized fragment feeds four MFMAs instead of two: measured on
+// MI355X 10-18% faster once there are enough tiles), whichever takes fewer
+// rounds of tiles, weighted by the measured cost per output element
+// (1.17 : 1); grouped expert products use 128x256 tiles.
+static hipError_t launch_linear_nv(const LinearArgs &a, hipStream_t st) {
+    if (a.offsets) return launch_prefill<kFmtNv, 128, 256, 2, 2, 3, 1, 4, 1>(a, st);
+    const int64_t cus = device_cus();
+    const int64_t t128 = ((a.rows + 127) / 128) * ((a.nout + 127) / 128);
+    const int64_t t256 = ((a.rows + 255) / 256) * ((a.nout + 255) / 256);
+    const double c128 = (double)((t128 + 2 * cus - 1) / (2 * cus)) * 2.0 * 128 * 128 * 1.17;
+    const double c256 = (double)((t256 + cus - 1) / cus) * 256.0 * 256;
+    if (c256 < c128) return launch_prefill<kFmtNv, 256, 256, 2, 2, 2, 1, 0, 1>(a, st);
+    return launch_prefill<kFmtNv, 128, 128, 2, 2, 2, 2, 0, 1>(a, st);
+}
+
 hipError_t launch_linear(const LinearArgs &a, void *ws, size_t ws_bytes, hipStream_t st) {
     (void)ws;
     (void)ws_bytes;
     if (a.fmt == kFmtMx) return launch_linear_mx(a, st);
-    // NVFP4: 128x256 tiles; products with K <= 4096 run faster as 128x128
-    // tiles with two workgroups per CU (measured on MI355X: one workgroup's
-    // dequantization overlaps the other's MFMAs, which the shorter K loop's
-    // per-tile overheads favour)
-    if (a.offsets == nullptr && a.K <= 4096) return launch_prefill<kFmtNv, 128, 128, 2, 2, 2, 2, 0, 1>(a, st);
-    return launch_prefill<kFmtNv, 128, 256, 2, 2, 3, 1, 4, 1>(a, st);
+    return launch_linear_nv(a, st);
 }
 
 size_t linear_workspace_bytes(int64_t rows, int64_t K, int64_t nout, int64_t E, int fmt) {

@@ -42,7 +42,7 @@ MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
 F16_PEAK_TFLOPS = 2500.0        # MI355X dense f16 / bf16 MFMA
 # 32x32x64 block-scaled FP4 MFMA issued back to back from registers with
 # random operands (no memory traffic), measured on MI355X: the chip lowers its
-# clock under that load (about 1.5 GHz against 2.4 GHz with constant operands)
+# clock under that load (about 1.6 GHz, against 2.1-2.3 GHz with constant operands)
 MFMA_RANDOM_FP4_TFLOPS = 6250.0
 SAMPLE_ROWS = 32                # rows per linear in the CPU baseline and the error report
 

@@ -45,7 +45,8 @@ constexpr int kCbszFp4 = 4;  // MFMA operand format code for E2M1
 // 32x32x64 block-scaled FP4 MFMA: lane l feeds row l%32 and the 32-element
 // block l/32 of the 64-wide K step; lane l, accumulator r holds
 // C[8*(r/4) + 4*(l/32) + r%4][l%32].  On gfx950 this shape runs FP4 at twice
-// the FP8 rate (about 9.3 PFLOP/s measured), the 16x16x128 shape does not.
+// the FP8 rate (8.8 PFLOP/s measured with constant operands, 6.3 with random
+// ones, at which the chip lowers its clock), the 16x16x128 shape does not.
 // OPSEL picks which byte of the scale registers this MFMA uses.
 template <int OPSEL>
 __device__ __forceinline__ v16f mfma32_fp4(v4i a, v4i b, v16f c, int sa, int sb) {

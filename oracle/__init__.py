@@ -77,6 +77,8 @@ def lib():
         L.or_e2m1_encode_n.restype = None
         L.or_e4m3_encode_n.argtypes = [p, i64, p]
         L.or_e4m3_encode_n.restype = None
+        L.or_mx_exponent_n.argtypes = [p, i64, p]
+        L.or_mx_exponent_n.restype = None
         L.or_quantize_weight.argtypes = [p, i32, i64, i64, i64, i64, i32, p, p, p]
         L.or_dequant.argtypes = [p, p, i64, i64, i32, f32, p]
         L.or_quantize_rows.argtypes = [p, i32, i64, i64, i32, f32, p, p]
@@ -101,6 +103,13 @@ def e2m1_encode_array(u: np.ndarray) -> np.ndarray:
     a = np.ascontiguousarray(u, dtype=np.float32)
     out = np.zeros(a.shape, np.uint8)
     lib().or_e2m1_encode_n(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def mx_exponent_array(amax: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(amax, dtype=np.float32)
+    out = np.zeros(a.shape, np.int16)
+    lib().or_mx_exponent_n(_ptr(a), a.size, _ptr(out))
     return out
 
 

@@ -126,6 +126,11 @@ int or_mx_exponent(float amax)
     return e;
 }
 
+void or_mx_exponent_n(const float *amax, int64_t n, int16_t *out)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = (int16_t)or_mx_exponent(amax[i]);
+}
+
 /* E4M3 (no infinities, 0x7F/0xFF are NaN): bias 7, largest finite 448. */
 uint8_t or_e4m3_encode(float x);
 

@@ -1,22 +1,22 @@
-"""Builds the test-support probe library tests/hwprobe/libe2m1_probe.so
-(gfx950) from e2m1_probe.hip with the library's compiler flags.  Called by
+"""Builds the test-support probe library tests/hwprobe/libencoder_probe.so
+(gfx950) from encoder_probe.hip with the library's compiler flags.  Called by
 the repository's build entry point; the GPU test that uses it fails when it
 is missing."""
 import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-OUT = os.path.join(HERE, "libe2m1_probe.so")
+OUT = os.path.join(HERE, "libencoder_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
 def build() -> str:
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fvisibility=hidden",
-           os.path.join(HERE, "e2m1_probe.hip"), "-o", OUT]
+           os.path.join(HERE, "encoder_probe.hip"), "-o", OUT]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for e2m1_probe.hip:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed for encoder_probe.hip:\n{r.stdout}\n{r.stderr}")
     return OUT
 
 

@@ -1,0 +1,52 @@
+// Test support (not part of the library): runs the library's own device
+// encoders over a range of float32 bit patterns, one result per output
+// byte, so that a test can compare every float32 input with the oracle:
+// the E2M1 conversion (sharq::e2m1_cvt8: the hardware FP32 -> FP4
+// conversion with scale 1 plus the canonical-zero fix), the E4M3 block-scale
+// encoder (sharq::e4m3_encode_sat) and the MX shared exponent
+// (sharq::mx_shared_exp, written as the E8M0 byte E + 127).
+#include "../../sparsity_prep_amd/csrc/device_util.h"
+
+__global__ void k_probe_e2m1(uint32_t base, uint32_t n, uint8_t *out) {
+    const uint32_t i = (blockIdx.x * blockDim.x + threadIdx.x) * 8u;
+    if (i >= n) return;
+    float u[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) u[k] = __uint_as_float(base + i + (uint32_t)k);
+    const uint32_t p = sharq::e2m1_cvt8(u, 1.0f);
+#pragma unroll
+    for (int k = 0; k < 8; k++) out[i + k] = (uint8_t)((p >> (4 * k)) & 0xFu);
+}
+
+__global__ void k_probe_scales(uint32_t base, uint32_t n, uint8_t *e4m3, uint8_t *e8m0) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const float t = __uint_as_float(base + i);
+    e4m3[i] = (uint8_t)sharq::e4m3_encode_sat(t);
+    e8m0[i] = (uint8_t)(sharq::mx_shared_exp(t) + 127);
+}
+
+// Codes of the n patterns base .. base + n - 1 (n a multiple of 8, at most
+// 2^31, base + n <= 2^32) into out[0 .. n); returns the HIP error code.
+extern "C" __attribute__((visibility("default"))) int probe_e2m1(uint32_t base, uint32_t n, uint8_t *out,
+                                                                  void *stream) {
+    if (n % 8u != 0u || n > (1u << 31) || (uint64_t)base + n > (1ull << 32) || out == nullptr)
+        return (int)hipErrorInvalidValue;
+    const uint32_t threads = n / 8u, block = 256u;
+    hipLaunchKernelGGL(k_probe_e2m1, dim3((threads + block - 1) / block), dim3(block), 0,
+                       (hipStream_t)stream, base, n, out);
+    return (int)hipGetLastError();
+}
+
+// E4M3 bytes and E8M0 bytes of the n patterns base .. base + n - 1 (same
+// limits as probe_e2m1; the patterns should be non-negative finite floats,
+// the encoders' domain).
+extern "C" __attribute__((visibility("default"))) int probe_scales(uint32_t base, uint32_t n, uint8_t *e4m3,
+                                                                    uint8_t *e8m0, void *stream) {
+    if (n > (1u << 31) || (uint64_t)base + n > (1ull << 32) || e4m3 == nullptr || e8m0 == nullptr)
+        return (int)hipErrorInvalidValue;
+    const uint32_t block = 256u;
+    hipLaunchKernelGGL(k_probe_scales, dim3((n + block - 1) / block), dim3(block), 0, (hipStream_t)stream, base,
+                       n, e4m3, e8m0);
+    return (int)hipGetLastError();
+}

@@ -988,14 +988,34 @@ static hipError_t launch_linear_mx(const LinearArgs &a, hipStream_t st) {
 // (each dequantized fragment feeds four MFMAs instead of two: measured on
 // MI355X 10-18% faster once there are enough tiles), whichever takes fewer
 // rounds of tiles, weighted by the measured cost per output element
-// (1.17 : 1); grouped expert products use 128x256 tiles.
+// (1.17 : 1); when 256x256 tiles fill some rounds and leave a partial one,
+// the columns of the full rounds run as 256x256 tiles and the rest as
+// 128x128 tiles in a second launch.  Grouped expert products use 128x256
+// tiles.
+static double nv_cost128(int64_t rows, int64_t cols, int64_t cus) {
+    const int64_t t = ((rows + 127) / 128) * ((cols + 127) / 128);
+    return (double)((t + 2 * cus - 1) / (2 * cus)) * 2.0 * 128 * 128 * 1.17;
+}
+static double nv_cost256(int64_t rows, int64_t cols, int64_t cus) {
+    const int64_t t = ((rows + 255) / 256) * ((cols + 255) / 256);
+    return (double)((t + cus - 1) / cus) * 256.0 * 256;
+}
+
 static hipError_t launch_linear_nv(const LinearArgs &a, hipStream_t st) {
     if (a.offsets) return launch_prefill<kFmtNv, 128, 256, 2, 2, 3, 1, 4, 1>(a, st);
     const int64_t cus = device_cus();
-    const int64_t t128 = ((a.rows + 127) / 128) * ((a.nout + 127) / 128);
-    const int64_t t256 = ((a.rows + 255) / 256) * ((a.nout + 255) / 256);
-    const double c128 = (double)((t128 + 2 * cus - 1) / (2 * cus)) * 2.0 * 128 * 128 * 1.17;
-    const double c256 = (double)((t256 + cus - 1) / cus) * 256.0 * 256;
+    const double c128 = nv_cost128(a.rows, a.nout, cus), c256 = nv_cost256(a.rows, a.nout, cus);
+    const int64_t mt = (a.rows + 255) / 256;
+    const int64_t full_rounds = (mt * ((a.nout + 255) / 256)) / cus;
+    const int64_t n_split = (full_rounds * cus / mt) * 256;
+    if (full_rounds >= 1 && n_split > 0 && n_split < a.nout) {
+        const double split = nv_cost256(a.rows, n_split, cus) + nv_cost128(a.rows, a.nout - n_split, cus);
+        if (split < 0.97 * (c128 < c256 ? c128 : c256)) {  // a second launch costs a little
+            const hipError_t e = launch_prefill<kFmtNv, 256, 256, 2, 2, 2, 1, 0, 1>(a, st, 0, n_split);
+            if (e != hipSuccess) return e;
+            return launch_prefill<kFmtNv, 128, 128, 2, 2, 2, 2, 0, 1>(a, st, n_split, a.nout);
+        }
+    }
     if (c256 < c128) return launch_prefill<kFmtNv, 256, 256, 2, 2, 2, 1, 0, 1>(a, st);
     return launch_prefill<kFmtNv, 128, 128, 2, 2, 2, 2, 0, 1>(a, st);
 }

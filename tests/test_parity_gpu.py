@@ -276,6 +276,32 @@ def test_linear(case):
     assert rel_fro(y, oracle.linear(o, ow)) <= TOL
 
 
+GATHER_CASES = [
+    # (fmt, T, K, nout, rows): one weight, output rows gathered through row_index
+    (0, 50, 1024, 64, 40),     # small-batch kernel
+    (0, 50, 1024, 3000, 40),   # few rows as 64x64 tiles
+    (0, 90, 640, 272, 300),    # prefill tiles, rows repeated
+    (1, 90, 640, 272, 300),
+    (1, 30, 512, 128, 7),
+]
+
+
+@pytest.mark.parametrize("case", GATHER_CASES, ids=lambda c: "fmt%d-T%d-K%d-N%d-rows%d" % c)
+def test_linear_dense_gather(case):
+    """A single weight with gathered token rows (no expert groups): output row
+    m is the product of prepared row row_index[m], on every dispatch path."""
+    fmt, T, K, nout, rows = case
+    x = synth.small_case(K, T, "bf16", outliers=3, tag=7 + rows)
+    pg = gpu_prepare(x, "bf16", K, 0, None, None, 0.0, 2, 4, fmt)
+    w = synth.small_weight(nout, K, tag=8 + nout)
+    qw = sq().quantize_weight(dev16(w, "bf16"), fmt=fmt)
+    row_index = np.random.default_rng(rows).integers(0, T, rows).astype(np.int32)
+    y = host(sq().linear(pg, qw, row_index=torch.from_numpy(row_index).cuda(), rows=rows))
+    _, ref = ref_linear(pg, qw, row_index=row_index)
+    assert y.shape == (rows, nout)
+    assert rel_fro(y, ref) <= TOL
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_linear_grouped(fmt):
     K, nout, E, T = 640, 96, 5, 90

@@ -178,7 +178,11 @@ SHARQ_API sharq_status sharq_quantize_weight(const void *w, int32_t w_dtype, int
                                    float *global_scale, void *workspace, size_t workspace_bytes,
                                    void *stream);
 
-/* Bytes of workspace sharq_linear needs (currently always 0). */
+/* Bytes of workspace sharq_linear needs for these arguments: 0, except for
+ * MXFP4 products of one weight (experts == 1) with at most 64 rows that run
+ * as independent products over equal K ranges summed in a fixed order
+ * (decode batches with long K); then S * rows * nout floats of partial
+ * products (S = 2, 4 or 8).  The value depends only on the arguments. */
 SHARQ_API size_t sharq_linear_workspace_size(int64_t rows, int64_t K, int64_t nout, int64_t experts,
                                    int32_t fmt);
 
@@ -211,6 +215,9 @@ SHARQ_API size_t sharq_linear_workspace_size(int64_t rows, int64_t K, int64_t no
  *   rows         output rows (T when row_index is NULL and experts == 1)
  *   y            [rows][ldy] FP32, ldy >= nout, 4-byte aligned (128-bit
  *                stores are used when y is 16-byte aligned and ldy % 4 == 0)
+ *   workspace    sharq_linear_workspace_size() bytes of device memory
+ *                (16-byte aligned), SHARQ_ERR_WORKSPACE when smaller; its
+ *                contents on entry do not matter
  * Contents of group_offsets and row_index are trusted (device memory is not
  * read on the host); out-of-range values are undefined behaviour.  Every
  * output element is summed in a fixed order (no atomics), so repeated calls

@@ -219,6 +219,8 @@ sharq_status sharq_linear(const uint8_t *b_codes, const uint8_t *b_scales, const
     a.y = y;
     a.ldy = ldy;
     a.y_vec = aligned(y, 16) && ldy % 4 == 0;
+    a.ksplit_tiles = 0;
+    a.split_stride = 0;
     return hip_status(launch_linear(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 

@@ -550,6 +550,20 @@ template <int FMT, int BM, int BN, int WGM, int WGN, int NS, int OCC, int LSPLIT
 __global__ __launch_bounds__(WGM * WGN * 64)
 __attribute__((amdgpu_waves_per_eu(OCC * WGM * WGN / 4, OCC * WGM * WGN / 4)))
 void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles, int64_t n_begin) {
+    if (a.ksplit_tiles > 0) {
+        // K range blockIdx.y: in the K-tiled layout tiles [t0, t0 + kt) of every
+        // operand are themselves a K-tiled array with K = 128 * kt
+        constexpr int64_t kScaleBytes = kTileK / (FMT == kFmtMx ? 32 : 16);  // per row and K tile
+        const int64_t t0 = (int64_t)blockIdx.y * a.ksplit_tiles;
+        a.b_codes += t0 * a.T * (kTileK / 2);
+        a.r_codes += t0 * a.T * (kTileK / 2);
+        a.b_scales += t0 * a.T * kScaleBytes;
+        a.r_scales += t0 * a.T * kScaleBytes;
+        a.w_codes += t0 * a.nout * (kTileK / 2);
+        a.w_scales += t0 * a.nout * kScaleBytes;
+        a.K = a.ksplit_tiles * kTileK;
+        a.y += (int64_t)blockIdx.y * a.split_stride;
+    }
     using G = DualGemm<FMT, BM, BN, WGM, WGN, NS, LSPLIT, RPS>;
     using L = typename G::L;
     constexpr int FM = G::FM, FN = G::FN;
@@ -863,7 +877,8 @@ static hipError_t launch_prefill(const LinearArgs &a, hipStream_t st, int64_t n_
         n_mtiles = (a.rows + BM - 1) / BM;
         blocks = ((n_ntiles * n_mtiles + 7) / 8) * 8;
     }
-    hipLaunchKernelGGL((k_dual_gemm<FMT, BM, BN, WGM, WGN, NS, OCC, LSPLIT, RPS>), dim3((unsigned)blocks),
+    const unsigned splits = a.ksplit_tiles > 0 ? (unsigned)(a.K / kTileK / a.ksplit_tiles) : 1u;
+    hipLaunchKernelGGL((k_dual_gemm<FMT, BM, BN, WGM, WGN, NS, OCC, LSPLIT, RPS>), dim3((unsigned)blocks, splits),
                        dim3(WGM * WGN * 64), 0,
                        st, a, n_ntiles, n_mtiles, n_begin);
     return hipGetLastError();
@@ -932,32 +947,103 @@ static hipError_t launch_mx_shape(int s, const LinearArgs &a, hipStream_t st, in
 // partial last round runs as two launches over column ranges: full rounds
 // of 256x256 tiles, then the remaining columns in the shape that fits them
 // best, instead of a last round that leaves CUs idle.
+// Sum of S partial products p[S][rows][nout] (row-major FP32) into y, the
+// partials added in the order s = 0, 1, ..., S-1.
+__global__ __launch_bounds__(256) void k_sum_partials(const float *p, int S, int64_t rows, int64_t nout, float *y,
+                                                      int64_t ldy) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t plane = rows * nout;
+    if (i >= plane) return;
+    const int64_t m = i / nout, n = i - m * nout;
+    float acc = p[i];
+    for (int s = 1; s < S; s++) acc = __fadd_rn(acc, p[(int64_t)s * plane + i]);
+    y[m * ldy + n] = acc;
+}
+
 // Up to 64 rows: the small-batch kernel (weight rows split over many
-// workgroups, K over their waves; every workgroup re-reads the token rows)
-// or one row of 64x64 tiles with two workgroups per CU, whichever this
-// model of MI355X measurements says is faster: the small kernel streams the
-// weight at about 3.5 / 2.2 / 1.6 / 1.2 TB/s for 16 / 32 / 48 / 64 rows
-// after about 3 us; the tiles take about 0.31 us per 128-wide K step and
-// round of tiles, or stream the weight at 4.5 TB/s, after about 1 us.
-static hipError_t launch_linear_mx_few_rows(const LinearArgs &a, hipStream_t st) {
+// workgroups, K over their waves; every workgroup re-reads the token rows),
+// one row of 64x64 tiles with two workgroups per CU, or those tiles over S
+// equal K ranges (S independent products into the workspace, then summed
+// in a fixed order), whichever this model of MI355X measurements says is
+// fastest (times in us): the small kernel streams the weight at about
+// 3.5 / 2.2 / 1.6 / 1.2 TB/s for 16 / 32 / 48 / 64 rows after about 3 us;
+// the tiles take about 0.31 us per 128-wide K step and round of tiles (two
+// per CU), or stream the weight at 4.5 TB/s, after about 1 us; a K split
+// adds the summing pass (about 4 us plus the partials' traffic at 3 TB/s)
+// and is taken only when it is 10% faster.  K splits are used from 17 rows on, in one launch whose second
+// grid dimension is the K range.  The model assumes the MI355X's 256 CUs,
+// so that the workspace size does not depend on the device.
+constexpr int64_t kFewRowsModelCus = 256;
+
+struct FewRowsPlan {
+    int kernel;  // 0 small-batch kernel, 1 64x64 tiles, 2 64x64 tiles over S K ranges
+    int S;
+};
+
+static FewRowsPlan plan_few_rows(int64_t rows, int64_t K, int64_t nout) {
     constexpr double kSmallTBps[4] = {3.5, 2.2, 1.6, 1.2};
+    const int fm = rows <= 16 ? 1 : rows <= 32 ? 2 : rows <= 48 ? 3 : 4;
+    const double w_mb = (double)nout * (double)K * (0.5 + 1.0 / 32.0) * 1e-6;
+    const int64_t tiles = (nout + 63) / 64, slots = 2 * kFewRowsModelCus, ksteps = K / 128;
+    auto t_tiles = [&](int S) {
+        const double rounds = (double)((tiles * S + slots - 1) / slots);
+        const double t_step = (double)(ksteps / S) * 0.31 * rounds, t_stream = w_mb / 4.5;
+        const double t = 1.0 + (t_step > t_stream ? t_step : t_stream);
+        // partials written once and read once, the sum written, at 3 TB/s
+        return S == 1 ? t : t + 4.0 + (double)(2 * S + 1) * (double)rows * (double)nout * 4.0 * 1e-6 / 3.0;
+    };
+    FewRowsPlan best{0, 1};
+    double t_best = 3.0 + w_mb / kSmallTBps[fm - 1];
+    if (t_tiles(1) < t_best) {
+        best = {1, 1};
+        t_best = t_tiles(1);
+    }
+    if (rows > 16) {
+        for (int S = 2; S <= 8; S *= 2) {
+            if (ksteps % S != 0 || ksteps / S < 4) continue;
+            const double t = t_tiles(S);
+            if (t < 0.9 * t_best) {  // only a clear gain pays for the extra pass
+                best = {2, S};
+                t_best = t;
+            }
+        }
+    }
+    return best;
+}
+
+static size_t few_rows_workspace(int64_t rows, int64_t K, int64_t nout) {
+    const FewRowsPlan pl = plan_few_rows(rows, K, nout);
+    return pl.kernel == 2 ? (size_t)pl.S * (size_t)rows * (size_t)nout * sizeof(float) : 0;
+}
+
+static hipError_t launch_linear_mx_few_rows(const LinearArgs &a, void *ws, size_t ws_bytes, hipStream_t st) {
+    const FewRowsPlan pl = plan_few_rows(a.rows, a.K, a.nout);
+    if (pl.kernel == 2 && ws != nullptr && ws_bytes >= few_rows_workspace(a.rows, a.K, a.nout)) {
+        // one launch: grid row s multiplies K range s into partial product s
+        float *part = static_cast<float *>(ws);
+        LinearArgs as = a;
+        as.ksplit_tiles = a.K / kTileK / pl.S;
+        as.split_stride = a.rows * a.nout;
+        as.y = part;
+        as.ldy = a.nout;
+        as.y_vec = a.nout % 4 == 0 && ((uintptr_t)part % 16) == 0;
+        const hipError_t e = launch_prefill<kFmtMx, 64, 64, 2, 2, 3, 2>(as, st);
+        if (e != hipSuccess) return e;
+        const int64_t n = a.rows * a.nout;
+        hipLaunchKernelGGL(k_sum_partials, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, pl.S, a.rows,
+                           a.nout, a.y, a.ldy);
+        return hipGetLastError();
+    }
+    if (pl.kernel >= 1) return launch_prefill<kFmtMx, 64, 64, 2, 2, 3, 2>(a, st);
     const int fm = a.rows <= 16 ? 1 : a.rows <= 32 ? 2 : a.rows <= 48 ? 3 : 4;
-    const double w_mb = (double)a.nout * (double)a.K * (0.5 + 1.0 / 32.0) * 1e-6;
-    const double t_small = 3.0 + w_mb / kSmallTBps[fm - 1];
-    const int64_t tiles = (a.nout + 63) / 64;
-    const int64_t slots = 2 * device_cus();
-    const double rounds = (double)((tiles + slots - 1) / slots);
-    const double t_step = (double)(a.K / 128) * 0.31 * rounds, t_stream = w_mb / 4.5;
-    const double t_tiled = 1.0 + (t_step > t_stream ? t_step : t_stream);
-    if (t_tiled < t_small) return launch_prefill<kFmtMx, 64, 64, 2, 2, 3, 2>(a, st);
     if (fm == 1) return launch_small<1>(a, st);
     if (fm == 2) return launch_small<2>(a, st);
     if (fm == 3) return launch_small<3>(a, st);
     return launch_small<4>(a, st);
 }
 
-static hipError_t launch_linear_mx(const LinearArgs &a, hipStream_t st) {
-    if (a.offsets == nullptr && a.rows <= 64) return launch_linear_mx_few_rows(a, st);
+static hipError_t launch_linear_mx(const LinearArgs &a, void *ws, size_t ws_bytes, hipStream_t st) {
+    if (a.offsets == nullptr && a.rows <= 64) return launch_linear_mx_few_rows(a, ws, ws_bytes, st);
     // grouped expert products: 128x256 tiles, two stages, two workgroups per CU
     // (measured on MI355X on the Qwen3-30B-A3B expert shapes: 5% faster than
     // one workgroup with three stages at K = 2048, 11% at K = 768, where one
@@ -1021,15 +1107,14 @@ static hipError_t launch_linear_nv(const LinearArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_linear(const LinearArgs &a, void *ws, size_t ws_bytes, hipStream_t st) {
-    (void)ws;
-    (void)ws_bytes;
-    if (a.fmt == kFmtMx) return launch_linear_mx(a, st);
+    if (a.fmt == kFmtMx) return launch_linear_mx(a, ws, ws_bytes, st);
     return launch_linear_nv(a, st);
 }
 
 size_t linear_workspace_bytes(int64_t rows, int64_t K, int64_t nout, int64_t E, int fmt) {
-    (void)rows; (void)K; (void)nout; (void)E; (void)fmt;
-    return 0;
+    // partial products of a K-split few-row MXFP4 product (dense weight only)
+    if (fmt != kFmtMx || E != 1 || rows <= 0 || rows > 64 || nout <= 0 || K <= 0 || K % 128 != 0) return 0;
+    return few_rows_workspace(rows, K, nout);
 }
 
 }  // namespace sharq

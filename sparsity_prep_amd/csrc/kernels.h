@@ -74,6 +74,9 @@ struct LinearArgs {
     float *y;
     int64_t ldy;
     bool y_vec;  // rows of y are 16-byte aligned: 128-bit stores
+    // K split (dense products only): grid row s multiplies K tiles
+    // [s*ksplit_tiles, (s+1)*ksplit_tiles) into y + s*split_stride; 0 = no split
+    int64_t ksplit_tiles, split_stride;
 };
 
 hipError_t launch_linear(const LinearArgs &a, void *ws, size_t ws_bytes, hipStream_t st);

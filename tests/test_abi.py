@@ -139,6 +139,7 @@ def test_linear_validation(L):
     assert lin(L, fmt=NV) == NULL                 # NVFP4 needs both tensor scales
     assert lin(L, y=MISALIGNED) == ALIGN
     assert lin(L, rows=0, T=0) == OK
+    assert lin(L, T=64, K=14336, nout=4096) == WORKSPACE   # a K-split product needs its workspace
     assert lin(L, T=0, rows=3, ridx=FAKE) == SHAPE
 
 
@@ -147,6 +148,13 @@ def test_workspace_sizes(L):
     assert L.sharq_prepare_workspace_size(100, 256, NV) >= 100 * 12
     assert L.sharq_quantize_weight_workspace_size(2, 64, 256, NV) >= 128 * 4
     assert L.sharq_linear_workspace_size(64, 256, 64, 1, MX) == 0
+    # decode batch with a long K: partial products of a K split (S * rows * nout floats)
+    need = L.sharq_linear_workspace_size(64, 14336, 4096, 1, MX)
+    assert need > 0 and need % (64 * 4096 * 4) == 0 and need // (64 * 4096 * 4) in (2, 4, 8)
+    assert L.sharq_linear_workspace_size(16, 14336, 4096, 1, MX) == 0     # 16 rows and fewer: no split
+    assert L.sharq_linear_workspace_size(64, 14336, 4096, 1, NV) == 0
+    assert L.sharq_linear_workspace_size(65, 14336, 4096, 1, MX) == 0
+    assert L.sharq_linear_workspace_size(64, 14336, 4096, 8, MX) == 0     # grouped products
 
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

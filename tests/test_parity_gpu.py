@@ -252,6 +252,7 @@ LINEAR_CASES = [
     (0, 1000, 384, 12200),  # 256x192 tiles (one full round), ragged rows and columns
     (0, 300, 128, 200), (0, 5, 128, 40), (1, 130, 128, 96),  # K = 128: a single stage / chunk
     (0, 64, 1024, 2128), (0, 40, 1024, 3000), (0, 9, 1024, 8240),  # few rows as 64x64 tiles
+    (0, 64, 14336, 2050), (0, 24, 14336, 3000), (0, 17, 14336, 4096),  # few rows over 8 / 8 / 4 K ranges, summed
     (1, 16, 256, 256), (1, 300, 640, 272), (1, 1, 512, 64), (1, 70, 1024, 130), (1, 257, 3584, 256),
     (1, 2049, 256, 4224),  # NVFP4 256x256 tiles (128x128 per wave), ragged rows and columns
     (1, 2049, 256, 8616),  # NVFP4 column split: 256x256 tiles for full rounds, 128x128 for the rest
@@ -280,6 +281,7 @@ GATHER_CASES = [
     # (fmt, T, K, nout, rows): one weight, output rows gathered through row_index
     (0, 50, 1024, 64, 40),     # small-batch kernel
     (0, 50, 1024, 3000, 40),   # few rows as 64x64 tiles
+    (0, 70, 14336, 2050, 40),  # few rows over K ranges, summed
     (0, 90, 640, 272, 300),    # prefill tiles, rows repeated
     (1, 90, 640, 272, 300),
     (1, 30, 512, 128, 7),

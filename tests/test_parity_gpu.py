@@ -458,6 +458,24 @@ def test_graph_replay_matches_eager(fmt, T):
     _check_graph_replays(step, out, y)
 
 
+def test_graph_replay_k_split_matches_eager():
+    """A few-row product that runs over K ranges (partial products in a
+    workspace allocated during capture, then summed) captured in one graph."""
+    K, nout, T = 14336, 3000, 24
+    w = synth.small_weight(nout, K, tag=37)
+    qw = sq().quantize_weight(dev16(w, "bf16"), fmt=0)
+    assert sq().lib().sharq_linear_workspace_size(T, K, nout, 1, 0) > 0   # this shape takes the K split
+    x = dev16(synth.small_case(K, T, "bf16", tag=38), "bf16")
+    out = sq().alloc_prepared(T, K, 0, x.device)
+    y = torch.empty((T, nout), dtype=torch.float32, device="cuda")
+
+    def step():
+        sq().prepare(x, norm=0, n=2, m=4, fmt=0, out=out)
+        sq().linear(out, qw, out=y)
+
+    _check_graph_replays(step, out, y)
+
+
 def test_graph_replay_grouped_matches_eager():
     """A grouped expert product over gathered rows, after a prep without a
     norm, captured in one HIP graph."""

@@ -131,12 +131,13 @@ SHARQ_API sharq_status sharq_prepare(const void *x, int32_t x_dtype, int64_t T, 
                            void *stream);
 
 /*
- * sharq_prepare_swiglu -- the same fused preparation for the input of a
- * down projection, computed straight from the gate/up product's FP32 output
- * instead of a stored bf16 activation (SharQ: Bridging Activation Sparsity
- * and FP4 Quantization for LLM Inference, Abstract: the fused preparation
- * absorbs the element-wise work around the linear layer; the down input of a
- * SwiGLU MLP is SiLU(gate) * up).  Per row t, for k < K:
+ * sharq_prepare_swiglu -- the fused preparation operator of sharq_prepare
+ * (SharQ: Bridging Activation Sparsity and FP4 Quantization for LLM
+ * Inference, Abstract: mask generation and residual construction in one
+ * operator) extended to the input of a SwiGLU down projection, SiLU(gate) *
+ * up, computed straight from the gate/up product's FP32 output instead of a
+ * stored bf16 activation (this fusion is not on the pages).  Per row t, for
+ * k < K:
  *   xhat[k] = fl32(SiLU(gate[k]) * up[k]),  SiLU(g) = fl32(g / fl32(1 + e^-g))
  * with e^y a fixed sequence of correctly rounded float operations: Cody-Waite
  * reduction y = n*ln2 + r (n = rint(fl32(y*1.44269504)), ln2 split as

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 3
+#define SHARQ_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define SHARQ_API __attribute__((visibility("default")))
@@ -72,7 +72,8 @@ typedef enum {
     SHARQ_ERR_NM = 3,          /* not 0 <= N <= M, or M not in {1,2,4,8,16}, or */
                                /* M does not divide K                           */
     SHARQ_ERR_DTYPE = 4,       /* unsupported element type                      */
-    SHARQ_ERR_ALIGN = 5,       /* pointer or row stride not 16-byte aligned     */
+    SHARQ_ERR_ALIGN = 5,       /* pointer or row stride less aligned than its   */
+                               /* argument requires                             */
     SHARQ_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required       */
     SHARQ_ERR_UNSUPPORTED = 7, /* format / norm / combination not built         */
     SHARQ_ERR_HIP = 8          /* a HIP call or kernel launch failed            */
@@ -165,8 +166,10 @@ SHARQ_API size_t sharq_quantize_weight_workspace_size(int64_t experts, int64_t n
  * read (SharQ: Bridging Activation Sparsity and FP4 Quantization for LLM Inference, Abstract: one weight payload, a scale view per path).
  * Round-to-nearest-even quantization, run once per weight, offline.
  *
- *   w            [experts][nout][K] F16 or BF16 (PyTorch Linear layout,
- *                Y = X W^T), contiguous, 16-byte aligned
+ *   w            [experts][nout][ldw] F16 or BF16 (PyTorch Linear layout,
+ *                Y = X W^T): element k of row n of expert e at
+ *                w[(e*nout + n)*ldw + k]; 16-byte aligned
+ *   ldw          row stride in elements, ldw >= K, ldw*2 % 16 == 0
  *   codes        experts * nout*K/2 bytes: per expert (expert-major) the
  *                nout x K E2M1 codes, K-tiled with rows = nout
  *   scales       experts * nout*K/B bytes, per expert K-tiled likewise
@@ -175,7 +178,7 @@ SHARQ_API size_t sharq_quantize_weight_workspace_size(int64_t experts, int64_t n
  *   workspace    sharq_quantize_weight_workspace_size() bytes
  */
 SHARQ_API sharq_status sharq_quantize_weight(const void *w, int32_t w_dtype, int64_t experts, int64_t nout,
-                                   int64_t K, int32_t fmt, uint8_t *codes, uint8_t *scales,
+                                   int64_t K, int64_t ldw, int32_t fmt, uint8_t *codes, uint8_t *scales,
                                    float *global_scale, void *workspace, size_t workspace_bytes,
                                    void *stream);
 
@@ -194,7 +197,8 @@ SHARQ_API size_t sharq_linear_workspace_size(int64_t rows, int64_t K, int64_t no
  *
  *   Y[r][o] = sum_k ( deq(backbone)[src(r)][k] + deq(residual)[src(r)][k] )
  *                   * deq(W[e(r)])[o][k]
- * in FP32 accumulation, with NVFP4 tensor scales applied as
+ * in FP32 accumulation (stored as FP32, or rounded to BF16 / F16), with
+ * NVFP4 tensor scales applied as
  * x_global_scale * w_global_scale[e] in the epilogue.  Both paths read the
  * same weight codes and scales.  The backbone is multiplied densely on its
  * zero-filled form (gfx950 has no block-scaled sparse FP4 matrix
@@ -214,11 +218,17 @@ SHARQ_API size_t sharq_linear_workspace_size(int64_t rows, int64_t K, int64_t no
  *   row_index    device int32 [rows] or NULL: output row r reads prepared row
  *                row_index[r] (0 <= row_index[r] < T); NULL reads row r
  *   rows         output rows (T when row_index is NULL and experts == 1)
- *   y            [rows][ldy] FP32, ldy >= nout, 4-byte aligned (128-bit
- *                stores are used when y is 16-byte aligned and ldy % 4 == 0)
- *   workspace    sharq_linear_workspace_size() bytes of device memory
- *                (16-byte aligned), SHARQ_ERR_WORKSPACE when smaller; its
- *                contents on entry do not matter
+ *   y            [rows][ldy] of y_dtype, ldy >= nout, aligned to its element
+ *                size (vector stores of four elements are used when y is
+ *                aligned to four elements and ldy % 4 == 0)
+ *   y_dtype      SHARQ_F32 (the FP32 accumulator itself), SHARQ_BF16 or
+ *                SHARQ_F16 (the FP32 accumulator rounded to nearest, ties
+ *                to even, after the NVFP4 tensor scales; F16 overflows to
+ *                infinity)
+ *   workspace    sharq_linear_workspace_size() bytes of device memory,
+ *                16-byte aligned (SHARQ_ERR_ALIGN otherwise),
+ *                SHARQ_ERR_WORKSPACE when smaller; its contents on entry do
+ *                not matter
  * Contents of group_offsets and row_index are trusted (device memory is not
  * read on the host); out-of-range values are undefined behaviour.  Every
  * output element is summed in a fixed order (no atomics), so repeated calls
@@ -229,8 +239,8 @@ SHARQ_API sharq_status sharq_linear(const uint8_t *b_codes, const uint8_t *b_sca
                           int64_t K, int32_t fmt, const uint8_t *w_codes, const uint8_t *w_scales,
                           const float *w_global_scale, int64_t experts, int64_t nout,
                           const int32_t *group_offsets, const int32_t *row_index, int64_t rows,
-                          float *y, int64_t ldy, void *workspace, size_t workspace_bytes,
-                          void *stream);
+                          void *y, int32_t y_dtype, int64_t ldy, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -24,8 +24,9 @@ LIB_PATH = os.path.join(_HERE, "libsharq.so")
 
 MXFP4, NVFP4 = 0, 1
 NORM_NONE, NORM_RMS, NORM_LAYER = 0, 1, 2
-_F16, _BF16 = 0, 1
+_F16, _BF16, _F32 = 0, 1, 2
 _DTYPE = {torch.float16: _F16, torch.bfloat16: _BF16}
+_OUT_DTYPE = {torch.float32: _F32, torch.bfloat16: _BF16, torch.float16: _F16}
 
 
 class SharqError(RuntimeError):
@@ -56,12 +57,12 @@ def lib() -> ctypes.CDLL:
         L.sharq_prepare_swiglu.restype = ctypes.c_int
         L.sharq_quantize_weight_workspace_size.argtypes = [i64, i64, i64, i32]
         L.sharq_quantize_weight_workspace_size.restype = sz
-        L.sharq_quantize_weight.argtypes = [p, i32, i64, i64, i64, i32, p, p, p, p, sz, p]
+        L.sharq_quantize_weight.argtypes = [p, i32, i64, i64, i64, i64, i32, p, p, p, p, sz, p]
         L.sharq_quantize_weight.restype = ctypes.c_int
         L.sharq_linear_workspace_size.argtypes = [i64, i64, i64, i64, i32]
         L.sharq_linear_workspace_size.restype = sz
         L.sharq_linear.argtypes = [p, p, p, p, p, i64, i64, i32, p, p, p, i64, i64, p, p, i64,
-                                   p, i64, p, sz, p]
+                                   p, i32, i64, p, sz, p]
         L.sharq_linear.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -167,19 +168,24 @@ def prepare_swiglu(gate_up: torch.Tensor, K: int, n: int = 2, m: int = 4, fmt: i
 
 
 def quantize_weight(w: torch.Tensor, fmt: int = MXFP4) -> QWeight:
-    """RTN quantization of W[nout, K] or W[E, nout, K] into one FP4 payload."""
+    """RTN quantization of W[nout, K] or W[E, nout, K] into one FP4 payload.
+    Rows may be strided (a column slice of a wider matrix): unit element
+    stride, row stride ldw, expert stride nout * ldw."""
     if w.dim() == 2:
         w = w.unsqueeze(0)
-    if w.dim() != 3 or w.dtype not in _DTYPE or not w.is_contiguous():
-        raise SharqError("w must be a contiguous float16/bfloat16 [E, nout, K] tensor")
+    if w.dim() != 3 or w.dtype not in _DTYPE or w.stride(2) != 1:
+        raise SharqError("w must be a float16/bfloat16 [E, nout, K] tensor with unit element stride")
     E, nout, K = w.shape
+    ldw = w.stride(1)
+    if E > 1 and w.stride(0) != nout * ldw:
+        raise SharqError("w: expert stride must be nout * row stride")
     B = block_size(fmt)
     u8 = dict(dtype=torch.uint8, device=w.device)
     q = QWeight(codes=torch.empty((E, nout * K // 2), **u8), scales=torch.empty((E, nout * K // B), **u8),
                 global_scale=torch.empty(E, dtype=torch.float32, device=w.device) if fmt == NVFP4 else None,
                 E=E, nout=nout, K=K, fmt=fmt)
     ws = _workspace(lib().sharq_quantize_weight_workspace_size(E, nout, K, fmt), w.device)
-    st = lib().sharq_quantize_weight(_ptr(w), _DTYPE[w.dtype], E, nout, K, fmt, _ptr(q.codes),
+    st = lib().sharq_quantize_weight(_ptr(w), _DTYPE[w.dtype], E, nout, K, ldw, fmt, _ptr(q.codes),
                                      _ptr(q.scales), _ptr(q.global_scale), _ptr(ws),
                                      0 if ws is None else ws.numel(), _stream(w.device))
     _check(st, "sharq_quantize_weight")
@@ -188,23 +194,27 @@ def quantize_weight(w: torch.Tensor, fmt: int = MXFP4) -> QWeight:
 
 def linear(prep: Prepared, wq: QWeight, group_offsets: Optional[torch.Tensor] = None,
            row_index: Optional[torch.Tensor] = None, rows: Optional[int] = None,
-           out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y = deq(backbone) W^T + deq(residual) W^T (float32), optionally grouped by expert."""
+           out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Y = deq(backbone) W^T + deq(residual) W^T, accumulated in float32 and
+    stored as float32 (default) or rounded to bfloat16 / float16 (the dtype
+    of `out` when given), optionally grouped by expert."""
     if prep.K != wq.K or prep.fmt != wq.fmt:
         raise SharqError("prepared activations and weight disagree on K or format")
     if rows is None:
         rows = row_index.numel() if row_index is not None else prep.T
     dev = prep.b_codes.device
     if out is None:
-        out = torch.empty((rows, wq.nout), dtype=torch.float32, device=dev)
-    elif (out.dim() != 2 or out.dtype != torch.float32 or out.shape[0] < rows or out.shape[1] != wq.nout
+        if out_dtype not in _OUT_DTYPE:
+            raise SharqError("out_dtype must be float32, bfloat16 or float16")
+        out = torch.empty((rows, wq.nout), dtype=out_dtype, device=dev)
+    elif (out.dim() != 2 or out.dtype not in _OUT_DTYPE or out.shape[0] < rows or out.shape[1] != wq.nout
           or out.stride(1) != 1):
-        raise SharqError("out must be a float32 [rows, nout] tensor with unit column stride")
+        raise SharqError("out must be a float32/bfloat16/float16 [rows, nout] tensor with unit column stride")
     ws = _workspace(lib().sharq_linear_workspace_size(rows, wq.K, wq.nout, wq.E, wq.fmt), dev)
     st = lib().sharq_linear(
         _ptr(prep.b_codes), _ptr(prep.b_scales), _ptr(prep.r_codes), _ptr(prep.r_scales),
         _ptr(prep.global_scale), prep.T, prep.K, prep.fmt, _ptr(wq.codes), _ptr(wq.scales),
         _ptr(wq.global_scale), wq.E, wq.nout, _ptr(group_offsets), _ptr(row_index), rows,
-        _ptr(out), out.stride(0), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+        _ptr(out), _OUT_DTYPE[out.dtype], out.stride(0), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
     _check(st, "sharq_linear")
     return out

@@ -141,16 +141,17 @@ size_t sharq_quantize_weight_workspace_size(int64_t experts, int64_t nout, int64
 }
 
 sharq_status sharq_quantize_weight(const void *w, int32_t w_dtype, int64_t experts, int64_t nout,
-                                   int64_t K, int32_t fmt, uint8_t *codes, uint8_t *scales,
+                                   int64_t K, int64_t ldw, int32_t fmt, uint8_t *codes, uint8_t *scales,
                                    float *global_scale, void *workspace, size_t workspace_bytes,
                                    void *stream) {
     if (!valid_fmt(fmt)) return SHARQ_ERR_UNSUPPORTED;
     if (w_dtype != SHARQ_BF16 && w_dtype != SHARQ_F16) return SHARQ_ERR_DTYPE;
-    if (experts < 1 || nout < 0 || K <= 0 || K % block_of(fmt) != 0) return SHARQ_ERR_SHAPE;
+    if (experts < 1 || nout < 0 || K <= 0 || K % block_of(fmt) != 0 || ldw < K) return SHARQ_ERR_SHAPE;
     if (nout == 0) return SHARQ_OK;
     if (!w || !codes || !scales) return SHARQ_ERR_NULL;
     if (fmt == SHARQ_NVFP4 && !global_scale) return SHARQ_ERR_NULL;
-    if (!aligned(w, 16) || !aligned(codes, 4) || (global_scale && !aligned(global_scale, 4)))
+    if (!aligned(w, 16) || (ldw * 2) % 16 != 0 || !aligned(codes, 4) ||
+        (global_scale && !aligned(global_scale, 4)))
         return SHARQ_ERR_ALIGN;
     const size_t need = quantize_weight_workspace_bytes(experts, nout, fmt);
     if (need > 0 && (!workspace || workspace_bytes < need)) return SHARQ_ERR_WORKSPACE;
@@ -160,6 +161,7 @@ sharq_status sharq_quantize_weight(const void *w, int32_t w_dtype, int64_t exper
     a.E = experts;
     a.nout = nout;
     a.K = K;
+    a.ldw = ldw;
     a.fmt = fmt;
     a.bf16 = w_dtype == SHARQ_BF16;
     a.codes = codes;
@@ -178,9 +180,10 @@ sharq_status sharq_linear(const uint8_t *b_codes, const uint8_t *b_scales, const
                           int32_t fmt, const uint8_t *w_codes, const uint8_t *w_scales,
                           const float *w_global_scale, int64_t experts, int64_t nout,
                           const int32_t *group_offsets, const int32_t *row_index, int64_t rows,
-                          float *y, int64_t ldy, void *workspace, size_t workspace_bytes,
-                          void *stream) {
+                          void *y, int32_t y_dtype, int64_t ldy, void *workspace,
+                          size_t workspace_bytes, void *stream) {
     if (!valid_fmt(fmt)) return SHARQ_ERR_UNSUPPORTED;
+    if (y_dtype != SHARQ_F32 && y_dtype != SHARQ_BF16 && y_dtype != SHARQ_F16) return SHARQ_ERR_DTYPE;
     if (T < 0 || K <= 0 || K % 128 != 0 || experts < 1 || nout < 0 || rows < 0 || ldy < nout)
         return SHARQ_ERR_SHAPE;
     if (experts == 1 && !group_offsets && !row_index && rows != T) return SHARQ_ERR_SHAPE;
@@ -193,12 +196,14 @@ sharq_status sharq_linear(const uint8_t *b_codes, const uint8_t *b_scales, const
     if (!aligned(b_codes, 16) || !aligned(r_codes, 16) || !aligned(w_codes, 16) ||
         !aligned(b_scales, 4) || !aligned(r_scales, 4) || !aligned(w_scales, 4))
         return SHARQ_ERR_ALIGN;
-    if (!aligned(y, 4)) return SHARQ_ERR_ALIGN;
+    const size_t ysize = y_dtype == SHARQ_F32 ? 4 : 2;
+    if (!aligned(y, ysize)) return SHARQ_ERR_ALIGN;
     // operands are addressed with 32-bit buffer offsets
     const int64_t limit = (int64_t)1 << 31;
     if (T * (K / 2) >= limit || nout * (K / 2) >= limit) return SHARQ_ERR_SHAPE;
     const size_t need = linear_workspace_bytes(rows, K, nout, experts, fmt);
     if (need > 0 && (!workspace || workspace_bytes < need)) return SHARQ_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 16)) return SHARQ_ERR_ALIGN;
     LinearArgs a;
     a.b_codes = b_codes;
     a.b_scales = b_scales;
@@ -217,8 +222,9 @@ sharq_status sharq_linear(const uint8_t *b_codes, const uint8_t *b_scales, const
     a.row_index = row_index;
     a.rows = rows;
     a.y = y;
+    a.ydt = y_dtype == SHARQ_F32 ? kOutF32 : (y_dtype == SHARQ_BF16 ? kOutBf16 : kOutF16);
     a.ldy = ldy;
-    a.y_vec = aligned(y, 16) && ldy % 4 == 0;
+    a.y_vec = aligned(y, 4 * ysize) && ldy % 4 == 0;
     a.ksplit_tiles = 0;
     a.split_stride = 0;
     return hip_status(launch_linear(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));

@@ -104,6 +104,40 @@ __device__ __forceinline__ v8h nv_group(v4i c, const NvScale &s) {
     return v8h{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
 }
 
+// Output element conversions, round to nearest even (the hardware
+// conversions; F16 overflows to infinity).
+__device__ __forceinline__ uint32_t out_bits16(float f, int ydt) {
+    return ydt == kOutBf16 ? (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f)
+                           : (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Four consecutive outputs Y[m][n..n+3] (columns >= nout are skipped) in the
+// output type: one vector store when the row allows it.
+__device__ __forceinline__ void store_out4(const LinearArgs &a, int64_t m, int64_t n, v4f v) {
+    if (a.ydt == kOutF32) {
+        float *yrow = static_cast<float *>(a.y) + m * a.ldy;
+        if (a.y_vec && n + 3 < a.nout) {
+            *reinterpret_cast<v4f *>(yrow + n) = v;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                if (n + i < a.nout) yrow[n + i] = v[i];
+        }
+    } else {
+        uint16_t *yrow = static_cast<uint16_t *>(a.y) + m * a.ldy;
+        const uint32_t h0 = out_bits16(v.x, a.ydt), h1 = out_bits16(v.y, a.ydt);
+        const uint32_t h2 = out_bits16(v.z, a.ydt), h3 = out_bits16(v.w, a.ydt);
+        if (a.y_vec && n + 3 < a.nout) {
+            *reinterpret_cast<uint2 *>(yrow + n) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        } else {
+            const uint32_t h[4] = {h0, h1, h2, h3};
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                if (n + i < a.nout) yrow[n + i] = (uint16_t)h[i];
+        }
+    }
+}
+
 // ============================================================================
 // Prefill: LDS-tiled pipeline (three stage buffers in the shapes used; two
 // supported) fed by direct global->LDS buffer loads (no register staging).
@@ -562,7 +596,7 @@ void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles, int64_t n_beg
         a.w_codes += t0 * a.nout * (kTileK / 2);
         a.w_scales += t0 * a.nout * kScaleBytes;
         a.K = a.ksplit_tiles * kTileK;
-        a.y += (int64_t)blockIdx.y * a.split_stride;
+        a.y = static_cast<float *>(a.y) + (int64_t)blockIdx.y * a.split_stride;  // FP32 partials
     }
     using G = DualGemm<FMT, BM, BN, WGM, WGN, NS, LSPLIT, RPS>;
     using L = typename G::L;
@@ -688,7 +722,6 @@ void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles, int64_t n_beg
     for (int i = 0; i < FM; i++) {
         const int64_t m = tr.m0 + wm * (FM * 32) + i * 32 + frow;
         if (m >= tr.m_end) continue;
-        float *yrow = a.y + m * a.ldy;
 #pragma unroll
         for (int j = 0; j < FN; j++) {
 #pragma unroll
@@ -697,14 +730,7 @@ void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles, int64_t n_beg
                 v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
                 if constexpr (FMT == kFmtNv) v = v4f{__fmul_rn(v.x, alpha), __fmul_rn(v.y, alpha),
                                                      __fmul_rn(v.z, alpha), __fmul_rn(v.w, alpha)};
-                if (a.y_vec && n + 3 < a.nout) {
-                    *reinterpret_cast<v4f *>(yrow + n) = v;
-                } else {
-                    if (n < a.nout) yrow[n] = v.x;
-                    if (n + 1 < a.nout) yrow[n + 1] = v.y;
-                    if (n + 2 < a.nout) yrow[n + 2] = v.z;
-                    if (n + 3 < a.nout) yrow[n + 3] = v.w;
-                }
+                store_out4(a, m, n, v);
             }
         }
     }
@@ -848,16 +874,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_dual_gemm_mx_small(LinearA
         }
         const int64_t m = f * 16 + r;
         if (m >= a.rows) continue;
-        float *yrow = a.y + m * a.ldy;
-        const int64_t n = n0 + (lane >> 4) * 4;
-        if (a.y_vec && n + 3 < a.nout) {
-            *reinterpret_cast<v4f *>(yrow + n) = s;
-        } else {
-            const float vals[4] = {s.x, s.y, s.z, s.w};
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                if (n + i < a.nout) yrow[n + i] = vals[i];
-        }
+        store_out4(a, m, n0 + (lane >> 4) * 4, s);
     }
 }
 
@@ -949,15 +966,19 @@ static hipError_t launch_mx_shape(int s, const LinearArgs &a, hipStream_t st, in
 // best, instead of a last round that leaves CUs idle.
 // Sum of S partial products p[S][rows][nout] (row-major FP32) into y, the
 // partials added in the order s = 0, 1, ..., S-1.
-__global__ __launch_bounds__(256) void k_sum_partials(const float *p, int S, int64_t rows, int64_t nout, float *y,
-                                                      int64_t ldy) {
+// The sum is stored in the output type of the product.
+__global__ __launch_bounds__(256) void k_sum_partials(const float *p, int S, int64_t rows, int64_t nout, void *y,
+                                                      int ydt, int64_t ldy) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t plane = rows * nout;
     if (i >= plane) return;
     const int64_t m = i / nout, n = i - m * nout;
     float acc = p[i];
     for (int s = 1; s < S; s++) acc = __fadd_rn(acc, p[(int64_t)s * plane + i]);
-    y[m * ldy + n] = acc;
+    if (ydt == kOutF32)
+        static_cast<float *>(y)[m * ldy + n] = acc;
+    else
+        static_cast<uint16_t *>(y)[m * ldy + n] = (uint16_t)out_bits16(acc, ydt);
 }
 
 // Up to 64 rows: the small-batch kernel (weight rows split over many
@@ -1025,13 +1046,14 @@ static hipError_t launch_linear_mx_few_rows(const LinearArgs &a, void *ws, size_
         as.ksplit_tiles = a.K / kTileK / pl.S;
         as.split_stride = a.rows * a.nout;
         as.y = part;
+        as.ydt = kOutF32;
         as.ldy = a.nout;
         as.y_vec = a.nout % 4 == 0 && ((uintptr_t)part % 16) == 0;
         const hipError_t e = launch_prefill<kFmtMx, 64, 64, 2, 2, 3, 2>(as, st);
         if (e != hipSuccess) return e;
         const int64_t n = a.rows * a.nout;
         hipLaunchKernelGGL(k_sum_partials, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, pl.S, a.rows,
-                           a.nout, a.y, a.ldy);
+                           a.nout, a.y, a.ydt, a.ldy);
         return hipGetLastError();
     }
     if (pl.kernel >= 1) return launch_prefill<kFmtMx, 64, 64, 2, 2, 3, 2>(a, st);

@@ -9,6 +9,7 @@ namespace sharq {
 
 enum { kNormNone = 0, kNormRms = 1, kNormLayer = 2 };
 enum { kFmtMx = 0, kFmtNv = 1 };
+enum { kOutF32 = 0, kOutBf16 = 1, kOutF16 = 2 };  // product output element type
 
 // K-tiled layout of every FP4 code and scale array (activations and
 // weights): K is cut into tiles of 128 elements (the last one may be
@@ -51,7 +52,7 @@ size_t prepare_workspace_bytes(int64_t T, int fmt);
 
 struct QuantWArgs {
     const uint16_t *w;
-    int64_t E, nout, K;
+    int64_t E, nout, K, ldw;  // element k of row n of expert e at w[(e*nout + n)*ldw + k]
     int fmt;
     bool bf16;
     uint8_t *codes, *scales;
@@ -71,9 +72,10 @@ struct LinearArgs {
     int64_t E, nout;
     const int32_t *offsets, *row_index;
     int64_t rows;
-    float *y;
+    void *y;     // [rows][ldy] elements of type ydt
+    int ydt;     // kOutF32, kOutBf16 or kOutF16 (rounded to nearest even)
     int64_t ldy;
-    bool y_vec;  // rows of y are 16-byte aligned: 128-bit stores
+    bool y_vec;  // y and its rows aligned to four elements: one vector store per four
     // K split (dense products only): grid row s multiplies K tiles
     // [s*ksplit_tiles, (s+1)*ksplit_tiles) into y + s*split_stride; 0 = no split
     int64_t ksplit_tiles, split_stride;

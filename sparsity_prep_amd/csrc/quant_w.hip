@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kQWaves * kWave) void k_quant_w(QuantWArgs a) {
         const int64_t e0 = ((c0 + c) * kWave + lane) * 8;
         if (e0 < K) {
             float v[8];
-            unpack8<BF16>(*reinterpret_cast<const uint4 *>(a.w + row * K + e0), v);
+            unpack8<BF16>(*reinterpret_cast<const uint4 *>(a.w + row * a.ldw + e0), v);
             uint32_t codes;
             const uint32_t sb = quant_block8<FMT>(v, G, G6, codes);
             // expert-major; each expert's [nout x K] payload is K-tiled
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kQWaves * kWave) void k_row_amax(QuantWArgs a, floa
     if (row >= a.E * a.nout) return;
     float m = 0.0f, v[8];
     for (int64_t e0 = (int64_t)lane * 8; e0 < a.K; e0 += kQChunk) {
-        unpack8<BF16>(*reinterpret_cast<const uint4 *>(a.w + row * a.K + e0), v);
+        unpack8<BF16>(*reinterpret_cast<const uint4 *>(a.w + row * a.ldw + e0), v);
 #pragma unroll
         for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
     }

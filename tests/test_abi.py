@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.sharq_abi_version() == 3
+    assert L.sharq_abi_version() == 4
     for code in range(9):
         assert L.sharq_status_string(code)
     assert L.sharq_status_string(99) == b"unknown status"
@@ -111,35 +111,44 @@ def test_prepare_swiglu_validation(L):
 
 
 def test_quantize_weight_validation(L):
-    q = L.sharq_quantize_weight
-    assert q(FAKE, BF16, 1, 16, 256, 9, FAKE, FAKE, None, None, 0, None) == UNSUPPORTED
-    assert q(FAKE, F32, 1, 16, 256, MX, FAKE, FAKE, None, None, 0, None) == DTYPE
-    assert q(FAKE, BF16, 0, 16, 256, MX, FAKE, FAKE, None, None, 0, None) == SHAPE
-    assert q(FAKE, BF16, 1, 16, 40, MX, FAKE, FAKE, None, None, 0, None) == SHAPE
-    assert q(None, BF16, 1, 16, 256, MX, FAKE, FAKE, None, None, 0, None) == NULL
-    assert q(FAKE, BF16, 1, 16, 256, NV, FAKE, FAKE, None, None, 0, None) == NULL
-    assert q(FAKE, BF16, 1, 16, 256, NV, FAKE, FAKE, FAKE, None, 0, None) == WORKSPACE
-    assert q(MISALIGNED, BF16, 1, 16, 256, MX, FAKE, FAKE, None, None, 0, None) == ALIGN
-    assert q(None, BF16, 1, 0, 256, MX, None, None, None, None, 0, None) == OK
+    def q(w=FAKE, dt=BF16, E=1, nout=16, K=256, ldw=None, fmt=MX, codes=FAKE, G=None, ws=None, wsb=0):
+        return L.sharq_quantize_weight(w, dt, E, nout, K, K if ldw is None else ldw, fmt, codes, FAKE, G,
+                                       ws, wsb, None)
+    assert q(fmt=9) == UNSUPPORTED
+    assert q(dt=F32) == DTYPE
+    assert q(E=0) == SHAPE
+    assert q(K=40) == SHAPE
+    assert q(ldw=128) == SHAPE                    # row stride shorter than a row
+    assert q(w=None) == NULL
+    assert q(fmt=NV) == NULL
+    assert q(fmt=NV, G=FAKE) == WORKSPACE
+    assert q(w=MISALIGNED) == ALIGN
+    assert q(ldw=256 + 4) == ALIGN                # rows not 16-byte aligned
+    assert q(w=None, nout=0) == OK
+    assert q(fmt=NV, G=FAKE, ws=MISALIGNED, wsb=1 << 20) == ALIGN
 
 
-def lin(L, T=4, K=256, fmt=MX, E=1, nout=64, offs=None, ridx=None, rows=None, y=FAKE, ldy=None,
-        bc=FAKE, xg=None, wg=None):
+def lin(L, T=4, K=256, fmt=MX, E=1, nout=64, offs=None, ridx=None, rows=None, y=FAKE, ydt=F32, ldy=None,
+        bc=FAKE, xg=None, wg=None, ws=None, wsb=0):
     return L.sharq_linear(bc, FAKE, FAKE, FAKE, xg, T, K, fmt, FAKE, FAKE, wg, E, nout, offs, ridx,
-                          T if rows is None else rows, y, nout if ldy is None else ldy, None, 0, None)
+                          T if rows is None else rows, y, ydt, nout if ldy is None else ldy, ws, wsb, None)
 
 
 def test_linear_validation(L):
     assert lin(L, fmt=5) == UNSUPPORTED
+    assert lin(L, ydt=7) == DTYPE                 # output must be F32, BF16 or F16
     assert lin(L, K=160) == SHAPE                 # not a multiple of 128
     assert lin(L, ldy=10) == SHAPE
     assert lin(L, rows=7) == SHAPE                # dense rows must equal T without a gather
     assert lin(L, E=4) == NULL                    # grouped needs offsets
     assert lin(L, bc=None) == NULL
     assert lin(L, fmt=NV) == NULL                 # NVFP4 needs both tensor scales
-    assert lin(L, y=MISALIGNED) == ALIGN
+    assert lin(L, y=MISALIGNED) == ALIGN          # 2 bytes past a boundary: not float-aligned
+    assert lin(L, y=ctypes.c_void_p(0x10001), ydt=BF16) == ALIGN
     assert lin(L, rows=0, T=0) == OK
     assert lin(L, T=64, K=14336, nout=4096) == WORKSPACE   # a K-split product needs its workspace
+    need = L.sharq_linear_workspace_size(64, 14336, 4096, 1, MX)
+    assert lin(L, T=64, K=14336, nout=4096, ws=ctypes.c_void_p(0x10004), wsb=need) == ALIGN
     assert lin(L, T=0, rows=3, ridx=FAKE) == SHAPE
 
 

@@ -514,3 +514,80 @@ def test_prepare_swiglu_column_convention():
     a = oracle.prepare_swiglu(gu, K, 2, 4, oracle.FMT_MXFP4, trace=True)
     assert np.array_equal(a.xhat[0], np.float32(100.0) * up)
     assert np.array_equal(a.xhat[1].view(np.uint32), (np.float32(0.0) * up).view(np.uint32))
+
+
+# ---------------------------------------------------------------- sampled-row entry points
+# The full-size GPU checks compare sampled rows: a sample of weight rows
+# quantized with the weight's own tensor scale (quantize_rows), and a subset
+# of activation rows (prepare / prepare_swiglu with rows=...), where the NVFP4
+# tensor scale must still come from every row of the tensor.
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_quantize_rows_is_plain_rtn(fmt):
+    K, NO = 512, 24
+    wb = synth.small_weight(NO, K, tag=61)[0]
+    wf = synth.bits_to_f32(wb, "bf16")
+    rows = np.array([17, 0, 5, 5, 23, 11])
+    G = 1.0
+    if fmt == 1:
+        G = float(np.float32(np.abs(wf).max()) / np.float32(2688.0))  # the whole weight's scale
+    c, s = oracle.quantize_rows(wb[rows], "bf16", fmt, G)
+    if fmt == 0:
+        codes, sc, _ = textbook_mx(wf[rows])
+    else:
+        codes, sc, _ = textbook_nv(wf[rows], G)
+    assert np.array_equal(unpack(c), codes)
+    assert np.array_equal(s, sc)
+    # and the same bytes as those rows of the whole-weight payload
+    wq = oracle.quantize_weight(wb, "bf16", fmt)
+    assert np.float32(G) == wq.gscale[0]
+    assert np.array_equal(c, wq.codes[0][rows])
+    assert np.array_equal(s, wq.scales[0][rows])
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("norm", [oracle.NORM_RMS, oracle.NORM_LAYER, oracle.NORM_NONE])
+def test_prepare_row_subset(fmt, norm):
+    K, T = 256, 40
+    x, g = _case(K, T=T, dist="t" if fmt else "normal", tag=62 + norm)
+    beta = synth.small_gamma(K, "bf16", tag=70) if norm == oracle.NORM_LAYER else None
+    gam = g if norm != oracle.NORM_NONE else None
+    xf = synth.bits_to_f32(x, "bf16")
+    hot = int(np.argmax(np.abs(xf).max(1)))
+    # out of order, repeated, and without the row that holds the largest value
+    rows = np.array([t for t in (39, 3, 3, 0, 21, 38, 7) if t != hot])
+    full = oracle.prepare(x, "bf16", K, norm, gam, beta, 1e-5, 2, 4, fmt, trace=True)
+    sub = oracle.prepare(x, "bf16", K, norm, gam, beta, 1e-5, 2, 4, fmt, rows=rows, trace=True)
+    for key in ("mask", "b_codes", "b_scales", "r_codes", "r_scales", "xhat", "deqb", "resid"):
+        assert np.array_equal(getattr(sub, key), getattr(full, key)[rows]), key
+    assert sub.G == full.G
+    if fmt == 1:
+        # NVFP4: the tensor scale is the whole tensor's amax / 2688 (textbook),
+        # not the subset's, and the subset's codes follow the textbook quantizer
+        G = float(np.float32(np.abs(full.xhat).max()) / np.float32(2688.0))
+        assert sub.G == np.float32(G)
+        assert np.abs(sub.xhat).max() < np.abs(full.xhat).max()
+        S = np.where(oracle.unpack_mask(sub.mask), sub.xhat, np.float32(0)).astype(np.float32)
+        codes, s, _ = textbook_nv(S, sub.G)
+        assert np.array_equal(unpack(sub.b_codes), codes)
+        assert np.array_equal(sub.b_scales, s)
+    else:
+        # MXFP4 has no tensor-level coupling: each row alone gives the same bytes
+        for i, t in enumerate(rows):
+            one = oracle.prepare(x[t:t + 1], "bf16", K, norm, gam, beta, 1e-5, 2, 4, fmt)
+            for key in ("mask", "b_codes", "b_scales", "r_codes", "r_scales"):
+                assert np.array_equal(getattr(one, key)[0], getattr(sub, key)[i]), (key, t)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_prepare_swiglu_row_subset(fmt):
+    K, T = 128, 24
+    gu = synth.small_gate_up(K, T, tag=63 + fmt)
+    rows = np.array([23, 1, 1, 12])
+    full = oracle.prepare_swiglu(gu, K, 2, 4, fmt, trace=True)
+    sub = oracle.prepare_swiglu(gu, K, 2, 4, fmt, rows=rows, trace=True)
+    for key in ("mask", "b_codes", "b_scales", "r_codes", "r_scales", "xhat"):
+        assert np.array_equal(getattr(sub, key), getattr(full, key)[rows]), key
+    assert sub.G == full.G
+    if fmt == 1:
+        assert full.G == np.float32(np.float32(np.abs(full.xhat).max()) / np.float32(2688.0))

@@ -3,23 +3,28 @@
 One step = the whole hot path over one batch: for each linear layer of the
 workload, the fused preparation (norm, 2:4 mask, FP4 backbone, residual, FP4
 residual) followed by the dual-path FP4 product.  The default workload is a
-Llama-3.1-8B-shaped prefill layer (2048 tokens; qkv 4096->6144 and gate_up
-4096->28672 with RMSNorm, down 14336->4096 without norm) in MXFP4.  Inputs
-are seeded synthetic tensors of the models' shapes, resident in HBM before
-the timed region; several copies of every input and weight are rotated so
-that the 256 MB Infinity Cache cannot serve a step from the previous one.
+Llama-3.1-8B-shaped prefill layer (2048 tokens) in MXFP4 with the layer's
+four linears in order: qkv 4096->6144 (RMSNorm), o_proj 4096->4096 (no norm),
+gate_up 4096->28672 (RMSNorm) and down 14336->4096, whose preparation reads
+gate_up's FP32 output and forms SiLU(gate)*up inside the prep kernel.
+Inputs are seeded synthetic tensors of the models' shapes, resident in HBM
+before the timed region; several copies of every input, weight and output are
+rotated so that the 256 MB Infinity Cache cannot serve a step from the
+previous one.
 
 Prints one JSON line: whole-step dual-product throughput (algorithmic
 TFLOP/s, 2*T*Nout*K*(1+N/M) per linear) with every timed step run as one
-captured HIP graph (--graph off: eager launches), prep GB/s, the roofline of
-the dominant kernel (the dual product) from per-launch times taken with HIP
-events on the launch stream (eager steps around every launch; for decode
-batches, graphs holding one phase over the rotated copies), with its
-HBM-side traffic from the committed counter summary under profiles/ while
-the kernel sources match it, the CPU oracle timed on a bounded sample on
-the host, the operator-level error of SharQ next to plain FP4
-round-to-nearest, the fused SiLU(gate)*up prep of the down projection next
-to the unfused chain, and the same linears as bf16 / FP8 GEMMs.
+captured HIP graph (--graph off: eager launches); per-launch kernel times
+from graphs that hold one phase (one linear's preps, or its products) over
+rotated copies, timed with HIP events around a replay on the launch stream
+(prep inputs rotated over enough copies to exceed twice the Infinity Cache);
+the roofline of the dominant kernel (the dual product) and of the prep from
+those times, with HBM-side traffic from the committed counter summaries under
+profiles/ while the kernel sources match them; the products with BF16
+output; the CPU oracle timed on a bounded sample on the host; the
+operator-level error of SharQ next to plain FP4 round-to-nearest; the fused
+SiLU(gate)*up prep against the unfused chain; and the same linears as bf16 /
+FP8 GEMMs.
 
     python bench.py [--gpus 1] [--steps 30] [--warmup 5]
                     [--workload llama|decode1|decode8|decode64|qwen|moe]
@@ -29,6 +34,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import platform
 import sys
@@ -40,11 +46,13 @@ import numpy as np
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
 F16_PEAK_TFLOPS = 2500.0        # MI355X dense f16 / bf16 MFMA
+INFINITY_CACHE_BYTES = 256 << 20
 # 32x32x64 block-scaled FP4 MFMA issued back to back from registers with
 # random operands (no memory traffic), measured on MI355X: the chip lowers its
 # clock under that load (about 1.6 GHz, against 2.1-2.3 GHz with constant operands)
 MFMA_RANDOM_FP4_TFLOPS = 6250.0
-SAMPLE_ROWS = 32                # rows per linear in the CPU baseline and the error report
+ERROR_ROWS = 32                 # rows per linear in the error report
+CPU_ROWS = 256                  # rows per linear (per thread for the threaded prep) in the CPU baseline
 
 
 def parse():
@@ -54,14 +62,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama")
     ap.add_argument("--rotate", type=int, default=None,
-                    help="copies of every input and weight rotated across steps (default: 3, and 8 for "
-                         "decode batches, so that the rotated set outgrows the 256 MB Infinity Cache)")
+                    help="copies of every input, weight and output rotated across steps (default: 3, and 8 "
+                         "for decode batches, so that the rotated set outgrows the 256 MB Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", choices=["on", "off"], default="on",
-                    help="run every timed step as one captured HIP graph (off: eager launches "
-                         "from the host, with HIP events around every launch)")
+                    help="run every timed step as one captured HIP graph (off: eager launches)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the fused SiLU(gate)*up prep and the bf16 / fp8 GEMM comparisons")
+                    help="skip the BF16-output products, the unfused SiLU chain and the bf16 / fp8 GEMMs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter calibration)")
     return ap.parse_args()
@@ -71,10 +78,11 @@ def block_of(fmt):
     return 32 if fmt == 0 else 16
 
 
-def prep_bytes(T, K, fmt):
-    """Algorithmic bytes of one prep: read X (bf16) once, write codes, scales and mask."""
-    per_row = 2 * K + K + 2 * K // block_of(fmt) + K // 8
-    return T * per_row
+def prep_bytes(T, K, fmt, swiglu=False):
+    """Algorithmic bytes of one prep: read the input once (bf16 X, or the FP32
+    gate and up halves for the SiLU(gate)*up prep), write codes, scales and mask."""
+    read = 8 * K if swiglu else 2 * K
+    return T * (read + K + 2 * K // block_of(fmt) + K // 8)
 
 
 def gemm_flops(rows, K, nout, n, m):
@@ -92,15 +100,25 @@ class Layer:
 
     prep_tokens rows are prepared; the product writes `rows` output rows
     (more than prep_tokens when a grouped product gathers rows of an MoE
-    expert batch through row_index)."""
+    expert batch through row_index).  When `src` is given, the prep input is
+    src's FP32 output [gate | up] (SiLU(gate)*up formed in the prep kernel)."""
 
-    def __init__(self, sq, torch, synth, wl, lin, prep_tokens, rotate, dev, route=None, gather=False):
-        self.lin, self.wl = lin, wl
+    def __init__(self, sq, torch, synth, wl, lin, prep_tokens, rotate, dev, route=None, gather=False,
+                 src=None, prep_copies=None):
+        self.lin, self.wl, self.src = lin, wl, src
         self.prep_tokens = prep_tokens
-        x = synth.activation(wl, lin, prep_tokens)
-        xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
-        self.x = [xt] + [xt.clone() for _ in range(rotate - 1)]
-        self.x_host = x
+        self.rotate = rotate
+        self.x = None
+        self.x_host = None
+        n_in = rotate if prep_copies is None else max(rotate, prep_copies)
+        if src is None:
+            x = synth.activation(wl, lin, prep_tokens)
+            xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+            self.x = [xt] + [xt.clone() for _ in range(n_in - 1)]
+            self.x_host = x
+        else:
+            n_in = rotate  # src's rotated outputs (each larger than the Infinity Cache)
+        self.n_in = n_in
         self.g = None
         if lin.norm:
             self.g = torch.from_numpy(synth.gamma(wl, lin).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -114,44 +132,59 @@ class Layer:
         self.E = q.E
         self.offs = self.ridx = None
         self.rows = prep_tokens
-        S = min(SAMPLE_ROWS, prep_tokens)
-        self.sample_tokens = np.arange(S)          # host rows of x feeding the sampled outputs
-        self.sample_experts = np.zeros(S, np.int64)
+        self.sample_tokens = np.arange(prep_tokens)  # host rows of the prep input feeding output row r
+        self.sample_experts = np.zeros(prep_tokens, np.int64)
         if route is not None:
             self.offs = torch.from_numpy(route.offsets).to(dev)
             self.rows = int(route.offsets[-1])
             if gather:
                 self.ridx = torch.from_numpy(route.row_index).to(dev)
-                self.sample_tokens = route.row_index[:S].astype(np.int64)
-            self.sample_experts = route.expert_of_row[:S].astype(np.int64)
-        experts = sorted(set(self.sample_experts.tolist()) | {0})
+                self.sample_tokens = route.row_index.astype(np.int64)
+            else:
+                self.sample_tokens = np.arange(self.rows)
+            self.sample_experts = route.expert_of_row.astype(np.int64)
+        experts = sorted(set(self.sample_experts[:max(ERROR_ROWS, CPU_ROWS)].tolist()) | {0})
         self.w_host = {e: w_bits[e] for e in experts}  # weight rows the host-side reports need
         del w_bits
-        self.prep = [sq.alloc_prepared(prep_tokens, lin.k, wl.fmt, dev) for _ in range(rotate)]
+        self.prep = [sq.alloc_prepared(prep_tokens, lin.k, wl.fmt, dev) for _ in range(n_in)]
         self.y = [torch.empty((self.rows, lin.nout), dtype=torch.float32, device=dev) for _ in range(rotate)]
+        self.y16 = None
+
+    @property
+    def swiglu(self):
+        return self.src is not None
 
     def run_prep(self, sq, i):
-        r = i % len(self.x)
-        sq.prepare(self.x[r], norm=self.lin.norm, gamma=self.g, eps=self.wl.eps, n=self.wl.n, m=self.wl.m,
-                   fmt=self.wl.fmt, out=self.prep[r])
+        r = i % self.n_in
+        if self.src is not None:
+            sq.prepare_swiglu(self.src.y[i % self.src.rotate], self.lin.k, n=self.wl.n, m=self.wl.m,
+                              fmt=self.wl.fmt, out=self.prep[r])
+        else:
+            sq.prepare(self.x[r], norm=self.lin.norm, gamma=self.g, eps=self.wl.eps, n=self.wl.n, m=self.wl.m,
+                       fmt=self.wl.fmt, out=self.prep[r])
 
-    def run_gemm(self, sq, i):
-        r = i % len(self.x)
-        sq.linear(self.prep[r], self.w[r], group_offsets=self.offs, row_index=self.ridx, rows=self.rows,
-                  out=self.y[r])
+    def run_gemm(self, sq, i, bf16=False):
+        r = i % self.rotate
+        out = self.y16[r] if bf16 else self.y[r]
+        sq.linear(self.prep[r], self.w[r], group_offsets=self.offs, row_index=self.ridx, rows=self.rows, out=out)
 
     def run(self, sq, i, ev=None):
-        r = i % len(self.x)
+        """Prep then product of rotated copy i % rotate (events around each, if given)."""
+        i = i % self.rotate
         if ev is not None:
             ev[0].record()
-        sq.prepare(self.x[r], norm=self.lin.norm, gamma=self.g, eps=self.wl.eps, n=self.wl.n, m=self.wl.m,
-                   fmt=self.wl.fmt, out=self.prep[r])
+        self.run_prep(sq, i)
         if ev is not None:
             ev[1].record()
-        sq.linear(self.prep[r], self.w[r], group_offsets=self.offs, row_index=self.ridx, rows=self.rows,
-                  out=self.y[r])
+        self.run_gemm(sq, i)
         if ev is not None:
             ev[2].record()
+
+    def prep_input_host(self, rows):
+        """Host copy of the prep input rows (bf16 bits, or FP32 [gate | up] rows of src's output)."""
+        if self.src is None:
+            return self.x_host[rows]
+        return self.src.y[0][rows].cpu().numpy()
 
 
 _ORACLE_W = {}
@@ -166,11 +199,27 @@ def oracle_weight(L, e):
     return _ORACLE_W[key]
 
 
-def host_info():
+def usable_cores():
+    """CPUs this process may run on: the affinity mask, limited by a cgroup CPU quota if one is set."""
     try:
-        ncpu = len(os.sched_getaffinity(0))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:
-        ncpu = os.cpu_count()
+        n = os.cpu_count() or 1
+    quota = None
+    for path in ("/sys/fs/cgroup/cpu.max",):
+        try:
+            q, per = open(path).read().split()[:2]
+            if q != "max":
+                quota = float(q) / float(per)
+        except (OSError, ValueError):
+            pass
+    if quota is not None:
+        n = max(1, min(n, int(math.floor(quota))))
+    return n, quota
+
+
+def host_info():
+    n, quota = usable_cores()
     model = platform.processor()
     try:
         with open("/proc/cpuinfo") as f:
@@ -183,81 +232,117 @@ def host_info():
     from threadpoolctl import threadpool_info
     blas = [f"{d.get('internal_api')} {d.get('version')} ({d.get('num_threads')} threads)"
             for d in threadpool_info() if d.get("user_api") == "blas"]
-    return {"cpus_usable": ncpu, "cpu_model": model, "blas": blas}
+    return {"cpus_usable": n, "cgroup_cpu_quota": quota, "cpu_count": os.cpu_count(), "cpu_model": model,
+            "blas": blas}
+
+
+def oracle_prep(L, rows):
+    """The oracle's preparation of the given input rows of layer L."""
+    import oracle
+    import synth
+    wl, lin = L.wl, L.lin
+    if L.swiglu:
+        return oracle.prepare_swiglu(L.prep_input_host(rows), lin.k, wl.n, wl.m, wl.fmt)
+    g = synth.gamma(wl, lin) if lin.norm else None
+    return oracle.prepare(L.x_host, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.n, wl.m, wl.fmt, rows=rows)
 
 
 def cpu_baseline(layers):
     """The oracle (C prep + float64 numpy product) on a bounded sample: the
-    first SAMPLE_ROWS tokens of every linear of the step (MoE: against expert
-    0).  The prep also runs on all usable cores (rows split over threads that
-    each call the same single-threaded oracle)."""
-    import oracle
-    import synth
-    from threadpoolctl import threadpool_info
-    t_prep = t_gemm = t_prep_all = 0.0
+    first CPU_ROWS input rows of every linear (MoE: against expert 0).  The
+    prep runs on every usable core (rows split over threads that each call the
+    single-threaded oracle on CPU_ROWS rows of their own; ctypes releases the
+    interpreter lock during the call) and once on one thread; the product
+    runs as float64 BLAS on the same number of threads."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores, _ = usable_cores()
+    t_prep1 = t_prep_all = t_gemm = 0.0
     flops = 0.0
-    pbytes = pbytes_all = 0
-    cores = host_info()["cpus_usable"]
+    b1 = b_all = 0
     for L in layers:
         wl, lin = L.wl, L.lin
-        S = min(SAMPLE_ROWS, L.prep_tokens)
-        x = L.x_host[:S]
-        g = synth.gamma(wl, lin) if lin.norm else None
+        S = min(CPU_ROWS, L.prep_tokens)
         dw = oracle_weight(L, 0).deq(0)  # offline on both sides: not timed
+        rows = np.arange(S)
+        if L.swiglu:
+            L._cpu_in = L.prep_input_host(np.arange(min(S * cores, L.prep_tokens)))
         t0 = time.perf_counter()
-        p = oracle.prepare(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.n, wl.m, wl.fmt)
+        p = oracle_prep_rows(L, rows)
         t1 = time.perf_counter()
-        _ = p.deq_backbone() @ dw.T + p.deq_residual() @ dw.T
-        t2 = time.perf_counter()
-        t_prep += t1 - t0
-        t_gemm += t2 - t1
+        with threadpool_limits(limits=cores, user_api="blas"):
+            t2 = time.perf_counter()
+            _ = p.deq_backbone() @ dw.T + p.deq_residual() @ dw.T
+            t3 = time.perf_counter()
+        t_prep1 += t1 - t0
+        t_gemm += t3 - t2
         flops += gemm_flops(S, lin.k, lin.nout, wl.n, wl.m)
-        pbytes += prep_bytes(S, lin.k, wl.fmt)
-        # all cores: S rows per thread
+        b1 += prep_bytes(S, lin.k, wl.fmt, L.swiglu)
         n_all = min(S * cores, L.prep_tokens)
         chunks = [c for c in np.array_split(np.arange(n_all), cores) if c.size]
-        t3 = time.perf_counter()
         with ThreadPoolExecutor(len(chunks)) as ex:
-            list(ex.map(lambda r: oracle.prepare(L.x_host, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.n,
-                                                 wl.m, wl.fmt, rows=r), chunks))
-        t_prep_all += time.perf_counter() - t3
-        pbytes_all += prep_bytes(n_all, lin.k, wl.fmt)
-    blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    total = t_prep + t_gemm
+            t4 = time.perf_counter()
+            list(ex.map(lambda r: oracle_prep_rows(L, r), chunks))
+            t_prep_all += time.perf_counter() - t4
+        b_all += prep_bytes(n_all, lin.k, wl.fmt, L.swiglu)
+        L._cpu_in = None
+    blas_threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    prep_all_gbps = b_all / t_prep_all / 1e9
+    t_prep_sample = b1 / (prep_all_gbps * 1e9)  # the sample's prep at the all-cores rate
+    total = t_prep_sample + t_gemm
     return {
-        "value": flops / total / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-        "sample": f"first {SAMPLE_ROWS} tokens of every linear (full weights); prep in single-threaded C "
-                  f"({pbytes / t_prep / 1e9:.3f} GB/s), product in float64 numpy "
-                  f"({flops / t_gemm / 1e9:.2f} GFLOP/s on {blas_threads} BLAS threads)",
-        "seconds": total, "prep_GBps_1thread": pbytes / t_prep / 1e9,
-        "prep_GBps_all_cores": pbytes_all / t_prep_all / 1e9, "gemm_GFLOPs": flops / t_gemm / 1e9,
-        "host": host_info(),
+        "value": flops / total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+        "sample": f"first {CPU_ROWS} input rows of every linear (full weights); prep in the single-threaded C "
+                  f"oracle on {len(chunks)} threads ({prep_all_gbps:.3f} GB/s; {b1 / t_prep1 / 1e9:.3f} GB/s on "
+                  f"one thread), product in float64 numpy ({flops / t_gemm / 1e9:.2f} GFLOP/s on {cores} BLAS "
+                  f"threads); value = sample product flops / (sample prep at the all-cores rate + product time)",
+        "seconds": t_prep1 + t_prep_all + t_gemm, "prep_GBps_1thread": b1 / t_prep1 / 1e9,
+        "prep_GBps_all_cores": prep_all_gbps, "prep_threads": len(chunks), "gemm_GFLOPs": flops / t_gemm / 1e9,
+        "blas_threads_default": int(blas_threads), "host": host_info(),
     }
+
+
+def oracle_prep_rows(L, rows):
+    """oracle_prep for the CPU baseline: swiglu layers read their cached host rows."""
+    import oracle
+    if L.swiglu:
+        wl = L.wl
+        return oracle.prepare_swiglu(L._cpu_in[rows], L.lin.k, wl.n, wl.m, wl.fmt)
+    return oracle_prep(L, rows)
 
 
 def error_report(layers):
     """Relative Frobenius error of sampled output rows against an unquantized
-    reference (the FP32 normalized activation times the bf16 weight, in
+    reference (the FP32 prepared activation x^ times the bf16 weight, in
     float64): SharQ on the GPU, SharQ in the oracle, plain FP4 round to
     nearest (N = M, no residual), the N = M ablation (residual kept, no
-    mask), and SharQ's activation side alone (unquantized weight)."""
+    mask), and SharQ's activation side alone (unquantized weight).  For a
+    SiLU(gate)*up input, x^ is that product of the sampled rows; NVFP4 RTN
+    and ablation rows then take the sample's own tensor scale."""
     import oracle
     import synth
     out = {}
     for L in layers:
         wl, lin = L.wl, L.lin
-        S = L.sample_tokens.size
-        x = L.x_host[L.sample_tokens]
-        g = synth.gamma(wl, lin) if lin.norm else None
-        xh = oracle.normalize(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps).astype(np.float64)
-        sh = oracle.prepare(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.n, wl.m, wl.fmt)
-        rtn = oracle.prepare(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.m, wl.m, wl.fmt)
+        S = min(ERROR_ROWS, L.rows)
+        toks = L.sample_tokens[:S]
+        exps = L.sample_experts[:S]
+        if L.swiglu:
+            sh = oracle.prepare_swiglu(L.prep_input_host(toks), lin.k, wl.n, wl.m, wl.fmt, trace=True)
+            xh = sh.xhat
+            rtn = oracle.prepare(xh, "f32", lin.k, oracle.NORM_NONE, None, None, 0.0, wl.m, wl.m, wl.fmt)
+        else:
+            x = L.x_host[toks]
+            g = synth.gamma(wl, lin) if lin.norm else None
+            xh = oracle.normalize(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps)
+            sh = oracle.prepare(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.n, wl.m, wl.fmt)
+            rtn = oracle.prepare(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.m, wl.m, wl.fmt)
+        xh = xh.astype(np.float64)
         xs = sh.deq_backbone() + sh.deq_residual()
         xa = rtn.deq_backbone() + rtn.deq_residual()
         ref = np.zeros((S, lin.nout))
         y = {k: np.zeros((S, lin.nout)) for k in ("sharq_oracle", "rtn", "nm_ablation", "activation_only")}
-        for e in sorted(set(L.sample_experts.tolist())):
-            sel = np.nonzero(L.sample_experts == e)[0]
+        for e in sorted(set(exps.tolist())):
+            sel = np.nonzero(exps == e)[0]
             wf = synth.bits_to_f32(L.w_host[e], wl.dtype).astype(np.float64)
             dw = oracle_weight(L, e).deq(0)
             ref[sel] = xh[sel] @ wf.T
@@ -288,7 +373,8 @@ def _event_ms(torch, fn, reps=20):
 
 
 def _replay_ms(torch, graph):
-    """Time of one replay of a captured graph (HIP events, after one warm replay)."""
+    """Time of one replay of a captured graph (HIP events on the current
+    stream, which the replay is launched on; after one warm replay)."""
     graph.replay()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -299,16 +385,31 @@ def _replay_ms(torch, graph):
     return a.elapsed_time(b)
 
 
+def _capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def phase_ms(torch, fn, launches):
+    """Per-launch time of a phase: a graph holding `launches` calls fn(i),
+    timed around one replay."""
+    g = _capture(torch, lambda: [fn(i) for i in range(launches)])
+    ms = _replay_ms(torch, g) / launches
+    del g
+    return ms
+
+
 def swiglu_report(sq, torch, wl, layers):
-    """The down projection's prep from the gate/up product's float32 output:
-    fused (SiLU(gate)*up computed inside the prep kernel) against an unfused
-    chain (torch SiLU*up to a bf16 tensor, then the bf16 prep)."""
-    gu_layer = next((L for L in layers if L.lin.name == "gate_up"), None)
-    down = next((L for L in layers if L.lin.name == "down"), None)
-    if gu_layer is None or down is None or gu_layer.rows != down.prep_tokens:
+    """The SiLU(gate)*up prep of the down projection (fused in the prep
+    kernel, as in the layer step) against the unfused chain: torch SiLU*up to a
+    bf16 tensor, then the bf16 prep."""
+    down = next((L for L in layers if L.swiglu), None)
+    if down is None:
         return None
-    Ys = gu_layer.y                     # rotated copies, so the Infinity Cache cannot hold the input
-    T, K = Ys[0].shape[0], Ys[0].shape[1] // 2
+    Ys = down.src.y                     # rotated copies, each larger than the Infinity Cache
+    T, K = Ys[0].shape[0], down.lin.k
     out = sq.alloc_prepared(T, K, wl.fmt, Ys[0].device)
     it = [0]
 
@@ -321,16 +422,15 @@ def swiglu_report(sq, torch, wl, layers):
 
     def unfused_chain():
         Y = nxt()
-        act.copy_(torch.nn.functional.silu(Y[:, :K]) * Y[:, K:])
+        act.copy_(torch.nn.functional.silu(Y[:, :K]) * Y[:, K:2 * K])
         sq.prepare(act, norm=0, n=wl.n, m=wl.m, fmt=wl.fmt, out=out)
 
     chain = _event_ms(torch, unfused_chain)
-    B = block_of(wl.fmt)
-    algo = T * (8 * K + K + 2 * K // B + K // 8)   # read gate and up (f32), write the prepared tensors
-    return {"rows": T, "K": K, "fused_us": round(fused * 1e3, 2), "fused_GBps": round(algo / (fused * 1e-3) / 1e9, 1),
+    return {"rows": T, "K": K, "fused_us": round(fused * 1e3, 2),
+            "fused_GBps": round(prep_bytes(T, K, wl.fmt, True) / (fused * 1e-3) / 1e9, 1),
             "unfused_torch_silu_bf16_then_prep_us": round(chain * 1e3, 2),
             "speedup": round(chain / fused, 3),
-            "bytes_note": "fused algorithmic bytes = read 2K f32 + write codes, scales, mask"}
+            "timing": "eager launches, HIP events around 20 of them"}
 
 
 def gemm_baselines(torch, synth, wl, layers, sharq_ms):
@@ -342,19 +442,25 @@ def gemm_baselines(torch, synth, wl, layers, sharq_ms):
     res = {}
     tot = {"bf16": 0.0, "fp8": 0.0}
     for L in layers:
-        w = torch.from_numpy(np.ascontiguousarray(L.w_host[0]).view(np.int16)).view(torch.bfloat16).to(L.x[0].device)
-        x = L.x[0]
+        dev = L.y[0].device
+        w = torch.from_numpy(np.ascontiguousarray(L.w_host[0]).view(np.int16)).view(torch.bfloat16).to(dev)
+        if L.x is not None:
+            x = L.x[0]
+        else:  # SiLU(gate)*up of src's output as a bf16 activation
+            Y = L.src.y[0]
+            x = (torch.nn.functional.silu(Y[:, :L.lin.k]) * Y[:, L.lin.k:2 * L.lin.k]).to(torch.bfloat16)
         bf = _event_ms(torch, lambda: torch.matmul(x, w.t()))
         r = {"bf16_us": round(bf * 1e3, 2)}
         tot["bf16"] += bf
         try:
             f8 = torch.float8_e4m3fn
             xq, wq = x.to(f8), w.to(f8)
-            one = torch.ones((), dtype=torch.float32, device=x.device)
+            one = torch.ones((), dtype=torch.float32, device=dev)
             fp8 = _event_ms(torch, lambda: torch._scaled_mm(xq, wq.t(), scale_a=one, scale_b=one,
                                                             out_dtype=torch.bfloat16))
             r["fp8_us"] = round(fp8 * 1e3, 2)
-            tot["fp8"] += fp8
+            if tot["fp8"] is not None:
+                tot["fp8"] += fp8
         except Exception as e:  # no FP8 GEMM in this torch build
             r["fp8_error"] = str(e)[:120]
             tot["fp8"] = None
@@ -385,28 +491,36 @@ def measured_traffic(name):
     return t if h.hexdigest() == t["source_sha256"] else None
 
 
+def prep_copies(x_bytes):
+    """Copies of a prep input that a prep-only timing graph rotates over:
+    together more than twice the Infinity Cache (at most 48)."""
+    return int(min(48, 2 * INFINITY_CACHE_BYTES // max(1, x_bytes) + 1))
+
+
 def build_layers(args, sq, torch, synth, dev):
-    if args.rotate is None and not args.workload.startswith("decode"):
-        args.rotate = 3
-    if args.workload == "llama":
-        wl = synth.WORKLOADS[1]
-        return wl, [Layer(sq, torch, synth, wl, lin, wl.tokens, args.rotate, dev) for lin in wl.linears]
-    if args.workload.startswith("decode"):
-        wl, tokens = synth.WORKLOADS[2], int(args.workload[len("decode"):])
-        if args.rotate is None:
-            args.rotate = 8
-        return wl, [Layer(sq, torch, synth, wl, lin, tokens, args.rotate, dev) for lin in wl.linears]
-    if args.workload == "qwen":
-        wl = synth.WORKLOADS[3]
-        return wl, [Layer(sq, torch, synth, wl, lin, wl.tokens, args.rotate, dev) for lin in wl.linears]
+    if args.rotate is None:
+        args.rotate = 8 if args.workload.startswith("decode") else 3
+    decode = args.workload.startswith("decode")
+    if args.workload in ("llama", "qwen") or decode:
+        wl = synth.WORKLOADS[3 if args.workload == "qwen" else (2 if decode else 1)]
+        tokens = int(args.workload[len("decode"):]) if decode else wl.tokens
+        layers = {}
+        for lin in wl.linears:
+            pc = None if decode else prep_copies(tokens * lin.k * 2)
+            layers[lin.name] = Layer(sq, torch, synth, wl, lin, tokens, args.rotate, dev,
+                                     src=layers.get(lin.swiglu_of), prep_copies=pc)
+        return wl, list(layers.values())
     if args.workload == "moe":
         wl = synth.WORKLOADS[4]
         route = synth.moe_routing(wl)
         rows = int(route.offsets[-1])
+        gu_lin, down_lin = wl.linears
         # gate_up: prep the unique tokens, the product gathers each expert's rows;
-        # down: prep the expert-sorted rows themselves
-        return wl, [Layer(sq, torch, synth, wl, wl.linears[0], wl.tokens, args.rotate, dev, route, gather=True),
-                    Layer(sq, torch, synth, wl, wl.linears[1], rows, args.rotate, dev, route)]
+        # down: prepared from gate_up's expert-sorted FP32 rows as SiLU(gate)*up
+        gu = Layer(sq, torch, synth, wl, gu_lin, wl.tokens, args.rotate, dev, route, gather=True,
+                   prep_copies=prep_copies(wl.tokens * gu_lin.k * 2))
+        down = Layer(sq, torch, synth, wl, down_lin, rows, args.rotate, dev, route, src=gu)
+        return wl, [gu, down]
     raise SystemExit(f"unknown workload {args.workload}")
 
 
@@ -443,18 +557,8 @@ def main():
 
     use_graph = args.graph == "on"
     decode = layers[0].prep_tokens <= 64
-    prep_ms = [0.0] * len(layers)
-    gemm_ms = [0.0] * len(layers)
 
-    def eager_steps(evs):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for s in range(args.steps):
-            for li, L in enumerate(layers):
-                L.run(sq, s, None if evs is None else evs[s][li])
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0
-
+    # ---- the timed steps
     if use_graph:
         # one captured graph per rotated copy, holding the whole step
         side = torch.cuda.Stream()
@@ -465,13 +569,7 @@ def main():
                     L.run(sq, i)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        step_graphs = []
-        for r in range(args.rotate):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for L in layers:
-                    L.run(sq, r)
-            step_graphs.append(g)
+        step_graphs = [_capture(torch, lambda r=r: [L.run(sq, r) for L in layers]) for r in range(args.rotate)]
         torch.cuda.synchronize()
         for i in range(args.warmup):
             step_graphs[i % args.rotate].replay()
@@ -481,43 +579,40 @@ def main():
             step_graphs[s % args.rotate].replay()
         torch.cuda.synchronize()
         ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    if use_graph and decode:
-        # per-launch times of decode kernels (a few microseconds each, shorter
-        # than a host launch): one graph per phase holding that phase once per
-        # timed step over the rotated copies, timed with HIP events around a replay
-        for li, L in enumerate(layers):
-            gp, gg = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gp):
-                for i in range(args.steps):
-                    L.run_prep(sq, i)
-            with torch.cuda.graph(gg):
-                for i in range(args.steps):
-                    L.run_gemm(sq, i)
-            prep_ms[li] = _replay_ms(torch, gp) / args.steps
-            gemm_ms[li] = _replay_ms(torch, gg) / args.steps
     else:
-        # per-launch times from eager steps with HIP events around every launch
-        # (same order and cache state as the step; each interval also holds the
-        # gap after the preceding launch)
-        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers]
-               for _ in range(args.steps)]
-        t_eager = eager_steps(evs)
-        if not use_graph:
-            ms_step = t_eager * 1e3 / args.steps
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         for s in range(args.steps):
-            for li in range(len(layers)):
-                e = evs[s][li]
-                prep_ms[li] += e[0].elapsed_time(e[1]) / args.steps
-                gemm_ms[li] += e[1].elapsed_time(e[2]) / args.steps
+            for L in layers:
+                L.run(sq, s)
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # ---- per-launch kernel times: graphs of one phase over rotated copies
+    prep_ms, gemm_ms = [], []
+    for L in layers:
+        n_prep = args.steps if decode else max(12, L.n_in)
+        n_gemm = args.steps if decode else 12
+        prep_ms.append(phase_ms(torch, lambda i, L=L: L.run_prep(sq, i), n_prep))
+        gemm_ms.append(phase_ms(torch, lambda i, L=L: L.run_gemm(sq, i), n_gemm))
+
     flops = [gemm_flops(L.rows, L.lin.k, L.lin.nout, wl.n, wl.m) for L in layers]
-    pbytes = [prep_bytes(L.prep_tokens, L.lin.k, wl.fmt) for L in layers]
+    pbytes = [prep_bytes(L.prep_tokens, L.lin.k, wl.fmt, L.swiglu) for L in layers]
     wbytes = [weight_bytes(L.E, L.lin.nout, L.lin.k, wl.fmt) for L in layers]
     gemm_tflops = sum(flops) / (sum(gemm_ms) * 1e-3) / 1e12
     prep_gbps = sum(pbytes) / (sum(prep_ms) * 1e-3) / 1e9
     value = sum(flops) / (ms_step * 1e-3) / 1e12
     nv = wl.fmt != 0
     tokens = layers[0].prep_tokens
+    plain = [i for i, L in enumerate(layers) if not L.swiglu]
+    fused = [i for i, L in enumerate(layers) if L.swiglu]
 
+    def kind_gbps(ix):
+        return None if not ix else round(sum(pbytes[i] for i in ix) / (sum(prep_ms[i] for i in ix) * 1e-3) / 1e9, 1)
+
+    timing = (f"graphs of one phase over rotated copies (prep inputs over enough copies to exceed twice the "
+              f"Infinity Cache; products over the step's {args.rotate} copies), HIP events around a replay, "
+              f"per launch = replay time / launches")
     result = {
         "metric": "prep GB/s + dual-GEMM TFLOP/s, % of HBM / MXFP4 MFMA peak, 1 MI355X",
         "value": round(value, 2),
@@ -533,41 +628,68 @@ def main():
         "data": "synthetic (seeded; model-shaped activations with outlier channels, N(0,0.02) weights)",
         "config": {"workload": f"{wl.name}" + ("" if tokens == wl.tokens else f"_T{tokens}"),
                    "tokens": tokens, "linears": {L.lin.name: [L.lin.k, L.lin.nout] for L in layers},
+                   "prep_input": {L.lin.name: ("SiLU(gate)*up of " + L.src.lin.name + " FP32 output")
+                                  if L.swiglu else ("bf16, " + ("RMSNorm" if L.lin.norm == 1 else "no norm"))
+                                  for L in layers},
                    "mask": f"{wl.n}:{wl.m}", "format": "NVFP4" if nv else "MXFP4",
                    "rotated_copies": args.rotate,
                    "launch": "one HIP graph per step" if use_graph else "eager launches"},
         "prep_GBps": round(prep_gbps, 1),
         "prep_frac_hbm": round(prep_gbps / HBM_PEAK_GBPS, 4),
+        "prep_GBps_bf16_input": kind_gbps(plain),
+        "prep_GBps_swiglu_input": kind_gbps(fused),
         "gemm_TFLOPs": round(gemm_tflops, 1),
         "gemm_frac_peak": round(gemm_tflops / MXFP4_PEAK_TFLOPS, 4),
         "per_linear": {L.lin.name: {"rows": L.rows, "prep_us": round(prep_ms[i] * 1e3, 2),
                                     "gemm_us": round(gemm_ms[i] * 1e3, 2),
+                                    "prep_bytes": pbytes[i],
                                     "prep_GBps": round(pbytes[i] / (prep_ms[i] * 1e-3) / 1e9, 1),
                                     "gemm_TFLOPs": round(flops[i] / (gemm_ms[i] * 1e-3) / 1e12, 1),
                                     "weight_stream_GBps": round(wbytes[i] / (gemm_ms[i] * 1e-3) / 1e9, 1)}
                        for i, L in enumerate(layers)},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": MXFP4_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / MXFP4_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "k_dual_gemm<NVFP4> (dual-path product, f16 MFMA)" if nv else "k_dual_gemm<MXFP4> (dual-path product)",
-                     "per_launch": "algorithmic 2*rows*Nout*K*(1+N/M) flops / HIP-event launch time, "
-                                   "summed over the linears",
-                     "timing": ("graphs of one phase over the rotated copies, HIP events around a replay"
-                                if use_graph and decode else "eager steps, HIP events around every launch")},
+        "roofline": {"bound": "hbm" if decode else "mfma", "achieved": round(gemm_tflops, 1),
+                     "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / MXFP4_PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "k_dual_gemm<NVFP4> (dual-path product, f16 MFMA)" if nv
+                     else "k_dual_gemm<MXFP4> (dual-path product)",
+                     "per_launch": "algorithmic 2*rows*Nout*K*(1+N/M) flops / launch time, summed over the linears",
+                     "timing": timing},
         "roofline_prep": {"bound": "hbm", "achieved": round(prep_gbps, 1), "peak": HBM_PEAK_GBPS,
-                          "unit": "GB/s", "frac": round(prep_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+                          "unit": "GB/s", "frac": round(prep_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                          "per_launch": "algorithmic bytes (input read once, codes, scales and mask written) / "
+                                        "launch time, summed over the linears",
+                          "timing": timing},
     }
+    if decode:
+        wstream = sum(wbytes) / (sum(gemm_ms) * 1e-3) / 1e9
+        result["roofline"].update({"achieved": round(wstream, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                   "frac": round(wstream / HBM_PEAK_GBPS, 4),
+                                   "per_launch": "FP4 weight payload bytes / launch time (the weight stream), "
+                                                 "summed over the linears",
+                                   "gemm_TFLOPs": round(gemm_tflops, 1)})
     if nv:
         result["roofline"]["frac_of_f16_peak"] = round(gemm_tflops / F16_PEAK_TFLOPS, 4)
-    if wl.name == "llama3.1-8b_prefill_T2048_mxfp4" and tokens == wl.tokens:
-        for key, fname in (("roofline", "k_dual_gemm_mxfp4_llama3.1-8b_prefill_T2048.traffic.json"),
-                           ("roofline_prep", "k_prep_mxfp4_llama3.1-8b_prefill_T2048.traffic.json")):
-            t = measured_traffic(fname)
-            if t is not None:
-                result[key]["traffic"] = t["bytes_per_step"]
-                result[key]["traffic_unit"] = "bytes per step (all launches of the kernel in one step)"
-                result[key]["algorithmic_bytes_per_step"] = t["algorithmic_bytes_per_step"]
-    result["roofline"]["mfma_ceiling_random_fp4_TFLOPs"] = MFMA_RANDOM_FP4_TFLOPS
+    for key, fname in (("roofline", f"k_dual_gemm_{wl.name}.traffic.json"),
+                       ("roofline_prep", f"k_prep_{wl.name}.traffic.json")):
+        t = measured_traffic(fname) if tokens == wl.tokens else None
+        if t is not None:
+            result[key]["traffic"] = t["bytes_per_step"]
+            result[key]["traffic_unit"] = "bytes per step (all launches of the kernel in one step)"
+            result[key]["algorithmic_bytes_per_step"] = t["algorithmic_bytes_per_step"]
+    if not decode:
+        result["roofline"]["mfma_ceiling_random_fp4_TFLOPs"] = MFMA_RANDOM_FP4_TFLOPS
     if not args.no_extras:
+        # products with BF16 output (the FP32 accumulator rounded to nearest even)
+        g16 = {}
+        for L in layers:
+            L.y16 = [torch.empty((L.rows, L.lin.nout), dtype=torch.bfloat16, device=dev) for _ in range(L.rotate)]
+            g16[L.lin.name] = phase_ms(torch, lambda i, L=L: L.run_gemm(sq, i, bf16=True),
+                                       args.steps if decode else 12)
+            L.y16 = None
+        result["bf16_output"] = {
+            "gemm_us": {k: round(v * 1e3, 2) for k, v in g16.items()},
+            "gemm_TFLOPs": round(sum(flops) / (sum(g16.values()) * 1e-3) / 1e12, 1),
+            "note": "same products, Y stored as BF16; FP32 Y is the parity contract and the headline"}
         result["swiglu_prep"] = swiglu_report(sq, torch, wl, layers)
         result["gemm_baselines"] = gemm_baselines(torch, synth, wl, layers, sum(prep_ms) + sum(gemm_ms))
     if not args.no_cpu_baseline:

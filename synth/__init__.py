@@ -29,12 +29,17 @@ FMT_MXFP4, FMT_NVFP4 = 0, 1
 
 @dataclasses.dataclass(frozen=True)
 class Linear:
-    """One linear layer of a workload: Y[T][nout] = prep(X[T][k]) . W[nout][k]^T."""
+    """One linear layer of a workload: Y[T][nout] = prep(X[T][k]) . W[nout][k]^T.
+
+    swiglu_of names the linear whose float32 output [gate | up] feeds this
+    one's preparation as SiLU(gate) * up (the down projection of a SwiGLU
+    MLP); its input is then not drawn at random in a layer step."""
     name: str
     k: int
     nout: int
     norm: int
     lin_id: int
+    swiglu_of: Optional[str] = None
 
 
 @dataclasses.dataclass(frozen=True)
@@ -57,10 +62,15 @@ class Workload:
     description: str = ""
 
 
+# A decoder layer's four linears in execution order: qkv (after the input
+# RMSNorm), o_proj (attention output, no norm), gate_up (after the
+# post-attention RMSNorm) and down (SiLU(gate) * up of gate_up's output, no
+# norm).  lin_id fixes each tensor's random stream.
 LLAMA_LINEARS = (
     Linear("qkv", 4096, 6144, NORM_RMS, 0),
+    Linear("o_proj", 4096, 4096, NORM_NONE, 3),
     Linear("gate_up", 4096, 28672, NORM_RMS, 1),
-    Linear("down", 14336, 4096, NORM_NONE, 2),
+    Linear("down", 14336, 4096, NORM_NONE, 2, swiglu_of="gate_up"),
 )
 
 WORKLOADS: Dict[int, Workload] = {
@@ -72,19 +82,20 @@ WORKLOADS: Dict[int, Workload] = {
     1: Workload(1, "llama3.1-8b_prefill_T2048_mxfp4", "bf16", 2048, LLAMA_LINEARS,
                 FMT_MXFP4, 2, 4, 1e-5, "normal", 0.005, None, 50.0,
                 description="Llama-3.1-8B-shaped prefill layer, 2048 tokens, "
-                            "qkv/gate_up/down, MXFP4 2:4"),
+                            "qkv/o_proj/gate_up/down (down prepared from SiLU(gate)*up), MXFP4 2:4"),
     2: Workload(2, "llama3.1-8b_decode_mxfp4", "bf16", 1, LLAMA_LINEARS,
                 FMT_MXFP4, 2, 4, 1e-5, "normal", 0.005, None, 50.0,
                 description="Llama-3.1-8B-shaped decode layer at 1, 8 and 64 tokens"),
     3: Workload(3, "qwen2.5-7b_prefill_T4096_nvfp4", "bf16", 4096,
                 (Linear("qkv", 3584, 4608, NORM_RMS, 0),
+                 Linear("o_proj", 3584, 3584, NORM_NONE, 3),
                  Linear("gate_up", 3584, 37888, NORM_RMS, 1),
-                 Linear("down", 18944, 3584, NORM_NONE, 2)),
+                 Linear("down", 18944, 3584, NORM_NONE, 2, swiglu_of="gate_up")),
                 FMT_NVFP4, 2, 4, 1e-6, "student_t3_half", 0.01, None, 40.0,
                 description="Qwen2.5-7B-shaped prefill layer, 4096 tokens, NVFP4 2:4"),
     4: Workload(4, "qwen3-30b-a3b_moe_T4096_mxfp4", "bf16", 4096,
                 (Linear("expert_gate_up", 2048, 1536, NORM_RMS, 0),
-                 Linear("expert_down", 768, 2048, NORM_NONE, 1)),
+                 Linear("expert_down", 768, 2048, NORM_NONE, 1, swiglu_of="expert_gate_up")),
                 FMT_MXFP4, 2, 4, 1e-6, "normal", 0.005, None, 50.0,
                 experts=128, topk=8,
                 description="Qwen3-30B-A3B-shaped MoE expert FFN, 4096 tokens, "

@@ -32,3 +32,29 @@ def test_prep_and_weight_bytes():
     assert bench.prep_bytes(T, K, 1) == T * (2 * K + K + 2 * K // 16 + K // 8)
     assert bench.weight_bytes(1, 28672, 4096, 0) == 28672 * 4096 * (0.5 + 1 / 32)
     assert bench.weight_bytes(128, 1536, 2048, 1) == 128 * 1536 * 2048 * (0.5 + 1 / 16)
+
+
+def test_swiglu_prep_reads_gate_and_up_as_fp32():
+    # the down projection's prep reads 2K float32 values per row instead of K bf16
+    T, K = 2048, 14336
+    assert bench.prep_bytes(T, K, 0, swiglu=True) == T * (8 * K + K + 2 * K // 32 + K // 8)
+
+
+def test_prep_timing_rotation_exceeds_the_infinity_cache():
+    x_bytes = 2048 * 4096 * 2
+    n = bench.prep_copies(x_bytes)
+    assert n * x_bytes > 2 * bench.INFINITY_CACHE_BYTES and n <= 48
+    assert bench.prep_copies(1) == 48
+
+
+def test_layer_workloads_have_four_linears_with_fused_down():
+    import synth
+    for cid in (1, 2, 3):
+        names = [lin.name for lin in synth.WORKLOADS[cid].linears]
+        assert names == ["qkv", "o_proj", "gate_up", "down"]
+        lins = {lin.name: lin for lin in synth.WORKLOADS[cid].linears}
+        assert lins["down"].swiglu_of == "gate_up" and lins["gate_up"].nout == 2 * lins["down"].k
+        assert lins["o_proj"].k == lins["o_proj"].nout == lins["qkv"].k and lins["o_proj"].norm == 0
+    moe = {lin.name: lin for lin in synth.WORKLOADS[4].linears}
+    assert moe["expert_down"].swiglu_of == "expert_gate_up"
+    assert moe["expert_gate_up"].nout == 2 * moe["expert_down"].k

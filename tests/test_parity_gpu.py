@@ -102,6 +102,11 @@ PREP_CASES = [
     (1, 0, "bf16", 2, 4, 5, 12288 + 16),   # NVFP4 amax, eight chunks per wave
     (1, 0, "bf16", 2, 4, 4, 18944),        # NVFP4 amax, sixteen chunks per wave
     (1, 0, "bf16", 2, 4, 2, 32768 + 256),  # NVFP4 amax, looped row
+    # MXFP4 norm rows from 2048 on run several rows per workgroup: a ragged last workgroup
+    (0, 1, "bf16", 2, 4, 2049, 4096),
+    (0, 2, "bf16", 2, 4, 2049, 8192),
+    (0, 1, "bf16", 2, 4, 4097, 4096),
+    (0, 2, "f16", 2, 4, 4097, 8192),
 ]
 
 
@@ -234,13 +239,38 @@ def ref_linear(pg, qw, row_index=None, offsets=None, out_rows=None, expert_of_ro
     else:
         ex = np.searchsorted(offsets, rows, side="right") - 1
     y = np.zeros((len(rows), qw.nout))
+    absum = np.zeros((len(rows), qw.nout))
     for e in np.unique(ex):
         sel = np.nonzero(ex == e)[0]
         a = oracle.dequant(bc[src[sel]], bs[src[sel]], K, fmt, G) + 0.0
         r = oracle.dequant(rc[src[sel]], rs[src[sel]], K, fmt, G)
         w = oracle.dequant(wc[e], ws[e], K, fmt, float(wG[e]))
         y[sel] = a @ w.T + r @ w.T
+        absum[sel] = np.abs(a) @ np.abs(w).T + np.abs(r) @ np.abs(w).T
+    ref_linear.absum = absum
     return rows, y
+
+
+def check_product(y: np.ndarray, ref: np.ndarray, K: int, what=""):
+    """Product parity: relative Frobenius error <= 1e-3 against the FP64
+    product of the same dequantized codes, and every element within the
+    FP32 accumulation bound 2*K*2^-24 * sum_k(|b_k w_k| + |r_k w_k|) (the FP4
+    products are exact; only the FP32 sums round)."""
+    err = rel_fro(y, ref)
+    assert err <= TOL, (what, err)
+    bound = 2.0 * K * 2.0 ** -24 * ref_linear.absum
+    diff = np.abs(y.astype(np.float64) - ref)
+    bad = diff > bound
+    assert not bad.any(), (what, int(bad.sum()), np.argwhere(bad)[:5], float((diff - bound).max()))
+    return err
+
+
+def fragment_rows(T: int, rng, frag: int = 32) -> np.ndarray:
+    """One random row from every 32-row fragment (every row tile of every
+    tile shape), plus the last row."""
+    starts = np.arange(0, T, frag)
+    rows = np.minimum(starts + rng.integers(0, frag, starts.size), T - 1)
+    return np.unique(np.concatenate([rows, [T - 1]]))
 
 
 LINEAR_CASES = [
@@ -269,12 +299,76 @@ def test_linear(case):
     qw = sq().quantize_weight(dev16(w, "bf16"), fmt=fmt)
     y = host(sq().linear(pg, qw))
     _, ref = ref_linear(pg, qw)
-    err = rel_fro(y, ref)
-    assert err <= TOL, err
+    check_product(y, ref, K, case)
     # and against the oracle end to end (its own prep and weight)
     o = oracle.prepare(x, "bf16", K, 1, g, None, 1e-5, 2, 4, fmt)
     ow = oracle.quantize_weight(w, "bf16", fmt)
     assert rel_fro(y, oracle.linear(o, ow)) <= TOL
+
+
+OUT_DTYPE_CASES = [
+    # (fmt, T, K, nout, grouped): one case per dispatch path
+    (0, 300, 640, 272, False),     # prefill tiles
+    (0, 2048, 256, 16384, False),  # 256x256 tiles
+    (0, 5, 768, 48, False),        # small-batch kernel
+    (0, 40, 1024, 3000, False),    # few rows as 64x64 tiles
+    (0, 24, 14336, 3000, False),   # few rows over K ranges, summed in the output type
+    (1, 300, 640, 272, False),     # NVFP4 (tensor scales applied before rounding)
+    (0, 90, 640, 96, True),        # grouped, gathered rows
+    (1, 90, 640, 96, True),
+]
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("case", OUT_DTYPE_CASES, ids=lambda c: "fmt%d-T%d-K%d-N%d-g%d" % c)
+def test_linear_output_dtype(case, out_dtype):
+    """Y stored as BF16 / F16: the FP32 accumulator rounded to nearest even.
+    Bit-equal to rounding the library's own FP32 output (same accumulation
+    order), and within one unit in the last place of the output type of the
+    FP64 product of the same codes."""
+    fmt, T, K, nout, grouped = case
+    x = synth.small_case(K, T, "bf16", outliers=3, tag=81 + T)
+    pg = gpu_prepare(x, "bf16", K, 0, None, None, 0.0, 2, 4, fmt)
+    E = 5 if grouped else 1
+    w = synth.small_weight(nout, K, experts=E, tag=82 + nout)
+    qw = sq().quantize_weight(dev16(w, "bf16"), fmt=fmt)
+    kw = {}
+    row_index = offsets = None
+    if grouped:
+        offsets = np.array([0, 130, 130, 141, 400, 401], np.int32)
+        row_index = np.random.default_rng(83).integers(0, T, offsets[-1]).astype(np.int32)
+        kw = dict(group_offsets=torch.from_numpy(offsets).cuda(), row_index=torch.from_numpy(row_index).cuda(),
+                  rows=int(offsets[-1]))
+    y32 = sq().linear(pg, qw, **kw)
+    y16 = sq().linear(pg, qw, out_dtype=out_dtype, **kw)
+    assert y16.dtype == out_dtype
+    torch.cuda.synchronize()
+    assert torch.equal(y16.view(torch.int16).cpu(), y32.to(out_dtype).view(torch.int16).cpu())
+    _, ref = ref_linear(pg, qw, row_index=row_index, offsets=offsets)
+    got = y16.double().cpu().numpy()
+    rr16 = torch.from_numpy(ref).to(out_dtype)                       # FP64 product rounded once
+    mag = rr16.abs()
+    above = (mag.view(torch.int16).to(torch.int32) + 1).to(torch.int16).view(out_dtype)
+    ulp = (above.double() - mag.double()).numpy()                    # spacing above |rr| in the type
+    diff = np.abs(got - rr16.double().numpy())
+    assert np.all(diff <= ulp), (case, int((diff > ulp).sum()))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_quantize_weight_strided_rows(fmt):
+    """A weight that is a column slice of a wider matrix (row stride ldw > K):
+    the payload equals the oracle's on the slice."""
+    E, nout, K, ld = 2, 40, 512, 768
+    wide = synth.small_weight(nout, ld, experts=E, tag=84 + fmt)
+    wd = dev16(wide, "bf16")
+    q = sq().quantize_weight(wd[:, :, 128:128 + K], fmt=fmt)
+    torch.cuda.synchronize()
+    o = oracle.quantize_weight(np.ascontiguousarray(wide[:, :, 128:128 + K]), "bf16", fmt)
+    codes, scales = weight_to_host(q)
+    assert np.array_equal(codes, o.codes)
+    assert np.array_equal(scales, o.scales)
+    if fmt == 1:
+        assert np.array_equal(host(q.global_scale), o.gscale)
 
 
 GATHER_CASES = [
@@ -301,7 +395,7 @@ def test_linear_dense_gather(case):
     y = host(sq().linear(pg, qw, row_index=torch.from_numpy(row_index).cuda(), rows=rows))
     _, ref = ref_linear(pg, qw, row_index=row_index)
     assert y.shape == (rows, nout)
-    assert rel_fro(y, ref) <= TOL
+    check_product(y, ref, K, case)
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
@@ -317,12 +411,12 @@ def test_linear_grouped(fmt):
     y = host(sq().linear(pg, qw, group_offsets=torch.from_numpy(offsets).cuda(),
                          row_index=torch.from_numpy(row_index).cuda(), rows=int(offsets[-1])))
     _, ref = ref_linear(pg, qw, row_index=row_index, offsets=offsets)
-    assert rel_fro(y, ref) <= TOL
+    check_product(y, ref, K, "grouped gathered")
     # contiguous grouped rows, no gather
     pg2 = gpu_prepare(synth.small_case(K, 401, "bf16", tag=9), "bf16", K, 0, None, None, 0.0, 2, 4, fmt)
     y2 = host(sq().linear(pg2, qw, group_offsets=torch.from_numpy(offsets).cuda(), rows=401))
     _, ref2 = ref_linear(pg2, qw, offsets=offsets)
-    assert rel_fro(y2, ref2) <= TOL
+    check_product(y2, ref2, K, "grouped contiguous")
 
 
 @pytest.mark.parametrize("fmt", [0, 1])
@@ -343,7 +437,7 @@ def test_linear_grouped_many_experts(fmt):
     y = host(sq().linear(pg, qw, group_offsets=torch.from_numpy(offsets).cuda(),
                          row_index=torch.from_numpy(row_index).cuda(), rows=int(offsets[-1])))
     _, ref = ref_linear(pg, qw, row_index=row_index, offsets=offsets)
-    assert rel_fro(y, ref) <= TOL
+    check_product(y, ref, K, "many experts")
 
 
 @pytest.mark.parametrize("T", [4, 300], ids=["short", "tiled"])
@@ -387,7 +481,7 @@ def test_linear_strided_unaligned_output(T):
     torch.cuda.synchronize()
     full = host(buf)
     _, ref = ref_linear(pg, qw)
-    assert rel_fro(full[:, 3:3 + nout], ref) <= TOL
+    check_product(full[:, 3:3 + nout], ref, K, "strided")
     assert np.isnan(full[:, :3]).all() and np.isnan(full[:, 3 + nout:]).all()
     dense = host(sq().linear(pg, qw))
     assert np.array_equal(full[:, 3:3 + nout], dense)
@@ -530,34 +624,89 @@ def _run_layer(wl, lin, tokens, prep_rows=None, out_rows=64, seed=0):
     _weight_sample_check(wl, lin, qw, w)
     y = host(sq().linear(p, qw))
     rng = np.random.default_rng(seed)
-    rows = np.arange(tokens) if tokens <= out_rows else np.sort(rng.choice(tokens, out_rows, replace=False))
+    rows = np.arange(tokens) if tokens <= out_rows else fragment_rows(tokens, rng)
     rows, ref = ref_linear(p, qw, out_rows=rows)
-    err = rel_fro(y[rows], ref)
+    err = check_product(y[rows], ref, lin.k, f"{wl.name}/{lin.name}")
     print(f"{wl.name}/{lin.name} T={tokens}: prep mismatches {stats['mismatched']} "
-          f"of {stats['elements']}, GEMM rel err {err:.2e}", flush=True)
-    assert err <= TOL
+          f"of {stats['elements']}, GEMM rel err {err:.2e} on {rows.size} rows", flush=True)
     return err
 
 
-@pytest.mark.parametrize("lin", [0, 1, 2], ids=["qkv", "gate_up", "down"])
-def test_llama8b_prefill_full(lin):
+def _linear(wl, name):
+    return next(L for L in wl.linears if L.name == name)
+
+
+# Every linear of the layer on a drawn input (down too: the prep without norm
+# on a bf16 activation); the fused SiLU(gate)*up path of the layer step is
+# checked separately below.
+@pytest.mark.parametrize("name", ["qkv", "o_proj", "gate_up", "down"])
+def test_llama8b_prefill_full(name):
     wl = synth.WORKLOADS[1]
-    _run_layer(wl, wl.linears[lin], wl.tokens)
+    _run_layer(wl, _linear(wl, name), wl.tokens)
 
 
 @pytest.mark.parametrize("tokens", synth.DECODE_TOKENS)
-@pytest.mark.parametrize("lin", [0, 1, 2], ids=["qkv", "gate_up", "down"])
-def test_llama8b_decode_full(lin, tokens):
+@pytest.mark.parametrize("name", ["qkv", "o_proj", "gate_up", "down"])
+def test_llama8b_decode_full(name, tokens):
     wl = synth.WORKLOADS[2]
-    _run_layer(wl, wl.linears[lin], tokens)
+    _run_layer(wl, _linear(wl, name), tokens)
 
 
-@pytest.mark.parametrize("lin", [0, 1, 2], ids=["qkv", "gate_up", "down"])
-def test_qwen25_7b_nvfp4_full(lin):
+@pytest.mark.parametrize("name", ["qkv", "o_proj", "gate_up", "down"])
+def test_qwen25_7b_nvfp4_full(name):
     wl = synth.WORKLOADS[3]
-    rng = np.random.default_rng(lin)
+    rng = np.random.default_rng(len(name))
     rows = np.unique(np.concatenate([[0, wl.tokens - 1], rng.choice(wl.tokens, 254, replace=False)]))
-    _run_layer(wl, wl.linears[lin], wl.tokens, prep_rows=rows)
+    _run_layer(wl, _linear(wl, name), wl.tokens, prep_rows=rows)
+
+
+def _run_fused_down(wl, tokens, seed=0):
+    """The layer step's MLP half as the benchmark runs it: gate_up prep and
+    product on the GPU, then the down projection prepared straight from
+    gate_up's FP32 output (SiLU(gate) * up inside the prep kernel) and
+    multiplied.  The oracle prepares the same FP32 rows (sampled rows; the
+    NVFP4 tensor scale over all rows) and multiplies the GPU's codes."""
+    gu_lin, down = _linear(wl, "gate_up"), _linear(wl, "down")
+    assert down.swiglu_of == "gate_up" and gu_lin.nout == 2 * down.k
+    x = synth.activation(wl, gu_lin, tokens)
+    g = synth.gamma(wl, gu_lin)
+    pg = gpu_prepare(x, wl.dtype, gu_lin.k, gu_lin.norm, g, None, wl.eps, wl.n, wl.m, wl.fmt)
+    qgu = sq().quantize_weight(dev16(synth.weight(wl, gu_lin), wl.dtype), fmt=wl.fmt)
+    ygu = sq().linear(pg, qgu)
+    pd = sq().prepare_swiglu(ygu, down.k, n=wl.n, m=wl.m, fmt=wl.fmt)
+    torch.cuda.synchronize()
+    gu_host = host(ygu)
+    rng = np.random.default_rng(seed)
+    rows = np.arange(tokens) if tokens <= 64 else np.unique(np.concatenate(
+        [fragment_rows(tokens, rng), rng.choice(tokens, 192, replace=False)]))
+    o = oracle.prepare_swiglu(gu_host, down.k, wl.n, wl.m, wl.fmt, rows=rows, trace=True)
+    gh = prepared_to_host(pd)
+    gh = {k: (v[rows] if isinstance(v, np.ndarray) else v) for k, v in gh.items()}
+    stats = compare_prepared(gh, o, wl.n, wl.m, f"{wl.name}/down fused T{tokens}")
+    assert stats["mismatched"] == 0, stats
+    if wl.fmt == oracle.FMT_NVFP4:
+        assert gh["G"] == o.G
+    qd = sq().quantize_weight(dev16(synth.weight(wl, down), wl.dtype), fmt=wl.fmt)
+    y = host(sq().linear(pd, qd))
+    out_rows = np.arange(tokens) if tokens <= 64 else fragment_rows(tokens, rng)
+    out_rows, ref = ref_linear(pd, qd, out_rows=out_rows)
+    err = check_product(y[out_rows], ref, down.k, f"{wl.name}/down fused")
+    print(f"{wl.name}/down fused T={tokens}: prep rows {rows.size} bit-exact, GEMM rel err {err:.2e}", flush=True)
+
+
+def test_llama8b_prefill_fused_down():
+    wl = synth.WORKLOADS[1]
+    _run_fused_down(wl, wl.tokens)
+
+
+@pytest.mark.parametrize("tokens", synth.DECODE_TOKENS)
+def test_llama8b_decode_fused_down(tokens):
+    _run_fused_down(synth.WORKLOADS[2], tokens)
+
+
+def test_qwen25_7b_nvfp4_fused_down():
+    wl = synth.WORKLOADS[3]
+    _run_fused_down(wl, wl.tokens)
 
 
 def test_single_linear_c0():
@@ -572,7 +721,10 @@ def test_qwen3_moe_full():
     ridx = torch.from_numpy(route.row_index).cuda()
     nrows = int(route.offsets[-1])
     rng = np.random.default_rng(4)
-    sample = np.sort(rng.choice(nrows, 96, replace=False))
+    # one row from every 32-row fragment of the sorted rows, and each expert's first and last row
+    nonempty = np.nonzero(np.diff(route.offsets))[0]
+    sample = np.unique(np.concatenate([fragment_rows(nrows, rng), route.offsets[nonempty],
+                                       route.offsets[nonempty + 1] - 1]))
     # gate_up: RMSNorm on the unique tokens, grouped product gathers rows
     lin = wl.linears[0]
     x = synth.activation(wl, lin, wl.tokens)
@@ -584,9 +736,8 @@ def test_qwen3_moe_full():
     _weight_sample_check(wl, lin, qw, w, nrows=32)
     y = host(sq().linear(p, qw, group_offsets=offs, row_index=ridx, rows=nrows))
     _, ref = ref_linear(p, qw, row_index=route.row_index, offsets=route.offsets, out_rows=sample)
-    err = rel_fro(y[sample], ref)
-    print(f"moe gate_up rel err {err:.2e}", flush=True)
-    assert err <= TOL
+    err = check_product(y[sample], ref, lin.k, "moe gate_up")
+    print(f"moe gate_up rel err {err:.2e} on {sample.size} rows", flush=True)
     # down: rows already sorted by expert, no norm
     lin = wl.linears[1]
     x = synth.activation(wl, lin, nrows)
@@ -598,6 +749,5 @@ def test_qwen3_moe_full():
     _weight_sample_check(wl, lin, qw, w, nrows=32)
     y = host(sq().linear(p, qw, group_offsets=offs, rows=nrows))
     _, ref = ref_linear(p, qw, offsets=route.offsets, out_rows=sample)
-    err = rel_fro(y[sample], ref)
-    print(f"moe down rel err {err:.2e}", flush=True)
-    assert err <= TOL
+    err = check_product(y[sample], ref, lin.k, "moe down")
+    print(f"moe down rel err {err:.2e} on {sample.size} rows", flush=True)

@@ -132,6 +132,30 @@ SHARQ_API sharq_status sharq_prepare(const void *x, int32_t x_dtype, int64_t T, 
                            void *stream);
 
 /*
+ * sharq_prepare_noalloc -- sharq_prepare for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments, outputs and results, without
+ * a workspace.  Its scratch (the NVFP4 per-row statistics) lives in a
+ * 1 MiB device array inside the library, one per GPU, kept until the
+ * process ends; the call itself allocates and frees nothing.
+ *   - NVFP4 needs T <= SHARQ_NOALLOC_MAX_ROWS; more rows return
+ *     SHARQ_ERR_WORKSPACE before any HIP call.  MXFP4 uses no scratch and
+ *     takes any T that sharq_prepare takes.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on
+ *     one GPU (different streams, or host threads) race and give undefined
+ *     results; calls ordered on one stream are safe.  The array's contents
+ *     on entry do not matter.
+ *   - The first call on a device looks up the array's device address with
+ *     that device current (HIP errors there return SHARQ_ERR_HIP).
+ */
+#define SHARQ_NOALLOC_MAX_ROWS 65536
+SHARQ_API sharq_status sharq_prepare_noalloc(const void *x, int32_t x_dtype, int64_t T, int64_t K, int64_t ldx,
+                                   int32_t norm, const void *gamma, const void *beta, float eps,
+                                   int32_t n, int32_t m, int32_t fmt, uint8_t *mask, uint8_t *b_codes,
+                                   uint8_t *b_scales, uint8_t *r_codes, uint8_t *r_scales,
+                                   float *global_scale, void *stream);
+
+/*
  * sharq_prepare_swiglu -- the fused preparation operator of sharq_prepare
  * (SharQ: Bridging Activation Sparsity and FP4 Quantization for LLM
  * Inference, Abstract: mask generation and residual construction in one

@@ -53,6 +53,9 @@ def lib() -> ctypes.CDLL:
         L.sharq_prepare.argtypes = [p, i32, i64, i64, i64, i32, p, p, f32, i32, i32, i32,
                                     p, p, p, p, p, p, p, sz, p]
         L.sharq_prepare.restype = ctypes.c_int
+        L.sharq_prepare_noalloc.argtypes = [p, i32, i64, i64, i64, i32, p, p, f32, i32, i32, i32,
+                                            p, p, p, p, p, p, p]
+        L.sharq_prepare_noalloc.restype = ctypes.c_int
         L.sharq_prepare_swiglu.argtypes = [p, i64, i64, i64, i32, i32, i32, p, p, p, p, p, p, p, sz, p]
         L.sharq_prepare_swiglu.restype = ctypes.c_int
         L.sharq_quantize_weight_workspace_size.argtypes = [i64, i64, i64, i32]
@@ -145,6 +148,25 @@ def prepare(x: torch.Tensor, norm: int = NORM_RMS, gamma: Optional[torch.Tensor]
         _ptr(out.r_scales), _ptr(out.global_scale), _ptr(ws), 0 if ws is None else ws.numel(),
         _stream(x.device))
     _check(st, "sharq_prepare")
+    return out
+
+
+def prepare_noalloc(x: torch.Tensor, out: Prepared, norm: int = NORM_RMS, gamma: Optional[torch.Tensor] = None,
+                    beta: Optional[torch.Tensor] = None, eps: float = 1e-5, n: int = 2, m: int = 4) -> Prepared:
+    """prepare() into caller-allocated outputs through the allocation-free
+    entry point (its scratch is the library's own device array; NVFP4 takes
+    at most SHARQ_NOALLOC_MAX_ROWS = 65536 rows; overlapping calls on one GPU
+    race)."""
+    if x.dim() != 2 or x.dtype not in _DTYPE or x.stride(1) != 1:
+        raise SharqError("x must be a 2-D row-major float16/bfloat16 tensor")
+    T, K = x.shape
+    if out.T != T or out.K != K:
+        raise SharqError("out does not match x's shape")
+    st = lib().sharq_prepare_noalloc(
+        _ptr(x), _DTYPE[x.dtype], T, K, x.stride(0), norm, _ptr(gamma), _ptr(beta), float(eps),
+        n, m, out.fmt, _ptr(out.mask), _ptr(out.b_codes), _ptr(out.b_scales), _ptr(out.r_codes),
+        _ptr(out.r_scales), _ptr(out.global_scale), _stream(x.device))
+    _check(st, "sharq_prepare_noalloc")
     return out
 
 

@@ -16,6 +16,7 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // the normalized MXFP4 prep launches one workgroup per row
 constexpr int64_t kMaxPrepRows = ((int64_t)1 << 31) - 64;
+static_assert(SHARQ_NOALLOC_MAX_ROWS == kNoallocRows, "header and library agree on the scratch size");
 
 int block_of(int32_t fmt) { return fmt == SHARQ_MXFP4 ? 32 : 16; }
 
@@ -37,7 +38,7 @@ const char *sharq_status_string(int status) {
         case SHARQ_ERR_NM: return "invalid N:M pattern";
         case SHARQ_ERR_DTYPE: return "unsupported element type";
         case SHARQ_ERR_ALIGN: return "pointer or stride not aligned";
-        case SHARQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case SHARQ_ERR_WORKSPACE: return "workspace missing or too small (or more rows than the built-in scratch holds)";
         case SHARQ_ERR_UNSUPPORTED: return "unsupported format or combination";
         case SHARQ_ERR_HIP: return "HIP launch failed";
     }
@@ -49,11 +50,18 @@ size_t sharq_prepare_workspace_size(int64_t T, int64_t K, int32_t fmt) {
     return prepare_workspace_bytes(T, fmt);
 }
 
-sharq_status sharq_prepare(const void *x, int32_t x_dtype, int64_t T, int64_t K, int64_t ldx,
-                           int32_t norm, const void *gamma, const void *beta, float eps, int32_t n,
-                           int32_t m, int32_t fmt, uint8_t *mask, uint8_t *b_codes, uint8_t *b_scales,
-                           uint8_t *r_codes, uint8_t *r_scales, float *global_scale, void *workspace,
-                           size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of sharq_prepare and sharq_prepare_noalloc, before any HIP
+// call, and the kernel arguments they describe.  need_ws: check the caller's
+// workspace (sharq_prepare) or the built-in scratch limit (noalloc).
+sharq_status prepare_args(const void *x, int32_t x_dtype, int64_t T, int64_t K, int64_t ldx, int32_t norm,
+                          const void *gamma, const void *beta, float eps, int32_t n, int32_t m, int32_t fmt,
+                          uint8_t *mask, uint8_t *b_codes, uint8_t *b_scales, uint8_t *r_codes,
+                          uint8_t *r_scales, float *global_scale, bool need_ws, void *workspace,
+                          size_t workspace_bytes, PrepArgs &a) {
     if (!valid_fmt(fmt)) return SHARQ_ERR_UNSUPPORTED;
     if (x_dtype != SHARQ_BF16 && x_dtype != SHARQ_F16) return SHARQ_ERR_DTYPE;
     if (norm != SHARQ_NORM_NONE && norm != SHARQ_NORM_RMS && norm != SHARQ_NORM_LAYER)
@@ -70,11 +78,15 @@ sharq_status sharq_prepare(const void *x, int32_t x_dtype, int64_t T, int64_t K,
     if ((gamma && !aligned(gamma, 16)) || (beta && !aligned(beta, 16))) return SHARQ_ERR_ALIGN;
     if (!aligned(b_codes, 4) || !aligned(r_codes, 4)) return SHARQ_ERR_ALIGN;
     if (global_scale && !aligned(global_scale, 4)) return SHARQ_ERR_ALIGN;
-    const size_t need = prepare_workspace_bytes(T, fmt);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return SHARQ_ERR_WORKSPACE;
-    if (need > 0 && !aligned(workspace, 16)) return SHARQ_ERR_ALIGN;
+    if (need_ws) {
+        const size_t need = prepare_workspace_bytes(T, fmt);
+        if (need > 0 && (!workspace || workspace_bytes < need)) return SHARQ_ERR_WORKSPACE;
+        if (need > 0 && !aligned(workspace, 16)) return SHARQ_ERR_ALIGN;
+    } else if (fmt == SHARQ_NVFP4 && T > kNoallocRows) {
+        return SHARQ_ERR_WORKSPACE;  // more rows than the built-in scratch holds
+    }
 
-    PrepArgs a{};
+    a = PrepArgs{};
     a.x = static_cast<const uint16_t *>(x);
     a.T = T;
     a.K = K;
@@ -94,7 +106,36 @@ sharq_status sharq_prepare(const void *x, int32_t x_dtype, int64_t T, int64_t K,
     a.r_scales = r_scales;
     a.global_scale = global_scale;
     a.off32 = K % 128 == 0 && T * (K / 2) < ((int64_t)1 << 32);
+    return SHARQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sharq_status sharq_prepare(const void *x, int32_t x_dtype, int64_t T, int64_t K, int64_t ldx,
+                           int32_t norm, const void *gamma, const void *beta, float eps, int32_t n,
+                           int32_t m, int32_t fmt, uint8_t *mask, uint8_t *b_codes, uint8_t *b_scales,
+                           uint8_t *r_codes, uint8_t *r_scales, float *global_scale, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    PrepArgs a{};
+    const sharq_status s = prepare_args(x, x_dtype, T, K, ldx, norm, gamma, beta, eps, n, m, fmt, mask, b_codes,
+                                        b_scales, r_codes, r_scales, global_scale, true, workspace,
+                                        workspace_bytes, a);
+    if (s != SHARQ_OK || T == 0) return s;
     return hip_status(launch_prepare(a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+sharq_status sharq_prepare_noalloc(const void *x, int32_t x_dtype, int64_t T, int64_t K, int64_t ldx,
+                                   int32_t norm, const void *gamma, const void *beta, float eps, int32_t n,
+                                   int32_t m, int32_t fmt, uint8_t *mask, uint8_t *b_codes,
+                                   uint8_t *b_scales, uint8_t *r_codes, uint8_t *r_scales,
+                                   float *global_scale, void *stream) {
+    PrepArgs a{};
+    const sharq_status s = prepare_args(x, x_dtype, T, K, ldx, norm, gamma, beta, eps, n, m, fmt, mask, b_codes,
+                                        b_scales, r_codes, r_scales, global_scale, false, nullptr, 0, a);
+    if (s != SHARQ_OK || T == 0) return s;
+    return hip_status(launch_prepare_noalloc(a, static_cast<hipStream_t>(stream)));
 }
 
 sharq_status sharq_prepare_swiglu(const float *gate_up, int64_t T, int64_t K, int64_t ld, int32_t n, int32_t m,

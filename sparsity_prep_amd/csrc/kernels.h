@@ -47,6 +47,10 @@ struct PrepArgs {
 };
 
 hipError_t launch_prepare(const PrepArgs &a, void *ws, hipStream_t st);
+// The same preparation with its scratch (NVFP4 per-row statistics, at most
+// kNoallocRows rows) in the library's own device array: allocates nothing.
+constexpr int64_t kNoallocRows = 65536;
+hipError_t launch_prepare_noalloc(const PrepArgs &a, hipStream_t st);
 hipError_t launch_prepare_swiglu(const PrepArgs &a, void *ws, hipStream_t st);
 size_t prepare_workspace_bytes(int64_t T, int fmt);
 

@@ -24,6 +24,8 @@
 //   NVFP4:                 a pre-pass writes per-row norm statistics and
 //                          amax, a one-block kernel reduces the tensor scale,
 //                          then the main pass streams (row, chunk-group) tasks.
+#include <mutex>
+
 #include "device_util.h"
 #include "kernels.h"
 
@@ -983,6 +985,51 @@ hipError_t launch_prepare(const PrepArgs &a, void *ws, hipStream_t st) {
 
 size_t prepare_workspace_bytes(int64_t T, int fmt) {
     return fmt == kFmtNv ? (size_t)(T > 0 ? T : 1) * sizeof(RowStats) : 0;
+}
+
+// ---------------------------------------------------------------- allocation-free preparation
+// Scratch of sharq_prepare_noalloc: the NVFP4 per-row statistics of up to
+// kNoallocRows rows, in a file-scope device array that every GPU the library
+// runs on holds until the process ends.  Host code never passes the array's
+// name (a host-side stand-in, not a device address) to a kernel: the device
+// address is looked up once per device, with that device current, and kept.
+// Every call on a device shares its array, so calls that overlap on one GPU
+// race; nothing in it has to start at zero (each launch writes every row's
+// statistics before the tensor-scale kernel reads them).
+static_assert(kNoallocRows * sizeof(RowStats) <= ((size_t)1 << 20), "scratch stays at 1 MiB");
+static __device__ __align__(256) RowStats scratch[kNoallocRows];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {nullptr};
+
+hipError_t scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_prepare_noalloc(const PrepArgs &a, hipStream_t st) {
+    if (a.T == 0) return hipSuccess;
+    void *ws = nullptr;
+    if (a.fmt == kFmtNv) {
+        if (a.T > kNoallocRows) return hipErrorInvalidValue;  // the entry point rejects this first
+        const hipError_t e = scratch_address(&ws);
+        if (e != hipSuccess) return e;
+    }
+    return launch_prepare(a, ws, st);
 }
 
 }  // namespace sharq

@@ -193,3 +193,17 @@ def test_gfx950_has_block_scaled_fp4_mfma_but_no_sparse_fp4(tmp_path):
                  "smfmac_scale_f32_16x16x128_f8f6f4", "smfmac_f32_16x16x128_f8f6f4"):
         assert not _compiles(tmp_path, "__global__ void k(v4i*a,v8i*b,v4f*c,int*x){int i=threadIdx.x;"
                              f"c[i]=__builtin_amdgcn_{name}(a[i],b[i],c[i],x[i],0,0);}}"), name
+
+
+def test_prepare_noalloc_validation(L):
+    def na(T=4, K=256, fmt=MX, x=FAKE, G=None, norm=1):
+        return L.sharq_prepare_noalloc(x, BF16, T, K, K, norm, FAKE, None, 1e-5, 2, 4, fmt, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, G, None)
+    assert na(fmt=3) == UNSUPPORTED
+    assert na(K=100) == SHAPE
+    assert na(x=None) == NULL
+    assert na(fmt=NV) == NULL
+    assert na(x=MISALIGNED) == ALIGN
+    # NVFP4 rows beyond the built-in scratch are refused before any HIP call
+    assert na(T=65536 + 1, fmt=NV, G=FAKE) == WORKSPACE
+    assert na(T=0, x=None) == OK

@@ -579,46 +579,59 @@ struct DualGemm {
     }
 };
 
-// OCC workgroups share a CU (LDS and registers are sized for that).
-template <int FMT, int BM, int BN, int WGM, int WGN, int NS, int OCC, int LSPLIT, int RPS>
-__global__ __launch_bounds__(WGM * WGN * 64)
-__attribute__((amdgpu_waves_per_eu(OCC * WGM * WGN / 4, OCC * WGM * WGN / 4)))
-void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles, int64_t n_begin) {
-    if (a.ksplit_tiles > 0) {
-        // K range blockIdx.y: in the K-tiled layout tiles [t0, t0 + kt) of every
-        // operand are themselves a K-tiled array with K = 128 * kt
-        constexpr int64_t kScaleBytes = kTileK / (FMT == kFmtMx ? 32 : 16);  // per row and K tile
-        const int64_t t0 = (int64_t)blockIdx.y * a.ksplit_tiles;
-        a.b_codes += t0 * a.T * (kTileK / 2);
-        a.r_codes += t0 * a.T * (kTileK / 2);
-        a.b_scales += t0 * a.T * kScaleBytes;
-        a.r_scales += t0 * a.T * kScaleBytes;
-        a.w_codes += t0 * a.nout * (kTileK / 2);
-        a.w_scales += t0 * a.nout * kScaleBytes;
-        a.K = a.ksplit_tiles * kTileK;
-        a.y = static_cast<float *>(a.y) + (int64_t)blockIdx.y * a.split_stride;  // FP32 partials
+// Item q of XCD x's share of a grouped product: the tiles of experts x,
+// x+8, x+16, ... in order, each expert's BM-row tiles times its n_ntiles
+// column tiles (column tiles fastest).  The experts' tile counts are placed
+// with a wave-wide prefix sum (64 experts per pass); false when q is past
+// the end.  Wave-uniform results.
+template <int BM>
+__device__ __forceinline__ bool xcd_group_item(const LinearArgs &a, int xcd, int64_t q, int64_t n_ntiles,
+                                               TileRows &tr, int64_t &nt) {
+    const int lane = threadIdx.x & 63;
+    const int64_t nexp = (a.E - xcd + 7) / 8;
+    int64_t acc = 0;
+    for (int64_t base = 0; base < nexp; base += 64) {
+        const int64_t j = base + lane;
+        int32_t lo = 0, hi = 0, ni = 0;
+        if (j < nexp) {
+            const int64_t e = xcd + 8 * j;
+            lo = a.offsets[e];
+            hi = a.offsets[e + 1];
+            ni = (int32_t)(((hi - lo + BM - 1) / BM) * n_ntiles);
+        }
+        int32_t incl = ni;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t up = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += up;
+        }
+        const int64_t first = acc + (incl - ni);
+        const uint64_t hit = __ballot(j < nexp && q >= first && q < first + ni);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            const int32_t lo_l = __builtin_amdgcn_readfirstlane(__shfl(lo, l, 64));
+            const int32_t hi_l = __builtin_amdgcn_readfirstlane(__shfl(hi, l, 64));
+            const int32_t first_l = __builtin_amdgcn_readfirstlane(__shfl((int32_t)(incl - ni), l, 64));
+            const int64_t local = q - acc - first_l;
+            nt = local % n_ntiles;
+            tr.m0 = lo_l + (local / n_ntiles) * BM;
+            tr.m_end = hi_l;
+            tr.expert = xcd + 8 * (base + l);
+            return true;
+        }
+        acc += __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
     }
+    return false;
+}
+
+// One BM x BN output tile: rows tr.m0 .. min(tr.m0 + BM, tr.m_end) - 1 of
+// expert tr.expert, columns n0 .. n0 + BN - 1.
+template <int FMT, int BM, int BN, int WGM, int WGN, int NS, int OCC, int LSPLIT, int RPS>
+__device__ __forceinline__ void dual_tile(const LinearArgs &a, const TileRows &tr, int64_t n0) {
     using G = DualGemm<FMT, BM, BN, WGM, WGN, NS, LSPLIT, RPS>;
     using L = typename G::L;
     constexpr int FM = G::FM, FN = G::FN;
     static_assert(FM >= 1 && FN >= 1, "tile too small for 32x32 fragments");
-    static_assert(L::BYTES * NS * OCC <= kLdsBytes, "stages do not fit the CU's LDS");
-
-    TileRows tr;
-    int64_t ntile;
-    if (a.offsets == nullptr) {
-        const int64_t t = xcd_tile(blockIdx.x, n_ntiles * n_mtiles);
-        if (t >= n_ntiles * n_mtiles) return;
-        const int64_t mt = t % n_mtiles;
-        ntile = t / n_mtiles;
-        tr.m0 = mt * BM;
-        tr.m_end = a.rows;
-        tr.expert = 0;
-    } else {
-        ntile = blockIdx.x % n_ntiles;
-        if (!grouped_tile_rows<BM>(a, blockIdx.x / n_ntiles, tr)) return;
-    }
-    const int64_t n0 = n_begin + ntile * BN;
     const int64_t K = a.K;
     constexpr int SB = L::SB;
     const uint32_t kb = (uint32_t)(K / 2), ks = (uint32_t)(K / kKS) * SB;  // per row: code / scale bytes
@@ -736,6 +749,63 @@ void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles, int64_t n_beg
     }
 }
 
+
+// A grid of tiles: dense products map blockIdx.x to a tile in XCD-aware
+// order; grouped products either find their expert tile from blockIdx.x
+// (n_mtiles = 0) or, as persistent workgroups (n_mtiles < 0), walk their
+// XCD's share of the expert tiles (see xcd_group_item), so that the tiles of
+// one expert run together on one XCD and share its weight and token rows in
+// that XCD's L2.  OCC workgroups share a CU (LDS and registers are sized for
+// that).
+template <int FMT, int BM, int BN, int WGM, int WGN, int NS, int OCC, int LSPLIT, int RPS, bool GROUPED>
+__global__ __launch_bounds__(WGM * WGN * 64)
+__attribute__((amdgpu_waves_per_eu(OCC * WGM * WGN / 4, OCC * WGM * WGN / 4)))
+void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles, int64_t n_begin) {
+    if (a.ksplit_tiles > 0) {
+        // K range blockIdx.y: in the K-tiled layout tiles [t0, t0 + kt) of every
+        // operand are themselves a K-tiled array with K = 128 * kt
+        constexpr int64_t kScaleBytes = kTileK / (FMT == kFmtMx ? 32 : 16);  // per row and K tile
+        const int64_t t0 = (int64_t)blockIdx.y * a.ksplit_tiles;
+        a.b_codes += t0 * a.T * (kTileK / 2);
+        a.r_codes += t0 * a.T * (kTileK / 2);
+        a.b_scales += t0 * a.T * kScaleBytes;
+        a.r_scales += t0 * a.T * kScaleBytes;
+        a.w_codes += t0 * a.nout * (kTileK / 2);
+        a.w_scales += t0 * a.nout * kScaleBytes;
+        a.K = a.ksplit_tiles * kTileK;
+        a.y = static_cast<float *>(a.y) + (int64_t)blockIdx.y * a.split_stride;  // FP32 partials
+    }
+    using L = typename DualGemm<FMT, BM, BN, WGM, WGN, NS, LSPLIT, RPS>::L;
+    static_assert(L::BYTES * NS * OCC <= kLdsBytes, "stages do not fit the CU's LDS");
+    if constexpr (!GROUPED) {
+        const int64_t t = xcd_tile(blockIdx.x, n_ntiles * n_mtiles);
+        if (t >= n_ntiles * n_mtiles) return;
+        TileRows tr;
+        tr.m0 = (t % n_mtiles) * BM;
+        tr.m_end = a.rows;
+        tr.expert = 0;
+        dual_tile<FMT, BM, BN, WGM, WGN, NS, OCC, LSPLIT, RPS>(a, tr, n_begin + (t / n_mtiles) * BN);
+        return;
+    }
+    // grouped: one tile found from blockIdx.x, or a persistent walk over
+    // this XCD's tiles; a single call site keeps the tile inlined
+    const bool persistent = n_mtiles < 0;
+    for (int64_t q = blockIdx.x / 8;; q += gridDim.x / 8) {
+        TileRows tr;
+        int64_t n0;
+        if (persistent) {
+            int64_t nt;
+            if (!xcd_group_item<BM>(a, (int)(blockIdx.x % 8), q, n_ntiles, tr, nt)) return;
+            n0 = n_begin + nt * BN;
+            __syncthreads();  // every wave is done with the previous tile's LDS stages
+        } else {
+            if (!grouped_tile_rows<BM>(a, blockIdx.x / n_ntiles, tr)) return;
+            n0 = n_begin + (blockIdx.x % n_ntiles) * BN;
+        }
+        dual_tile<FMT, BM, BN, WGM, WGN, NS, OCC, LSPLIT, RPS>(a, tr, n0);
+        if (!persistent) return;
+    }
+}
 // ============================================================================
 // Decode / small-T.  A workgroup of kSmallWaves waves owns 16 weight rows and
 // splits K between its waves (wave w takes the w-th contiguous share of the
@@ -881,21 +951,31 @@ __global__ __launch_bounds__(kSmallWaves * 64) void k_dual_gemm_mx_small(LinearA
 // ============================================================================
 // launcher
 // ============================================================================
+static int device_cus();
+
 // Output columns [n_begin, n_end) of the product (all of them by default).
-template <int FMT, int BM, int BN, int WGM, int WGN, int NS = 3, int OCC = 1, int LSPLIT = 0, int RPS = 1>
-static hipError_t launch_prefill(const LinearArgs &a, hipStream_t st, int64_t n_begin = 0, int64_t n_end = -1) {
+// Grouped products: `persistent` launches OCC workgroups per CU that walk
+// their XCD's share of the expert tiles; otherwise one workgroup per tile
+// (an upper bound of tiles is launched, the extra workgroups exit).
+template <int FMT, int BM, int BN, int WGM, int WGN, int NS = 3, int OCC = 1, int LSPLIT = 0, int RPS = 1,
+          bool GROUPED = false>
+static hipError_t launch_prefill(const LinearArgs &a, hipStream_t st, int64_t n_begin = 0, int64_t n_end = -1,
+                                 bool persistent = false) {
     if (n_end < 0) n_end = a.nout;
     const int64_t n_ntiles = (n_end - n_begin + BN - 1) / BN;
     int64_t blocks;
     int64_t n_mtiles = 0;
-    if (a.offsets) {
+    if (a.offsets && persistent) {
+        blocks = (int64_t)((device_cus() + 7) / 8) * 8 * OCC;
+        n_mtiles = -1;
+    } else if (a.offsets) {
         blocks = n_ntiles * ((a.rows + BM - 1) / BM + a.E);  // upper bound; extra blocks exit
     } else {
         n_mtiles = (a.rows + BM - 1) / BM;
         blocks = ((n_ntiles * n_mtiles + 7) / 8) * 8;
     }
     const unsigned splits = a.ksplit_tiles > 0 ? (unsigned)(a.K / kTileK / a.ksplit_tiles) : 1u;
-    hipLaunchKernelGGL((k_dual_gemm<FMT, BM, BN, WGM, WGN, NS, OCC, LSPLIT, RPS>), dim3((unsigned)blocks, splits),
+    hipLaunchKernelGGL((k_dual_gemm<FMT, BM, BN, WGM, WGN, NS, OCC, LSPLIT, RPS, GROUPED>), dim3((unsigned)blocks, splits),
                        dim3(WGM * WGN * 64), 0,
                        st, a, n_ntiles, n_mtiles, n_begin);
     return hipGetLastError();
@@ -1070,7 +1150,7 @@ static hipError_t launch_linear_mx(const LinearArgs &a, void *ws, size_t ws_byte
     // (measured on MI355X on the Qwen3-30B-A3B expert shapes: 5% faster than
     // one workgroup with three stages at K = 2048, 11% at K = 768, where one
     // workgroup's output stores overlap the other's MFMAs)
-    if (a.offsets) return launch_prefill<kFmtMx, 128, 256, 2, 2, 2, 2, 0, 1>(a, st);
+    if (a.offsets) return launch_prefill<kFmtMx, 128, 256, 2, 2, 2, 2, 0, 1, true>(a, st, 0, -1, a.E >= 16);
     const int64_t cus = device_cus();
     double t_one = 0.0;
     const int one = best_shape(a.rows, a.nout, cus, &t_one);
@@ -1110,7 +1190,7 @@ static double nv_cost256(int64_t rows, int64_t cols, int64_t cus) {
 }
 
 static hipError_t launch_linear_nv(const LinearArgs &a, hipStream_t st) {
-    if (a.offsets) return launch_prefill<kFmtNv, 128, 256, 2, 2, 3, 1, 4, 1>(a, st);
+    if (a.offsets) return launch_prefill<kFmtNv, 128, 256, 2, 2, 3, 1, 4, 1, true>(a, st);
     const int64_t cus = device_cus();
     const double c128 = nv_cost128(a.rows, a.nout, cus), c256 = nv_cost256(a.rows, a.nout, cus);
     const int64_t mt = (a.rows + 255) / 256;

@@ -12,12 +12,11 @@
 // the four lanes of a DPP quad and an NVFP4 block (16) a lane pair.  The row
 // is read from HBM exactly once; everything else happens in registers.
 //
-//   MX + norm, K <= 8192:  a workgroup of four waves per row (from 2048 rows
-//                          on, 2 or 4 consecutive rows per workgroup, the
-//                          next row loaded during the current one); the row
-//                          stays in registers across the FP64 norm reduction
-//                          (whose per-wave partials meet in LDS) and the
-//                          quantization pass;
+//   MX + norm, K <= 8192:  a workgroup of four waves per row; the row stays
+//                          in registers across the FP64 norm reduction (whose
+//                          per-wave partials meet in LDS) and the
+//                          quantization pass, whose stores are buffer stores
+//                          at scalar + per-lane-constant offsets;
 //   MX + norm, larger K:   one wave per row, the quantization pass re-reads
 //                          the row (L2 hit);
 //   no norm:               tasks are (row, group of chunks), fully parallel;
@@ -34,7 +33,6 @@ namespace sharq {
 constexpr int kPrepWaves = 4;        // waves per workgroup
 constexpr int kChunk = 512;          // elements per wave-wide 128-bit load
 constexpr int kStreamChunks = 2;     // chunks per task when rows are split (measured: 2 beats 4 and 8)
-constexpr int64_t kPrepRowsGrid = 1024;   // row workgroups that fill the GPU (four per CU)
 
 struct RowStats {  // per-row statistics written by the NVFP4 pre-pass
     float r, mu, amax, pad;
@@ -215,27 +213,65 @@ __device__ __forceinline__ uint4 param_raw(const uint16_t *p, int64_t e0, uint32
 // ---------------------------------------------------------------- per-chunk body
 // Normalized values v of one lane -> mask byte, backbone and residual codes
 // and scales, stored at element offset e0 of row `row`.
-// Per-lane constant parts of the K-tiled offsets of a wave-wide chunk (512
-// elements, chunk index ch along K, which starts on a K-tile boundary): lane
-// l writes K tile 4ch + l/16, elements (l%16)*8 .. +7 of it.  With these the
-// byte offset of the lane's codes (scales) in the 32-bit path is
-// ch * T * 256 (ch * T * 512/B) + row * 64 (row * 128/B) + co (so), a
-// scalar base plus this constant.
+//
+// Store addressing (K % 128 == 0 and every output array below 4 GiB, the
+// usual case): buffer stores whose byte offset is a wave-uniform part (row
+// and chunk, in a scalar register) plus a per-lane constant, so no per-lane
+// address arithmetic runs per store.  A wave-wide chunk (512 elements, chunk
+// index ch along K) starts on a K-tile boundary: lane l holds elements
+// (l%16)*8 .. +7 of K tile 4ch + l/16.  Its code dword lies at
+// ch*T*256 + row*64 + [q*T*64 + (l%16)*4], q = l/16, the bracket being the
+// per-lane constant.  The tile's block-scale bytes of the row (4 MX, 8
+// NVFP4) are gathered by DPP into dwords and stored by one lane per dword.
+// Other shapes take per-lane 64-bit K-tiled offsets.
 struct LaneOff {
-    uint32_t co, so;
+    uint32_t co;  // code dword
+    uint32_t so;  // scale dword (lanes that store one)
 };
 
 template <int FMT>
 __device__ __forceinline__ LaneOff lane_offsets(const PrepArgs &a, int lane) {
-    constexpr uint32_t B = FMT == kFmtMx ? 32 : 16;
-    const uint32_t q = (uint32_t)lane >> 4, w = ((uint32_t)lane & 15u) * 8u;
-    return {q * (uint32_t)(a.T * (kTileK / 2)) + w / 2, q * (uint32_t)(a.T * (kTileK / B)) + w / B};
+    constexpr uint32_t SPT = FMT == kFmtMx ? 4 : 8;  // scale bytes per row per K tile
+    const uint32_t q = (uint32_t)lane >> 4, w = (uint32_t)lane & 15u;
+    return {q * (uint32_t)(a.T * (kTileK / 2)) + w * 4u,
+            q * (uint32_t)a.T * SPT + (FMT == kFmtMx ? 0u : (w >= 8u ? 4u : 0u))};
+}
+
+// Scale bytes of a lane's block, gathered so that one lane per dword holds
+// the dword of the K tile's scales of this row: MX (four blocks of four
+// lanes) in lanes 16q+12..15; NVFP4 (eight blocks of two lanes) bytes 0-3 in
+// lanes 16q+6, 7 and bytes 4-7 in lanes 16q+14, 15.
+template <int FMT>
+__device__ __forceinline__ uint32_t gather_scales(uint32_t sb, int lane) {
+    constexpr int kRowShr = 0x110;  // DPP row_shr:n = 0x110 + n (within rows of 16 lanes)
+    if constexpr (FMT == kFmtMx) {
+        uint32_t v = sb << (8 * ((lane >> 2) & 3));
+        v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowShr + 4, 0xF, 0xF, true);
+        v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowShr + 8, 0xF, 0xF, true);
+        return v;
+    } else {
+        uint32_t v = sb << (8 * ((lane >> 1) & 3));
+        v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowShr + 2, 0xF, 0xF, true);
+        v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowShr + 4, 0xF, 0xF, true);
+        return v;
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ bool scale_store_lane(int lane) {
+    return FMT == kFmtMx ? (lane & 15) == 12 : (lane & 7) == 6;
 }
 
 // Decompose eight consecutive normalized values (elements 8*lane .. +7 of
 // chunk ch of `row`; row and ch wave-uniform) and store their share of the
-// mask, codes and scales.
-template <int FMT, int M, int FAST24>
+// mask, codes and scales.  OFF32 (K % 128 == 0, every output array below
+// 2 GiB): buffer stores at scalar + per-lane-constant offsets, the same
+// instructions on every lane and call (lanes that store no scale dword, and
+// every lane when there is no mask, write out of range, which the buffer
+// unit drops), so the compiler can count outstanding memory operations
+// exactly and a row loop never waits for its stores.  Otherwise per-lane
+// 64-bit K-tiled offsets.
+template <int FMT, int M, int FAST24, bool OFF32>
 __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, int64_t ch, int lane, LaneOff lo,
                                                 const float v[8], float G, double rG6) {
     bool kp[8];
@@ -259,17 +295,22 @@ __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, 
     const int64_t K = a.K;
     constexpr int LPB = FMT == kFmtMx ? 4 : 2;  // lanes per scale block
     constexpr int B = FMT == kFmtMx ? 32 : 16;
-    if (a.mask) (a.mask + row * (K / 8) + ch * (kChunk / 8))[lane] = (uint8_t)keep;
-    if (a.off32) {  // K % 128 == 0 and each array < 4 GiB
-        const uint32_t cb = (uint32_t)ch * (uint32_t)(a.T * (kChunk / 2));
-        const uint32_t sb = (uint32_t)ch * (uint32_t)(a.T * (kChunk / B));
-        *reinterpret_cast<uint32_t *>(a.b_codes + row * (kTileK / 2) + cb + lo.co) = bc;
-        *reinterpret_cast<uint32_t *>(a.r_codes + row * (kTileK / 2) + cb + lo.co) = rc;
-        if ((lane % LPB) == 0) {
-            (a.b_scales + row * (kTileK / B) + sb)[lo.so] = (uint8_t)bs;
-            (a.r_scales + row * (kTileK / B) + sb)[lo.so] = (uint8_t)rs;
-        }
+    if constexpr (OFF32) {
+        constexpr uint32_t SPT = FMT == kFmtMx ? 4 : 8;
+        const uint32_t T = (uint32_t)a.T, r32 = (uint32_t)row, c32 = (uint32_t)ch;
+        const int soc = __builtin_amdgcn_readfirstlane((int)(c32 * T * (kChunk / 2) + r32 * (kTileK / 2)));
+        const int sos = __builtin_amdgcn_readfirstlane((int)(c32 * T * (4 * SPT) + r32 * SPT));
+        const int som = __builtin_amdgcn_readfirstlane((int)(r32 * (uint32_t)(K / 8) + c32 * (kChunk / 8)));
+        const uint32_t ncodes = T * (uint32_t)(K / 2), nsc = T * (uint32_t)(K / B);
+        const uint32_t nmask = a.mask ? T * (uint32_t)(K / 8) : 0u;  // no mask: every store dropped
+        __builtin_amdgcn_raw_buffer_store_b32(bc, make_rsrc(a.b_codes, ncodes), (int)lo.co, soc, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(rc, make_rsrc(a.r_codes, ncodes), (int)lo.co, soc, 0);
+        const uint32_t sv = scale_store_lane<FMT>(lane) ? lo.so : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b32(gather_scales<FMT>(bs, lane), make_rsrc(a.b_scales, nsc), (int)sv, sos, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(gather_scales<FMT>(rs, lane), make_rsrc(a.r_scales, nsc), (int)sv, sos, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)keep, make_rsrc(a.mask, nmask), lane, som, 0);
     } else {
+        if (a.mask) (a.mask + row * (K / 8) + ch * (kChunk / 8))[lane] = (uint8_t)keep;
         const int64_t e0 = ch * kChunk + lane * 8;
         const int64_t co = ktile_offset<2>(row, e0, a.T, K);
         const int64_t so = ktile_offset<B>(row, e0, a.T, K);
@@ -282,59 +323,63 @@ __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, 
     }
 }
 
-// ---------------------------------------------------------------- MX, norm, row split over a workgroup
-// A workgroup of NWG waves handles `rpw` consecutive rows, one at a time;
-// wave w owns chunks w, w+NWG, ... of a row (at most CPW of them, held in
-// registers).  The next row's words are loaded before the current row is
-// reduced and quantized, so its latency hides behind the current row's
-// arithmetic.  Each wave reduces its FP64 partial sums, the NWG partials
-// meet in LDS (two slots, alternating by row) and every wave adds them in
-// the same fixed order, so all waves derive the same r (and mu).  gamma and
-// beta are loaded once per workgroup.
-template <bool BF16, int NORM, int M, int FAST24, int CPW, int NWG>
-__global__ __launch_bounds__(NWG * kWave) void k_prep_mx_split(PrepArgs a, int64_t rpw) {
-    __shared__ double part[2][2][NWG];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const LaneOff lo = lane_offsets<kFmtMx>(a, lane);
-    const int64_t row0 = xcd_block(blockIdx.x, gridDim.x) * rpw;
-    const int64_t row_end = row0 + rpw < a.T ? row0 + rpw : a.T;
-    if (row0 >= row_end) return;
-    const int64_t K = a.K;
+// Either store path, chosen per launch.
+template <int FMT, int M, int FAST24>
+__device__ __forceinline__ void decompose_any(const PrepArgs &a, int64_t row, int64_t ch, int lane, LaneOff lo,
+                                              const float v[8], float G, double rG6) {
+    if (a.off32)
+        decompose_store<FMT, M, FAST24, true>(a, row, ch, lane, lo, v, G, rG6);
+    else
+        decompose_store<FMT, M, FAST24, false>(a, row, ch, lane, lo, v, G, rG6);
+}
 
-    bool in[CPW];
-    uint4 graw[CPW], braw[CPW], raw[CPW];
-    constexpr uint32_t kOnePair = BF16 ? 0x3F803F80u : 0x3C003C00u;  // 1.0, 1.0
-#pragma unroll
-    for (int j = 0; j < CPW; j++) {
-        const int64_t e0 = ((int64_t)(wave + NWG * j) * kWave + lane) * 8;
-        in[j] = e0 < K;
-        raw[j] = in[j] ? *reinterpret_cast<const uint4 *>(a.x + row0 * a.ldx + e0) : make_uint4(0, 0, 0, 0);
-        graw[j] = in[j] ? param_raw<true>(a.gamma, e0, kOnePair) : make_uint4(0, 0, 0, 0);
-        braw[j] = in[j] ? param_raw<NORM == kNormLayer>(a.beta, e0, 0u) : make_uint4(0, 0, 0, 0);
-    }
-    for (int64_t row = row0; row < row_end; row++) {
-        const int slot = (int)(row & 1);
-        uint4 nraw[CPW];
-        const bool more = row + 1 < row_end;
+// ---------------------------------------------------------------- MX, norm, one row per workgroup
+// A workgroup of NWG waves handles one row; wave w owns chunks w, w+NWG, ...
+// of it (at most CPW of them, held in registers from one batch of loads).
+// Each wave reduces its FP64 partial sums, the NWG partials meet in LDS and
+// every wave adds them in the same fixed order, so all waves derive the same
+// r (and mu).  Row loads are buffer loads from the row's scalar base, so no
+// per-lane address arithmetic.
+template <bool BF16, int NORM, int M, int FAST24, int CPW, int NWG, bool FULL>
+struct NormRows {
+    static constexpr uint32_t kOnePair = BF16 ? 0x3F803F80u : 0x3C003C00u;  // 1.0, 1.0
+
+    // Row `row`'s words (chunks past the row's end read as zeros).
+    static __device__ __forceinline__ void load_row(const PrepArgs &a, int64_t row, int wave, int lane,
+                                                    const bool (&in)[CPW], uint4 (&raw)[CPW]) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(a.x + row * a.ldx, (uint32_t)(a.K * 2));
 #pragma unroll
         for (int j = 0; j < CPW; j++) {
-            const int64_t e0 = ((int64_t)(wave + NWG * j) * kWave + lane) * 8;
-            nraw[j] = (more && in[j]) ? *reinterpret_cast<const uint4 *>(a.x + (row + 1) * a.ldx + e0)
-                                      : make_uint4(0, 0, 0, 0);
+            const uint32_t off = (uint32_t)(((wave + NWG * j) * kWave + lane) * 16);
+            raw[j] = bload128(r, in[j] ? off : kOutOfRange);
         }
-        float v[8];
-        double s1 = 0.0;
+    }
+
+    // Norm statistics of one row (every wave of the workgroup gets the same),
+    // then the decomposition of the wave's chunks.
+    static __device__ __forceinline__ void row(const PrepArgs &a, int64_t row, int slot, int wave, int lane,
+                                               LaneOff lo, const bool (&in)[CPW], const uint4 (&raw)[CPW],
+                                               const float (&gf)[CPW][8], const float (&bf)[CPW][8],
+                                               double (&part)[2][2][NWG]) {
+        const int64_t K = a.K;
+        float xf[CPW][8];
+#pragma unroll
+        for (int j = 0; j < CPW; j++) unpack8<BF16>(raw[j], xf[j]);  // out-of-range words are 0
+        double s1 = 0.0, s1b = 0.0;
 #pragma unroll
         for (int j = 0; j < CPW; j++) {
-            unpack8<BF16>(raw[j], v);
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                if constexpr (NORM == kNormRms) s1 = __fma_rn((double)v[i], (double)v[i], s1);  // x*x exact in double
-                else s1 += (double)v[i];
+            for (int i = 0; i < 8; i += 2) {
+                if constexpr (NORM == kNormRms) {
+                    s1 = __fma_rn((double)xf[j][i], (double)xf[j][i], s1);  // x*x exact in double
+                    s1b = __fma_rn((double)xf[j][i + 1], (double)xf[j][i + 1], s1b);
+                } else {
+                    s1 += (double)xf[j][i];
+                    s1b += (double)xf[j][i + 1];
+                }
             }
         }
-        s1 = wave_sum_f64(s1);
+        s1 = wave_sum_f64(s1 + s1b);
         if (lane == 0) part[slot][0][wave] = s1;
         __syncthreads();
         s1 = part[slot][0][0];
@@ -349,10 +394,9 @@ __global__ __launch_bounds__(NWG * kWave) void k_prep_mx_split(PrepArgs a, int64
 #pragma unroll
             for (int j = 0; j < CPW; j++) {
                 if (in[j]) {
-                    unpack8<BF16>(raw[j], v);
 #pragma unroll
                     for (int i = 0; i < 8; i++) {
-                        const double d = (double)v[i] - mud;
+                        const double d = (double)xf[j][i] - mud;
                         s2 += d * d;  // d*d is rounded on its own, as in the definition
                     }
                 }
@@ -369,30 +413,23 @@ __global__ __launch_bounds__(NWG * kWave) void k_prep_mx_split(PrepArgs a, int64
 #pragma unroll
         for (int j = 0; j < CPW; j++) {
             if (in[j]) {
-                float g[8], b[8];
-                unpack8<BF16>(graw[j], g);
-                unpack8<BF16>(braw[j], b);
-                unpack8<BF16>(raw[j], v);
-                normalize8<NORM>(v, g, b, r, mu);
-                decompose_store<kFmtMx, M, FAST24>(a, row, wave + NWG * j, lane, lo, v, 1.0f, 6.0f);
+                normalize8<NORM>(xf[j], gf[j], bf[j], r, mu);
+                decompose_store<kFmtMx, M, FAST24, true>(a, row, wave + NWG * j, lane, lo, xf[j], 1.0f, 0.0);
             }
         }
-#pragma unroll
-        for (int j = 0; j < CPW; j++) raw[j] = nraw[j];
     }
-}
+};
 
-// ---------------------------------------------------------------- MX, norm, one row per workgroup
-// A workgroup of NWG waves handles one row; wave w owns chunks w, w+NWG, ...
-// of it (at most CPW of them, held in registers from one batch of loads).
-// Each wave reduces its FP64 partial sums, the NWG partials meet in LDS and
-// every wave adds them in the same fixed order, so all waves derive the same
-// r (and mu).  Used below kPrepRowsGrid * 2 rows, where it beats the split
-// kernel run with one row per workgroup (measured on MI355X: about 15% at
-// a few hundred rows).
-template <bool BF16, int NORM, int M, int FAST24, int CPW, int NWG>
-__global__ __launch_bounds__(NWG * kWave) void k_prep_mx_row(PrepArgs a) {
-    __shared__ double part[2][NWG];
+// One row per workgroup, FULL: K == CPW * NWG * 512 (every chunk of every
+// wave is in the row).  Launched only with the 32-bit store offsets
+// (K % 128 == 0, outputs below 2 GiB).  One row per workgroup beat two or
+// four consecutive rows with the next row prefetched (measured on MI355X at
+// 2048 and 4096 rows of 4096): with no second register buffer 8 waves fit
+// on a SIMD, so every row of such a launch is resident and loading at once.
+template <bool BF16, int NORM, int M, int FAST24, int CPW, int NWG, bool FULL>
+__global__ __launch_bounds__(NWG * kWave) void k_prep_mx_rows(PrepArgs a) {
+    using R = NormRows<BF16, NORM, M, FAST24, CPW, NWG, FULL>;
+    __shared__ double part[2][2][NWG];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const LaneOff lo = lane_offsets<kFmtMx>(a, lane);
@@ -401,74 +438,19 @@ __global__ __launch_bounds__(NWG * kWave) void k_prep_mx_row(PrepArgs a) {
     const int64_t K = a.K;
 
     bool in[CPW];
-    uint4 graw[CPW], braw[CPW], raw[CPW];
-    constexpr uint32_t kOnePair = BF16 ? 0x3F803F80u : 0x3C003C00u;  // 1.0, 1.0
+    float gf[CPW][8], bf[CPW][8];
 #pragma unroll
     for (int j = 0; j < CPW; j++) {
         const int64_t e0 = ((int64_t)(wave + NWG * j) * kWave + lane) * 8;
-        in[j] = e0 < K;
-        raw[j] = in[j] ? *reinterpret_cast<const uint4 *>(a.x + row * a.ldx + e0) : make_uint4(0, 0, 0, 0);
+        in[j] = FULL || e0 < K;
+        const uint4 g = in[j] ? param_raw<true>(a.gamma, e0, R::kOnePair) : make_uint4(0, 0, 0, 0);
+        const uint4 b = in[j] ? param_raw<NORM == kNormLayer>(a.beta, e0, 0u) : make_uint4(0, 0, 0, 0);
+        unpack8<BF16>(g, gf[j]);
+        unpack8<BF16>(b, bf[j]);
     }
-#pragma unroll
-    for (int j = 0; j < CPW; j++) {
-        const int64_t e0 = ((int64_t)(wave + NWG * j) * kWave + lane) * 8;
-        graw[j] = in[j] ? param_raw<true>(a.gamma, e0, kOnePair) : make_uint4(0, 0, 0, 0);
-        braw[j] = in[j] ? param_raw<NORM == kNormLayer>(a.beta, e0, 0u) : make_uint4(0, 0, 0, 0);
-    }
-    float v[8];
-    double s1 = 0.0;
-#pragma unroll
-    for (int j = 0; j < CPW; j++) {
-        unpack8<BF16>(raw[j], v);
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            if constexpr (NORM == kNormRms) s1 = __fma_rn((double)v[i], (double)v[i], s1);  // x*x exact in double
-            else s1 += (double)v[i];
-        }
-    }
-    s1 = wave_sum_f64(s1);
-    if (lane == 0) part[0][wave] = s1;
-    __syncthreads();
-    s1 = part[0][0];
-#pragma unroll
-    for (int w = 1; w < NWG; w++) s1 += part[0][w];
-    float r, mu = 0.0f;
-    if constexpr (NORM == kNormRms) {
-        r = (float)(1.0 / sqrt(s1 / (double)K + (double)a.eps));
-    } else {
-        const double mud = s1 / (double)K;
-        double s2 = 0.0;
-#pragma unroll
-        for (int j = 0; j < CPW; j++) {
-            if (in[j]) {
-                unpack8<BF16>(raw[j], v);
-#pragma unroll
-                for (int i = 0; i < 8; i++) {
-                    const double d = (double)v[i] - mud;
-                    s2 += d * d;  // d*d is rounded on its own, as in the definition
-                }
-            }
-        }
-        s2 = wave_sum_f64(s2);
-        if (lane == 0) part[1][wave] = s2;
-        __syncthreads();
-        s2 = part[1][0];
-#pragma unroll
-        for (int w = 1; w < NWG; w++) s2 += part[1][w];
-        mu = (float)mud;
-        r = (float)(1.0 / sqrt(s2 / (double)K + (double)a.eps));
-    }
-#pragma unroll
-    for (int j = 0; j < CPW; j++) {
-        if (in[j]) {
-            float g[8], b[8];
-            unpack8<BF16>(graw[j], g);
-            unpack8<BF16>(braw[j], b);
-            unpack8<BF16>(raw[j], v);
-            normalize8<NORM>(v, g, b, r, mu);
-            decompose_store<kFmtMx, M, FAST24>(a, row, wave + NWG * j, lane, lo, v, 1.0f, 0.0);
-        }
-    }
+    uint4 x[CPW];
+    R::load_row(a, row, wave, lane, in, x);
+    R::row(a, row, 0, wave, lane, lo, in, x, gf, bf, part);
 }
 
 // ---------------------------------------------------------------- MX, norm, two reads
@@ -518,7 +500,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_mx_2pass(PrepArgs a
             load_param8<BF16, NORM == kNormLayer>(a.beta, e0, b, 0.0f);
             unpack8<BF16>(*reinterpret_cast<const uint4 *>(xr + e0), v);
             normalize8<NORM>(v, g, b, r, mu);
-            decompose_store<kFmtMx, M, FAST24>(a, row, ch, lane, lo, v, 1.0f, 0.0);
+            decompose_any<kFmtMx, M, FAST24>(a, row, ch, lane, lo, v, 1.0f, 0.0);
         }
     }
 }
@@ -546,7 +528,7 @@ __device__ __forceinline__ void stream_load(const PrepArgs &a, int64_t task, int
     }
 }
 
-template <bool BF16, int NORM, int FMT, int M, int FAST24>
+template <bool BF16, int NORM, int FMT, int M, int FAST24, bool OFF32>
 __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_stream(PrepArgs a, const RowStats *stats) {
     const int lane = threadIdx.x & 63;
     const int64_t K = a.K;
@@ -581,7 +563,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_stream(PrepArgs a, 
                 unpack8<BF16>(braw[c], b);
                 normalize8<NORM>(v, g, b, r, mu);
             }
-            decompose_store<FMT, M, FAST24>(a, row, c0 + c, lane, lo, v, G, rG6);
+            decompose_store<FMT, M, FAST24, OFF32>(a, row, c0 + c, lane, lo, v, G, rG6);
         }
     }
 }
@@ -650,7 +632,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_swiglu(PrepArgs a) 
         if (e0 < K) {
             float v[8];
             swiglu8(gr, K, e0, v);
-            decompose_store<FMT, M, FAST24>(a, row, c0 + c, lane, lo, v, G, rG6);
+            decompose_any<FMT, M, FAST24>(a, row, c0 + c, lane, lo, v, G, rG6);
         }
     }
 }
@@ -845,30 +827,33 @@ __global__ __launch_bounds__(1024) void k_nv_tensor_scale(const RowStats *stats,
 __global__ void k_fill_f32(float *p, float v) { *p = v; }
 
 // ---------------------------------------------------------------- launcher
+// The rows kernel for CPW chunks per wave: full rows (K = CPW * 4 * 512)
+// on the 2:4 path get the instantiation without bounds checks.
+template <bool BF16, int NORM, int M, int FAST24, int CPW>
+static void launch_rows(const PrepArgs &a, bool full, hipStream_t st) {
+    const dim3 grid((unsigned)round_up8(a.T)), blk(kPrepWaves * kWave);
+    if (FAST24 && full)
+        hipLaunchKernelGGL((k_prep_mx_rows<BF16, NORM, M, FAST24, CPW, kPrepWaves, true>), grid, blk, 0, st, a);
+    else
+        hipLaunchKernelGGL((k_prep_mx_rows<BF16, NORM, M, FAST24, CPW, kPrepWaves, false>), grid, blk, 0, st, a);
+}
+
 template <bool BF16, int NORM, int FMT, int M, int FAST24>
 static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
     const dim3 blk(kPrepWaves * kWave);
     const int64_t K = a.K;
     if constexpr (FMT == kFmtMx && NORM != kNormNone) {
-        const dim3 grid((unsigned)round_up8((a.T + kPrepWaves - 1) / kPrepWaves));
-        // rows per workgroup: about two workgroups per CU once T allows it;
-        // below that one row per workgroup with all of its words loaded at once
-        const int64_t rpw = a.T >= 4 * kPrepRowsGrid ? 4 : (a.T >= 2 * kPrepRowsGrid ? 2 : 1);
-        const dim3 rows((unsigned)round_up8((a.T + rpw - 1) / rpw));
-        // four waves of two chunks beat eight waves of one at K = 4096 (MI355X)
-        if (K <= (int64_t)kChunk * kPrepWaves * 2) {
-            if (rpw > 1)
-                hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 2, kPrepWaves>), rows, blk, 0, st, a, rpw);
-            else
-                hipLaunchKernelGGL((k_prep_mx_row<BF16, NORM, M, FAST24, 2, kPrepWaves>), rows, blk, 0, st, a);
-        } else if (K <= (int64_t)kChunk * kPrepWaves * 4) {
-            if (rpw > 1)
-                hipLaunchKernelGGL((k_prep_mx_split<BF16, NORM, M, FAST24, 4, kPrepWaves>), rows, blk, 0, st, a, rpw);
-            else
-                hipLaunchKernelGGL((k_prep_mx_row<BF16, NORM, M, FAST24, 4, kPrepWaves>), rows, blk, 0, st, a);
-        }
-        else
+        constexpr int64_t kWg = (int64_t)kChunk * kPrepWaves;  // elements per chunk round of the workgroup
+        if (!a.off32 || K > 4 * kWg) {
+            const dim3 grid((unsigned)round_up8((a.T + kPrepWaves - 1) / kPrepWaves));
             hipLaunchKernelGGL((k_prep_mx_2pass<BF16, NORM, M, FAST24>), grid, blk, 0, st, a);
+        } else if (K <= kWg) {
+            launch_rows<BF16, NORM, M, FAST24, 1>(a, K == kWg, st);
+        } else if (K <= 2 * kWg) {
+            launch_rows<BF16, NORM, M, FAST24, 2>(a, K == 2 * kWg, st);
+        } else {
+            launch_rows<BF16, NORM, M, FAST24, 4>(a, K == 4 * kWg, st);
+        }
         if (a.global_scale) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, a.global_scale, 1.0f);
         return hipGetLastError();
     }
@@ -908,8 +893,12 @@ static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
     // prefetch of a next task)
     const int64_t waves = tasks;
     const dim3 grid((unsigned)round_up8((waves + kPrepWaves - 1) / kPrepWaves));
-    if constexpr (FMT == kFmtNv || NORM == kNormNone)
-        hipLaunchKernelGGL((k_prep_stream<BF16, NORM, FMT, M, FAST24>), grid, blk, 0, st, a, stats);
+    if constexpr (FMT == kFmtNv || NORM == kNormNone) {
+        if (a.off32)
+            hipLaunchKernelGGL((k_prep_stream<BF16, NORM, FMT, M, FAST24, true>), grid, blk, 0, st, a, stats);
+        else
+            hipLaunchKernelGGL((k_prep_stream<BF16, NORM, FMT, M, FAST24, false>), grid, blk, 0, st, a, stats);
+    }
     return hipGetLastError();
 }
 

@@ -195,6 +195,34 @@ def test_gfx950_has_block_scaled_fp4_mfma_but_no_sparse_fp4(tmp_path):
                              f"c[i]=__builtin_amdgcn_{name}(a[i],b[i],c[i],x[i],0,0);}}"), name
 
 
+LLVM_MC = "/opt/rocm/llvm/bin/llvm-mc"
+
+
+def _assembles(tmp_path, line):
+    src = tmp_path / "probe.s"
+    src.write_text(line + "\n")
+    r = subprocess.run([LLVM_MC, "-arch=amdgcn", "-mcpu=gfx950", str(src), "-o", os.devnull],
+                       capture_output=True, text=True)
+    return r.returncode == 0
+
+
+@pytest.mark.skipif(not os.path.exists(LLVM_MC), reason="llvm-mc not available")
+def test_gfx950_assembler_sparse_matrix_instructions(tmp_path):
+    """The gfx950 assembler's sparse matrix instructions: f16, bf16, fp8 and
+    int8 operands with an index register and no scale operands; no FP4
+    (f8f6f4) or block-scaled sparse form exists, while the dense
+    block-scaled FP4 instruction does."""
+    ops = "v[0:15], v[16:19], v[20:27], v28"
+    for mnemonic in ("v_smfmac_f32_32x32x32_f16", "v_smfmac_f32_32x32x32_bf16",
+                     "v_smfmac_f32_32x32x64_fp8_fp8", "v_smfmac_i32_32x32x64_i8"):
+        assert _assembles(tmp_path, f"{mnemonic} {ops}"), mnemonic
+    assert _assembles(tmp_path, "v_mfma_scale_f32_32x32x64_f8f6f4 v[0:15], v[16:23], v[24:31], v[0:15], v32, v33")
+    for line in ("v_smfmac_f32_32x32x128_fp4_fp4 " + ops, "v_smfmac_f32_32x32x64_f8f6f4 " + ops,
+                 "v_smfmac_scale_f32_32x32x64_f8f6f4 " + ops + ", v29, v30",
+                 "v_smfmac_f32_16x16x128_fp4 v[0:3], v[16:19], v[20:27], v28"):
+        assert not _assembles(tmp_path, line), line
+
+
 def test_prepare_noalloc_validation(L):
     def na(T=4, K=256, fmt=MX, x=FAKE, G=None, norm=1):
         return L.sharq_prepare_noalloc(x, BF16, T, K, K, norm, FAKE, None, 1e-5, 2, 4, fmt, FAKE, FAKE, FAKE,

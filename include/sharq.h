@@ -19,9 +19,14 @@
  *     stream) and runs asynchronously; no call synchronizes with the host.
  *   - Arguments are validated on the host before any HIP call; a failed check
  *     returns its status code and enqueues nothing.  SHARQ_ERR_HIP reports a
- *     failed launch; faults inside a kernel surface at the caller's next
- *     synchronization, as usual with HIP.  On any error the outputs are
- *     unspecified.
+ *     failed launch (sharq_last_hip_error() gives the hipError_t); faults
+ *     inside a kernel surface at the caller's next synchronization, as usual
+ *     with HIP.  On any error the outputs are unspecified.
+ *   - Check mode: with the environment variable SHARQ_DEBUG=1 every entry
+ *     point also waits for its own launches on `stream` (except while the
+ *     stream is being captured into a HIP graph) and returns SHARQ_ERR_HIP,
+ *     with the entry point's name and the HIP error on stderr, when they
+ *     failed.  The variable is read on every call.
  *   - Element formats:
  *       E2M1   FP4 code: bit 3 sign, bits 0-2 magnitude index into
  *              {0, 0.5, 1, 1.5, 2, 3, 4, 6}; a zero magnitude is always 0x0.
@@ -55,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 4
+#define SHARQ_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define SHARQ_API __attribute__((visibility("default")))
@@ -88,6 +93,11 @@ SHARQ_API int sharq_abi_version(void);
 
 /* Static, NUL-terminated description of a status code. */
 SHARQ_API const char *sharq_status_string(int status);
+
+/* The hipError_t (0 = hipSuccess) of the calling thread's most recent entry
+ * point call that reached HIP (launches, and in check mode the wait); calls
+ * rejected by argument validation leave it unchanged. */
+SHARQ_API int sharq_last_hip_error(void);
 
 /* Bytes of workspace sharq_prepare needs for T rows (0 for MXFP4). */
 SHARQ_API size_t sharq_prepare_workspace_size(int64_t T, int64_t K, int32_t fmt);

@@ -46,6 +46,7 @@ def lib() -> ctypes.CDLL:
         p, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
                                 ctypes.c_size_t)
         L.sharq_abi_version.restype = ctypes.c_int
+        L.sharq_last_hip_error.restype = ctypes.c_int
         L.sharq_status_string.argtypes = [ctypes.c_int]
         L.sharq_status_string.restype = ctypes.c_char_p
         L.sharq_prepare_workspace_size.argtypes = [i64, i64, i32]
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
 def _check(status: int, what: str):
     if status != 0:
         msg = lib().sharq_status_string(status).decode()
+        if status == 8:  # SHARQ_ERR_HIP
+            msg += f", hipError {lib().sharq_last_hip_error()}"
         raise SharqError(f"{what}: status {status} ({msg})")
 
 

@@ -6,6 +6,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
+#include <cstdlib>
+
 #include "kernels.h"
 
 using namespace sharq;
@@ -22,13 +25,41 @@ int block_of(int32_t fmt) { return fmt == SHARQ_MXFP4 ? 32 : 16; }
 
 bool valid_fmt(int32_t fmt) { return fmt == SHARQ_MXFP4 || fmt == SHARQ_NVFP4; }
 
-sharq_status hip_status(hipError_t e) { return e == hipSuccess ? SHARQ_OK : SHARQ_ERR_HIP; }
+// hipError_t of this thread's most recent entry-point call that reached HIP.
+thread_local int g_last_hip_error = 0;
+
+bool debug_mode() {
+    const char *v = std::getenv("SHARQ_DEBUG");
+    return v != nullptr && v[0] == '1' && v[1] == '\0';
+}
+
+// Status of an entry point's launches on `st`.  With SHARQ_DEBUG=1 the call
+// also waits for them (unless the stream is being captured into a graph, where
+// waiting is not allowed) and reports any error the kernels raised, naming the
+// entry point on stderr.
+sharq_status finish(const char *what, hipError_t e, hipStream_t st) {
+    const bool debug = debug_mode();
+    if (e == hipSuccess && debug) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(st, &cs);
+        if (e == hipSuccess && cs == hipStreamCaptureStatusNone) {
+            e = hipStreamSynchronize(st);
+            if (e == hipSuccess) e = hipGetLastError();
+        }
+    }
+    g_last_hip_error = (int)e;
+    if (e == hipSuccess) return SHARQ_OK;
+    if (debug) std::fprintf(stderr, "sharq: %s: %s\n", what, hipGetErrorString(e));
+    return SHARQ_ERR_HIP;
+}
 
 }  // namespace
 
 extern "C" {
 
 int sharq_abi_version(void) { return SHARQ_ABI_VERSION; }
+
+int sharq_last_hip_error(void) { return g_last_hip_error; }
 
 const char *sharq_status_string(int status) {
     switch (status) {
@@ -123,7 +154,8 @@ sharq_status sharq_prepare(const void *x, int32_t x_dtype, int64_t T, int64_t K,
                                         b_scales, r_codes, r_scales, global_scale, true, workspace,
                                         workspace_bytes, a);
     if (s != SHARQ_OK || T == 0) return s;
-    return hip_status(launch_prepare(a, workspace, static_cast<hipStream_t>(stream)));
+    return finish("sharq_prepare", launch_prepare(a, workspace, static_cast<hipStream_t>(stream)),
+                  static_cast<hipStream_t>(stream));
 }
 
 sharq_status sharq_prepare_noalloc(const void *x, int32_t x_dtype, int64_t T, int64_t K, int64_t ldx,
@@ -135,7 +167,8 @@ sharq_status sharq_prepare_noalloc(const void *x, int32_t x_dtype, int64_t T, in
     const sharq_status s = prepare_args(x, x_dtype, T, K, ldx, norm, gamma, beta, eps, n, m, fmt, mask, b_codes,
                                         b_scales, r_codes, r_scales, global_scale, false, nullptr, 0, a);
     if (s != SHARQ_OK || T == 0) return s;
-    return hip_status(launch_prepare_noalloc(a, static_cast<hipStream_t>(stream)));
+    return finish("sharq_prepare_noalloc", launch_prepare_noalloc(a, static_cast<hipStream_t>(stream)),
+                  static_cast<hipStream_t>(stream));
 }
 
 sharq_status sharq_prepare_swiglu(const float *gate_up, int64_t T, int64_t K, int64_t ld, int32_t n, int32_t m,
@@ -173,7 +206,8 @@ sharq_status sharq_prepare_swiglu(const float *gate_up, int64_t T, int64_t K, in
     a.off32 = K % 128 == 0 && T * (K / 2) < ((int64_t)1 << 32);
     a.gu = gate_up;
     a.ldgu = ld;
-    return hip_status(launch_prepare_swiglu(a, workspace, static_cast<hipStream_t>(stream)));
+    return finish("sharq_prepare_swiglu", launch_prepare_swiglu(a, workspace, static_cast<hipStream_t>(stream)),
+                  static_cast<hipStream_t>(stream));
 }
 
 size_t sharq_quantize_weight_workspace_size(int64_t experts, int64_t nout, int64_t K, int32_t fmt) {
@@ -208,7 +242,8 @@ sharq_status sharq_quantize_weight(const void *w, int32_t w_dtype, int64_t exper
     a.codes = codes;
     a.scales = scales;
     a.global_scale = global_scale;
-    return hip_status(launch_quantize_weight(a, workspace, static_cast<hipStream_t>(stream)));
+    return finish("sharq_quantize_weight", launch_quantize_weight(a, workspace, static_cast<hipStream_t>(stream)),
+                  static_cast<hipStream_t>(stream));
 }
 
 size_t sharq_linear_workspace_size(int64_t rows, int64_t K, int64_t nout, int64_t experts,
@@ -268,7 +303,8 @@ sharq_status sharq_linear(const uint8_t *b_codes, const uint8_t *b_scales, const
     a.y_vec = aligned(y, 4 * ysize) && ldy % 4 == 0;
     a.ksplit_tiles = 0;
     a.split_stride = 0;
-    return hip_status(launch_linear(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+    return finish("sharq_linear", launch_linear(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream)),
+                  static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

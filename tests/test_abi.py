@@ -47,10 +47,21 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.sharq_abi_version() == 4
+    assert L.sharq_abi_version() == 5
     for code in range(9):
         assert L.sharq_status_string(code)
     assert L.sharq_status_string(99) == b"unknown status"
+
+
+def test_last_hip_error_untouched_by_validation(L, monkeypatch):
+    """Calls rejected before any HIP call leave the last HIP error at its
+    previous value (no HIP call has run in this process), check mode or not."""
+    assert L.sharq_last_hip_error() == 0
+    for debug in ("0", "1"):
+        monkeypatch.setenv("SHARQ_DEBUG", debug)
+        assert prep(L, x=None) == NULL
+        assert lin(L, bc=None) == NULL
+        assert L.sharq_last_hip_error() == 0
 
 
 FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: validation fails first

@@ -12,11 +12,12 @@
 // the four lanes of a DPP quad and an NVFP4 block (16) a lane pair.  The row
 // is read from HBM exactly once; everything else happens in registers.
 //
-//   MX + norm, K <= 8192:  a workgroup of four waves per row; the row stays
-//                          in registers across the FP64 norm reduction (whose
-//                          per-wave partials meet in LDS) and the
-//                          quantization pass, whose stores are buffer stores
-//                          at scalar + per-lane-constant offsets;
+//   MX + norm, K <= 8192:  a workgroup of two (K <= 2048) or four waves per
+//                          row; the row stays in registers across the FP64
+//                          norm reduction (whose per-wave partials meet in
+//                          LDS) and the quantization pass, whose stores are
+//                          buffer stores at scalar + per-lane-constant
+//                          offsets;
 //   MX + norm, larger K:   one wave per row, the quantization pass re-reads
 //                          the row (L2 hit);
 //   no norm:               tasks are (row, group of chunks), fully parallel;
@@ -32,7 +33,7 @@ namespace sharq {
 
 constexpr int kPrepWaves = 4;        // waves per workgroup
 constexpr int kChunk = 512;          // elements per wave-wide 128-bit load
-constexpr int kStreamChunks = 2;     // chunks per task when rows are split (measured: 2 beats 4 and 8)
+constexpr int kStreamChunks = 1;     // chunks per task when rows are split (measured: 1 beats 2, 4 and 8)
 
 struct RowStats {  // per-row statistics written by the NVFP4 pre-pass
     float r, mu, amax, pad;
@@ -607,17 +608,21 @@ __device__ __forceinline__ void swiglu8(const float *row, int64_t K, int64_t e0,
     v[6] = silu_times(g1.z, u1.z); v[7] = silu_times(g1.w, u1.w);
 }
 
-// (row, kStreamChunks chunks) tasks, one per wave.
+// (row, kSwiChunks chunks) tasks, one per wave: one 512-element chunk per
+// task (measured on MI355X at 2048 x 14336: 4% faster than two, 10% faster
+// than four; more waves in flight hide the FP32 loads better).
+constexpr int kSwiChunks = 1;
+
 template <int FMT, int M, int FAST24>
 __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_swiglu(PrepArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t K = a.K;
-    const int64_t tpr = (K + (int64_t)kChunk * kStreamChunks - 1) / ((int64_t)kChunk * kStreamChunks);
+    const int64_t tpr = (K + (int64_t)kChunk * kSwiChunks - 1) / ((int64_t)kChunk * kSwiChunks);
     const int64_t task = xcd_block(blockIdx.x, gridDim.x) * kPrepWaves + wave;
     const int64_t row = task / tpr;
     if (row >= a.T) return;
-    const int64_t c0 = (task - row * tpr) * kStreamChunks;
+    const int64_t c0 = (task - row * tpr) * kSwiChunks;
     const float *gr = a.gu + row * a.ldgu;
     const LaneOff lo = lane_offsets<FMT>(a, lane);
     float G = 1.0f;
@@ -627,7 +632,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_swiglu(PrepArgs a) 
         rG6 = 1.0 / (double)__fmul_rn(6.0f, G);
     }
 #pragma unroll
-    for (int c = 0; c < kStreamChunks; c++) {
+    for (int c = 0; c < kSwiChunks; c++) {
         const int64_t e0 = (c0 + c) * kChunk + lane * 8;
         if (e0 < K) {
             float v[8];
@@ -827,15 +832,16 @@ __global__ __launch_bounds__(1024) void k_nv_tensor_scale(const RowStats *stats,
 __global__ void k_fill_f32(float *p, float v) { *p = v; }
 
 // ---------------------------------------------------------------- launcher
-// The rows kernel for CPW chunks per wave: full rows (K = CPW * 4 * 512)
-// on the 2:4 path get the instantiation without bounds checks.
-template <bool BF16, int NORM, int M, int FAST24, int CPW>
+// The rows kernel for NWG waves of CPW chunks each: full rows
+// (K = CPW * NWG * 512) on the 2:4 path get the instantiation without bounds
+// checks.
+template <bool BF16, int NORM, int M, int FAST24, int CPW, int NWG>
 static void launch_rows(const PrepArgs &a, bool full, hipStream_t st) {
-    const dim3 grid((unsigned)round_up8(a.T)), blk(kPrepWaves * kWave);
+    const dim3 grid((unsigned)round_up8(a.T)), blk(NWG * kWave);
     if (FAST24 && full)
-        hipLaunchKernelGGL((k_prep_mx_rows<BF16, NORM, M, FAST24, CPW, kPrepWaves, true>), grid, blk, 0, st, a);
+        hipLaunchKernelGGL((k_prep_mx_rows<BF16, NORM, M, FAST24, CPW, NWG, true>), grid, blk, 0, st, a);
     else
-        hipLaunchKernelGGL((k_prep_mx_rows<BF16, NORM, M, FAST24, CPW, kPrepWaves, false>), grid, blk, 0, st, a);
+        hipLaunchKernelGGL((k_prep_mx_rows<BF16, NORM, M, FAST24, CPW, NWG, false>), grid, blk, 0, st, a);
 }
 
 template <bool BF16, int NORM, int FMT, int M, int FAST24>
@@ -848,11 +854,16 @@ static hipError_t launch_prep_t(const PrepArgs &a, void *ws, hipStream_t st) {
             const dim3 grid((unsigned)round_up8((a.T + kPrepWaves - 1) / kPrepWaves));
             hipLaunchKernelGGL((k_prep_mx_2pass<BF16, NORM, M, FAST24>), grid, blk, 0, st, a);
         } else if (K <= kWg) {
-            launch_rows<BF16, NORM, M, FAST24, 1>(a, K == kWg, st);
+            // rows of up to 2048: two waves of two chunks (measured on MI355X
+            // at 4096 x 2048: 10% faster than four waves of one chunk, as fast
+            // as one wave of four)
+            launch_rows<BF16, NORM, M, FAST24, 2, 2>(a, K == kWg, st);
         } else if (K <= 2 * kWg) {
-            launch_rows<BF16, NORM, M, FAST24, 2>(a, K == 2 * kWg, st);
+            // rows of up to 4096: four waves of two chunks (two waves of four
+            // were 5% slower at 2048 x 4096, eight waves of one 12% slower)
+            launch_rows<BF16, NORM, M, FAST24, 2, kPrepWaves>(a, K == 2 * kWg, st);
         } else {
-            launch_rows<BF16, NORM, M, FAST24, 4>(a, K == 4 * kWg, st);
+            launch_rows<BF16, NORM, M, FAST24, 4, kPrepWaves>(a, K == 4 * kWg, st);
         }
         if (a.global_scale) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, a.global_scale, 1.0f);
         return hipGetLastError();
@@ -942,7 +953,7 @@ static hipError_t launch_swiglu_t(const PrepArgs &a, void *ws, hipStream_t st) {
     } else if (a.global_scale) {
         hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, a.global_scale, 1.0f);
     }
-    const int64_t tpr = (a.K + (int64_t)kChunk * kStreamChunks - 1) / ((int64_t)kChunk * kStreamChunks);
+    const int64_t tpr = (a.K + (int64_t)kChunk * kSwiChunks - 1) / ((int64_t)kChunk * kSwiChunks);
     const int64_t tasks = a.T * tpr;
     const dim3 grid((unsigned)round_up8((tasks + kPrepWaves - 1) / kPrepWaves));
     hipLaunchKernelGGL((k_prep_swiglu<FMT, M, FAST24>), grid, blk, 0, st, a);

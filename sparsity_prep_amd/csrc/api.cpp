@@ -303,6 +303,7 @@ sharq_status sharq_linear(const uint8_t *b_codes, const uint8_t *b_scales, const
     a.y_vec = aligned(y, 4 * ysize) && ldy % 4 == 0;
     a.ksplit_tiles = 0;
     a.split_stride = 0;
+    a.xcd_band = 0;
     return finish("sharq_linear", launch_linear(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream)),
                   static_cast<hipStream_t>(stream));
 }

@@ -281,6 +281,23 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t wg, int64_t ntiles) {
     return (wg % 8) * per_xcd + wg / 8;
 }
 
+// Launches of several rounds of tiles: XCD x owns a band of RB row tiles and
+// 1/G of the column tiles (G = 8 / bands, bands = n_mtiles / RB), row tiles
+// fastest, so one band's token rows serve every column tile the XCD runs
+// while its weight columns stream through (on MI355X at 2048 x 28672 x 4096,
+// bands of two 256-row tiles: L2 hits up, 3% faster than column runs).
+// Returns the tile index col * n_mtiles + row, or n_mtiles * n_ntiles past
+// the XCD's share; the launcher sizes the grid as 8 * RB * ceil(n_ntiles / G).
+__device__ __forceinline__ int64_t xcd_tile_band(int64_t wg, int64_t n_mtiles, int64_t n_ntiles, int64_t RB) {
+    const int64_t G = 8 / (n_mtiles / RB);
+    const int64_t x = wg % 8, q = wg / 8;
+    const int64_t per = (n_ntiles + G - 1) / G;
+    const int64_t col = (x % G) * per + q / RB;
+    const int64_t row = (x / G) * RB + q % RB;
+    if (q / RB >= per || col >= n_ntiles) return n_mtiles * n_ntiles;
+    return col * n_mtiles + row;
+}
+
 // WGM x WGN waves: WGM along the token rows, WGN along the weight rows; NS
 // LDS stages (2 or 3).
 // LSPLIT (three stages only): the last LSPLIT of a stage's direct loads are
@@ -778,7 +795,8 @@ void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles, int64_t n_beg
     using L = typename DualGemm<FMT, BM, BN, WGM, WGN, NS, LSPLIT, RPS>::L;
     static_assert(L::BYTES * NS * OCC <= kLdsBytes, "stages do not fit the CU's LDS");
     if constexpr (!GROUPED) {
-        const int64_t t = xcd_tile(blockIdx.x, n_ntiles * n_mtiles);
+        const int64_t t = a.xcd_band > 0 ? xcd_tile_band(blockIdx.x, n_mtiles, n_ntiles, a.xcd_band)
+                                         : xcd_tile(blockIdx.x, n_ntiles * n_mtiles);
         if (t >= n_ntiles * n_mtiles) return;
         TileRows tr;
         tr.m0 = (t % n_mtiles) * BM;
@@ -965,6 +983,8 @@ static hipError_t launch_prefill(const LinearArgs &a, hipStream_t st, int64_t n_
     const int64_t n_ntiles = (n_end - n_begin + BN - 1) / BN;
     int64_t blocks;
     int64_t n_mtiles = 0;
+    LinearArgs ab = a;
+    ab.xcd_band = 0;
     if (a.offsets && persistent) {
         blocks = (int64_t)((device_cus() + 7) / 8) * 8 * OCC;
         n_mtiles = -1;
@@ -973,11 +993,21 @@ static hipError_t launch_prefill(const LinearArgs &a, hipStream_t st, int64_t n_
     } else {
         n_mtiles = (a.rows + BM - 1) / BM;
         blocks = ((n_ntiles * n_mtiles + 7) / 8) * 8;
+        // MXFP4 launches of more than one round: XCD bands of two row tiles,
+        // when 2 or 4 bands split the rows (each band then shared by 4 or 2
+        // XCDs, so no XCD streams the whole weight)
+        constexpr int64_t RB = 2;
+        if (FMT == kFmtMx && a.ksplit_tiles == 0 && n_ntiles * n_mtiles > (int64_t)device_cus() * OCC &&
+            (n_mtiles == 2 * RB || n_mtiles == 4 * RB)) {
+            const int64_t G = 8 / (n_mtiles / RB);
+            ab.xcd_band = RB;
+            blocks = 8 * RB * ((n_ntiles + G - 1) / G);
+        }
     }
     const unsigned splits = a.ksplit_tiles > 0 ? (unsigned)(a.K / kTileK / a.ksplit_tiles) : 1u;
     hipLaunchKernelGGL((k_dual_gemm<FMT, BM, BN, WGM, WGN, NS, OCC, LSPLIT, RPS, GROUPED>), dim3((unsigned)blocks, splits),
                        dim3(WGM * WGN * 64), 0,
-                       st, a, n_ntiles, n_mtiles, n_begin);
+                       st, ab, n_ntiles, n_mtiles, n_begin);
     return hipGetLastError();
 }
 

@@ -83,6 +83,10 @@ struct LinearArgs {
     // K split (dense products only): grid row s multiplies K tiles
     // [s*ksplit_tiles, (s+1)*ksplit_tiles) into y + s*split_stride; 0 = no split
     int64_t ksplit_tiles, split_stride;
+    // dense tile order: 0 = each XCD takes a run of column tiles (all row
+    // tiles of each), RB > 0 = each XCD takes a band of RB row tiles and a
+    // share of the column tiles (set by the launcher)
+    int64_t xcd_band;
 };
 
 hipError_t launch_linear(const LinearArgs &a, void *ws, size_t ws_bytes, hipStream_t st);

@@ -278,7 +278,8 @@ LINEAR_CASES = [
     (0, 16, 256, 256), (0, 300, 640, 272), (0, 513, 1024, 520), (0, 1, 512, 64), (0, 5, 768, 48),
     (0, 17, 1280, 100), (0, 64, 4096, 256), (0, 65, 384, 1000), (0, 2, 14336, 64),
     (0, 3, 8320, 40), (0, 48, 4480, 1000),  # small batch: 17 / 9 K chunks over the workgroup's 8 waves
-    (0, 2048, 256, 16384),  # large enough that 256x256 tiles are chosen
+    (0, 2048, 256, 16384),  # 256x256 tiles, two rounds in XCD bands of two row tiles (4 bands)
+    (0, 1000, 128, 33000),  # two full rounds in 2 bands (ragged last row tile), remaining columns split off
     (0, 1000, 384, 12200),  # 256x192 tiles (one full round), ragged rows and columns
     (0, 300, 128, 200), (0, 5, 128, 40), (1, 130, 128, 96),  # K = 128: a single stage / chunk
     (0, 64, 1024, 2128), (0, 40, 1024, 3000), (0, 9, 1024, 8240),  # few rows as 64x64 tiles

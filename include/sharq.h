@@ -35,6 +35,24 @@
  *              scale 2^(byte-127), exponent floor(log2 amax) - 2 (OCP MX v1.0).
  *       NVFP4  E2M1 + one E4M3 scale byte per 16 elements along K, times one
  *              FP32 scale per tensor, amax(tensor)/2688.
+ *       NVFP4_SP24  NVFP4 whose backbone is stored in the compressed form of
+ *              gfx950's 2:4 sparse f16 matrix instruction, so that products
+ *              run the backbone on it (2:4 masks only, K % 128 == 0,
+ *              T*K/2 < 2^32).  Per row and K tile (elements e = 0..127 of
+ *              the tile) the backbone takes 48 bytes: bytes 4c..4c+3 hold
+ *              chunk c = 4p + 2h + u (p, h, u in {0, 1}): the kept codes of
+ *              elements 32p + 16u + 8h + [0, 8), then of
+ *              64 + 32p + 16u + 8h + [0, 8), two per group of four in
+ *              ascending position, code v of the chunk in nibble v % 2 of
+ *              byte v / 2; bytes 32 + 4(2p + h) .. +3 hold in bits
+ *              16u + 2v, 16u + 2v + 1 the position (0..3) within its group
+ *              of code v of chunk 4p + 2h + u.  These 48-byte rows are
+ *              K-tiled like the other arrays (T*K*3/8 bytes).  The tile's
+ *              eight backbone block scales are stored in the order of blocks
+ *              0, 1, 4, 5, 2, 3, 6, 7 (block b = elements 16b..16b+15).  The
+ *              residual, the mask and the tensor scale are those of NVFP4;
+ *              weights are NVFP4 (sharq_quantize_weight treats NVFP4_SP24 as
+ *              NVFP4).
  *   - The N:M mask keeps, in every group of M consecutive elements along K,
  *     the N elements of largest magnitude; equal magnitudes favour the lower
  *     index.  Mask bitmap: bit k%8 of byte k/8 of the row.
@@ -60,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 5
+#define SHARQ_ABI_VERSION 6
 
 #if defined(__GNUC__)
 #define SHARQ_API __attribute__((visibility("default")))
@@ -86,7 +104,7 @@ typedef enum {
 
 typedef enum { SHARQ_F16 = 0, SHARQ_BF16 = 1, SHARQ_F32 = 2 } sharq_dtype;
 typedef enum { SHARQ_NORM_NONE = 0, SHARQ_NORM_RMS = 1, SHARQ_NORM_LAYER = 2 } sharq_norm;
-typedef enum { SHARQ_MXFP4 = 0, SHARQ_NVFP4 = 1 } sharq_format;
+typedef enum { SHARQ_MXFP4 = 0, SHARQ_NVFP4 = 1, SHARQ_NVFP4_SP24 = 2 } sharq_format;
 
 /* Version of this ABI (SHARQ_ABI_VERSION). */
 SHARQ_API int sharq_abi_version(void);
@@ -122,10 +140,14 @@ SHARQ_API size_t sharq_prepare_workspace_size(int64_t T, int64_t K, int32_t fmt)
  *                optional for LAYER (NULL = 0), both ignored for NONE
  *   eps          added to the mean square / variance
  *   n, m         N:M mask, 0 <= n <= m, m in {1,2,4,8,16}, K % m == 0
- *   fmt          SHARQ_MXFP4 (K % 32 == 0) or SHARQ_NVFP4 (K % 16 == 0)
+ *   fmt          SHARQ_MXFP4 (K % 32 == 0), SHARQ_NVFP4 (K % 16 == 0) or
+ *                SHARQ_NVFP4_SP24 (n = 2, m = 4, K % 128 == 0, T*K/2 < 2^32;
+ *                SHARQ_ERR_NM / SHARQ_ERR_SHAPE otherwise)
  *   mask         [T][K/8] row-major bitmap or NULL (not written)
  *   b_codes      T*K/2 bytes, backbone E2M1 codes, K-tiled, 4-byte aligned
+ *                (NVFP4_SP24: T*K*3/8 bytes in the compressed form)
  *   b_scales     T*K/B bytes, backbone block scales (E8M0 or E4M3), K-tiled
+ *                (NVFP4_SP24: in its block order)
  *   r_codes      T*K/2 bytes, residual codes, K-tiled, 4-byte aligned
  *   r_scales     T*K/B bytes, residual block scales, K-tiled
  *   global_scale one device float: NVFP4 tensor scale (written); MXFP4: may
@@ -234,9 +256,12 @@ SHARQ_API size_t sharq_linear_workspace_size(int64_t rows, int64_t K, int64_t no
  * in FP32 accumulation (stored as FP32, or rounded to BF16 / F16), with
  * NVFP4 tensor scales applied as
  * x_global_scale * w_global_scale[e] in the epilogue.  Both paths read the
- * same weight codes and scales.  The backbone is multiplied densely on its
- * zero-filled form (gfx950 has no block-scaled sparse FP4 matrix
- * instruction).
+ * same weight codes and scales.  MXFP4 and NVFP4 multiply the backbone
+ * densely on its zero-filled form (gfx950 has no block-scaled sparse FP4
+ * matrix instruction); NVFP4_SP24 activations (weights in NVFP4) multiply
+ * their compressed backbone with the 2:4 sparse f16 instruction on exactly
+ * dequantized values.  The three give the same products up to the order of
+ * the FP32 additions.
  *
  *   b_codes, b_scales, r_codes, r_scales  prepared activations, T rows,
  *                as written by sharq_prepare (K-tiled)

@@ -331,3 +331,80 @@ def unpack_codes(packed: np.ndarray) -> np.ndarray:
 def unpack_mask(mask: np.ndarray) -> np.ndarray:
     """[.., K/8] bytes -> [.., K] booleans (bit k%8 of byte k/8)."""
     return np.unpackbits(mask, axis=-1, bitorder="little").astype(bool)
+
+
+# ---------------------------------------------------------------- compressed 2:4 backbone
+
+def sp24_pack(prep: Prepared):
+    """The NVFP4 backbone of `prep` (2:4 mask, K % 128 == 0) in the compressed
+    form that gfx950's 2:4 sparse f16 matrix instruction takes (the library's
+    NVFP4_SP24 format).  A re-arrangement of the oracle's own outputs, written
+    from the layout's definition: per row and K tile of 128 elements, 48 bytes
+    -- bytes 4c..4c+3 hold chunk c = 4p + 2h + u, the kept codes of elements
+    32p + 16u + 8h + [0, 8) and then of 64 + 32p + 16u + 8h + [0, 8), two per
+    group of four in ascending position (code v in nibble v % 2 of byte
+    v // 2); bytes 32 + 4(2p + h) .. +3 hold, at bits 16u + 2v, the position
+    of code v of chunk 4p + 2h + u within its group of four.  Block scales of
+    a tile in the order of blocks 0, 1, 4, 5, 2, 3, 6, 7.
+
+    Returns (records [rows, K/128, 48] uint8, scales [rows, K/16] uint8)."""
+    codes = unpack_codes(prep.b_codes)
+    keep = unpack_mask(prep.mask)
+    rows, K = codes.shape
+    if K % 128:
+        raise ValueError("the compressed backbone needs whole K tiles")
+    rec = np.zeros((rows, K // 128, 48), np.uint8)
+    r = np.arange(rows)
+    for t in range(K // 128):
+        for p in (0, 1):
+            for h in (0, 1):
+                for u in (0, 1):
+                    c = 4 * p + 2 * h + u
+                    vals, pos = [], []
+                    for base in (32 * p + 16 * u + 8 * h, 64 + 32 * p + 16 * u + 8 * h):
+                        for g in (0, 1):
+                            e0 = t * 128 + base + 4 * g
+                            k4 = keep[:, e0:e0 + 4]
+                            if not (k4.sum(axis=1) == 2).all():
+                                raise ValueError("the compressed backbone needs exactly two kept per group of four")
+                            first = np.argsort(~k4, axis=1, kind="stable")[:, :2]  # kept positions, ascending
+                            for j in (0, 1):
+                                vals.append(codes[r, e0 + first[:, j]])
+                                pos.append(first[:, j])
+                    for b in range(4):
+                        rec[:, t, 4 * c + b] = vals[2 * b] | (vals[2 * b + 1] << 4)
+                    word = np.zeros(rows, np.uint32)
+                    for v in range(8):
+                        word |= pos[v].astype(np.uint32) << np.uint32(16 * u + 2 * v)
+                    off = 32 + 4 * (2 * p + h)
+                    for b in range(4):
+                        rec[:, t, off + b] |= ((word >> np.uint32(8 * b)) & np.uint32(0xFF)).astype(np.uint8)
+    order = np.array([0, 1, 4, 5, 2, 3, 6, 7])
+    sc = prep.b_scales.reshape(rows, K // 128, 8)[:, :, order].reshape(rows, K // 16)
+    return rec, sc
+
+
+def sp24_unpack(rec: np.ndarray, K: int):
+    """Inverse of sp24_pack's code layout: dense backbone codes [rows, K/2]
+    (zero at the positions not kept) and the mask bitmap [rows, K/8]."""
+    rows = rec.shape[0]
+    codes = np.zeros((rows, K), np.uint8)
+    keep = np.zeros((rows, K), bool)
+    r = np.arange(rows)
+    for t in range(K // 128):
+        for c in range(8):
+            p, h, u = c >> 2, (c >> 1) & 1, c & 1
+            word = np.zeros(rows, np.uint32)
+            off = 32 + 4 * (2 * p + h)
+            for b in range(4):
+                word |= rec[:, t, off + b].astype(np.uint32) << np.uint32(8 * b)
+            for v in range(8):
+                base = (32 * p + 16 * u + 8 * h) if v < 4 else (64 + 32 * p + 16 * u + 8 * h)
+                g = (v % 4) // 2
+                position = ((word >> np.uint32(16 * u + 2 * v)) & np.uint32(3)).astype(np.int64)
+                e = t * 128 + base + 4 * g + position
+                nib = (rec[:, t, 4 * c + v // 2] >> (4 * (v % 2))) & 0xF
+                codes[r, e] = nib
+                keep[r, e] = True
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, np.packbits(keep, axis=1, bitorder="little")

@@ -22,7 +22,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsharq.so")
 
-MXFP4, NVFP4 = 0, 1
+MXFP4, NVFP4, NVFP4_SP24 = 0, 1, 2  # NVFP4_SP24: NVFP4, backbone in the 2:4 compressed form
 NORM_NONE, NORM_RMS, NORM_LAYER = 0, 1, 2
 _F16, _BF16, _F32 = 0, 1, 2
 _DTYPE = {torch.float16: _F16, torch.bfloat16: _BF16}
@@ -100,7 +100,7 @@ def block_size(fmt: int) -> int:
 class Prepared:
     """Output of the fused preparation operator (on the GPU).  Codes and
     scales are K-tiled flat byte arrays (see layout.ktile_to_rows)."""
-    b_codes: torch.Tensor     # uint8 [T*K/2]
+    b_codes: torch.Tensor     # uint8 [T*K/2] (NVFP4_SP24: [T*K*3/8], the compressed form)
     b_scales: torch.Tensor    # uint8 [T*K/B]
     r_codes: torch.Tensor     # uint8 [T*K/2]
     r_scales: torch.Tensor    # uint8 [T*K/B]
@@ -127,11 +127,12 @@ class QWeight:
 def alloc_prepared(T: int, K: int, fmt: int, device, with_mask: bool = True) -> Prepared:
     B = block_size(fmt)
     u8 = dict(dtype=torch.uint8, device=device)
+    bb = T * K * 3 // 8 if fmt == NVFP4_SP24 else T * K // 2
     return Prepared(
-        b_codes=torch.empty(T * K // 2, **u8), b_scales=torch.empty(T * K // B, **u8),
+        b_codes=torch.empty(bb, **u8), b_scales=torch.empty(T * K // B, **u8),
         r_codes=torch.empty(T * K // 2, **u8), r_scales=torch.empty(T * K // B, **u8),
         mask=torch.empty((T, K // 8), **u8) if with_mask else None,
-        global_scale=torch.empty(1, dtype=torch.float32, device=device) if fmt == NVFP4 else None,
+        global_scale=torch.empty(1, dtype=torch.float32, device=device) if fmt != MXFP4 else None,
         T=T, K=K, fmt=fmt)
 
 
@@ -195,7 +196,10 @@ def prepare_swiglu(gate_up: torch.Tensor, K: int, n: int = 2, m: int = 4, fmt: i
 def quantize_weight(w: torch.Tensor, fmt: int = MXFP4) -> QWeight:
     """RTN quantization of W[nout, K] or W[E, nout, K] into one FP4 payload.
     Rows may be strided (a column slice of a wider matrix): unit element
-    stride, row stride ldw, expert stride nout * ldw."""
+    stride, row stride ldw, expert stride nout * ldw.  NVFP4_SP24 names the
+    NVFP4 payload (weights are never compressed)."""
+    if fmt == NVFP4_SP24:
+        fmt = NVFP4
     if w.dim() == 2:
         w = w.unsqueeze(0)
     if w.dim() != 3 or w.dtype not in _DTYPE or w.stride(2) != 1:
@@ -223,7 +227,7 @@ def linear(prep: Prepared, wq: QWeight, group_offsets: Optional[torch.Tensor] = 
     """Y = deq(backbone) W^T + deq(residual) W^T, accumulated in float32 and
     stored as float32 (default) or rounded to bfloat16 / float16 (the dtype
     of `out` when given), optionally grouped by expert."""
-    if prep.K != wq.K or prep.fmt != wq.fmt:
+    if prep.K != wq.K or (NVFP4 if prep.fmt == NVFP4_SP24 else prep.fmt) != wq.fmt:
         raise SharqError("prepared activations and weight disagree on K or format")
     if rows is None:
         rows = row_index.numel() if row_index is not None else prep.T
@@ -235,7 +239,7 @@ def linear(prep: Prepared, wq: QWeight, group_offsets: Optional[torch.Tensor] = 
     elif (out.dim() != 2 or out.dtype not in _OUT_DTYPE or out.shape[0] < rows or out.shape[1] != wq.nout
           or out.stride(1) != 1):
         raise SharqError("out must be a float32/bfloat16/float16 [rows, nout] tensor with unit column stride")
-    ws = _workspace(lib().sharq_linear_workspace_size(rows, wq.K, wq.nout, wq.E, wq.fmt), dev)
+    ws = _workspace(lib().sharq_linear_workspace_size(rows, wq.K, wq.nout, wq.E, prep.fmt), dev)
     st = lib().sharq_linear(
         _ptr(prep.b_codes), _ptr(prep.b_scales), _ptr(prep.r_codes), _ptr(prep.r_scales),
         _ptr(prep.global_scale), prep.T, prep.K, prep.fmt, _ptr(wq.codes), _ptr(wq.scales),

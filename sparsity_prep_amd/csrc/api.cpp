@@ -23,7 +23,22 @@ static_assert(SHARQ_NOALLOC_MAX_ROWS == kNoallocRows, "header and library agree 
 
 int block_of(int32_t fmt) { return fmt == SHARQ_MXFP4 ? 32 : 16; }
 
-bool valid_fmt(int32_t fmt) { return fmt == SHARQ_MXFP4 || fmt == SHARQ_NVFP4; }
+bool valid_fmt(int32_t fmt) { return fmt == SHARQ_MXFP4 || fmt == SHARQ_NVFP4 || fmt == SHARQ_NVFP4_SP24; }
+
+bool is_nv(int32_t fmt) { return fmt == SHARQ_NVFP4 || fmt == SHARQ_NVFP4_SP24; }
+
+// quantization format of the kernels (the compressed backbone is a store
+// option of NVFP4)
+int kernel_fmt(int32_t fmt) { return fmt == SHARQ_MXFP4 ? kFmtMx : kFmtNv; }
+
+// NVFP4_SP24 preparation: the 2:4 mask, whole K tiles and 32-bit store
+// offsets (the compressed store path)
+sharq_status sp24_shape(int32_t fmt, int64_t T, int64_t K, int32_t n, int32_t m) {
+    if (fmt != SHARQ_NVFP4_SP24) return SHARQ_OK;
+    if (n != 2 || m != 4) return SHARQ_ERR_NM;
+    if (K % 128 != 0 || T * (K / 2) >= ((int64_t)1 << 32)) return SHARQ_ERR_SHAPE;
+    return SHARQ_OK;
+}
 
 // hipError_t of this thread's most recent entry-point call that reached HIP.
 thread_local int g_last_hip_error = 0;
@@ -78,7 +93,7 @@ const char *sharq_status_string(int status) {
 
 size_t sharq_prepare_workspace_size(int64_t T, int64_t K, int32_t fmt) {
     (void)K;
-    return prepare_workspace_bytes(T, fmt);
+    return prepare_workspace_bytes(T, kernel_fmt(fmt));
 }
 
 }  // extern "C"
@@ -101,19 +116,20 @@ sharq_status prepare_args(const void *x, int32_t x_dtype, int64_t T, int64_t K, 
     if (T >= kMaxPrepRows) return SHARQ_ERR_SHAPE;  // one workgroup per row must fit the grid
     if (m != 1 && m != 2 && m != 4 && m != 8 && m != 16) return SHARQ_ERR_NM;
     if (n < 0 || n > m || K % m != 0) return SHARQ_ERR_NM;
+    if (const sharq_status sp = sp24_shape(fmt, T, K, n, m); sp != SHARQ_OK) return sp;
     if (T == 0) return SHARQ_OK;
     if (!x || !b_codes || !b_scales || !r_codes || !r_scales) return SHARQ_ERR_NULL;
     if (norm != SHARQ_NORM_NONE && !gamma) return SHARQ_ERR_NULL;
-    if (fmt == SHARQ_NVFP4 && !global_scale) return SHARQ_ERR_NULL;
+    if (is_nv(fmt) && !global_scale) return SHARQ_ERR_NULL;
     if (!aligned(x, 16) || (ldx * 2) % 16 != 0) return SHARQ_ERR_ALIGN;
     if ((gamma && !aligned(gamma, 16)) || (beta && !aligned(beta, 16))) return SHARQ_ERR_ALIGN;
     if (!aligned(b_codes, 4) || !aligned(r_codes, 4)) return SHARQ_ERR_ALIGN;
     if (global_scale && !aligned(global_scale, 4)) return SHARQ_ERR_ALIGN;
     if (need_ws) {
-        const size_t need = prepare_workspace_bytes(T, fmt);
+        const size_t need = prepare_workspace_bytes(T, kernel_fmt(fmt));
         if (need > 0 && (!workspace || workspace_bytes < need)) return SHARQ_ERR_WORKSPACE;
         if (need > 0 && !aligned(workspace, 16)) return SHARQ_ERR_ALIGN;
-    } else if (fmt == SHARQ_NVFP4 && T > kNoallocRows) {
+    } else if (is_nv(fmt) && T > kNoallocRows) {
         return SHARQ_ERR_WORKSPACE;  // more rows than the built-in scratch holds
     }
 
@@ -128,7 +144,8 @@ sharq_status prepare_args(const void *x, int32_t x_dtype, int64_t T, int64_t K, 
     a.n = n;
     a.m = m;
     a.norm = norm;
-    a.fmt = fmt;
+    a.fmt = kernel_fmt(fmt);
+    a.sp = fmt == SHARQ_NVFP4_SP24;
     a.bf16 = x_dtype == SHARQ_BF16;
     a.mask = mask;
     a.b_codes = b_codes;
@@ -180,13 +197,14 @@ sharq_status sharq_prepare_swiglu(const float *gate_up, int64_t T, int64_t K, in
     if (T >= kMaxPrepRows) return SHARQ_ERR_SHAPE;
     if (m != 1 && m != 2 && m != 4 && m != 8 && m != 16) return SHARQ_ERR_NM;
     if (n < 0 || n > m || K % m != 0) return SHARQ_ERR_NM;
+    if (const sharq_status sp = sp24_shape(fmt, T, K, n, m); sp != SHARQ_OK) return sp;
     if (T == 0) return SHARQ_OK;
     if (!gate_up || !b_codes || !b_scales || !r_codes || !r_scales) return SHARQ_ERR_NULL;
-    if (fmt == SHARQ_NVFP4 && !global_scale) return SHARQ_ERR_NULL;
+    if (is_nv(fmt) && !global_scale) return SHARQ_ERR_NULL;
     if (!aligned(gate_up, 16) || (ld * 4) % 16 != 0) return SHARQ_ERR_ALIGN;
     if (!aligned(b_codes, 4) || !aligned(r_codes, 4)) return SHARQ_ERR_ALIGN;
     if (global_scale && !aligned(global_scale, 4)) return SHARQ_ERR_ALIGN;
-    const size_t need = prepare_workspace_bytes(T, fmt);
+    const size_t need = prepare_workspace_bytes(T, kernel_fmt(fmt));
     if (need > 0 && (!workspace || workspace_bytes < need)) return SHARQ_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace, 16)) return SHARQ_ERR_ALIGN;
 
@@ -196,7 +214,8 @@ sharq_status sharq_prepare_swiglu(const float *gate_up, int64_t T, int64_t K, in
     a.n = n;
     a.m = m;
     a.norm = SHARQ_NORM_NONE;
-    a.fmt = fmt;
+    a.fmt = kernel_fmt(fmt);
+    a.sp = fmt == SHARQ_NVFP4_SP24;
     a.mask = mask;
     a.b_codes = b_codes;
     a.b_scales = b_scales;
@@ -212,7 +231,7 @@ sharq_status sharq_prepare_swiglu(const float *gate_up, int64_t T, int64_t K, in
 
 size_t sharq_quantize_weight_workspace_size(int64_t experts, int64_t nout, int64_t K, int32_t fmt) {
     (void)K;
-    return quantize_weight_workspace_bytes(experts, nout, fmt);
+    return quantize_weight_workspace_bytes(experts, nout, kernel_fmt(fmt));
 }
 
 sharq_status sharq_quantize_weight(const void *w, int32_t w_dtype, int64_t experts, int64_t nout,
@@ -224,11 +243,11 @@ sharq_status sharq_quantize_weight(const void *w, int32_t w_dtype, int64_t exper
     if (experts < 1 || nout < 0 || K <= 0 || K % block_of(fmt) != 0 || ldw < K) return SHARQ_ERR_SHAPE;
     if (nout == 0) return SHARQ_OK;
     if (!w || !codes || !scales) return SHARQ_ERR_NULL;
-    if (fmt == SHARQ_NVFP4 && !global_scale) return SHARQ_ERR_NULL;
+    if (is_nv(fmt) && !global_scale) return SHARQ_ERR_NULL;
     if (!aligned(w, 16) || (ldw * 2) % 16 != 0 || !aligned(codes, 4) ||
         (global_scale && !aligned(global_scale, 4)))
         return SHARQ_ERR_ALIGN;
-    const size_t need = quantize_weight_workspace_bytes(experts, nout, fmt);
+    const size_t need = quantize_weight_workspace_bytes(experts, nout, kernel_fmt(fmt));
     if (need > 0 && (!workspace || workspace_bytes < need)) return SHARQ_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace, 16)) return SHARQ_ERR_ALIGN;
     QuantWArgs a;
@@ -237,7 +256,7 @@ sharq_status sharq_quantize_weight(const void *w, int32_t w_dtype, int64_t exper
     a.nout = nout;
     a.K = K;
     a.ldw = ldw;
-    a.fmt = fmt;
+    a.fmt = kernel_fmt(fmt);
     a.bf16 = w_dtype == SHARQ_BF16;
     a.codes = codes;
     a.scales = scales;
@@ -268,7 +287,7 @@ sharq_status sharq_linear(const uint8_t *b_codes, const uint8_t *b_scales, const
     if (T == 0) return SHARQ_ERR_SHAPE;  // rows to produce but nothing to read
     if (!b_codes || !b_scales || !r_codes || !r_scales || !w_codes || !w_scales || !y)
         return SHARQ_ERR_NULL;
-    if (fmt == SHARQ_NVFP4 && (!x_global_scale || !w_global_scale)) return SHARQ_ERR_NULL;
+    if (is_nv(fmt) && (!x_global_scale || !w_global_scale)) return SHARQ_ERR_NULL;
     if (!aligned(b_codes, 16) || !aligned(r_codes, 16) || !aligned(w_codes, 16) ||
         !aligned(b_scales, 4) || !aligned(r_scales, 4) || !aligned(w_scales, 4))
         return SHARQ_ERR_ALIGN;
@@ -277,7 +296,8 @@ sharq_status sharq_linear(const uint8_t *b_codes, const uint8_t *b_scales, const
     // operands are addressed with 32-bit buffer offsets
     const int64_t limit = (int64_t)1 << 31;
     if (T * (K / 2) >= limit || nout * (K / 2) >= limit) return SHARQ_ERR_SHAPE;
-    const size_t need = linear_workspace_bytes(rows, K, nout, experts, fmt);
+    const int kfmt = fmt == SHARQ_MXFP4 ? kFmtMx : (fmt == SHARQ_NVFP4 ? kFmtNv : kFmtNvSp);
+    const size_t need = linear_workspace_bytes(rows, K, nout, experts, kfmt);
     if (need > 0 && (!workspace || workspace_bytes < need)) return SHARQ_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace, 16)) return SHARQ_ERR_ALIGN;
     LinearArgs a;
@@ -288,7 +308,7 @@ sharq_status sharq_linear(const uint8_t *b_codes, const uint8_t *b_scales, const
     a.x_gscale = x_global_scale;
     a.T = T;
     a.K = K;
-    a.fmt = fmt;
+    a.fmt = kfmt;
     a.w_codes = w_codes;
     a.w_scales = w_scales;
     a.w_gscale = w_global_scale;

@@ -7,10 +7,13 @@
 //
 // Y[m][n] = sum_k (Qb[m][k] + Qr[m][k]) * W[n][k], evaluated as two matrix
 // products into one FP32 accumulator: every weight fragment is read from LDS
-// once and feeds the backbone MFMA and the residual MFMA.  The backbone is
-// multiplied densely on its zero-filled form: gfx950's sparse matrix
-// instructions (smfmac) take fp8, bf8, f16 or bf16 operands without block
-// scales, so none holds MXFP4.
+// once and feeds the backbone MFMA and the residual MFMA.  MXFP4 multiplies
+// the backbone densely on its zero-filled form: gfx950's sparse matrix
+// instructions (smfmac) take fp8, bf8, f16, bf16 or int8 operands without
+// block scales, so none holds MXFP4.  NVFP4, which is multiplied as exactly
+// dequantized f16 values, can feed its backbone to the 2:4 sparse f16
+// instruction when the preparation stored it in that instruction's
+// compressed form (NVFP4_SP24).
 //
 //   MXFP4: v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands and per-lane
 //          E8M0 scales (16x16x128 in the small-T kernel).
@@ -28,6 +31,8 @@
 // fragment the B operand, so every group of four accumulator values is four
 // consecutive output columns of one token row and leaves as one 128-bit
 // store.  Each lane feeds 16 bytes of codes (32 elements of one row).
+#include <type_traits>
+
 #include "device_util.h"
 #include "kernels.h"
 
@@ -39,6 +44,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v16h __attribute__((ext_vector_type(16)));
 
 constexpr int kCbszFp4 = 4;  // MFMA operand format code for E2M1
 
@@ -104,11 +110,53 @@ __device__ __forceinline__ v8h nv_group(v4i c, const NvScale &s) {
     return v8h{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
 }
 
+// 2:4 compressed backbone (NVFP4_SP24): the eight kept codes of one
+// 16-element half u of the lane's sub-step, one code dword; codes 0-3 come
+// from block u of unit T (scale pair `lo`), codes 4-7 from block u of unit
+// 2+T (scale pair `hi`), exact in f16 as above.
+template <int u>
+__device__ __forceinline__ v8h sp_group(uint32_t word, const NvScale &lo, const NvScale &hi) {
+    const v2h ml = {lo.mp[u], lo.mp[u]}, mh = {hi.mp[u], hi.mp[u]};
+    const v2h a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, lo.p2[u], 0) * ml;
+    const v2h a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, lo.p2[u], 1) * ml;
+    const v2h a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, hi.p2[u], 2) * mh;
+    const v2h a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, hi.p2[u], 3) * mh;
+    return v8h{a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+}
+
+// gfx950 2:4 sparse f16 MFMA, D = A * B + D: A (tokens) holds the eight kept
+// values of K 16h..16h+15 of its row (h = lane / 32), two per group of four
+// at the 2-bit positions in bits 16u.. of `idx` (index half u = ABID); B
+// (weights) holds K 8h..8h+7 in halves 0-7 and K 16+8h..16+8h+7 in halves
+// 8-15.  Written as inline assembly with the accumulator in the
+// accumulation registers: the compiler's builtin moved every accumulator of
+// a 256x256 tile out of and back into them around each instruction.  The
+// compiler does not know this is a matrix instruction, so the caller keeps
+// other matrix instructions on the same accumulator at a distance (see the
+// NVFP4_SP24 branch of DualGemm::mma); every accumulator's last writer is a
+// compiler-visible MFMA (a residual product), so the epilogue's reads are
+// spaced by the compiler.
+template <int ABID>
+__device__ __forceinline__ void smfmac32_f16(v16f &acc, v8h a, v16h b, uint32_t idx) {
+    if constexpr (ABID == 0)
+        asm volatile("v_smfmac_f32_32x32x32_f16 %0, %1, %2, %3" : "+a"(acc) : "v"(a), "v"(b), "v"(idx));
+    else
+        asm volatile("v_smfmac_f32_32x32x32_f16 %0, %1, %2, %3 abid:1" : "+a"(acc) : "v"(a), "v"(b), "v"(idx));
+}
+
 // Output element conversions, round to nearest even (the hardware
 // conversions; F16 overflows to infinity).
 __device__ __forceinline__ uint32_t out_bits16(float f, int ydt) {
     return ydt == kOutBf16 ? (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f)
                            : (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// One output Y[m][n] in the output type.
+__device__ __forceinline__ void store_out1(const LinearArgs &a, int64_t m, int64_t n, float v) {
+    if (a.ydt == kOutF32)
+        static_cast<float *>(a.y)[m * a.ldy + n] = v;
+    else
+        static_cast<uint16_t *>(a.y)[m * a.ldy + n] = (uint16_t)out_bits16(v, a.ydt);
 }
 
 // Four consecutive outputs Y[m][n..n+3] (columns >= nout are skipped) in the
@@ -326,6 +374,10 @@ struct DualGemm {
 
     __amdgpu_buffer_rsrc_t rW, rWs, rXb, rXr, rXbs, rXrs;
     uint32_t w_off[L::W_LD], x_off[L::X_LD], s_off[L::SC_LD];
+    // NVFP4_SP24: the compressed backbone's rows are 48 bytes per stage (three
+    // of the row's four 16-byte LDS units), so its loads have offsets of
+    // their own
+    uint32_t xb_off[FMT == kFmtNvSp ? L::X_LD : 1];
     // 16-row code load j of this wave: slot (wave * LD + j) mod the loads per
     // array (when the waves do not divide the loads evenly, the surplus ones
     // repeat a slot: identical bytes to identical places)
@@ -358,10 +410,15 @@ struct DualGemm {
         } else if (idx < L::W_LD + 2 * L::X_LD) {
             const int j = (idx - L::W_LD) >> 1;
             const uint32_t cx = (uint32_t)stp * tx * kRowBytes;
-            if (((idx - L::W_LD) & 1) == 0)
-                lds_load16(rXb, st + L::XB_CODES + x_slot(wave, j) * 1024, x_off[j], cx);
-            else
+            if (((idx - L::W_LD) & 1) == 0) {
+                if constexpr (FMT == kFmtNvSp)
+                    lds_load16(rXb, st + L::XB_CODES + x_slot(wave, j) * 1024, xb_off[j],
+                               (uint32_t)stp * tx * kSpRowBytes);
+                else
+                    lds_load16(rXb, st + L::XB_CODES + x_slot(wave, j) * 1024, x_off[j], cx);
+            } else {
                 lds_load16(rXr, st + L::XR_CODES + x_slot(wave, j) * 1024, x_off[j], cx);
+            }
         } else {
             const int k = idx - L::W_LD - 2 * L::X_LD;
             lds_load4(s_rsrc[k], st + s_lds[k], s_off[k], (uint32_t)stp * s_rows[k] * L::SB);
@@ -378,6 +435,10 @@ struct DualGemm {
     // weights, wm*FM*32 + l%32 for tokens; fragment j / i adds 32 rows, which
     // keeps the swizzle).
     int rd_w[2], rd_x[2], rd_ws[2], rd_xs[2];
+    // NVFP4_SP24 backbone: the lane's 8 code bytes and index dword of
+    // sub-step T (logical units T and 2 of its 48-byte row) and its scale
+    // dword (the row's scales of units T and 2+T)
+    int rd_xbc[2], rd_xbm[2], rd_xbs[2];
 
     __device__ __forceinline__ void init_reads() {
         const int frow = lane & 31, q = lane >> 5;
@@ -389,6 +450,10 @@ struct DualGemm {
             const int sc = FMT == kFmtMx ? 2 * q : 2 * (2 * q + t);
             rd_ws[t] = (wn * (FN * 32) + frow) * L::SB + sc;
             rd_xs[t] = (wm * (FM * 32) + frow) * L::SB + sc;
+            const int xrow = wm * (FM * 32) + frow;
+            rd_xbc[t] = xrow * kRowBytes + swz_unit(frow, t) * 16 + 8 * q;
+            rd_xbm[t] = xrow * kRowBytes + swz_unit(frow, 2) * 16 + 4 * (2 * t + q);
+            rd_xbs[t] = xrow * L::SB + 4 * t;
         }
     }
 
@@ -402,10 +467,18 @@ struct DualGemm {
             f.w[r] = *reinterpret_cast<const v4i *>(cur + (rd_w[T] + (L::W_CODES + r * 32 * kRowBytes)));
         } else {
             const int i = (r - FN) >> 1;
-            if (((r - FN) & 1) == 0)
-                f.xb[i] = *reinterpret_cast<const v4i *>(cur + (rd_x[T] + (L::XB_CODES + i * 32 * kRowBytes)));
-            else
+            if (((r - FN) & 1) == 0) {
+                if constexpr (FMT == kFmtNvSp) {
+                    const uint8_t *b = cur + L::XB_CODES + i * 32 * kRowBytes;
+                    const uint2 c = *reinterpret_cast<const uint2 *>(b + rd_xbc[T]);
+                    const uint32_t ix = *reinterpret_cast<const uint32_t *>(b + rd_xbm[T]);
+                    f.xb[i] = v4i{(int)c.x, (int)c.y, (int)ix, 0};
+                } else {
+                    f.xb[i] = *reinterpret_cast<const v4i *>(cur + (rd_x[T] + (L::XB_CODES + i * 32 * kRowBytes)));
+                }
+            } else {
                 f.xr[i] = *reinterpret_cast<const v4i *>(cur + (rd_x[T] + (L::XR_CODES + i * 32 * kRowBytes)));
+            }
         }
     }
 
@@ -416,10 +489,14 @@ struct DualGemm {
             s.w[r] = *reinterpret_cast<const uint16_t *>(cur + (rd_ws[T] + (L::W_SC + r * 32 * L::SB)));
         } else {
             const int i = (r - FN) >> 1;
-            if (((r - FN) & 1) == 0)
-                s.xb[i] = *reinterpret_cast<const uint16_t *>(cur + (rd_xs[T] + (L::XB_SC + i * 32 * L::SB)));
-            else
+            if (((r - FN) & 1) == 0) {
+                if constexpr (FMT == kFmtNvSp)
+                    s.xb[i] = *reinterpret_cast<const uint32_t *>(cur + (rd_xbs[T] + (L::XB_SC + i * 32 * L::SB)));
+                else
+                    s.xb[i] = *reinterpret_cast<const uint16_t *>(cur + (rd_xs[T] + (L::XB_SC + i * 32 * L::SB)));
+            } else {
                 s.xr[i] = *reinterpret_cast<const uint16_t *>(cur + (rd_xs[T] + (L::XR_SC + i * 32 * L::SB)));
+            }
         }
     }
 
@@ -499,6 +576,102 @@ struct DualGemm {
                         else
                             read_next<BR>(r, fo, so);
                     }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else if constexpr (FMT == kFmtNvSp) {
+            // NVFP4_SP24: per 32 K of a fragment pair one 2:4 sparse f16 MFMA
+            // on the compressed backbone (eight kept values per lane) and two
+            // dense f16 MFMAs on the residual, all three reading the same
+            // dequantized weight halves; the token fragment is the A operand
+            // (accumulators hold token rows, see the epilogue).  Pipelined
+            // like the NVFP4 branch below: half u+1 (or the next token
+            // fragment) is dequantized while the MFMAs of half u run.
+            constexpr int NOTHER = MODE == 0 ? 2 * NREAD_FRAGS : NREAD_NEXT;
+            constexpr int NLOAD = MODE == 0 ? LSPLIT : L::PER_STAGE - LSPLIT;
+            constexpr int LLO = MODE == 0 ? L::PER_STAGE - LSPLIT : 0;
+            constexpr int PER_I_OTHER = (NOTHER + FM - 1) / FM;
+            constexpr int PER_I_LOAD = (NLOAD + FM - 1) / FM;
+            NvScale sw[FN], sxr[FM], sbl[FM], sbh[FM];
+#pragma unroll
+            for (int j = 0; j < FN; j++) sw[j] = nv_scale(s.w[j]);
+#pragma unroll
+            for (int i = 0; i < FM; i++) {
+                sxr[i] = nv_scale(s.xr[i]);
+                sbl[i] = nv_scale(s.xb[i] & 0xFFFFu);
+                sbh[i] = nv_scale(s.xb[i] >> 16);
+            }
+            v16h wd[FN][2];
+            v8h xb[2][2], xr[2][4];
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                wd[j][0] = __builtin_shufflevector(nv_group<0>(f.w[j], sw[j]), nv_group<1>(f.w[j], sw[j]), 0, 1, 2,
+                                                   3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+            xb[0][0] = sp_group<0>((uint32_t)f.xb[0].x, sbl[0], sbh[0]);
+            xr[0][0] = nv_group<0>(f.xr[0], sxr[0]);
+            xr[0][1] = nv_group<1>(f.xr[0], sxr[0]);
+#pragma unroll
+            for (int i = 0; i < FM; i++) {
+                const int cb = i & 1;
+                const uint32_t ix = (uint32_t)f.xb[i].z;
+                auto half = [&](auto uc) {
+                    constexpr int u = decltype(uc)::value;
+                    if constexpr (u == 0) {
+                        if (i == 0) {
+#pragma unroll
+                            for (int j = 0; j < FN; j++)
+                                wd[j][1] = __builtin_shufflevector(nv_group<2>(f.w[j], sw[j]), nv_group<3>(f.w[j], sw[j]),
+                                                                   0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+                        }
+                        xb[cb][1] = sp_group<1>((uint32_t)f.xb[i].y, sbl[i], sbh[i]);
+                        xr[cb][2] = nv_group<2>(f.xr[i], sxr[i]);
+                        xr[cb][3] = nv_group<3>(f.xr[i], sxr[i]);
+                    } else if (i + 1 < FM) {
+                        xb[cb ^ 1][0] = sp_group<0>((uint32_t)f.xb[i + 1].x, sbl[i + 1], sbh[i + 1]);
+                        xr[cb ^ 1][0] = nv_group<0>(f.xr[i + 1], sxr[i + 1]);
+                        xr[cb ^ 1][1] = nv_group<1>(f.xr[i + 1], sxr[i + 1]);
+                    }
+                    // The compiler sees the sparse MFMAs only as assembly, so
+                    // it neither orders nor spaces them against the MFMAs that
+                    // read or write the same accumulators: the groups
+                    // [sparse x FN] [residual t=2u x FN] [residual t=2u+1 x FN]
+                    // are fenced in this order, which puts FN matrix
+                    // instructions between any two uses of one accumulator,
+                    // and with FN < 4 a pause pads the sparse group.
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < FN; j++) smfmac32_f16<u>(acc[i][j], xb[cb][u], wd[j][u], ix);
+                    if constexpr (FN < 4) asm volatile("s_nop 7\n\ts_nop 7");
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < FN; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            xr[cb][2 * u], __builtin_shufflevector(wd[j][u], wd[j][u], 0, 1, 2, 3, 4, 5, 6, 7), acc[i][j],
+                            0, 0, 0);
+#pragma unroll
+                    for (int j = 0; j < FN; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            xr[cb][2 * u + 1],
+                            __builtin_shufflevector(wd[j][u], wd[j][u], 8, 9, 10, 11, 12, 13, 14, 15), acc[i][j], 0, 0,
+                            0);
+#pragma unroll
+                    for (int k = 0; k < 2 * FN; k++) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                half(std::integral_constant<int, 0>{});
+                half(std::integral_constant<int, 1>{});
+#pragma unroll
+                for (int k = i * PER_I_LOAD; k < (i + 1) * PER_I_LOAD && k < NLOAD; k++)
+                    this->template issue_one<BL>(LLO + k, stage);
+#pragma unroll
+                for (int k = i * PER_I_OTHER; k < (i + 1) * PER_I_OTHER && k < NOTHER; k++) {
+                    if (MODE == 0)
+                        read_sub1<BR>(k, fo, so);
+                    else
+                        read_next<BR>(k, fo, so);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -657,7 +830,8 @@ __device__ __forceinline__ void dual_tile(const LinearArgs &a, const TileRows &t
     G g;
     g.rW = make_rsrc(a.w_codes + tr.expert * a.nout * kb, nout * kb);
     g.rWs = make_rsrc(a.w_scales + tr.expert * a.nout * ks, nout * ks);
-    g.rXb = make_rsrc(a.b_codes, (uint32_t)a.T * kb);
+    const uint32_t kbb = FMT == kFmtNvSp ? (uint32_t)(K / kKS) * kSpRowBytes : kb;  // backbone bytes per row
+    g.rXb = make_rsrc(a.b_codes, (uint32_t)a.T * kbb);
     g.rXr = make_rsrc(a.r_codes, (uint32_t)a.T * kb);
     g.rXbs = make_rsrc(a.b_scales, (uint32_t)a.T * ks);
     g.rXrs = make_rsrc(a.r_scales, (uint32_t)a.T * ks);
@@ -686,6 +860,8 @@ __device__ __forceinline__ void dual_tile(const LinearArgs &a, const TileRows &t
         const int64_t m = tr.m0 + row;
         const int64_t src = m < tr.m_end ? (a.row_index ? (int64_t)a.row_index[m] : m) : -1;
         g.x_off[j] = src >= 0 ? (uint32_t)src * kRowBytes + unit * 16 : kOutOfRange;
+        if constexpr (FMT == kFmtNvSp)  // units 0-2 of the 48-byte row; LDS unit 3 stays zero
+            g.xb_off[j] = src >= 0 && unit < 3 ? (uint32_t)src * kSpRowBytes + unit * 16 : kOutOfRange;
     }
     // scale slots: 4 bytes per lane, SB/4 lanes per row
 #pragma unroll
@@ -745,9 +921,28 @@ __device__ __forceinline__ void dual_tile(const LinearArgs &a, const TileRows &t
     // ---- epilogue: accumulator group q of fragment (i, j) is Y[m][n..n+3];
     // NVFP4 applies the two tensor scales here
     float alpha = 1.0f;
-    if constexpr (FMT == kFmtNv) alpha = __fmul_rn(*a.x_gscale, a.w_gscale[tr.expert]);
+    if constexpr (FMT != kFmtMx) alpha = __fmul_rn(*a.x_gscale, a.w_gscale[tr.expert]);
     const int frow = g.lane & 31, fq = g.lane >> 5;
     const int wm = g.wm, wn = g.wn;
+    if constexpr (FMT == kFmtNvSp) {
+        // token fragments were the A operand: accumulator r of fragment (i, j)
+        // is Y[m][n] with m = row 8(r/4) + 4*fq + r%4 of the token fragment
+        // and n = column frow of the weight fragment
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+#pragma unroll
+            for (int j = 0; j < FN; j++) {
+                const int64_t n = n0 + wn * (FN * 32) + j * 32 + frow;
+                if (n >= a.nout) continue;
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int64_t m = tr.m0 + wm * (FM * 32) + i * 32 + 8 * (r / 4) + 4 * fq + (r % 4);
+                    if (m < tr.m_end) store_out1(a, m, n, __fmul_rn(acc[i][j][r], alpha));
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < FM; i++) {
         const int64_t m = tr.m0 + wm * (FM * 32) + i * 32 + frow;
@@ -758,7 +953,7 @@ __device__ __forceinline__ void dual_tile(const LinearArgs &a, const TileRows &t
             for (int q = 0; q < 4; q++) {
                 const int64_t n = n0 + wn * (FN * 32) + j * 32 + 8 * q + 4 * fq;
                 v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                if constexpr (FMT == kFmtNv) v = v4f{__fmul_rn(v.x, alpha), __fmul_rn(v.y, alpha),
+                if constexpr (FMT != kFmtMx) v = v4f{__fmul_rn(v.x, alpha), __fmul_rn(v.y, alpha),
                                                      __fmul_rn(v.z, alpha), __fmul_rn(v.w, alpha)};
                 store_out4(a, m, n, v);
             }
@@ -778,7 +973,7 @@ template <int FMT, int BM, int BN, int WGM, int WGN, int NS, int OCC, int LSPLIT
 __global__ __launch_bounds__(WGM * WGN * 64)
 __attribute__((amdgpu_waves_per_eu(OCC * WGM * WGN / 4, OCC * WGM * WGN / 4)))
 void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles, int64_t n_begin) {
-    if (a.ksplit_tiles > 0) {
+    if (a.ksplit_tiles > 0) {  // MXFP4 only
         // K range blockIdx.y: in the K-tiled layout tiles [t0, t0 + kt) of every
         // operand are themselves a K-tiled array with K = 128 * kt
         constexpr int64_t kScaleBytes = kTileK / (FMT == kFmtMx ? 32 : 16);  // per row and K tile
@@ -1209,7 +1404,8 @@ static hipError_t launch_linear_mx(const LinearArgs &a, void *ws, size_t ws_byte
 // (1.17 : 1); when 256x256 tiles fill some rounds and leave a partial one,
 // the columns of the full rounds run as 256x256 tiles and the rest as
 // 128x128 tiles in a second launch.  Grouped expert products use 128x256
-// tiles.
+// tiles.  NVFP4_SP24 (backbone on the 2:4 sparse f16 MFMA) uses the same
+// shapes.
 static double nv_cost128(int64_t rows, int64_t cols, int64_t cus) {
     const int64_t t = ((rows + 127) / 128) * ((cols + 127) / 128);
     return (double)((t + 2 * cus - 1) / (2 * cus)) * 2.0 * 128 * 128 * 1.17;
@@ -1219,8 +1415,9 @@ static double nv_cost256(int64_t rows, int64_t cols, int64_t cus) {
     return (double)((t + cus - 1) / cus) * 256.0 * 256;
 }
 
+template <int FMT>
 static hipError_t launch_linear_nv(const LinearArgs &a, hipStream_t st) {
-    if (a.offsets) return launch_prefill<kFmtNv, 128, 256, 2, 2, 3, 1, 4, 1, true>(a, st);
+    if (a.offsets) return launch_prefill<FMT, 128, 256, 2, 2, 3, 1, 4, 1, true>(a, st);
     const int64_t cus = device_cus();
     const double c128 = nv_cost128(a.rows, a.nout, cus), c256 = nv_cost256(a.rows, a.nout, cus);
     const int64_t mt = (a.rows + 255) / 256;
@@ -1229,18 +1426,19 @@ static hipError_t launch_linear_nv(const LinearArgs &a, hipStream_t st) {
     if (full_rounds >= 1 && n_split > 0 && n_split < a.nout) {
         const double split = nv_cost256(a.rows, n_split, cus) + nv_cost128(a.rows, a.nout - n_split, cus);
         if (split < 0.97 * (c128 < c256 ? c128 : c256)) {  // a second launch costs a little
-            const hipError_t e = launch_prefill<kFmtNv, 256, 256, 2, 2, 2, 1, 0, 1>(a, st, 0, n_split);
+            const hipError_t e = launch_prefill<FMT, 256, 256, 2, 2, 2, 1, 0, 1>(a, st, 0, n_split);
             if (e != hipSuccess) return e;
-            return launch_prefill<kFmtNv, 128, 128, 2, 2, 2, 2, 0, 1>(a, st, n_split, a.nout);
+            return launch_prefill<FMT, 128, 128, 2, 2, 2, 2, 0, 1>(a, st, n_split, a.nout);
         }
     }
-    if (c256 < c128) return launch_prefill<kFmtNv, 256, 256, 2, 2, 2, 1, 0, 1>(a, st);
-    return launch_prefill<kFmtNv, 128, 128, 2, 2, 2, 2, 0, 1>(a, st);
+    if (c256 < c128) return launch_prefill<FMT, 256, 256, 2, 2, 2, 1, 0, 1>(a, st);
+    return launch_prefill<FMT, 128, 128, 2, 2, 2, 2, 0, 1>(a, st);
 }
 
 hipError_t launch_linear(const LinearArgs &a, void *ws, size_t ws_bytes, hipStream_t st) {
     if (a.fmt == kFmtMx) return launch_linear_mx(a, ws, ws_bytes, st);
-    return launch_linear_nv(a, st);
+    if (a.fmt == kFmtNvSp) return launch_linear_nv<kFmtNvSp>(a, st);
+    return launch_linear_nv<kFmtNv>(a, st);
 }
 
 size_t linear_workspace_bytes(int64_t rows, int64_t K, int64_t nout, int64_t E, int fmt) {

@@ -9,6 +9,13 @@ namespace sharq {
 
 enum { kNormNone = 0, kNormRms = 1, kNormLayer = 2 };
 enum { kFmtMx = 0, kFmtNv = 1 };
+// Product operand format: NVFP4 whose backbone is stored in the compressed
+// form of the 2:4 sparse f16 matrix instruction (LinearArgs::fmt only; the
+// preparation keeps fmt = kFmtNv and sets PrepArgs::sp).
+constexpr int kFmtNvSp = 2;
+// Bytes per row and K tile of the compressed backbone: 32 code bytes (two
+// kept codes of every group of four) and 16 bytes of 2-bit positions.
+constexpr int kSpRowBytes = 48;
 enum { kOutF32 = 0, kOutBf16 = 1, kOutF16 = 2 };  // product output element type
 
 // K-tiled layout of every FP4 code and scale array (activations and
@@ -40,6 +47,7 @@ struct PrepArgs {
     uint8_t *mask, *b_codes, *b_scales, *r_codes, *r_scales;
     float *global_scale;
     bool off32;  // K % 128 == 0 and T*K/2 < 2^32: 32-bit K-tiled offsets
+    bool sp;     // NVFP4 backbone in the 2:4 compressed form (needs off32 and 2:4)
     // SiLU(gate)*up source (sharq_prepare_swiglu): rows of gu with stride ldgu
     // floats, gate in [0, K), up in [K, 2K); x is unused then
     const float *gu;

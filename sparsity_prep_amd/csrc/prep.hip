@@ -228,14 +228,31 @@ __device__ __forceinline__ uint4 param_raw(const uint16_t *p, int64_t e0, uint32
 struct LaneOff {
     uint32_t co;  // code dword
     uint32_t so;  // scale dword (lanes that store one)
+    // NVFP4_SP24 backbone (lanes that store one, else out of range): chunk
+    // dword, index dword, scale dword
+    uint32_t spc, spi, sps;
 };
 
+// NVFP4_SP24 backbone of one K tile and row (48 bytes, lane w = lane % 16
+// holds elements 8w..8w+7): lanes 8..15 store chunk c = 4p + 2h + u of the
+// kept codes (p = bit 2 of w, h = bit 0, u = bit 1; the first four codes from
+// lane w-8, the last four their own) at byte 4c; lanes 10, 11, 14 and 15
+// store the index dword of (p, h) at byte 32 + 4(2p + h); lanes 10 and 14
+// store the tile's scale dwords (blocks 0, 1, 4, 5 and 2, 3, 6, 7).
 template <int FMT>
 __device__ __forceinline__ LaneOff lane_offsets(const PrepArgs &a, int lane) {
     constexpr uint32_t SPT = FMT == kFmtMx ? 4 : 8;  // scale bytes per row per K tile
     const uint32_t q = (uint32_t)lane >> 4, w = (uint32_t)lane & 15u;
-    return {q * (uint32_t)(a.T * (kTileK / 2)) + w * 4u,
-            q * (uint32_t)a.T * SPT + (FMT == kFmtMx ? 0u : (w >= 8u ? 4u : 0u))};
+    LaneOff o{q * (uint32_t)(a.T * (kTileK / 2)) + w * 4u,
+              q * (uint32_t)a.T * SPT + (FMT == kFmtMx ? 0u : (w >= 8u ? 4u : 0u)), kOutOfRange, kOutOfRange,
+              kOutOfRange};
+    if (FMT == kFmtNv && a.sp) {
+        const uint32_t tile = q * (uint32_t)a.T * kSpRowBytes, p = (w >> 2) & 1u, h = w & 1u, u = (w >> 1) & 1u;
+        if (w >= 8u) o.spc = tile + 4u * (4u * p + 2u * h + u);
+        if (w >= 8u && u == 1u) o.spi = tile + 32u + 4u * (2u * p + h);
+        if (w == 10u || w == 14u) o.sps = q * (uint32_t)a.T * SPT + (w == 10u ? 0u : 4u);
+    }
+    return o;
 }
 
 // Scale bytes of a lane's block, gathered so that one lane per dword holds
@@ -258,6 +275,34 @@ __device__ __forceinline__ uint32_t gather_scales(uint32_t sb, int lane) {
     }
 }
 
+// The backbone's scale bytes in the NVFP4_SP24 order: the dword of blocks
+// 0, 1, 4, 5 of the K tile in lane 16q+10, that of blocks 2, 3, 6, 7 in lane
+// 16q+14 (block b is held by lanes 2b and 2b+1).
+__device__ __forceinline__ uint32_t gather_scales_sp(uint32_t sb, int lane) {
+    constexpr int kRowShr = 0x110;
+    const int w = lane & 15;
+    uint32_t v = sb << (8 * (((w >> 1) & 1) | (((w >> 3) & 1) << 1)));
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowShr + 2, 0xF, 0xF, true);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowShr + 8, 0xF, 0xF, true);
+    return v;
+}
+
+// 2:4 compression of a lane's eight backbone codes (exactly two kept per
+// group of four): the kept codes of each group in ascending position (four
+// codes, 16 bits) and their positions (2 bits each, 8 bits).
+__device__ __forceinline__ void compress24(uint32_t codes, const bool kp[8], uint32_t &cc, uint32_t &ix) {
+    cc = 0;
+    ix = 0;
+#pragma unroll
+    for (int g = 0; g < 2; g++) {
+        const uint32_t p0 = kp[4 * g] ? 0u : (kp[4 * g + 1] ? 1u : 2u);
+        const uint32_t p1 = kp[4 * g + 3] ? 3u : (kp[4 * g + 2] ? 2u : 1u);
+        const uint32_t c0 = (codes >> (16 * g + 4 * p0)) & 0xFu, c1 = (codes >> (16 * g + 4 * p1)) & 0xFu;
+        cc |= (c0 | (c1 << 4)) << (8 * g);
+        ix |= (p0 | (p1 << 2)) << (4 * g);
+    }
+}
+
 template <int FMT>
 __device__ __forceinline__ bool scale_store_lane(int lane) {
     return FMT == kFmtMx ? (lane & 15) == 12 : (lane & 7) == 6;
@@ -272,9 +317,10 @@ __device__ __forceinline__ bool scale_store_lane(int lane) {
 // unit drops), so the compiler can count outstanding memory operations
 // exactly and a row loop never waits for its stores.  Otherwise per-lane
 // 64-bit K-tiled offsets.
-template <int FMT, int M, int FAST24, bool OFF32>
+template <int FMT, int M, int FAST24, bool OFF32, bool SP = false>
 __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, int64_t ch, int lane, LaneOff lo,
                                                 const float v[8], float G, double rG6) {
+    static_assert(!SP || (FMT == kFmtNv && M == 4 && FAST24 && OFF32), "the compressed backbone is NVFP4 2:4");
     bool kp[8];
     select8<M, FAST24>(v, a.n, lane, kp);
     float S[8], dq[8], R[8];
@@ -304,10 +350,30 @@ __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, 
         const int som = __builtin_amdgcn_readfirstlane((int)(r32 * (uint32_t)(K / 8) + c32 * (kChunk / 8)));
         const uint32_t ncodes = T * (uint32_t)(K / 2), nsc = T * (uint32_t)(K / B);
         const uint32_t nmask = a.mask ? T * (uint32_t)(K / 8) : 0u;  // no mask: every store dropped
-        __builtin_amdgcn_raw_buffer_store_b32(bc, make_rsrc(a.b_codes, ncodes), (int)lo.co, soc, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(rc, make_rsrc(a.r_codes, ncodes), (int)lo.co, soc, 0);
         const uint32_t sv = scale_store_lane<FMT>(lane) ? lo.so : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b32(gather_scales<FMT>(bs, lane), make_rsrc(a.b_scales, nsc), (int)sv, sos, 0);
+        if constexpr (SP) {
+            constexpr int kRowShr = 0x110;
+            uint32_t cc, ix;
+            compress24(bc, kp, cc, ix);
+            const uint32_t chunk = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cc, kRowShr + 8, 0xF, 0xF, true) |
+                                   (cc << 16);
+            const uint32_t ix16 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ix, kRowShr + 8, 0xF, 0xF, true) |
+                                  (ix << 8);
+            const uint32_t ix32 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ix16, kRowShr + 2, 0xF, 0xF, true) |
+                                  (ix16 << 16);
+            const int sob = __builtin_amdgcn_readfirstlane(
+                (int)(c32 * T * (4 * kSpRowBytes) + r32 * kSpRowBytes));
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.b_codes, T * (uint32_t)(K / kTileK) * kSpRowBytes);
+            __builtin_amdgcn_raw_buffer_store_b32(chunk, rb, (int)lo.spc, sob, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(ix32, rb, (int)lo.spi, sob, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(gather_scales_sp(bs, lane), make_rsrc(a.b_scales, nsc), (int)lo.sps,
+                                                  sos, 0);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b32(bc, make_rsrc(a.b_codes, ncodes), (int)lo.co, soc, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(gather_scales<FMT>(bs, lane), make_rsrc(a.b_scales, nsc), (int)sv,
+                                                  sos, 0);
+        }
+        __builtin_amdgcn_raw_buffer_store_b32(rc, make_rsrc(a.r_codes, ncodes), (int)lo.co, soc, 0);
         __builtin_amdgcn_raw_buffer_store_b32(gather_scales<FMT>(rs, lane), make_rsrc(a.r_scales, nsc), (int)sv, sos, 0);
         __builtin_amdgcn_raw_buffer_store_b8((uint8_t)keep, make_rsrc(a.mask, nmask), lane, som, 0);
     } else {
@@ -328,6 +394,12 @@ __device__ __forceinline__ void decompose_store(const PrepArgs &a, int64_t row, 
 template <int FMT, int M, int FAST24>
 __device__ __forceinline__ void decompose_any(const PrepArgs &a, int64_t row, int64_t ch, int lane, LaneOff lo,
                                               const float v[8], float G, double rG6) {
+    if constexpr (FMT == kFmtNv && M == 4 && FAST24) {
+        if (a.sp) {
+            decompose_store<FMT, M, FAST24, true, true>(a, row, ch, lane, lo, v, G, rG6);
+            return;
+        }
+    }
     if (a.off32)
         decompose_store<FMT, M, FAST24, true>(a, row, ch, lane, lo, v, G, rG6);
     else
@@ -563,6 +635,12 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_stream(PrepArgs a, 
                 unpack8<BF16>(graw[c], g);
                 unpack8<BF16>(braw[c], b);
                 normalize8<NORM>(v, g, b, r, mu);
+            }
+            if constexpr (FMT == kFmtNv && M == 4 && FAST24 && OFF32) {
+                if (a.sp) {
+                    decompose_store<FMT, M, FAST24, true, true>(a, row, c0 + c, lane, lo, v, G, rG6);
+                    continue;
+                }
             }
             decompose_store<FMT, M, FAST24, OFF32>(a, row, c0 + c, lane, lo, v, G, rG6);
         }

@@ -22,7 +22,7 @@ int main(void) {
     void *P = (void *)(uintptr_t)0x10000, *MIS = (void *)(uintptr_t)0x10002;
     uint8_t *U = (uint8_t *)P;
     float *F = (float *)P;
-    const int BF = SHARQ_BF16, MX = SHARQ_MXFP4, NV = SHARQ_NVFP4;
+    const int BF = SHARQ_BF16, MX = SHARQ_MXFP4, NV = SHARQ_NVFP4, SP = SHARQ_NVFP4_SP24;
 
     EXPECT(sharq_abi_version(), SHARQ_ABI_VERSION);
     for (int s = 0; s < 10; s++)
@@ -60,6 +60,23 @@ int main(void) {
                                  U, U, F, NULL),
            SHARQ_ERR_WORKSPACE);
     EXPECT(sharq_prepare_noalloc(P, BF, 4, 256, 256, 1, P, NULL, 1e-5f, 2, 4, MX, U, U, U, U, U, NULL, NULL),
+           SHARQ_ERR_HIP);
+
+    /* NVFP4_SP24: the 2:4 mask, whole K tiles, 32-bit code offsets */
+    EXPECT(sharq_prepare(P, BF, 4, 256, 256, 1, P, NULL, 1e-5f, 4, 8, SP, U, U, U, U, U, F, NULL, 0, NULL),
+           SHARQ_ERR_NM);
+    EXPECT(sharq_prepare(P, BF, 4, 160, 160, 1, P, NULL, 1e-5f, 2, 4, SP, U, U, U, U, U, F, NULL, 0, NULL),
+           SHARQ_ERR_SHAPE);
+    EXPECT(sharq_prepare(P, BF, (int64_t)1 << 24, 512, 512, 1, P, NULL, 1e-5f, 2, 4, SP, U, U, U, U, U, F, NULL, 0,
+                         NULL),
+           SHARQ_ERR_SHAPE);
+    EXPECT(sharq_prepare(P, BF, 4, 256, 256, 1, P, NULL, 1e-5f, 2, 4, SP, U, U, U, U, U, NULL, NULL, 0, NULL),
+           SHARQ_ERR_NULL);
+    EXPECT(sharq_prepare_swiglu(F, 4, 160, 320, 2, 4, SP, U, U, U, U, U, F, NULL, 0, NULL), SHARQ_ERR_SHAPE);
+    EXPECT(sharq_linear(U, U, U, U, NULL, 4, 256, SP, U, U, F, 1, 64, NULL, NULL, 4, P, SHARQ_F32, 64, NULL, 0,
+                        NULL),
+           SHARQ_ERR_NULL);
+    EXPECT(sharq_linear(U, U, U, U, F, 4, 256, SP, U, U, F, 1, 64, NULL, NULL, 4, P, SHARQ_F32, 64, NULL, 0, NULL),
            SHARQ_ERR_HIP);
 
     /* sharq_prepare_swiglu */

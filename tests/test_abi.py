@@ -16,7 +16,7 @@ LIB = os.path.join(ROOT, "sparsity_prep_amd", "libsharq.so")
 
 OK, NULL, SHAPE, NM, DTYPE, ALIGN, WORKSPACE, UNSUPPORTED = 0, 1, 2, 3, 4, 5, 6, 7
 BF16, F16, F32 = 1, 0, 2
-MX, NV = 0, 1
+MX, NV, SP = 0, 1, 2
 
 
 @pytest.fixture(scope="module")
@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.sharq_abi_version() == 5
+    assert L.sharq_abi_version() == 6
     for code in range(9):
         assert L.sharq_status_string(code)
     assert L.sharq_status_string(99) == b"unknown status"
@@ -95,6 +95,26 @@ def test_prepare_validation(L):
     assert prep(L, fmt=NV, G=FAKE) == WORKSPACE
     assert prep(L, fmt=NV, G=FAKE, ws=FAKE, wsb=1) == WORKSPACE
     assert prep(L, T=0, x=None) == OK              # empty tensor is a no-op, no HIP call
+
+
+def test_prepare_sp24_validation(L):
+    # the compressed backbone exists for the 2:4 mask only
+    assert prep(L, fmt=SP, G=FAKE, n=1, m=4) == NM
+    assert prep(L, fmt=SP, G=FAKE, n=4, m=8) == NM
+    # whole K tiles and 32-bit code offsets (T*K/2 < 2^32)
+    assert prep(L, fmt=SP, G=FAKE, K=160) == SHAPE
+    assert prep(L, fmt=SP, G=FAKE, T=2**24, K=512) == SHAPE
+    assert prep(L, fmt=SP, G=FAKE, T=2**24 - 1, K=512) == WORKSPACE  # just under: shape accepted
+    assert prep(L, fmt=SP) == NULL                 # NVFP4 tensor scale
+    assert prep(L, fmt=SP, G=FAKE) == WORKSPACE
+    assert swiglu(L, fmt=SP, G=FAKE, n=1) == NM
+    assert swiglu(L, fmt=SP, G=FAKE, K=160) == SHAPE
+    assert swiglu(L, fmt=SP) == NULL
+    assert swiglu(L, fmt=SP, G=FAKE) == WORKSPACE
+    assert lin(L, fmt=SP) == NULL                  # both tensor scales
+    assert lin(L, fmt=SP, xg=FAKE, wg=FAKE, y=MISALIGNED) == ALIGN
+    assert L.sharq_prepare_workspace_size(100, 256, SP) == L.sharq_prepare_workspace_size(100, 256, NV)
+    assert L.sharq_linear_workspace_size(64, 14336, 4096, 1, SP) == 0
 
 
 def swiglu(L, gu=FAKE, T=4, K=256, ld=None, n=2, m=4, fmt=MX, bc=FAKE, G=None, ws=None, wsb=0):

@@ -591,3 +591,66 @@ def test_prepare_swiglu_row_subset(fmt):
     assert sub.G == full.G
     if fmt == 1:
         assert full.G == np.float32(np.float32(np.abs(full.xhat).max()) / np.float32(2688.0))
+
+
+# ---------------------------------------------------------------- compressed 2:4 backbone (NVFP4_SP24)
+
+def _sp24_case(T, K, seed):
+    x = synth.small_case(K, T, "bf16", outliers=3, mult=40.0, tag=seed)
+    g = synth.small_gamma(K, "bf16", tag=seed + 1)
+    return oracle.prepare(x, "bf16", K, 1, g, None, 1e-5, 2, 4, oracle.FMT_NVFP4)
+
+
+def test_sp24_pack_round_trip():
+    """Unpacking the compressed backbone gives back the dense backbone codes
+    and the mask, and its scales are a permutation of each tile's eight."""
+    p = _sp24_case(7, 384, 21)
+    rec, sc = oracle.sp24_pack(p)
+    assert rec.shape == (7, 3, 48) and sc.shape == p.b_scales.shape
+    codes, mask = oracle.sp24_unpack(rec, 384)
+    assert np.array_equal(codes, p.b_codes) and np.array_equal(mask, p.mask)
+    assert np.array_equal(np.sort(sc.reshape(7, 3, 8), -1), np.sort(p.b_scales.reshape(7, 3, 8), -1))
+
+
+def test_sp24_pack_feeds_the_sparse_instruction():
+    """The compressed backbone, read the way the product reads it (in
+    sub-step p, lane half h takes chunk (p, h, u) with index half u; the
+    weight lane of half h' takes elements 32(2h' + p) + 16u + [0, 16) of its
+    row), and multiplied by the host model of the 2:4 sparse f16 instruction,
+    gives the dense product of the backbone codes over the tile's 128
+    elements; each (p, u) covers elements 32p + 16u + [0, 16) and
+    64 + 32p + 16u + [0, 16)."""
+    from smfmac_model import model
+    p = _sp24_case(32, 128, 33)
+    rec, _ = oracle.sp24_pack(p)
+    grid = np.array([oracle.e2m1_decode(c) for c in range(16)])
+    bb = grid[oracle.unpack_codes(p.b_codes)]           # [32, 128] backbone code values
+    rng = np.random.default_rng(4)
+    w = rng.integers(-3, 4, (32, 128)).astype(np.float64)  # 32 weight rows of one tile
+    total = np.zeros((32, 32))
+    for pp in (0, 1):
+        for u in (0, 1):
+            A = np.zeros((64, 8))
+            idx = np.zeros(64, np.int64)
+            Bl = np.zeros((64, 16))
+            for l in range(64):
+                row, h = l % 32, l // 32
+                c = 4 * pp + 2 * h + u
+                for v in range(8):
+                    A[l, v] = grid[(rec[row, 0, 4 * c + v // 2] >> (4 * (v % 2))) & 0xF]
+                word = int.from_bytes(bytes(rec[row, 0, 32 + 4 * (2 * pp + h):36 + 4 * (2 * pp + h)]), "little")
+                idx[l] = (word >> (16 * u)) & 0xFFFF
+                Bl[l] = w[l % 32, 32 * (2 * h + pp) + 16 * u + np.arange(16)]
+            D = model(A, Bl, idx)
+            cols = np.concatenate([32 * pp + 16 * u + np.arange(16), 64 + 32 * pp + 16 * u + np.arange(16)])
+            assert np.array_equal(D, bb[:, cols] @ w[:, cols].T), (pp, u)
+            total += D
+    assert np.array_equal(total, bb @ w.T)
+
+
+def test_sp24_pack_needs_a_2of4_mask():
+    x = synth.small_case(128, 3, "bf16", outliers=1, mult=10.0, tag=2)
+    g = synth.small_gamma(128, "bf16", tag=2)
+    p = oracle.prepare(x, "bf16", 128, 1, g, None, 1e-5, 1, 4, oracle.FMT_NVFP4)
+    with pytest.raises(ValueError):
+        oracle.sp24_pack(p)

@@ -25,32 +25,10 @@ import os
 import numpy as np
 import pytest
 
+from smfmac_model import lanes_to_matrix as _lanes, model as _model
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 PROBE = os.path.join(HERE, "hwprobe", "libsmfmac_probe.so")
-
-
-def _model(A, B, idx16):
-    Ad = np.zeros((32, 32))
-    for l in range(64):
-        h = l // 32
-        for v in range(8):
-            p = (int(idx16[l]) >> (2 * v)) & 3
-            Ad[l % 32, 16 * h + 4 * (v // 2) + p] += A[l, v]
-    Bd = np.zeros((32, 32))
-    for l in range(64):
-        h = l // 32
-        for k in range(16):
-            K = 8 * h + k if k < 8 else 16 + 8 * h + (k - 8)
-            Bd[K, l % 32] = B[l, k]
-    return Ad @ Bd
-
-
-def _lanes(D):
-    M = np.zeros((32, 32))
-    for l in range(64):
-        for r in range(16):
-            M[8 * (r // 4) + 4 * (l // 32) + r % 4, l % 32] = D[l, r]
-    return M
 
 
 def _probe():

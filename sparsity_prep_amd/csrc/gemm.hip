@@ -135,10 +135,16 @@ __device__ __forceinline__ v8h sp_group(uint32_t word, const NvScale &lo, const 
 // other matrix instructions on the same accumulator at a distance (see the
 // NVFP4_SP24 branch of DualGemm::mma); every accumulator's last writer is a
 // compiler-visible MFMA (a residual product), so the epilogue's reads are
-// spaced by the compiler.
-template <int ABID>
+// spaced by the compiler.  Nor does it space the vector instructions that
+// produce the operands from the matrix instruction that reads them: PAD puts
+// two wait states in front (the first instruction of a group).
+template <int ABID, bool PAD = false>
 __device__ __forceinline__ void smfmac32_f16(v16f &acc, v8h a, v16h b, uint32_t idx) {
-    if constexpr (ABID == 0)
+    if constexpr (PAD && ABID == 0)
+        asm volatile("s_nop 1\n\tv_smfmac_f32_32x32x32_f16 %0, %1, %2, %3" : "+a"(acc) : "v"(a), "v"(b), "v"(idx));
+    else if constexpr (PAD)
+        asm volatile("s_nop 1\n\tv_smfmac_f32_32x32x32_f16 %0, %1, %2, %3 abid:1" : "+a"(acc) : "v"(a), "v"(b), "v"(idx));
+    else if constexpr (ABID == 0)
         asm volatile("v_smfmac_f32_32x32x32_f16 %0, %1, %2, %3" : "+a"(acc) : "v"(a), "v"(b), "v"(idx));
     else
         asm volatile("v_smfmac_f32_32x32x32_f16 %0, %1, %2, %3 abid:1" : "+a"(acc) : "v"(a), "v"(b), "v"(idx));
@@ -583,10 +589,16 @@ struct DualGemm {
             // NVFP4_SP24: per 32 K of a fragment pair one 2:4 sparse f16 MFMA
             // on the compressed backbone (eight kept values per lane) and two
             // dense f16 MFMAs on the residual, all three reading the same
-            // dequantized weight halves; the token fragment is the A operand
-            // (accumulators hold token rows, see the epilogue).  Pipelined
-            // like the NVFP4 branch below: half u+1 (or the next token
-            // fragment) is dequantized while the MFMAs of half u run.
+            // dequantized weight half; the token fragment is the A operand
+            // (accumulators hold token rows, see the epilogue).
+            //
+            // Per token fragment i, halves u = 0, 1 (K halves of the
+            // sub-step).  The vector work runs one half ahead and is threaded
+            // between the dense MFMAs of the current half (the sparse ones
+            // are assembly, which the scheduler does not move): half (i, 0)
+            // dequantizes half 1 of token fragment i (on i = 0 also half 1
+            // of every weight fragment), half (i, 1) decodes the scales of
+            // token fragment i+1 and dequantizes its half 0.
             constexpr int NOTHER = MODE == 0 ? 2 * NREAD_FRAGS : NREAD_NEXT;
             constexpr int NLOAD = MODE == 0 ? LSPLIT : L::PER_STAGE - LSPLIT;
             constexpr int LLO = MODE == 0 ? L::PER_STAGE - LSPLIT : 0;
@@ -595,12 +607,9 @@ struct DualGemm {
             NvScale sw[FN], sxr[FM], sbl[FM], sbh[FM];
 #pragma unroll
             for (int j = 0; j < FN; j++) sw[j] = nv_scale(s.w[j]);
-#pragma unroll
-            for (int i = 0; i < FM; i++) {
-                sxr[i] = nv_scale(s.xr[i]);
-                sbl[i] = nv_scale(s.xb[i] & 0xFFFFu);
-                sbh[i] = nv_scale(s.xb[i] >> 16);
-            }
+            sxr[0] = nv_scale(s.xr[0]);
+            sbl[0] = nv_scale(s.xb[0] & 0xFFFFu);
+            sbh[0] = nv_scale(s.xb[0] >> 16);
             v16h wd[FN][2];
             v8h xb[2][2], xr[2][4];
 #pragma unroll
@@ -616,31 +625,17 @@ struct DualGemm {
                 const uint32_t ix = (uint32_t)f.xb[i].z;
                 auto half = [&](auto uc) {
                     constexpr int u = decltype(uc)::value;
-                    if constexpr (u == 0) {
-                        if (i == 0) {
-#pragma unroll
-                            for (int j = 0; j < FN; j++)
-                                wd[j][1] = __builtin_shufflevector(nv_group<2>(f.w[j], sw[j]), nv_group<3>(f.w[j], sw[j]),
-                                                                   0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-                        }
-                        xb[cb][1] = sp_group<1>((uint32_t)f.xb[i].y, sbl[i], sbh[i]);
-                        xr[cb][2] = nv_group<2>(f.xr[i], sxr[i]);
-                        xr[cb][3] = nv_group<3>(f.xr[i], sxr[i]);
-                    } else if (i + 1 < FM) {
-                        xb[cb ^ 1][0] = sp_group<0>((uint32_t)f.xb[i + 1].x, sbl[i + 1], sbh[i + 1]);
-                        xr[cb ^ 1][0] = nv_group<0>(f.xr[i + 1], sxr[i + 1]);
-                        xr[cb ^ 1][1] = nv_group<1>(f.xr[i + 1], sxr[i + 1]);
-                    }
-                    // The compiler sees the sparse MFMAs only as assembly, so
-                    // it neither orders nor spaces them against the MFMAs that
-                    // read or write the same accumulators: the groups
-                    // [sparse x FN] [residual t=2u x FN] [residual t=2u+1 x FN]
-                    // are fenced in this order, which puts FN matrix
-                    // instructions between any two uses of one accumulator,
-                    // and with FN < 4 a pause pads the sparse group.
+                    // The sparse MFMAs first, fenced: the residual MFMAs on
+                    // the same accumulators come FN matrix instructions later
+                    // (with FN < 4 a pause pads the group).
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int j = 0; j < FN; j++) smfmac32_f16<u>(acc[i][j], xb[cb][u], wd[j][u], ix);
+                    for (int j = 0; j < FN; j++) {
+                        if (j == 0)
+                            smfmac32_f16<u, true>(acc[i][j], xb[cb][u], wd[j][u], ix);
+                        else
+                            smfmac32_f16<u, false>(acc[i][j], xb[cb][u], wd[j][u], ix);
+                    }
                     if constexpr (FN < 4) asm volatile("s_nop 7\n\ts_nop 7");
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -654,26 +649,46 @@ struct DualGemm {
                             xr[cb][2 * u + 1],
                             __builtin_shufflevector(wd[j][u], wd[j][u], 8, 9, 10, 11, 12, 13, 14, 15), acc[i][j], 0, 0,
                             0);
+                    // vector work for the next half
+                    if constexpr (u == 0) {
+                        if (i == 0) {
+#pragma unroll
+                            for (int j = 0; j < FN; j++)
+                                wd[j][1] = __builtin_shufflevector(nv_group<2>(f.w[j], sw[j]), nv_group<3>(f.w[j], sw[j]),
+                                                                   0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+                        }
+                        xb[cb][1] = sp_group<1>((uint32_t)f.xb[i].y, sbl[i], sbh[i]);
+                        xr[cb][2] = nv_group<2>(f.xr[i], sxr[i]);
+                        xr[cb][3] = nv_group<3>(f.xr[i], sxr[i]);
+                    } else {
+                        if (i + 1 < FM) {
+                            sxr[i + 1] = nv_scale(s.xr[i + 1]);
+                            sbl[i + 1] = nv_scale(s.xb[i + 1] & 0xFFFFu);
+                            sbh[i + 1] = nv_scale(s.xb[i + 1] >> 16);
+                            xb[cb ^ 1][0] = sp_group<0>((uint32_t)f.xb[i + 1].x, sbl[i + 1], sbh[i + 1]);
+                            xr[cb ^ 1][0] = nv_group<0>(f.xr[i + 1], sxr[i + 1]);
+                            xr[cb ^ 1][1] = nv_group<1>(f.xr[i + 1], sxr[i + 1]);
+                        }
+#pragma unroll
+                        for (int k = i * PER_I_LOAD; k < (i + 1) * PER_I_LOAD && k < NLOAD; k++)
+                            this->template issue_one<BL>(LLO + k, stage);
+#pragma unroll
+                        for (int k = i * PER_I_OTHER; k < (i + 1) * PER_I_OTHER && k < NOTHER; k++) {
+                            if (MODE == 0)
+                                read_sub1<BR>(k, fo, so);
+                            else
+                                read_next<BR>(k, fo, so);
+                        }
+                    }
 #pragma unroll
                     for (int k = 0; k < 2 * FN; k++) {
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 };
                 half(std::integral_constant<int, 0>{});
                 half(std::integral_constant<int, 1>{});
-#pragma unroll
-                for (int k = i * PER_I_LOAD; k < (i + 1) * PER_I_LOAD && k < NLOAD; k++)
-                    this->template issue_one<BL>(LLO + k, stage);
-#pragma unroll
-                for (int k = i * PER_I_OTHER; k < (i + 1) * PER_I_OTHER && k < NOTHER; k++) {
-                    if (MODE == 0)
-                        read_sub1<BR>(k, fo, so);
-                    else
-                        read_next<BR>(k, fo, so);
-                }
-                __builtin_amdgcn_sched_barrier(0);
             }
         } else {
             // NVFP4: dequantize each fragment once per sub-step, four f16

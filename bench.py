@@ -13,8 +13,8 @@ rotated so that the 256 MB Infinity Cache cannot serve a step from the
 previous one.
 
 Prints one JSON line: whole-step dual-product throughput (algorithmic
-TFLOP/s, 2*T*Nout*K*(1+N/M) per linear) with every timed step run as one
-captured HIP graph (--graph off: eager launches); per-launch kernel times
+TFLOP/s, 2*T*Nout*K*(1+N/M) per linear) over the K timed steps, captured as
+one HIP graph after the W warmup steps (--graph off: eager launches); per-launch kernel times
 from graphs that hold one phase (one linear's preps, or its products) over
 rotated copies, timed with HIP events around a replay on the launch stream
 (prep inputs rotated over enough copies to exceed twice the Infinity Cache);
@@ -71,7 +71,13 @@ def parse():
                     help="skip the BF16-output products, the unfused SiLU chain and the bf16 / fp8 GEMMs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter calibration)")
+    ap.add_argument("--nv-backbone", choices=["sp24", "dense"], default="sp24",
+                    help="NVFP4 2:4 workloads: store the backbone in the compressed 2:4 form and multiply it on "
+                         "the sparse f16 matrix instruction (sp24), or zero-filled on the dense one (dense)")
     return ap.parse_args()
+
+
+FMT_NVFP4_SP24 = 2  # the library's NVFP4 preparation with the backbone in the compressed 2:4 form
 
 
 def block_of(fmt):
@@ -80,9 +86,12 @@ def block_of(fmt):
 
 def prep_bytes(T, K, fmt, swiglu=False):
     """Algorithmic bytes of one prep: read the input once (bf16 X, or the FP32
-    gate and up halves for the SiLU(gate)*up prep), write codes, scales and mask."""
+    gate and up halves for the SiLU(gate)*up prep), write codes, scales and
+    mask.  The compressed 2:4 backbone holds K/4 code bytes and K/8 bytes of
+    2-bit positions per row instead of K/2 code bytes."""
     read = 8 * K if swiglu else 2 * K
-    return T * (read + K + 2 * K // block_of(fmt) + K // 8)
+    codes = K // 2 + (3 * K // 8 if fmt == FMT_NVFP4_SP24 else K // 2)
+    return T * (read + codes + 2 * K // block_of(fmt) + K // 8)
 
 
 def gemm_flops(rows, K, nout, n, m):
@@ -104,8 +113,9 @@ class Layer:
     src's FP32 output [gate | up] (SiLU(gate)*up formed in the prep kernel)."""
 
     def __init__(self, sq, torch, synth, wl, lin, prep_tokens, rotate, dev, route=None, gather=False,
-                 src=None, prep_copies=None):
+                 src=None, prep_copies=None, pfmt=None):
         self.lin, self.wl, self.src = lin, wl, src
+        self.pfmt = wl.fmt if pfmt is None else pfmt  # preparation format (weights: wl.fmt)
         self.prep_tokens = prep_tokens
         self.rotate = rotate
         self.x = None
@@ -146,7 +156,7 @@ class Layer:
         experts = sorted(set(self.sample_experts[:max(ERROR_ROWS, CPU_ROWS)].tolist()) | {0})
         self.w_host = {e: w_bits[e] for e in experts}  # weight rows the host-side reports need
         del w_bits
-        self.prep = [sq.alloc_prepared(prep_tokens, lin.k, wl.fmt, dev) for _ in range(n_in)]
+        self.prep = [sq.alloc_prepared(prep_tokens, lin.k, self.pfmt, dev) for _ in range(n_in)]
         self.y = [torch.empty((self.rows, lin.nout), dtype=torch.float32, device=dev) for _ in range(rotate)]
         self.y16 = None
 
@@ -158,10 +168,10 @@ class Layer:
         r = i % self.n_in
         if self.src is not None:
             sq.prepare_swiglu(self.src.y[i % self.src.rotate], self.lin.k, n=self.wl.n, m=self.wl.m,
-                              fmt=self.wl.fmt, out=self.prep[r])
+                              fmt=self.pfmt, out=self.prep[r])
         else:
             sq.prepare(self.x[r], norm=self.lin.norm, gamma=self.g, eps=self.wl.eps, n=self.wl.n, m=self.wl.m,
-                       fmt=self.wl.fmt, out=self.prep[r])
+                       fmt=self.pfmt, out=self.prep[r])
 
     def run_gemm(self, sq, i, bf16=False):
         r = i % self.rotate
@@ -372,17 +382,21 @@ def _event_ms(torch, fn, reps=20):
     return a.elapsed_time(b) / reps
 
 
-def _replay_ms(torch, graph):
-    """Time of one replay of a captured graph (HIP events on the current
-    stream, which the replay is launched on; after one warm replay)."""
+def _replay_ms(torch, graph, reps=3):
+    """Time of one replay of a captured graph: the median of `reps` replays
+    after a warm one (HIP events on the current stream, which the replay is
+    launched on)."""
     graph.replay()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    graph.replay()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return sorted(ts)[len(ts) // 2]
 
 
 def _capture(torch, fn):
@@ -410,24 +424,24 @@ def swiglu_report(sq, torch, wl, layers):
         return None
     Ys = down.src.y                     # rotated copies, each larger than the Infinity Cache
     T, K = Ys[0].shape[0], down.lin.k
-    out = sq.alloc_prepared(T, K, wl.fmt, Ys[0].device)
+    out = sq.alloc_prepared(T, K, down.pfmt, Ys[0].device)
     it = [0]
 
     def nxt():
         it[0] += 1
         return Ys[it[0] % len(Ys)]
 
-    fused = _event_ms(torch, lambda: sq.prepare_swiglu(nxt(), K, n=wl.n, m=wl.m, fmt=wl.fmt, out=out))
+    fused = _event_ms(torch, lambda: sq.prepare_swiglu(nxt(), K, n=wl.n, m=wl.m, fmt=down.pfmt, out=out))
     act = torch.empty((T, K), dtype=torch.bfloat16, device=Ys[0].device)
 
     def unfused_chain():
         Y = nxt()
         act.copy_(torch.nn.functional.silu(Y[:, :K]) * Y[:, K:2 * K])
-        sq.prepare(act, norm=0, n=wl.n, m=wl.m, fmt=wl.fmt, out=out)
+        sq.prepare(act, norm=0, n=wl.n, m=wl.m, fmt=down.pfmt, out=out)
 
     chain = _event_ms(torch, unfused_chain)
     return {"rows": T, "K": K, "fused_us": round(fused * 1e3, 2),
-            "fused_GBps": round(prep_bytes(T, K, wl.fmt, True) / (fused * 1e-3) / 1e9, 1),
+            "fused_GBps": round(prep_bytes(T, K, down.pfmt, True) / (fused * 1e-3) / 1e9, 1),
             "unfused_torch_silu_bf16_then_prep_us": round(chain * 1e3, 2),
             "speedup": round(chain / fused, 3),
             "timing": "eager launches, HIP events around 20 of them"}
@@ -497,6 +511,15 @@ def prep_copies(x_bytes):
     return int(min(48, 2 * INFINITY_CACHE_BYTES // max(1, x_bytes) + 1))
 
 
+def prep_format(wl, args):
+    """The preparation's format: NVFP4 2:4 workloads whose K are whole 128-element
+    tiles store the backbone compressed (unless --nv-backbone dense)."""
+    if (wl.fmt == 1 and wl.n == 2 and wl.m == 4 and args.nv_backbone == "sp24"
+            and all(lin.k % 128 == 0 for lin in wl.linears)):
+        return FMT_NVFP4_SP24
+    return wl.fmt
+
+
 def build_layers(args, sq, torch, synth, dev):
     if args.rotate is None:
         args.rotate = 8 if args.workload.startswith("decode") else 3
@@ -504,11 +527,12 @@ def build_layers(args, sq, torch, synth, dev):
     if args.workload in ("llama", "qwen") or decode:
         wl = synth.WORKLOADS[3 if args.workload == "qwen" else (2 if decode else 1)]
         tokens = int(args.workload[len("decode"):]) if decode else wl.tokens
+        pfmt = prep_format(wl, args)
         layers = {}
         for lin in wl.linears:
             pc = None if decode else prep_copies(tokens * lin.k * 2)
             layers[lin.name] = Layer(sq, torch, synth, wl, lin, tokens, args.rotate, dev,
-                                     src=layers.get(lin.swiglu_of), prep_copies=pc)
+                                     src=layers.get(lin.swiglu_of), prep_copies=pc, pfmt=pfmt)
         return wl, list(layers.values())
     if args.workload == "moe":
         wl = synth.WORKLOADS[4]
@@ -550,36 +574,67 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    for i in range(args.warmup):
+    use_graph = args.graph == "on"
+    decode = layers[0].prep_tokens <= 64
+
+    # untimed runs of the whole step before any capture
+    for i in range(2):
         for L in layers:
             L.run(sq, i)
     torch.cuda.synchronize()
 
-    use_graph = args.graph == "on"
-    decode = layers[0].prep_tokens <= 64
-
-    # ---- the timed steps
+    # the W warmup steps and the K timed steps, each captured as one graph
+    # (consecutive layer steps rotating over the buffer copies, as a model's
+    # forward pass over its layers would be captured); captured here, before
+    # the phase timings, so that no capture idles the GPU right before the
+    # timed replay
+    warm = steps_graph = None
     if use_graph:
-        # one captured graph per rotated copy, holding the whole step
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            for i in range(2):
-                for L in layers:
-                    L.run(sq, i)
+            for L in layers:
+                L.run(sq, 0)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        step_graphs = [_capture(torch, lambda r=r: [L.run(sq, r) for L in layers]) for r in range(args.rotate)]
+        if args.warmup > 0:
+            warm = _capture(torch, lambda: [L.run(sq, s) for s in range(args.warmup) for L in layers])
+        steps_graph = _capture(torch, lambda: [L.run(sq, s) for s in range(args.steps) for L in layers])
         torch.cuda.synchronize()
-        for i in range(args.warmup):
-            step_graphs[i % args.rotate].replay()
+
+    # untimed steps for about 30 ms: a GPU that was idle runs its first
+    # milliseconds at a lower clock (~10% slower layer steps, measured)
+    t_settle = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t_settle < 0.03:
+        for L in layers:
+            L.run(sq, i)
+        torch.cuda.synchronize()
+        i += 1
+
+    # ---- per-launch kernel times: graphs of one phase over rotated copies,
+    # measured before the timed steps so that those too start on a GPU that
+    # has been busy for a while
+    prep_ms, gemm_ms = [], []
+    for L in layers:
+        n_prep = args.steps if decode else max(12, L.n_in)
+        n_gemm = args.steps if decode else 12
+        prep_ms.append(phase_ms(torch, lambda i, L=L: L.run_prep(sq, i), n_prep))
+        gemm_ms.append(phase_ms(torch, lambda i, L=L: L.run_gemm(sq, i), n_gemm))
+
+    # ---- W warmup steps, then exactly K timed steps
+    if use_graph:
+        if warm is not None:
+            warm.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for s in range(args.steps):
-            step_graphs[s % args.rotate].replay()
+        steps_graph.replay()
         torch.cuda.synchronize()
         ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     else:
+        for i in range(args.warmup):
+            for L in layers:
+                L.run(sq, i)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for s in range(args.steps):
@@ -588,21 +643,14 @@ def main():
         torch.cuda.synchronize()
         ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # ---- per-launch kernel times: graphs of one phase over rotated copies
-    prep_ms, gemm_ms = [], []
-    for L in layers:
-        n_prep = args.steps if decode else max(12, L.n_in)
-        n_gemm = args.steps if decode else 12
-        prep_ms.append(phase_ms(torch, lambda i, L=L: L.run_prep(sq, i), n_prep))
-        gemm_ms.append(phase_ms(torch, lambda i, L=L: L.run_gemm(sq, i), n_gemm))
-
     flops = [gemm_flops(L.rows, L.lin.k, L.lin.nout, wl.n, wl.m) for L in layers]
-    pbytes = [prep_bytes(L.prep_tokens, L.lin.k, wl.fmt, L.swiglu) for L in layers]
+    pbytes = [prep_bytes(L.prep_tokens, L.lin.k, L.pfmt, L.swiglu) for L in layers]
     wbytes = [weight_bytes(L.E, L.lin.nout, L.lin.k, wl.fmt) for L in layers]
     gemm_tflops = sum(flops) / (sum(gemm_ms) * 1e-3) / 1e12
     prep_gbps = sum(pbytes) / (sum(prep_ms) * 1e-3) / 1e9
     value = sum(flops) / (ms_step * 1e-3) / 1e12
     nv = wl.fmt != 0
+    sp24 = layers[0].pfmt == FMT_NVFP4_SP24
     tokens = layers[0].prep_tokens
     plain = [i for i, L in enumerate(layers) if not L.swiglu]
     fused = [i for i, L in enumerate(layers) if L.swiglu]
@@ -611,8 +659,8 @@ def main():
         return None if not ix else round(sum(pbytes[i] for i in ix) / (sum(prep_ms[i] for i in ix) * 1e-3) / 1e9, 1)
 
     timing = (f"graphs of one phase over rotated copies (prep inputs over enough copies to exceed twice the "
-              f"Infinity Cache; products over the step's {args.rotate} copies), HIP events around a replay, "
-              f"per launch = replay time / launches")
+              f"Infinity Cache; products over the step's {args.rotate} copies), HIP events around a replay (median "
+              f"of three after a warm one), per launch = replay time / launches; measured before the timed steps")
     result = {
         "metric": "prep GB/s + dual-GEMM TFLOP/s, % of HBM / MXFP4 MFMA peak, 1 MI355X",
         "value": round(value, 2),
@@ -624,7 +672,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4-e2m1 (nvfp4) -> f16 mfma -> fp32" if nv else "fp4-e2m1 (mxfp4) x fp4 -> fp32",
+        "dtype": ("fp4-e2m1 (nvfp4) -> f16 mfma (2:4 sparse backbone) -> fp32" if sp24 else
+                  "fp4-e2m1 (nvfp4) -> f16 mfma -> fp32") if nv else "fp4-e2m1 (mxfp4) x fp4 -> fp32",
         "data": "synthetic (seeded; model-shaped activations with outlier channels, N(0,0.02) weights)",
         "config": {"workload": f"{wl.name}" + ("" if tokens == wl.tokens else f"_T{tokens}"),
                    "tokens": tokens, "linears": {L.lin.name: [L.lin.k, L.lin.nout] for L in layers},
@@ -632,8 +681,10 @@ def main():
                                   if L.swiglu else ("bf16, " + ("RMSNorm" if L.lin.norm == 1 else "no norm"))
                                   for L in layers},
                    "mask": f"{wl.n}:{wl.m}", "format": "NVFP4" if nv else "MXFP4",
+                   "backbone": ("compressed 2:4 (kept codes + 2-bit positions), sparse f16 MFMA" if sp24 else
+                                "zero-filled, dense MFMA"),
                    "rotated_copies": args.rotate,
-                   "launch": "one HIP graph per step" if use_graph else "eager launches"},
+                   "launch": "the K timed steps as one HIP graph" if use_graph else "eager launches"},
         "prep_GBps": round(prep_gbps, 1),
         "prep_frac_hbm": round(prep_gbps / HBM_PEAK_GBPS, 4),
         "prep_GBps_bf16_input": kind_gbps(plain),
@@ -650,7 +701,9 @@ def main():
         "roofline": {"bound": "hbm" if decode else "mfma", "achieved": round(gemm_tflops, 1),
                      "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / MXFP4_PEAK_TFLOPS, 4),
                      "traffic": None,
-                     "kernel": "k_dual_gemm<NVFP4> (dual-path product, f16 MFMA)" if nv
+                     "kernel": ("k_dual_gemm<NVFP4_SP24> (dual-path product: 2:4 sparse f16 MFMA backbone, "
+                                "dense f16 MFMA residual)" if sp24 else
+                                "k_dual_gemm<NVFP4> (dual-path product, f16 MFMA)") if nv
                      else "k_dual_gemm<MXFP4> (dual-path product)",
                      "per_launch": "algorithmic 2*rows*Nout*K*(1+N/M) flops / launch time, summed over the linears",
                      "timing": timing},

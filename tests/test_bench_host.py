@@ -34,6 +34,19 @@ def test_prep_and_weight_bytes():
     assert bench.weight_bytes(128, 1536, 2048, 1) == 128 * 1536 * 2048 * (0.5 + 1 / 16)
 
 
+def test_compressed_backbone_prep_bytes_and_format_choice():
+    import types
+    import synth
+    T, K = 4096, 3584
+    # backbone: K/4 kept code bytes + K/8 position bytes; residual K/2; NVFP4 scales; mask
+    assert bench.prep_bytes(T, K, bench.FMT_NVFP4_SP24) == T * (2 * K + K // 2 + 3 * K // 8 + 2 * K // 16 + K // 8)
+    sp, dense = types.SimpleNamespace(nv_backbone="sp24"), types.SimpleNamespace(nv_backbone="dense")
+    assert bench.prep_format(synth.WORKLOADS[3], sp) == bench.FMT_NVFP4_SP24
+    assert bench.prep_format(synth.WORKLOADS[3], dense) == synth.FMT_NVFP4
+    for cid in (1, 2, 4):   # MXFP4 workloads keep the zero-filled backbone
+        assert bench.prep_format(synth.WORKLOADS[cid], sp) == synth.FMT_MXFP4
+
+
 def test_swiglu_prep_reads_gate_and_up_as_fp32():
     # the down projection's prep reads 2K float32 values per row instead of K bf16
     T, K = 2048, 14336

@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 6
+#define SHARQ_ABI_VERSION 7
 
 #if defined(__GNUC__)
 #define SHARQ_API __attribute__((visibility("default")))
@@ -238,6 +238,23 @@ SHARQ_API sharq_status sharq_quantize_weight(const void *w, int32_t w_dtype, int
                                    float *global_scale, void *workspace, size_t workspace_bytes,
                                    void *stream);
 
+/*
+ * sharq_quantize_weight_gate_up -- sharq_quantize_weight for the gate/up
+ * weight of a SwiGLU MLP, stored in the row order sharq_linear_swiglu
+ * reads: w holds the gate rows in [0, nout/2) and the up rows in
+ * [nout/2, nout) of every expert (the usual stacked layout); the payload
+ * stores them interleaved in groups of 32 rows, payload row 64p + c = gate
+ * row 32p + c and payload row 64p + 32 + c = up row 32p + c (c < 32).  Codes,
+ * scales and tensor scales are those of sharq_quantize_weight of the
+ * reordered rows.  nout % 64 == 0 (SHARQ_ERR_SHAPE otherwise); other
+ * arguments, workspace and errors as sharq_quantize_weight.  (A layout of
+ * this library, not of the pages.)
+ */
+SHARQ_API sharq_status sharq_quantize_weight_gate_up(const void *w, int32_t w_dtype, int64_t experts, int64_t nout,
+                                           int64_t K, int64_t ldw, int32_t fmt, uint8_t *codes,
+                                           uint8_t *scales, float *global_scale, void *workspace,
+                                           size_t workspace_bytes, void *stream);
+
 /* Bytes of workspace sharq_linear needs for these arguments: 0, except for
  * MXFP4 products of one weight (experts == 1) with at most 64 rows that run
  * as independent products over equal K ranges summed in a fixed order
@@ -300,6 +317,44 @@ SHARQ_API sharq_status sharq_linear(const uint8_t *b_codes, const uint8_t *b_sca
                           const int32_t *group_offsets, const int32_t *row_index, int64_t rows,
                           void *y, int32_t y_dtype, int64_t ldy, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/*
+ * sharq_linear_swiglu -- the dual-path FP4 product of a SwiGLU MLP's gate/up
+ * linear with the preparation of the down projection's input fused into its
+ * epilogue: the fused preparation operator (SharQ: Bridging Activation
+ * Sparsity and FP4 Quantization for LLM Inference, Abstract: mask
+ * generation and residual construction in one operator) applied to
+ * SiLU(gate) * up while the FP32 product is still in registers, so neither
+ * the product nor the activation goes through memory (this fusion is not on
+ * the pages).  MXFP4 only.
+ *
+ * With Y the product sharq_linear computes (FP32, same accumulation order)
+ * on a weight payload from sharq_quantize_weight_gate_up, and gate / up the
+ * de-interleaved halves of each row of Y (gate[k] = Y[r][64(k/32) + k%32],
+ * up[k] = Y[r][64(k/32) + 32 + k%32], k < nout/2), every output row r is
+ * the sharq_prepare_swiglu preparation (same SiLU, same N:M selection, same
+ * MXFP4 backbone and residual) of that row: an MXFP4 prepared activation of
+ * rows x nout/2 elements.
+ *
+ *   b_codes .. rows  inputs as sharq_linear (activations MXFP4, weights from
+ *                sharq_quantize_weight_gate_up; nout % 256 == 0)
+ *   n, m         N:M mask of the output, 0 <= n <= m, m in {1, 2, 4}
+ *                (m = 8 or 16: SHARQ_ERR_UNSUPPORTED)
+ *   mask         [rows][nout/16] bitmap or NULL (not written), 4-byte aligned
+ *   out_b_codes, out_b_scales, out_r_codes, out_r_scales  the prepared
+ *                output, K-tiled with rows = rows and K = nout/2 (as
+ *                sharq_prepare writes it); code arrays 8-byte aligned
+ *   y            NULL, or [rows][ldy] FP32 (ldy >= nout, 4-byte aligned):
+ *                also receives Y itself, in the interleaved column order
+ * No workspace.  Validation and errors as sharq_linear.
+ */
+SHARQ_API sharq_status sharq_linear_swiglu(const uint8_t *b_codes, const uint8_t *b_scales, const uint8_t *r_codes,
+                                 const uint8_t *r_scales, int64_t T, int64_t K, const uint8_t *w_codes,
+                                 const uint8_t *w_scales, int64_t experts, int64_t nout,
+                                 const int32_t *group_offsets, const int32_t *row_index, int64_t rows,
+                                 int32_t n, int32_t m, uint8_t *mask, uint8_t *out_b_codes,
+                                 uint8_t *out_b_scales, uint8_t *out_r_codes, uint8_t *out_r_scales, float *y,
+                                 int64_t ldy, void *stream);
 
 #ifdef __cplusplus
 }

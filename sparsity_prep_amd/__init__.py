@@ -63,11 +63,16 @@ def lib() -> ctypes.CDLL:
         L.sharq_quantize_weight_workspace_size.restype = sz
         L.sharq_quantize_weight.argtypes = [p, i32, i64, i64, i64, i64, i32, p, p, p, p, sz, p]
         L.sharq_quantize_weight.restype = ctypes.c_int
+        L.sharq_quantize_weight_gate_up.argtypes = [p, i32, i64, i64, i64, i64, i32, p, p, p, p, sz, p]
+        L.sharq_quantize_weight_gate_up.restype = ctypes.c_int
         L.sharq_linear_workspace_size.argtypes = [i64, i64, i64, i64, i32]
         L.sharq_linear_workspace_size.restype = sz
         L.sharq_linear.argtypes = [p, p, p, p, p, i64, i64, i32, p, p, p, i64, i64, p, p, i64,
                                    p, i32, i64, p, sz, p]
         L.sharq_linear.restype = ctypes.c_int
+        L.sharq_linear_swiglu.argtypes = [p, p, p, p, i64, i64, p, p, i64, i64, p, p, i64, i32, i32,
+                                          p, p, p, p, p, p, i64, p]
+        L.sharq_linear_swiglu.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -193,11 +198,14 @@ def prepare_swiglu(gate_up: torch.Tensor, K: int, n: int = 2, m: int = 4, fmt: i
     return out
 
 
-def quantize_weight(w: torch.Tensor, fmt: int = MXFP4) -> QWeight:
+def quantize_weight(w: torch.Tensor, fmt: int = MXFP4, gate_up: bool = False) -> QWeight:
     """RTN quantization of W[nout, K] or W[E, nout, K] into one FP4 payload.
     Rows may be strided (a column slice of a wider matrix): unit element
     stride, row stride ldw, expert stride nout * ldw.  NVFP4_SP24 names the
-    NVFP4 payload (weights are never compressed)."""
+    NVFP4 payload (weights are never compressed).  gate_up: W stacks a
+    SwiGLU gate (rows [0, nout/2)) and up (rows [nout/2, nout)) weight; the
+    payload holds them interleaved in 32-row groups, the order linear_swiglu
+    reads."""
     if fmt == NVFP4_SP24:
         fmt = NVFP4
     if w.dim() == 2:
@@ -214,10 +222,10 @@ def quantize_weight(w: torch.Tensor, fmt: int = MXFP4) -> QWeight:
                 global_scale=torch.empty(E, dtype=torch.float32, device=w.device) if fmt == NVFP4 else None,
                 E=E, nout=nout, K=K, fmt=fmt)
     ws = _workspace(lib().sharq_quantize_weight_workspace_size(E, nout, K, fmt), w.device)
-    st = lib().sharq_quantize_weight(_ptr(w), _DTYPE[w.dtype], E, nout, K, ldw, fmt, _ptr(q.codes),
-                                     _ptr(q.scales), _ptr(q.global_scale), _ptr(ws),
-                                     0 if ws is None else ws.numel(), _stream(w.device))
-    _check(st, "sharq_quantize_weight")
+    entry = lib().sharq_quantize_weight_gate_up if gate_up else lib().sharq_quantize_weight
+    st = entry(_ptr(w), _DTYPE[w.dtype], E, nout, K, ldw, fmt, _ptr(q.codes), _ptr(q.scales),
+               _ptr(q.global_scale), _ptr(ws), 0 if ws is None else ws.numel(), _stream(w.device))
+    _check(st, "sharq_quantize_weight_gate_up" if gate_up else "sharq_quantize_weight")
     return q
 
 
@@ -246,4 +254,34 @@ def linear(prep: Prepared, wq: QWeight, group_offsets: Optional[torch.Tensor] = 
         _ptr(wq.global_scale), wq.E, wq.nout, _ptr(group_offsets), _ptr(row_index), rows,
         _ptr(out), _OUT_DTYPE[out.dtype], out.stride(0), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
     _check(st, "sharq_linear")
+    return out
+
+
+def linear_swiglu(prep: Prepared, wq: QWeight, n: int = 2, m: int = 4, group_offsets: Optional[torch.Tensor] = None,
+                  row_index: Optional[torch.Tensor] = None, rows: Optional[int] = None, with_mask: bool = True,
+                  out: Optional[Prepared] = None, y: Optional[torch.Tensor] = None) -> Prepared:
+    """The gate/up product (MXFP4, weight from quantize_weight(..., gate_up=True))
+    with the down projection's preparation in its epilogue: returns the
+    MXFP4 prepared activation SiLU(gate) * up of [rows, nout/2].  y: an
+    optional float32 [rows, nout] tensor that also receives the product (in
+    the interleaved column order)."""
+    if prep.fmt != MXFP4 or wq.fmt != MXFP4 or prep.K != wq.K:
+        raise SharqError("linear_swiglu takes MXFP4 activations and weights of the same K")
+    if rows is None:
+        rows = row_index.numel() if row_index is not None else prep.T
+    dev = prep.b_codes.device
+    Kd = wq.nout // 2
+    if out is None:
+        out = alloc_prepared(rows, Kd, MXFP4, dev, with_mask)
+    elif out.T != rows or out.K != Kd or out.fmt != MXFP4:
+        raise SharqError("out does not match [rows, nout/2] MXFP4")
+    if y is not None and (y.dim() != 2 or y.dtype != torch.float32 or y.shape[0] < rows or y.shape[1] != wq.nout
+                          or y.stride(1) != 1):
+        raise SharqError("y must be a float32 [rows, nout] tensor with unit column stride")
+    st = lib().sharq_linear_swiglu(
+        _ptr(prep.b_codes), _ptr(prep.b_scales), _ptr(prep.r_codes), _ptr(prep.r_scales), prep.T, prep.K,
+        _ptr(wq.codes), _ptr(wq.scales), wq.E, wq.nout, _ptr(group_offsets), _ptr(row_index), rows, n, m,
+        _ptr(out.mask), _ptr(out.b_codes), _ptr(out.b_scales), _ptr(out.r_codes), _ptr(out.r_scales),
+        _ptr(y), 0 if y is None else y.stride(0), _stream(dev))
+    _check(st, "sharq_linear_swiglu")
     return out

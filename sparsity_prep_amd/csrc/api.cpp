@@ -234,13 +234,18 @@ size_t sharq_quantize_weight_workspace_size(int64_t experts, int64_t nout, int64
     return quantize_weight_workspace_bytes(experts, nout, kernel_fmt(fmt));
 }
 
-sharq_status sharq_quantize_weight(const void *w, int32_t w_dtype, int64_t experts, int64_t nout,
-                                   int64_t K, int64_t ldw, int32_t fmt, uint8_t *codes, uint8_t *scales,
-                                   float *global_scale, void *workspace, size_t workspace_bytes,
-                                   void *stream) {
+}  // extern "C"
+
+namespace {
+
+sharq_status quantize_weight_impl(const char *what, bool interleave, const void *w, int32_t w_dtype,
+                                  int64_t experts, int64_t nout, int64_t K, int64_t ldw, int32_t fmt,
+                                  uint8_t *codes, uint8_t *scales, float *global_scale, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
     if (!valid_fmt(fmt)) return SHARQ_ERR_UNSUPPORTED;
     if (w_dtype != SHARQ_BF16 && w_dtype != SHARQ_F16) return SHARQ_ERR_DTYPE;
     if (experts < 1 || nout < 0 || K <= 0 || K % block_of(fmt) != 0 || ldw < K) return SHARQ_ERR_SHAPE;
+    if (interleave && nout % 64 != 0) return SHARQ_ERR_SHAPE;
     if (nout == 0) return SHARQ_OK;
     if (!w || !codes || !scales) return SHARQ_ERR_NULL;
     if (is_nv(fmt) && !global_scale) return SHARQ_ERR_NULL;
@@ -261,8 +266,29 @@ sharq_status sharq_quantize_weight(const void *w, int32_t w_dtype, int64_t exper
     a.codes = codes;
     a.scales = scales;
     a.global_scale = global_scale;
-    return finish("sharq_quantize_weight", launch_quantize_weight(a, workspace, static_cast<hipStream_t>(stream)),
+    a.gate_up_interleave = interleave;
+    return finish(what, launch_quantize_weight(a, workspace, static_cast<hipStream_t>(stream)),
                   static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+sharq_status sharq_quantize_weight(const void *w, int32_t w_dtype, int64_t experts, int64_t nout,
+                                   int64_t K, int64_t ldw, int32_t fmt, uint8_t *codes, uint8_t *scales,
+                                   float *global_scale, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+    return quantize_weight_impl("sharq_quantize_weight", false, w, w_dtype, experts, nout, K, ldw, fmt, codes,
+                                scales, global_scale, workspace, workspace_bytes, stream);
+}
+
+sharq_status sharq_quantize_weight_gate_up(const void *w, int32_t w_dtype, int64_t experts, int64_t nout,
+                                           int64_t K, int64_t ldw, int32_t fmt, uint8_t *codes,
+                                           uint8_t *scales, float *global_scale, void *workspace,
+                                           size_t workspace_bytes, void *stream) {
+    return quantize_weight_impl("sharq_quantize_weight_gate_up", true, w, w_dtype, experts, nout, K, ldw, fmt,
+                                codes, scales, global_scale, workspace, workspace_bytes, stream);
 }
 
 size_t sharq_linear_workspace_size(int64_t rows, int64_t K, int64_t nout, int64_t experts,
@@ -324,7 +350,70 @@ sharq_status sharq_linear(const uint8_t *b_codes, const uint8_t *b_scales, const
     a.ksplit_tiles = 0;
     a.split_stride = 0;
     a.xcd_band = 0;
+    a.p_mask = a.p_b_codes = a.p_b_scales = a.p_r_codes = a.p_r_scales = nullptr;
+    a.p_n = a.p_m = 0;
     return finish("sharq_linear", launch_linear(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream)),
+                  static_cast<hipStream_t>(stream));
+}
+
+sharq_status sharq_linear_swiglu(const uint8_t *b_codes, const uint8_t *b_scales, const uint8_t *r_codes,
+                                 const uint8_t *r_scales, int64_t T, int64_t K, const uint8_t *w_codes,
+                                 const uint8_t *w_scales, int64_t experts, int64_t nout,
+                                 const int32_t *group_offsets, const int32_t *row_index, int64_t rows,
+                                 int32_t n, int32_t m, uint8_t *mask, uint8_t *out_b_codes,
+                                 uint8_t *out_b_scales, uint8_t *out_r_codes, uint8_t *out_r_scales, float *y,
+                                 int64_t ldy, void *stream) {
+    if (T < 0 || K <= 0 || K % 128 != 0 || experts < 1 || nout < 0 || nout % 256 != 0 || rows < 0)
+        return SHARQ_ERR_SHAPE;
+    if (m != 1 && m != 2 && m != 4 && m != 8 && m != 16) return SHARQ_ERR_NM;
+    if (n < 0 || n > m) return SHARQ_ERR_NM;
+    if (m > 4) return SHARQ_ERR_UNSUPPORTED;  // mask groups held inside one lane
+    if (experts == 1 && !group_offsets && !row_index && rows != T) return SHARQ_ERR_SHAPE;
+    if (experts > 1 && !group_offsets) return SHARQ_ERR_NULL;
+    if (y && ldy < nout) return SHARQ_ERR_SHAPE;
+    if (rows == 0 || nout == 0) return SHARQ_OK;
+    if (T == 0) return SHARQ_ERR_SHAPE;
+    if (!b_codes || !b_scales || !r_codes || !r_scales || !w_codes || !w_scales || !out_b_codes ||
+        !out_b_scales || !out_r_codes || !out_r_scales)
+        return SHARQ_ERR_NULL;
+    if (!aligned(b_codes, 16) || !aligned(r_codes, 16) || !aligned(w_codes, 16) || !aligned(b_scales, 4) ||
+        !aligned(r_scales, 4) || !aligned(w_scales, 4) || !aligned(out_b_codes, 8) || !aligned(out_r_codes, 8) ||
+        (mask && !aligned(mask, 4)) || (y && !aligned(y, 4)))
+        return SHARQ_ERR_ALIGN;
+    const int64_t limit = (int64_t)1 << 31;
+    if (T * (K / 2) >= limit || nout * (K / 2) >= limit) return SHARQ_ERR_SHAPE;
+    LinearArgs a;
+    a.b_codes = b_codes;
+    a.b_scales = b_scales;
+    a.r_codes = r_codes;
+    a.r_scales = r_scales;
+    a.x_gscale = nullptr;
+    a.T = T;
+    a.K = K;
+    a.fmt = kFmtMx;
+    a.w_codes = w_codes;
+    a.w_scales = w_scales;
+    a.w_gscale = nullptr;
+    a.E = experts;
+    a.nout = nout;
+    a.offsets = experts > 1 ? group_offsets : nullptr;
+    a.row_index = row_index;
+    a.rows = rows;
+    a.y = y;
+    a.ydt = kOutF32;
+    a.ldy = y ? ldy : nout;
+    a.y_vec = y && aligned(y, 16) && ldy % 4 == 0;
+    a.ksplit_tiles = 0;
+    a.split_stride = 0;
+    a.xcd_band = 0;
+    a.p_mask = mask;
+    a.p_b_codes = out_b_codes;
+    a.p_b_scales = out_b_scales;
+    a.p_r_codes = out_r_codes;
+    a.p_r_scales = out_r_scales;
+    a.p_n = n;
+    a.p_m = m;
+    return finish("sharq_linear_swiglu", launch_linear_swiglu(a, static_cast<hipStream_t>(stream)),
                   static_cast<hipStream_t>(stream));
 }
 

@@ -235,4 +235,58 @@ __device__ __forceinline__ float e4m3_value(uint32_t s) {
     return e == 0u ? (float)f * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (f << 20));
 }
 
+// ---------------------------------------------------------------- selection
+// keep bit i of the result is set when element i (of the 8 owned by the lane)
+// is among the N largest magnitudes of its M-group; equal magnitudes favour
+// the lower index.  M in {1,2,4,8}: groups lie inside the lane.
+template <int M>
+__device__ __forceinline__ uint32_t select_in_lane(const float v[8], int n) {
+    uint32_t key[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) key[i] = __float_as_uint(v[i]) & 0x7FFFFFFFu;
+    uint32_t keep = 0;
+#pragma unroll
+    for (int g = 0; g < 8; g += M) {
+#pragma unroll
+        for (int i = 0; i < M; i++) {
+            int rank = 0;
+#pragma unroll
+            for (int j = 0; j < M; j++) {
+                if (j == i) continue;
+                const bool beats = j < i ? key[g + j] >= key[g + i] : key[g + j] > key[g + i];
+                rank += beats ? 1 : 0;
+            }
+            keep |= (rank < n ? 1u : 0u) << (g + i);
+        }
+    }
+    return keep;
+}
+
+// ---------------------------------------------------------------- SiLU(gate) * up source
+// The activation of a down projection computed from the gate/up product's
+// float rows: x = fl32(SiLU(gate) * up), SiLU(g) = g / (1 + e^-g), with e^y
+// evaluated by fixed correctly rounded float steps: Cody-Waite reduction
+// y = n ln2 + r (n = rint(y log2 e), ln2 as a 15-bit head plus a tail), the
+// degree-6 Taylor polynomial of e^r in Horner form, scaling by 2^n; 0 below
+// -87 (never subnormal), +inf above 88.
+__device__ __forceinline__ float exp32_fixed(float y) {
+    if (!(y <= 88.0f)) return __builtin_inff();
+    if (y < -87.0f) return 0.0f;
+    const float n = __builtin_rintf(__fmul_rn(y, 1.44269504f));
+    const float r = __fsub_rn(__fsub_rn(y, __fmul_rn(n, 0.693145752f)), __fmul_rn(n, 1.42860677e-6f));
+    float p = 0.00138888889f;                      // 1/720
+    p = __fadd_rn(__fmul_rn(p, r), 0.00833333333f);  // 1/120
+    p = __fadd_rn(__fmul_rn(p, r), 0.0416666667f);   // 1/24
+    p = __fadd_rn(__fmul_rn(p, r), 0.166666667f);    // 1/6
+    p = __fadd_rn(__fmul_rn(p, r), 0.5f);
+    p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+    p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+    return __builtin_ldexpf(p, (int)n);
+}
+
+__device__ __forceinline__ float silu_times(float g, float u) {
+    const float d = __fadd_rn(1.0f, exp32_fixed(-g));
+    return __fmul_rn(__fdiv_rn(g, d), u);
+}
+
 }  // namespace sharq

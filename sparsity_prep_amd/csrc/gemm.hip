@@ -829,9 +829,95 @@ __device__ __forceinline__ bool xcd_group_item(const LinearArgs &a, int xcd, int
     return false;
 }
 
+// SwiGLU epilogue (MXFP4): the tile's weight rows are gate/up pairs
+// interleaved in 32-row groups (gate_up_row), so fragments 2p and 2p+1 of a
+// wave hold gate and up of the same 32 hidden columns hc0 .. hc0+31 at the
+// same accumulator positions: lane l, value 4q + e is column 8q + 4fq + e
+// (fq = l / 32) of row l % 32, which makes the 32 columns one MX block held
+// by lanes l and l ^ 32, sixteen values each, in four aligned groups of
+// four.  Each value becomes x = fl32(SiLU(gate) * up) and the block is
+// decomposed as the preparation operator does it (N:M mask, backbone codes
+// and E8M0 scale, residual against the dequantized backbone, its codes and
+// scale), then stored in the next linear's K-tiled layout (rows = a.rows,
+// K = nout / 2): lane fq writes bytes 8fq .. 8fq+7 of the block's 16 code
+// bytes of each path (the partner's nibbles come by one lane exchange),
+// lane 0..31 the block's four mask bytes and the backbone scale, lane
+// 32..63 the residual scale.
+template <int M, int FM, int FN>
+__device__ __forceinline__ void swiglu_epilogue(const LinearArgs &a, const v16f (&acc)[FM][FN], const TileRows &tr,
+                                                int64_t n0, int lane, int wm, int wn) {
+    static_assert(FN % 2 == 0, "gate/up fragment pairs");
+    static_assert(M == 1 || M == 2 || M == 4, "mask groups inside the lane");
+    const int frow = lane & 31, fq = lane >> 5;
+    const int64_t Kd = a.nout / 2, Td = a.rows;
+    const int64_t hb = (n0 + wn * (FN * 32)) / 2;  // hidden column of the wave's first pair
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+        const int64_t m = tr.m0 + wm * (FM * 32) + i * 32 + frow;
+        const bool row_ok = m < tr.m_end;
+#pragma unroll
+        for (int jp = 0; jp < FN / 2; jp++) {
+            const int64_t hc0 = hb + jp * 32;
+            if (hc0 >= Kd) continue;  // wave-uniform: columns past the product
+            float h[16], S[16], dq[16], R[16];
+#pragma unroll
+            for (int k = 0; k < 16; k++) h[k] = silu_times(acc[i][2 * jp][k], acc[i][2 * jp + 1][k]);
+            const uint32_t keep = select_in_lane<M>(h, a.p_n) | (select_in_lane<M>(h + 8, a.p_n) << 8);
+            float am = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 16; k++) {
+                S[k] = (keep >> k) & 1u ? h[k] : 0.0f;
+                am = fmaxf(am, fabsf(S[k]));
+            }
+            am = fmaxf(am, __shfl_xor(am, 32, 64));
+            const int Eb = mx_shared_exp(am);
+            const float sb = e8m0_operand(Eb);
+            const uint32_t bc0 = e2m1_cvt8(S, sb), bc1 = e2m1_cvt8(S + 8, sb);
+            e2m1_dec8(bc0, sb, dq);
+            e2m1_dec8(bc1, sb, dq + 8);
+            float ar = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 16; k++) {
+                R[k] = __fsub_rn(h[k], dq[k]);
+                ar = fmaxf(ar, fabsf(R[k]));
+            }
+            ar = fmaxf(ar, __shfl_xor(ar, 32, 64));
+            const int Er = mx_shared_exp(ar);
+            const float sr = e8m0_operand(Er);
+            const uint32_t rc0 = e2m1_cvt8(R, sr), rc1 = e2m1_cvt8(R + 8, sr);
+            // block code bytes: lane fq = 0 holds columns 0-3, 8-11 (bc0) and
+            // 16-19, 24-27 (bc1), lane fq = 1 columns 4-7, 12-15, 20-23, 28-31
+            const uint32_t bx = __shfl_xor(fq ? bc0 : bc1, 32, 64);
+            const uint32_t rx = __shfl_xor(fq ? rc0 : rc1, 32, 64);
+            const uint32_t bl = fq ? bx : bc0, bh = fq ? bc1 : bx;  // words of lane 0..31 / 32..63
+            const uint32_t rl = fq ? rx : rc0, rh = fq ? rc1 : rx;
+            const uint2 bw = make_uint2((bl & 0xFFFFu) | (bh << 16), (bl >> 16) | (bh & 0xFFFF0000u));
+            const uint2 rw = make_uint2((rl & 0xFFFFu) | (rh << 16), (rl >> 16) | (rh & 0xFFFF0000u));
+            // mask: byte q of the block = nibble q of lane fq = 0 | nibble q of lane fq = 1 << 4
+            const uint32_t sp = (keep & 0xFu) | ((keep & 0xF0u) << 4) | ((keep & 0xF00u) << 8) | ((keep & 0xF000u) << 12);
+            const uint32_t mw = sp | (__shfl_xor(sp, 32, 64) << 4);
+            if (row_ok) {
+                const int64_t kt = hc0 / kTileK;
+                const int64_t co = kt * Td * (kTileK / 2) + m * (kTileK / 2) + (hc0 % kTileK) / 2 + 8 * fq;
+                *reinterpret_cast<uint2 *>(a.p_b_codes + co) = bw;
+                *reinterpret_cast<uint2 *>(a.p_r_codes + co) = rw;
+                const int64_t so = kt * Td * (kTileK / 32) + m * (kTileK / 32) + (hc0 % kTileK) / 32;
+                if (fq == 0) {
+                    a.p_b_scales[so] = (uint8_t)(Eb + 127);
+                    if (a.p_mask) *reinterpret_cast<uint32_t *>(a.p_mask + m * (Kd / 8) + hc0 / 8) = mw;
+                } else {
+                    a.p_r_scales[so] = (uint8_t)(Er + 127);
+                }
+            }
+        }
+    }
+}
+
 // One BM x BN output tile: rows tr.m0 .. min(tr.m0 + BM, tr.m_end) - 1 of
 // expert tr.expert, columns n0 .. n0 + BN - 1.
-template <int FMT, int BM, int BN, int WGM, int WGN, int NS, int OCC, int LSPLIT, int RPS>
+// EPI = 0: the product to y; EPI = M (1, 2 or 4): the SwiGLU epilogue with
+// M-element mask groups (MXFP4), and the product to y when y is not null.
+template <int FMT, int BM, int BN, int WGM, int WGN, int NS, int OCC, int LSPLIT, int RPS, int EPI = 0>
 __device__ __forceinline__ void dual_tile(const LinearArgs &a, const TileRows &tr, int64_t n0) {
     using G = DualGemm<FMT, BM, BN, WGM, WGN, NS, LSPLIT, RPS>;
     using L = typename G::L;
@@ -958,21 +1044,27 @@ __device__ __forceinline__ void dual_tile(const LinearArgs &a, const TileRows &t
         }
         return;
     }
+    if (EPI == 0 || a.y != nullptr) {
 #pragma unroll
-    for (int i = 0; i < FM; i++) {
-        const int64_t m = tr.m0 + wm * (FM * 32) + i * 32 + frow;
-        if (m >= tr.m_end) continue;
+        for (int i = 0; i < FM; i++) {
+            const int64_t m = tr.m0 + wm * (FM * 32) + i * 32 + frow;
+            if (m >= tr.m_end) continue;
 #pragma unroll
-        for (int j = 0; j < FN; j++) {
+            for (int j = 0; j < FN; j++) {
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int64_t n = n0 + wn * (FN * 32) + j * 32 + 8 * q + 4 * fq;
-                v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                if constexpr (FMT != kFmtMx) v = v4f{__fmul_rn(v.x, alpha), __fmul_rn(v.y, alpha),
-                                                     __fmul_rn(v.z, alpha), __fmul_rn(v.w, alpha)};
-                store_out4(a, m, n, v);
+                for (int q = 0; q < 4; q++) {
+                    const int64_t n = n0 + wn * (FN * 32) + j * 32 + 8 * q + 4 * fq;
+                    v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    if constexpr (FMT != kFmtMx) v = v4f{__fmul_rn(v.x, alpha), __fmul_rn(v.y, alpha),
+                                                         __fmul_rn(v.z, alpha), __fmul_rn(v.w, alpha)};
+                    store_out4(a, m, n, v);
+                }
             }
         }
+    }
+    if constexpr (EPI != 0) {
+        static_assert(FMT == kFmtMx, "the SwiGLU epilogue is MXFP4");
+        swiglu_epilogue<EPI, FM, FN>(a, acc, tr, n0, g.lane, wm, wn);
     }
 }
 
@@ -984,7 +1076,7 @@ __device__ __forceinline__ void dual_tile(const LinearArgs &a, const TileRows &t
 // one expert run together on one XCD and share its weight and token rows in
 // that XCD's L2.  OCC workgroups share a CU (LDS and registers are sized for
 // that).
-template <int FMT, int BM, int BN, int WGM, int WGN, int NS, int OCC, int LSPLIT, int RPS, bool GROUPED>
+template <int FMT, int BM, int BN, int WGM, int WGN, int NS, int OCC, int LSPLIT, int RPS, bool GROUPED, int EPI>
 __global__ __launch_bounds__(WGM * WGN * 64)
 __attribute__((amdgpu_waves_per_eu(OCC * WGM * WGN / 4, OCC * WGM * WGN / 4)))
 void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles, int64_t n_begin) {
@@ -1012,7 +1104,7 @@ void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles, int64_t n_beg
         tr.m0 = (t % n_mtiles) * BM;
         tr.m_end = a.rows;
         tr.expert = 0;
-        dual_tile<FMT, BM, BN, WGM, WGN, NS, OCC, LSPLIT, RPS>(a, tr, n_begin + (t / n_mtiles) * BN);
+        dual_tile<FMT, BM, BN, WGM, WGN, NS, OCC, LSPLIT, RPS, EPI>(a, tr, n_begin + (t / n_mtiles) * BN);
         return;
     }
     // grouped: one tile found from blockIdx.x, or a persistent walk over
@@ -1030,7 +1122,7 @@ void k_dual_gemm(LinearArgs a, int64_t n_ntiles, int64_t n_mtiles, int64_t n_beg
             if (!grouped_tile_rows<BM>(a, blockIdx.x / n_ntiles, tr)) return;
             n0 = n_begin + (blockIdx.x % n_ntiles) * BN;
         }
-        dual_tile<FMT, BM, BN, WGM, WGN, NS, OCC, LSPLIT, RPS>(a, tr, n0);
+        dual_tile<FMT, BM, BN, WGM, WGN, NS, OCC, LSPLIT, RPS, EPI>(a, tr, n0);
         if (!persistent) return;
     }
 }
@@ -1186,7 +1278,7 @@ static int device_cus();
 // their XCD's share of the expert tiles; otherwise one workgroup per tile
 // (an upper bound of tiles is launched, the extra workgroups exit).
 template <int FMT, int BM, int BN, int WGM, int WGN, int NS = 3, int OCC = 1, int LSPLIT = 0, int RPS = 1,
-          bool GROUPED = false>
+          bool GROUPED = false, int EPI = 0>
 static hipError_t launch_prefill(const LinearArgs &a, hipStream_t st, int64_t n_begin = 0, int64_t n_end = -1,
                                  bool persistent = false) {
     if (n_end < 0) n_end = a.nout;
@@ -1215,7 +1307,7 @@ static hipError_t launch_prefill(const LinearArgs &a, hipStream_t st, int64_t n_
         }
     }
     const unsigned splits = a.ksplit_tiles > 0 ? (unsigned)(a.K / kTileK / a.ksplit_tiles) : 1u;
-    hipLaunchKernelGGL((k_dual_gemm<FMT, BM, BN, WGM, WGN, NS, OCC, LSPLIT, RPS, GROUPED>), dim3((unsigned)blocks, splits),
+    hipLaunchKernelGGL((k_dual_gemm<FMT, BM, BN, WGM, WGN, NS, OCC, LSPLIT, RPS, GROUPED, EPI>), dim3((unsigned)blocks, splits),
                        dim3(WGM * WGN * 64), 0,
                        st, ab, n_ntiles, n_mtiles, n_begin);
     return hipGetLastError();
@@ -1260,9 +1352,12 @@ static double shape_time(int s, int64_t rows, int64_t cols, int64_t cus) {
     return (double)((tiles + cus - 1) / cus) * t.bm * t.bn * t.cost;
 }
 
-static int best_shape(int64_t rows, int64_t cols, int64_t cus, double *t_best) {
+// Fastest shape by the model; even_fn: only shapes whose waves hold an even
+// number of 32-column fragments (the SwiGLU epilogue's gate/up pairs).
+static int best_shape(int64_t rows, int64_t cols, int64_t cus, double *t_best, bool even_fn = false) {
     int best = 0;
     for (int s = 0; s < kNumMxShapes; s++) {
+        if (even_fn && s == 3) continue;  // 256x192: three fragments per wave
         const double t = shape_time(s, rows, cols, cus);
         if (s == 0 || t < *t_best) {
             best = s;
@@ -1272,12 +1367,14 @@ static int best_shape(int64_t rows, int64_t cols, int64_t cus, double *t_best) {
     return best;
 }
 
+template <int EPI = 0>
 static hipError_t launch_mx_shape(int s, const LinearArgs &a, hipStream_t st, int64_t n_begin, int64_t n_end) {
     // split loads over two sub-steps, two LDS reads per MFMA slot
-    if (s == 0) return launch_prefill<kFmtMx, 256, 256, 4, 2, 3, 1, 4, 2>(a, st, n_begin, n_end);
-    if (s == 1) return launch_prefill<kFmtMx, 128, 256, 2, 2, 3, 1, 4, 2>(a, st, n_begin, n_end);
-    if (s == 3) return launch_prefill<kFmtMx, 256, 192, 4, 2, 3, 1, 4, 2>(a, st, n_begin, n_end);
-    return launch_prefill<kFmtMx, 128, 128, 2, 2>(a, st, n_begin, n_end);
+    if (s == 0) return launch_prefill<kFmtMx, 256, 256, 4, 2, 3, 1, 4, 2, false, EPI>(a, st, n_begin, n_end);
+    if (s == 1) return launch_prefill<kFmtMx, 128, 256, 2, 2, 3, 1, 4, 2, false, EPI>(a, st, n_begin, n_end);
+    if constexpr (EPI == 0)
+        if (s == 3) return launch_prefill<kFmtMx, 256, 192, 4, 2, 3, 1, 4, 2>(a, st, n_begin, n_end);
+    return launch_prefill<kFmtMx, 128, 128, 2, 2, 3, 1, 0, 1, false, EPI>(a, st, n_begin, n_end);
 }
 
 // A product whose 256x256 tiles fill some rounds of the CUs and leave a
@@ -1382,6 +1479,37 @@ static hipError_t launch_linear_mx_few_rows(const LinearArgs &a, void *ws, size_
     if (fm == 2) return launch_small<2>(a, st);
     if (fm == 3) return launch_small<3>(a, st);
     return launch_small<4>(a, st);
+}
+
+// SwiGLU-epilogue products (MXFP4): the tile shapes of launch_linear_mx whose
+// waves hold gate/up fragment pairs, at any row count (no few-row kernels).
+template <int EPI>
+static hipError_t launch_mx_swiglu(const LinearArgs &a, hipStream_t st) {
+    if (a.offsets)
+        return launch_prefill<kFmtMx, 128, 256, 2, 2, 2, 2, 0, 1, true, EPI>(a, st, 0, -1, a.E >= 16);
+    const int64_t cus = device_cus();
+    double t_one = 0.0;
+    const int one = best_shape(a.rows, a.nout, cus, &t_one, true);
+    const int64_t mt = (a.rows + 255) / 256;
+    const int64_t full_rounds = (mt * ((a.nout + 255) / 256)) / cus;
+    const int64_t n_split = (full_rounds * cus / mt) * 256;
+    if (full_rounds >= 1 && n_split > 0 && n_split < a.nout) {
+        double t_rem = 0.0;
+        const int rem = best_shape(a.rows, a.nout - n_split, cus, &t_rem, true);
+        const double t_main = (double)((mt * (n_split / 256) + cus - 1) / cus) * 256 * 256;
+        if (t_main + t_rem < 0.97 * t_one) {
+            const hipError_t e = launch_mx_shape<EPI>(0, a, st, 0, n_split);
+            if (e != hipSuccess) return e;
+            return launch_mx_shape<EPI>(rem, a, st, n_split, a.nout);
+        }
+    }
+    return launch_mx_shape<EPI>(one, a, st, 0, a.nout);
+}
+
+hipError_t launch_linear_swiglu(const LinearArgs &a, hipStream_t st) {
+    if (a.p_m == 1) return launch_mx_swiglu<1>(a, st);
+    if (a.p_m == 2) return launch_mx_swiglu<2>(a, st);
+    return launch_mx_swiglu<4>(a, st);
 }
 
 static hipError_t launch_linear_mx(const LinearArgs &a, void *ws, size_t ws_bytes, hipStream_t st) {

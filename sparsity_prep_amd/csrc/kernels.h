@@ -69,7 +69,18 @@ struct QuantWArgs {
     bool bf16;
     uint8_t *codes, *scales;
     float *global_scale;
+    // gate/up weight (gate rows [0, nout/2), up rows [nout/2, nout)) stored
+    // with the two halves interleaved in 32-row groups: payload row
+    // 64p + c holds gate row 32p + c, row 64p + 32 + c up row 32p + c
+    bool gate_up_interleave;
 };
+
+// Payload row of source row n of a gate/up weight of nout rows, interleaved
+// as above.
+__host__ __device__ inline int64_t gate_up_row(int64_t n, int64_t nout) {
+    const int64_t h = nout / 2, up = n >= h ? 1 : 0, r = n - up * h;
+    return (r / 32) * 64 + up * 32 + r % 32;
+}
 
 hipError_t launch_quantize_weight(const QuantWArgs &a, void *ws, hipStream_t st);
 size_t quantize_weight_workspace_bytes(int64_t E, int64_t nout, int fmt);
@@ -95,9 +106,17 @@ struct LinearArgs {
     // tiles of each), RB > 0 = each XCD takes a band of RB row tiles and a
     // share of the column tiles (set by the launcher)
     int64_t xcd_band;
+    // SwiGLU epilogue (launch_linear_swiglu, MXFP4): the weight rows are a
+    // gate/up pair interleaved in 32-row groups (gate_up_row); the product's
+    // FP32 rows become the next linear's prepared MXFP4 activation of rows x
+    // nout/2 elements, x = SiLU(gate) * up with an N:M mask (M in {1, 2, 4});
+    // y (FP32, may be null) additionally receives the product itself
+    uint8_t *p_mask, *p_b_codes, *p_b_scales, *p_r_codes, *p_r_scales;
+    int p_n, p_m;
 };
 
 hipError_t launch_linear(const LinearArgs &a, void *ws, size_t ws_bytes, hipStream_t st);
+hipError_t launch_linear_swiglu(const LinearArgs &a, hipStream_t st);
 size_t linear_workspace_bytes(int64_t rows, int64_t K, int64_t nout, int64_t E, int fmt);
 
 }  // namespace sharq

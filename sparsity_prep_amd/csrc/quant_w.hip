@@ -69,7 +69,8 @@ __global__ __launch_bounds__(kQWaves * kWave) void k_quant_w(QuantWArgs a) {
             uint32_t codes;
             const uint32_t sb = quant_block8<FMT>(v, G, G6, codes);
             // expert-major; each expert's [nout x K] payload is K-tiled
-            const int64_t ex = row / a.nout, n = row - ex * a.nout;
+            const int64_t ex = row / a.nout, ns = row - ex * a.nout;
+            const int64_t n = a.gate_up_interleave ? gate_up_row(ns, a.nout) : ns;
             *reinterpret_cast<uint32_t *>(a.codes + ex * a.nout * (K / 2) + ktile_offset<2>(n, e0, a.nout, K)) = codes;
             if ((lane % LPB) == 0) a.scales[ex * a.nout * (K / B) + ktile_offset<B>(n, e0, a.nout, K)] = (uint8_t)sb;
         }

@@ -109,6 +109,19 @@ int main(void) {
                         NULL),
            SHARQ_ERR_HIP);
 
+    /* sharq_quantize_weight_gate_up, sharq_linear_swiglu */
+    EXPECT(sharq_quantize_weight_gate_up(P, BF, 1, 96, 256, 256, MX, U, U, NULL, NULL, 0, NULL), SHARQ_ERR_SHAPE);
+    EXPECT(sharq_quantize_weight_gate_up(P, BF, 1, 128, 256, 256, MX, U, U, NULL, NULL, 0, NULL), SHARQ_ERR_HIP);
+    EXPECT(sharq_linear_swiglu(U, U, U, U, 4, 256, U, U, 1, 320, NULL, NULL, 4, 2, 4, U, U, U, U, U, NULL, 0, NULL),
+           SHARQ_ERR_SHAPE);
+    EXPECT(sharq_linear_swiglu(U, U, U, U, 4, 256, U, U, 1, 512, NULL, NULL, 4, 2, 8, U, U, U, U, U, NULL, 0, NULL),
+           SHARQ_ERR_UNSUPPORTED);
+    EXPECT(sharq_linear_swiglu(U, U, U, U, 4, 256, U, U, 1, 512, NULL, NULL, 4, 2, 4, U, MIS, U, U, U, NULL, 0,
+                               NULL),
+           SHARQ_ERR_ALIGN);
+    EXPECT(sharq_linear_swiglu(U, U, U, U, 4, 256, U, U, 1, 512, NULL, NULL, 4, 2, 4, U, U, U, U, U, F, 512, NULL),
+           SHARQ_ERR_HIP);
+
     /* check mode: the failed launch is reported the same way */
     setenv("SHARQ_DEBUG", "1", 1);
     EXPECT(sharq_linear(U, U, U, U, NULL, 4, 256, MX, U, U, NULL, 1, 64, NULL, NULL, 4, P, SHARQ_F32, 64, NULL, 0,

@@ -18,6 +18,7 @@ size_t quantize_weight_workspace_bytes(int64_t E, int64_t nout, int fmt) {
     return fmt == kFmtNv ? (size_t)(E * nout > 0 ? E * nout : 1) * sizeof(float) : 0;
 }
 hipError_t launch_linear(const LinearArgs &, void *, size_t, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_linear_swiglu(const LinearArgs &, hipStream_t) { return hipErrorInvalidValue; }
 size_t linear_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int) { return 0; }
 
 }  // namespace sharq

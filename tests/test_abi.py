@@ -34,7 +34,8 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     names = declared_symbols()
-    for n in ("sharq_prepare", "sharq_prepare_swiglu", "sharq_linear", "sharq_quantize_weight"):
+    for n in ("sharq_prepare", "sharq_prepare_swiglu", "sharq_linear", "sharq_quantize_weight",
+              "sharq_linear_swiglu", "sharq_quantize_weight_gate_up"):
         assert n in names
 
 
@@ -47,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.sharq_abi_version() == 6
+    assert L.sharq_abi_version() == 7
     for code in range(9):
         assert L.sharq_status_string(code)
     assert L.sharq_status_string(99) == b"unknown status"
@@ -157,6 +158,41 @@ def test_quantize_weight_validation(L):
     assert q(ldw=256 + 4) == ALIGN                # rows not 16-byte aligned
     assert q(w=None, nout=0) == OK
     assert q(fmt=NV, G=FAKE, ws=MISALIGNED, wsb=1 << 20) == ALIGN
+
+
+def test_quantize_weight_gate_up_validation(L):
+    def q(nout=128, K=256, fmt=MX, codes=FAKE, w=FAKE):
+        return L.sharq_quantize_weight_gate_up(w, BF16, 1, nout, K, K, fmt, codes, FAKE, None, None, 0, None)
+    assert q(nout=96) == SHAPE                    # gate/up pairs of 32-row groups: nout % 64
+    assert q(fmt=9) == UNSUPPORTED
+    assert q(w=None) == NULL
+    assert q(codes=MISALIGNED) == ALIGN
+    assert q(nout=0, w=None) == OK
+
+
+def lsw(L, T=4, K=256, E=1, nout=512, offs=None, ridx=None, rows=None, n=2, m=4, mask=FAKE, obc=FAKE, obs=FAKE,
+        orc=FAKE, ors=FAKE, y=None, ldy=0, bc=FAKE):
+    return L.sharq_linear_swiglu(bc, FAKE, FAKE, FAKE, T, K, FAKE, FAKE, E, nout, offs, ridx,
+                                 T if rows is None else rows, n, m, mask, obc, obs, orc, ors, y, ldy, None)
+
+
+def test_linear_swiglu_validation(L):
+    assert lsw(L, K=160) == SHAPE                 # K not a multiple of 128
+    assert lsw(L, nout=320) == SHAPE              # hidden width nout/2 not whole 128-element tiles
+    assert lsw(L, rows=7) == SHAPE                # dense rows must equal T without a gather
+    assert lsw(L, n=5) == NM
+    assert lsw(L, m=3) == NM
+    assert lsw(L, m=8) == UNSUPPORTED             # mask groups wider than a lane's four
+    assert lsw(L, E=4) == NULL                    # grouped needs offsets
+    assert lsw(L, y=FAKE, ldy=100) == SHAPE       # product output narrower than nout
+    assert lsw(L, bc=None) == NULL
+    assert lsw(L, obs=None) == NULL
+    assert lsw(L, mask=None, obc=MISALIGNED) == ALIGN
+    assert lsw(L, mask=MISALIGNED) == ALIGN
+    assert lsw(L, y=MISALIGNED, ldy=512) == ALIGN
+    assert lsw(L, T=0, rows=0, bc=None) == OK
+    assert lsw(L, nout=0, bc=None) == OK
+    assert lsw(L, T=1 << 24, K=256) == SHAPE      # T*K/2 at the 2 GiB operand limit
 
 
 def lin(L, T=4, K=256, fmt=MX, E=1, nout=64, offs=None, ridx=None, rows=None, y=FAKE, ydt=F32, ldy=None,

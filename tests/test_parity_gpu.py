@@ -441,6 +441,27 @@ def test_linear_grouped_many_experts(fmt):
     check_product(y, ref, K, "many experts")
 
 
+def test_linear_grouped_ragged_experts():
+    """Persistent grouped MXFP4 product (16 experts or more, workgroups
+    walking their XCD's expert tiles) over ragged experts: 260 rows (three
+    128-row tiles, the last holding 4 rows), 129, 65, 33, 32, 31, 1 and 0
+    rows, gathered rows."""
+    K, nout, E, T = 384, 320, 24, 200
+    x = synth.small_case(K, T, "bf16", outliers=2, tag=51)
+    pg = gpu_prepare(x, "bf16", K, 0, None, None, 0.0, 2, 4, 0)
+    w = synth.small_weight(nout, K, experts=E, tag=52)
+    qw = sq().quantize_weight(dev16(w, "bf16"), fmt=0)
+    rng = np.random.default_rng(53)
+    counts = rng.integers(0, 40, E)
+    counts[[2, 5, 9, 11, 16, 17, 20, 23]] = [260, 129, 65, 33, 32, 31, 1, 0]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    row_index = rng.integers(0, T, offsets[-1]).astype(np.int32)
+    y = host(sq().linear(pg, qw, group_offsets=torch.from_numpy(offsets).cuda(),
+                         row_index=torch.from_numpy(row_index).cuda(), rows=int(offsets[-1])))
+    _, ref = ref_linear(pg, qw, row_index=row_index, offsets=offsets)
+    check_product(y, ref, K, "ragged experts")
+
+
 @pytest.mark.parametrize("T", [4, 300], ids=["short", "tiled"])
 def test_nvfp4_every_block_scale(T):
     """NVFP4 product where the 16-element blocks take every finite E4M3
@@ -752,3 +773,142 @@ def test_qwen3_moe_full():
     _, ref = ref_linear(p, qw, offsets=route.offsets, out_rows=sample)
     err = check_product(y[sample], ref, lin.k, "moe down")
     print(f"moe down rel err {err:.2e} on {sample.size} rows", flush=True)
+
+
+# ---------------------------------------------------------------- SwiGLU epilogue (sharq_linear_swiglu)
+
+def gate_up_source_rows(nout: int) -> np.ndarray:
+    """Source row (of the stacked [gate; up] weight) of every payload row of
+    sharq_quantize_weight_gate_up: payload row 64p + c is gate row 32p + c,
+    payload row 64p + 32 + c is up row 32p + c."""
+    r = np.arange(nout)
+    p, c = r // 64, r % 64
+    return np.where(c < 32, 32 * p + c, nout // 2 + 32 * p + c - 32)
+
+
+def deinterleave(y: np.ndarray) -> np.ndarray:
+    """Columns of a product in payload order -> [gate | up] rows."""
+    out = np.empty_like(y)
+    out[:, gate_up_source_rows(y.shape[1])] = y
+    return out
+
+
+def test_quantize_weight_gate_up():
+    """The interleaved payload equals the oracle's RTN of the reordered rows."""
+    K, nout, E = 384, 320, 3
+    w = synth.small_weight(nout, K, experts=E, tag=71)
+    q = sq().quantize_weight(dev16(w, "bf16"), fmt=0, gate_up=True)
+    torch.cuda.synchronize()
+    wc, ws = weight_to_host(q)
+    src = gate_up_source_rows(nout)
+    for e in range(E):
+        o = oracle.quantize_weight(np.ascontiguousarray(w[e][src]), "bf16", 0)
+        assert np.array_equal(wc[e], o.codes[0]) and np.array_equal(ws[e], o.scales[0]), e
+
+
+def _check_swiglu(pg, qw, n, m, what, row_index=None, offsets=None, rows=None, out_rows=None):
+    """linear_swiglu against (1) the oracle's FP64 product of the same codes
+    (its optional FP32 product output, within the FP32 accumulation bound)
+    and (2) the oracle's SiLU(gate) * up preparation of that FP32 product
+    (bit-exact); the prepared output without the product output, and the
+    library's own two-kernel chain (product, then sharq_prepare_swiglu), must
+    give identical bytes."""
+    ri = None if row_index is None else torch.from_numpy(row_index).cuda()
+    go = None if offsets is None else torch.from_numpy(offsets).cuda()
+    if rows is None:
+        rows = len(row_index) if row_index is not None else (int(offsets[-1]) if offsets is not None else pg.T)
+    y = torch.full((rows, qw.nout), float("nan"), dtype=torch.float32, device="cuda")
+    pd = sq().linear_swiglu(pg, qw, n=n, m=m, group_offsets=go, row_index=ri, rows=rows, y=y)
+    pd2 = sq().linear_swiglu(pg, qw, n=n, m=m, group_offsets=go, row_index=ri, rows=rows)
+    chain = sq().prepare_swiglu(torch.from_numpy(deinterleave(host(y))).cuda(), qw.nout // 2, n=n, m=m, fmt=0)
+    torch.cuda.synchronize()
+    yh = host(y)
+    sel, ref = ref_linear(pg, qw, row_index=row_index, offsets=offsets, out_rows=out_rows)
+    err = check_product(yh[sel], ref, pg.K, what)
+    gh = prepared_to_host(pd)
+    for other in (pd2, chain):
+        oh = prepared_to_host(other)
+        for k in ("mask", "b_codes", "b_scales", "r_codes", "r_scales"):
+            assert np.array_equal(gh[k], oh[k]), (what, k)
+    gu = deinterleave(yh[sel])
+    o = oracle.prepare_swiglu(gu, qw.nout // 2, n, m, 0, trace=True)
+    gh = {k: (v[sel] if isinstance(v, np.ndarray) else v) for k, v in gh.items()}
+    stats = compare_prepared(gh, o, n, m, what)
+    assert stats["mismatched"] == 0, (what, stats)
+    return err
+
+
+SWIGLU_LINEAR_CASES = [
+    # (T, K, nout, n, m): tile shapes 256x256, 128x256, 128x128, the column
+    # split, ragged rows, every in-lane mask width
+    (300, 640, 512, 2, 4), (513, 1024, 768, 2, 4), (1, 256, 256, 2, 4), (64, 384, 1280, 1, 4),
+    (257, 512, 2304, 2, 2), (130, 256, 512, 1, 1), (96, 256, 512, 4, 4), (2049, 256, 8448, 2, 4),
+    (40, 256, 512, 0, 4), (4096, 128, 1024, 3, 4),
+]
+
+
+@pytest.mark.parametrize("case", SWIGLU_LINEAR_CASES, ids=[str(c) for c in SWIGLU_LINEAR_CASES])
+def test_linear_swiglu(case):
+    T, K, nout, n, m = case
+    tag = SWIGLU_LINEAR_CASES.index(case)
+    x = synth.small_case(K, T, "bf16", outliers=3, tag=700 + tag)
+    pg = gpu_prepare(x, "bf16", K, 0, None, None, 0.0, 2, 4, 0)
+    w = synth.small_weight(nout, K, tag=800 + tag)
+    qw = sq().quantize_weight(dev16(w, "bf16"), fmt=0, gate_up=True)
+    out_rows = None if T <= 600 else fragment_rows(T, np.random.default_rng(tag))
+    _check_swiglu(pg, qw, n, m, str(case), out_rows=out_rows)
+
+
+@pytest.mark.parametrize("E", [5, 24], ids=["grouped", "persistent"])
+def test_linear_swiglu_grouped(E):
+    """Expert products over gathered rows (five experts: one workgroup per
+    tile; 24: persistent workgroups walking their XCD's experts), ragged and
+    empty experts."""
+    K, nout, T = 384, 512, 200
+    x = synth.small_case(K, T, "bf16", outliers=2, tag=91)
+    pg = gpu_prepare(x, "bf16", K, 0, None, None, 0.0, 2, 4, 0)
+    w = synth.small_weight(nout, K, experts=E, tag=92)
+    qw = sq().quantize_weight(dev16(w, "bf16"), fmt=0, gate_up=True)
+    rng = np.random.default_rng(93)
+    counts = rng.integers(0, 60, E)
+    counts[0], counts[E - 1] = 0, 260
+    counts[E // 2] = 129
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    row_index = rng.integers(0, T, offsets[-1]).astype(np.int32)
+    _check_swiglu(pg, qw, 2, 4, f"grouped E={E}", row_index=row_index, offsets=offsets)
+
+
+def test_llama8b_gate_up_swiglu_full():
+    """Llama-3.1-8B gate_up (2048 x 28672 x 4096) with the down projection's
+    preparation in its epilogue, in the benchmark's launch configuration;
+    product and prepared rows from every 32-row fragment checked."""
+    wl = synth.WORKLOADS[1]
+    gu_lin, down = _linear(wl, "gate_up"), _linear(wl, "down")
+    x = synth.activation(wl, gu_lin, wl.tokens)
+    g = synth.gamma(wl, gu_lin)
+    pg = gpu_prepare(x, wl.dtype, gu_lin.k, gu_lin.norm, g, None, wl.eps, wl.n, wl.m, wl.fmt)
+    qw = sq().quantize_weight(dev16(synth.weight(wl, gu_lin), wl.dtype), fmt=wl.fmt, gate_up=True)
+    rows = fragment_rows(wl.tokens, np.random.default_rng(5))
+    err = _check_swiglu(pg, qw, wl.n, wl.m, "llama gate_up swiglu", out_rows=rows)
+    assert qw.nout // 2 == down.k
+    print(f"llama gate_up swiglu: rows {rows.size}, GEMM rel err {err:.2e}", flush=True)
+
+
+def test_qwen3_moe_gate_up_swiglu_full():
+    """Qwen3-30B-A3B expert gate_up (32768 gathered rows, 128 experts) with
+    the expert down projection's preparation in its epilogue."""
+    wl = synth.WORKLOADS[4]
+    route = synth.moe_routing(wl)
+    nrows = int(route.offsets[-1])
+    lin = wl.linears[0]
+    x = synth.activation(wl, lin, wl.tokens)
+    g = synth.gamma(wl, lin)
+    pg = gpu_prepare(x, wl.dtype, lin.k, lin.norm, g, None, wl.eps, wl.n, wl.m, wl.fmt)
+    qw = sq().quantize_weight(dev16(synth.weight(wl, lin), wl.dtype), fmt=wl.fmt, gate_up=True)
+    rng = np.random.default_rng(6)
+    nonempty = np.nonzero(np.diff(route.offsets))[0]
+    rows = np.unique(np.concatenate([fragment_rows(nrows, rng), route.offsets[nonempty],
+                                     route.offsets[nonempty + 1] - 1]))
+    err = _check_swiglu(pg, qw, wl.n, wl.m, "moe gate_up swiglu", row_index=route.row_index,
+                        offsets=route.offsets, out_rows=rows)
+    print(f"moe gate_up swiglu: rows {rows.size}, GEMM rel err {err:.2e}", flush=True)

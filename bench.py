@@ -71,6 +71,9 @@ def parse():
                     help="skip the BF16-output products, the unfused SiLU chain and the bf16 / fp8 GEMMs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter calibration)")
+    ap.add_argument("--swiglu-epilogue", choices=["on", "off"], default="on",
+                    help="MXFP4 prefill and MoE: the gate_up product prepares the down projection's input in its "
+                         "epilogue (sharq_linear_swiglu); off: gate_up's FP32 output, then the SiLU(gate)*up prep")
     ap.add_argument("--nv-backbone", choices=["sp24", "dense"], default="sp24",
                     help="NVFP4 2:4 workloads: store the backbone in the compressed 2:4 form and multiply it on "
                          "the sparse f16 matrix instruction (sp24), or zero-filled on the dense one (dense)")
@@ -94,6 +97,14 @@ def prep_bytes(T, K, fmt, swiglu=False):
     return T * (read + codes + 2 * K // block_of(fmt) + K // 8)
 
 
+def gate_up_source_rows(nout):
+    """Row of the stacked [gate; up] weight held by each payload row of
+    sharq_quantize_weight_gate_up (groups of 32 interleaved)."""
+    r = np.arange(nout)
+    p, c = r // 64, r % 64
+    return np.where(c < 32, 32 * p + c, nout // 2 + 32 * p + c - 32)
+
+
 def gemm_flops(rows, K, nout, n, m):
     """Algorithmic flops of the dual product: backbone (N/M dense) + residual."""
     return 2.0 * rows * nout * K * (1.0 + n / m)
@@ -113,8 +124,14 @@ class Layer:
     src's FP32 output [gate | up] (SiLU(gate)*up formed in the prep kernel)."""
 
     def __init__(self, sq, torch, synth, wl, lin, prep_tokens, rotate, dev, route=None, gather=False,
-                 src=None, prep_copies=None, pfmt=None):
+                 src=None, prep_copies=None, pfmt=None, gate_up_order=False):
         self.lin, self.wl, self.src = lin, wl, src
+        # SwiGLU epilogue: this layer's product prepares epi_dst's input
+        # (its weight rows interleaved as sharq_quantize_weight_gate_up
+        # stores them); epi_src: this layer's input comes from that epilogue
+        self.gate_up_order = gate_up_order
+        self.epi_dst = None
+        self.epi_src = None
         self.pfmt = wl.fmt if pfmt is None else pfmt  # preparation format (weights: wl.fmt)
         self.prep_tokens = prep_tokens
         self.rotate = rotate
@@ -134,7 +151,7 @@ class Layer:
             self.g = torch.from_numpy(synth.gamma(wl, lin).view(np.int16)).view(torch.bfloat16).to(dev)
         w_bits = synth.weight(wl, lin)
         w = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-        q = sq.quantize_weight(w, fmt=wl.fmt)
+        q = sq.quantize_weight(w, fmt=wl.fmt, gate_up=gate_up_order)
         del w
         self.w = [q] + [sq.QWeight(q.codes.clone(), q.scales.clone(),
                                    None if q.global_scale is None else q.global_scale.clone(),
@@ -166,6 +183,14 @@ class Layer:
 
     def run_prep(self, sq, i):
         r = i % self.n_in
+        if self.epi_src is not None:
+            return  # prepared by the epilogue of epi_src's product
+        self.run_prep_kernel(sq, i)
+
+    def run_prep_kernel(self, sq, i):
+        """This linear's preparation as its own kernel (the SiLU(gate)*up prep
+        on src's FP32 output for a down projection)."""
+        r = i % self.n_in
         if self.src is not None:
             sq.prepare_swiglu(self.src.y[i % self.src.rotate], self.lin.k, n=self.wl.n, m=self.wl.m,
                               fmt=self.pfmt, out=self.prep[r])
@@ -175,8 +200,28 @@ class Layer:
 
     def run_gemm(self, sq, i, bf16=False):
         r = i % self.rotate
+        if self.epi_dst is not None and not bf16:
+            d = self.epi_dst
+            sq.linear_swiglu(self.prep[r], self.w[r], n=self.wl.n, m=self.wl.m, group_offsets=self.offs,
+                             row_index=self.ridx, rows=self.rows, out=d.prep[i % d.n_in])
+            return
         out = self.y16[r] if bf16 else self.y[r]
         sq.linear(self.prep[r], self.w[r], group_offsets=self.offs, row_index=self.ridx, rows=self.rows, out=out)
+
+    def fill_outputs(self, sq, torch):
+        """SwiGLU-epilogue layers: their FP32 products in the usual [gate | up]
+        column order in self.y (for the host-side reports and the stand-alone
+        SiLU prep timing), from the epilogue's optional product output."""
+        if self.epi_dst is None:
+            return
+        src = torch.from_numpy(gate_up_source_rows(self.lin.nout)).to(self.y[0].device)
+        tmp = torch.empty_like(self.y[0])
+        for r in range(self.rotate):
+            sq.linear_swiglu(self.prep[r], self.w[r], n=self.wl.n, m=self.wl.m, group_offsets=self.offs,
+                             row_index=self.ridx, rows=self.rows, out=self.epi_dst.prep[r % self.epi_dst.n_in],
+                             y=tmp)
+            self.y[r][:, src] = tmp
+        del tmp
 
     def run(self, sq, i, ev=None):
         """Prep then product of rotated copy i % rotate (events around each, if given)."""
@@ -520,6 +565,20 @@ def prep_format(wl, args):
     return wl.fmt
 
 
+def swiglu_epilogue(args, wl, decode):
+    """The layer step prepares the down projection inside the gate_up
+    product (MXFP4 prefill and MoE workloads)."""
+    return getattr(args, "swiglu_epilogue", "on") == "on" and wl.fmt == 0 and not decode
+
+
+def link_epilogues(layers, epi):
+    if not epi:
+        return
+    for L in layers.values():
+        if L.src is not None:
+            L.src.epi_dst, L.epi_src = L, L.src
+
+
 def build_layers(args, sq, torch, synth, dev):
     if args.rotate is None:
         args.rotate = 8 if args.workload.startswith("decode") else 3
@@ -528,11 +587,15 @@ def build_layers(args, sq, torch, synth, dev):
         wl = synth.WORKLOADS[3 if args.workload == "qwen" else (2 if decode else 1)]
         tokens = int(args.workload[len("decode"):]) if decode else wl.tokens
         pfmt = prep_format(wl, args)
+        epi = swiglu_epilogue(args, wl, decode)
+        srcs = {lin.swiglu_of for lin in wl.linears if lin.swiglu_of}
         layers = {}
         for lin in wl.linears:
             pc = None if decode else prep_copies(tokens * lin.k * 2)
             layers[lin.name] = Layer(sq, torch, synth, wl, lin, tokens, args.rotate, dev,
-                                     src=layers.get(lin.swiglu_of), prep_copies=pc, pfmt=pfmt)
+                                     src=layers.get(lin.swiglu_of), prep_copies=pc, pfmt=pfmt,
+                                     gate_up_order=epi and lin.name in srcs)
+        link_epilogues(layers, epi)
         return wl, list(layers.values())
     if args.workload == "moe":
         wl = synth.WORKLOADS[4]
@@ -541,9 +604,11 @@ def build_layers(args, sq, torch, synth, dev):
         gu_lin, down_lin = wl.linears
         # gate_up: prep the unique tokens, the product gathers each expert's rows;
         # down: prepared from gate_up's expert-sorted FP32 rows as SiLU(gate)*up
+        epi = swiglu_epilogue(args, wl, False)
         gu = Layer(sq, torch, synth, wl, gu_lin, wl.tokens, args.rotate, dev, route, gather=True,
-                   prep_copies=prep_copies(wl.tokens * gu_lin.k * 2))
+                   prep_copies=prep_copies(wl.tokens * gu_lin.k * 2), gate_up_order=epi)
         down = Layer(sq, torch, synth, wl, down_lin, rows, args.rotate, dev, route, src=gu)
+        link_epilogues({"gu": gu, "down": down}, epi)
         return wl, [gu, down]
     raise SystemExit(f"unknown workload {args.workload}")
 
@@ -581,6 +646,8 @@ def main():
     for i in range(2):
         for L in layers:
             L.run(sq, i)
+    for L in layers:
+        L.fill_outputs(sq, torch)
     torch.cuda.synchronize()
 
     # the W warmup steps and the K timed steps, each captured as one graph
@@ -615,11 +682,15 @@ def main():
     # ---- per-launch kernel times: graphs of one phase over rotated copies,
     # measured before the timed steps so that those too start on a GPU that
     # has been busy for a while
-    prep_ms, gemm_ms = [], []
+    # prep_ms: the prep kernels (the down projection's SiLU(gate)*up prep
+    # timed on its own even when the layer step runs it in gate_up's
+    # epilogue); step_prep_ms: the step's own prep launches
+    prep_ms, gemm_ms, step_prep_ms = [], [], []
     for L in layers:
         n_prep = args.steps if decode else max(12, L.n_in)
         n_gemm = args.steps if decode else 12
-        prep_ms.append(phase_ms(torch, lambda i, L=L: L.run_prep(sq, i), n_prep))
+        prep_ms.append(phase_ms(torch, lambda i, L=L: L.run_prep_kernel(sq, i), n_prep))
+        step_prep_ms.append(0.0 if L.epi_src is not None else prep_ms[-1])
         gemm_ms.append(phase_ms(torch, lambda i, L=L: L.run_gemm(sq, i), n_gemm))
 
     # ---- W warmup steps, then exactly K timed steps
@@ -654,6 +725,7 @@ def main():
     tokens = layers[0].prep_tokens
     plain = [i for i, L in enumerate(layers) if not L.swiglu]
     fused = [i for i, L in enumerate(layers) if L.swiglu]
+    epi = any(L.epi_dst is not None for L in layers)
 
     def kind_gbps(ix):
         return None if not ix else round(sum(pbytes[i] for i in ix) / (sum(prep_ms[i] for i in ix) * 1e-3) / 1e9, 1)
@@ -684,6 +756,8 @@ def main():
                    "backbone": ("compressed 2:4 (kept codes + 2-bit positions), sparse f16 MFMA" if sp24 else
                                 "zero-filled, dense MFMA"),
                    "rotated_copies": args.rotate,
+                   "down_prep": ("in the gate_up product's epilogue (sharq_linear_swiglu)" if epi else
+                                 "its own kernel on gate_up's FP32 output") if fused else None,
                    "launch": "the K timed steps as one HIP graph" if use_graph else "eager launches"},
         "prep_GBps": round(prep_gbps, 1),
         "prep_frac_hbm": round(prep_gbps / HBM_PEAK_GBPS, 4),
@@ -692,6 +766,7 @@ def main():
         "gemm_TFLOPs": round(gemm_tflops, 1),
         "gemm_frac_peak": round(gemm_tflops / MXFP4_PEAK_TFLOPS, 4),
         "per_linear": {L.lin.name: {"rows": L.rows, "prep_us": round(prep_ms[i] * 1e3, 2),
+                                    "prep_in_step_us": round(step_prep_ms[i] * 1e3, 2),
                                     "gemm_us": round(gemm_ms[i] * 1e3, 2),
                                     "prep_bytes": pbytes[i],
                                     "prep_GBps": round(pbytes[i] / (prep_ms[i] * 1e-3) / 1e9, 1),
@@ -705,12 +780,17 @@ def main():
                                 "dense f16 MFMA residual)" if sp24 else
                                 "k_dual_gemm<NVFP4> (dual-path product, f16 MFMA)") if nv
                      else "k_dual_gemm<MXFP4> (dual-path product)",
-                     "per_launch": "algorithmic 2*rows*Nout*K*(1+N/M) flops / launch time, summed over the linears",
+                     "per_launch": "algorithmic 2*rows*Nout*K*(1+N/M) flops / launch time, summed over the linears"
+                                   + ("; the gate_up launch also prepares the down projection's input in its "
+                                      "epilogue (sharq_linear_swiglu)" if epi else ""),
                      "timing": timing},
         "roofline_prep": {"bound": "hbm", "achieved": round(prep_gbps, 1), "peak": HBM_PEAK_GBPS,
                           "unit": "GB/s", "frac": round(prep_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                           "per_launch": "algorithmic bytes (input read once, codes, scales and mask written) / "
-                                        "launch time, summed over the linears",
+                                        "launch time, summed over the linears' prep kernels"
+                                        + ("; the down projection's SiLU(gate)*up prep kernel is timed on gate_up's "
+                                           "FP32 output, while the layer step prepares that input in the gate_up "
+                                           "product's epilogue instead" if epi else ""),
                           "timing": timing},
     }
     if decode:
@@ -744,7 +824,7 @@ def main():
             "gemm_TFLOPs": round(sum(flops) / (sum(g16.values()) * 1e-3) / 1e12, 1),
             "note": "same products, Y stored as BF16; FP32 Y is the parity contract and the headline"}
         result["swiglu_prep"] = swiglu_report(sq, torch, wl, layers)
-        result["gemm_baselines"] = gemm_baselines(torch, synth, wl, layers, sum(prep_ms) + sum(gemm_ms))
+        result["gemm_baselines"] = gemm_baselines(torch, synth, wl, layers, sum(step_prep_ms) + sum(gemm_ms))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layers)
         result["error_report"] = error_report(layers)

@@ -531,10 +531,12 @@ def gemm_baselines(torch, synth, wl, layers, sharq_ms):
     return res
 
 
-def measured_traffic(name):
+def measured_traffic(name, epi=False):
     """HBM-side bytes per step of a kernel family from the committed counter
     summary under profiles/ (FETCH_SIZE / WRITE_SIZE scaled by a plain copy),
-    or None when the kernel sources changed after the counters were taken."""
+    or None when the kernel sources changed after the counters were taken or
+    the counters come from the other layer-step mode (SwiGLU epilogue on or
+    off)."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", name)
@@ -546,6 +548,8 @@ def measured_traffic(name):
             with open(os.path.join(root, src), "rb") as f:
                 h.update(f.read())
     except (OSError, ValueError, KeyError):
+        return None
+    if t.get("swiglu_epilogue", False) != epi:
         return None
     return t if h.hexdigest() == t["source_sha256"] else None
 
@@ -804,7 +808,7 @@ def main():
         result["roofline"]["frac_of_f16_peak"] = round(gemm_tflops / F16_PEAK_TFLOPS, 4)
     for key, fname in (("roofline", f"k_dual_gemm_{wl.name}.traffic.json"),
                        ("roofline_prep", f"k_prep_{wl.name}.traffic.json")):
-        t = measured_traffic(fname) if tokens == wl.tokens else None
+        t = measured_traffic(fname, epi) if tokens == wl.tokens else None
         if t is not None:
             result[key]["traffic"] = t["bytes_per_step"]
             result[key]["traffic_unit"] = "bytes per step (all launches of the kernel in one step)"

@@ -616,6 +616,40 @@ def test_graph_replay_grouped_matches_eager():
     _check_graph_replays(step, out, y)
 
 
+@pytest.mark.parametrize("grouped", [False, True], ids=["dense", "grouped"])
+def test_graph_replay_swiglu_matches_eager(grouped):
+    """The MLP half of a layer as the benchmark runs it -- gate_up prep, the
+    gate_up product with the down projection's preparation in its epilogue,
+    the down product -- captured in one HIP graph."""
+    K, nout, T = 512, 768, 300
+    E = 20 if grouped else 1
+    w = synth.small_weight(nout, K, experts=E, tag=37)
+    qgu = sq().quantize_weight(dev16(w, "bf16"), fmt=0, gate_up=True)
+    qd = sq().quantize_weight(dev16(synth.small_weight(K, nout // 2, experts=E, tag=38), "bf16"), fmt=0)
+    x = dev16(synth.small_case(K, T, "bf16", tag=39), "bf16")
+    g = dev16(synth.small_gamma(K, tag=40), "bf16")
+    offs = ridx = None
+    rows = T
+    if grouped:
+        rng = np.random.default_rng(41)
+        counts = rng.integers(0, 60, E)
+        counts[3] = 0
+        offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        rows = int(offsets[-1])
+        offs = torch.from_numpy(offsets).cuda()
+        ridx = torch.from_numpy(rng.integers(0, T, rows).astype(np.int32)).cuda()
+    p = sq().alloc_prepared(T, K, 0, x.device)
+    pd = sq().alloc_prepared(rows, nout // 2, 0, x.device)
+    y = torch.empty((rows, K), dtype=torch.float32, device="cuda")
+
+    def step():
+        sq().prepare(x, norm=1, gamma=g, eps=1e-5, n=2, m=4, fmt=0, out=p)
+        sq().linear_swiglu(p, qgu, n=2, m=4, group_offsets=offs, row_index=ridx, rows=rows, out=pd)
+        sq().linear(pd, qd, group_offsets=offs, rows=rows, out=y)
+
+    _check_graph_replays(step, pd, y)
+
+
 # ---------------------------------------------------------------- full-size workloads
 
 def _weight_sample_check(wl, lin, qw, w_bits, nrows=128, seed=0):

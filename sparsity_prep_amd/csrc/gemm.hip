@@ -1483,11 +1483,18 @@ static hipError_t launch_linear_mx_few_rows(const LinearArgs &a, void *ws, size_
 
 // SwiGLU-epilogue products (MXFP4): the tile shapes of launch_linear_mx whose
 // waves hold gate/up fragment pairs, at any row count (no few-row kernels).
+// Launches of at least two rounds of 128x256 tiles at two workgroups per CU
+// take that shape (two stages): one workgroup's SwiGLU epilogue, about 4000
+// vector instructions per wave, overlaps the other's matrix work (Llama
+// gate_up 2048 x 28672 x 4096 on MI355X: 2% faster than 256x256 tiles with
+// the column split).
 template <int EPI>
 static hipError_t launch_mx_swiglu(const LinearArgs &a, hipStream_t st) {
     if (a.offsets)
         return launch_prefill<kFmtMx, 128, 256, 2, 2, 2, 2, 0, 1, true, EPI>(a, st, 0, -1, a.E >= 16);
     const int64_t cus = device_cus();
+    if (((a.rows + 127) / 128) * ((a.nout + 255) / 256) >= 2 * 2 * cus)
+        return launch_prefill<kFmtMx, 128, 256, 2, 2, 2, 2, 0, 1, false, EPI>(a, st);
     double t_one = 0.0;
     const int one = best_shape(a.rows, a.nout, cus, &t_one, true);
     const int64_t mt = (a.rows + 255) / 256;

@@ -878,6 +878,7 @@ SWIGLU_LINEAR_CASES = [
     (300, 640, 512, 2, 4), (513, 1024, 768, 2, 4), (1, 256, 256, 2, 4), (64, 384, 1280, 1, 4),
     (257, 512, 2304, 2, 2), (130, 256, 512, 1, 1), (96, 256, 512, 4, 4), (2049, 256, 8448, 2, 4),
     (40, 256, 512, 0, 4), (4096, 128, 1024, 3, 4),
+    (2100, 128, 16384, 2, 4),  # two or more rounds of 128x256 tiles at two workgroups per CU, ragged rows
 ]
 
 

@@ -73,6 +73,8 @@ def lib():
         L.or_exp32.restype = f32
         L.or_silu32.argtypes = [f32]
         L.or_silu32.restype = f32
+        L.or_silu32_n.argtypes = [p, i64, p]
+        L.or_silu32_n.restype = None
         L.or_e2m1_encode_n.argtypes = [p, i64, p]
         L.or_e2m1_encode_n.restype = None
         L.or_e4m3_encode_n.argtypes = [p, i64, p]
@@ -231,6 +233,13 @@ def exp32(y: float) -> float:
 
 def silu32(g: float) -> float:
     return float(lib().or_silu32(float(g)))
+
+
+def silu32_array(g: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(g, dtype=np.float32)
+    out = np.empty(a.shape, np.float32)
+    lib().or_silu32_n(_ptr(a), a.size, _ptr(out))
+    return out
 
 
 def normalize(x: np.ndarray, dtype: str, K: int, norm: int, gamma, beta, eps: float) -> np.ndarray:

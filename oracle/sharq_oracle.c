@@ -364,6 +364,11 @@ float or_silu32(float g)
     return g / d;
 }
 
+void or_silu32_n(const float *g, int64_t n, float *out)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = or_silu32(g[i]);
+}
+
 /* ------------------------------------------------------------------ */
 /* public entry points                                                 */
 /* ------------------------------------------------------------------ */

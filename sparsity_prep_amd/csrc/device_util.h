@@ -262,6 +262,29 @@ __device__ __forceinline__ uint32_t select_in_lane(const float v[8], int n) {
     return keep;
 }
 
+// 2:4 (the workloads' pattern): element i is kept iff it beats at least two
+// of the three others.  The six magnitude comparisons (|a| >= |b| on floats,
+// which orders finite values, subnormals and +-0 exactly like the bit
+// patterns without sign) are taken as wave-wide lane masks (ballot), the
+// majority logic runs on those masks in scalar registers, and each lane reads
+// its keep flags back as lane masks (inverse ballot) to select the kept
+// values, so no per-lane 0/1 values are materialized.  Inactive lanes
+// contribute 0 bits and never read theirs.
+__device__ __forceinline__ void select_2of4(const float v[8], uint64_t km[8]) {
+#pragma unroll
+    for (int g = 0; g < 8; g += 4) {
+        const float a0 = fabsf(v[g]), a1 = fabsf(v[g + 1]), a2 = fabsf(v[g + 2]), a3 = fabsf(v[g + 3]);
+        // lower index wins ties
+        const uint64_t c01 = __builtin_amdgcn_ballot_w64(a0 >= a1), c02 = __builtin_amdgcn_ballot_w64(a0 >= a2);
+        const uint64_t c03 = __builtin_amdgcn_ballot_w64(a0 >= a3), c12 = __builtin_amdgcn_ballot_w64(a1 >= a2);
+        const uint64_t c13 = __builtin_amdgcn_ballot_w64(a1 >= a3), c23 = __builtin_amdgcn_ballot_w64(a2 >= a3);
+        km[g] = (c01 & c02) | (c01 & c03) | (c02 & c03);
+        km[g + 1] = (~c01 & c12) | (~c01 & c13) | (c12 & c13);
+        km[g + 2] = (~c02 & ~c12) | (~c02 & c23) | (~c12 & c23);
+        km[g + 3] = (~c03 & ~c13) | (~c03 & ~c23) | (~c13 & ~c23);
+    }
+}
+
 // ---------------------------------------------------------------- SiLU(gate) * up source
 // The activation of a down projection computed from the gate/up product's
 // float rows: x = fl32(SiLU(gate) * up), SiLU(g) = g / (1 + e^-g), with e^y
@@ -287,6 +310,51 @@ __device__ __forceinline__ float exp32_fixed(float y) {
 __device__ __forceinline__ float silu_times(float g, float u) {
     const float d = __fadd_rn(1.0f, exp32_fixed(-g));
     return __fmul_rn(__fdiv_rn(g, d), u);
+}
+
+// The same value for |g| <= 80, in fewer instructions.  e^-g: no range
+// tests (-g lies inside [-87, 88]), and y - n * ln2_head as one fused
+// multiply-add, the same number because n * ln2_head is exact (|n| <= 116
+// and a 15-bit head).  g / d (1 <= d <= 1 + e^80, far from overflow and
+// underflow): the hardware reciprocal refined by one Newton step, the
+// product with g corrected once by its exact remainder (Markstein's
+// correction), which gives the correctly rounded quotient, its sign taken
+// from g; the device results equal the oracle's on every float32 g of the
+// range.
+__device__ __forceinline__ float silu_times_inrange(float g, float u) {
+    const float y = -g;
+    const float n = __builtin_rintf(__fmul_rn(y, 1.44269504f));
+    const float r = __fsub_rn(__builtin_fmaf(-n, 0.693145752f, y), __fmul_rn(n, 1.42860677e-6f));
+    float p = 0.00138888889f;
+    p = __fadd_rn(__fmul_rn(p, r), 0.00833333333f);
+    p = __fadd_rn(__fmul_rn(p, r), 0.0416666667f);
+    p = __fadd_rn(__fmul_rn(p, r), 0.166666667f);
+    p = __fadd_rn(__fmul_rn(p, r), 0.5f);
+    p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+    p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+    const float d = __fadd_rn(1.0f, __builtin_ldexpf(p, (int)n));
+    float z = __builtin_amdgcn_rcpf(d);
+    z = __builtin_fmaf(__builtin_fmaf(-d, z, 1.0f), z, z);
+    const float q0 = __fmul_rn(g, z);
+    const float q = __builtin_fmaf(__builtin_fmaf(-q0, d, g), z, q0);
+    return __fmul_rn(__builtin_copysignf(q, g), u);  // g = -0: the correction's sum gives +0
+}
+
+// h[k] = silu_times(g[k], u[k]) for N values per lane: the short form when
+// every value of every active lane lies in [-80, 80] (a wave-uniform
+// branch), else the general one.
+template <int N>
+__device__ __forceinline__ void silu_times_n(const float *g, const float *u, float *h) {
+    bool in = true;
+#pragma unroll
+    for (int k = 0; k < N; k++) in = in && fabsf(g[k]) <= 80.0f;  // false for NaN
+    if (__all(in)) {
+#pragma unroll
+        for (int k = 0; k < N; k++) h[k] = silu_times_inrange(g[k], u[k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < N; k++) h[k] = silu_times(g[k], u[k]);
+    }
 }
 
 }  // namespace sharq

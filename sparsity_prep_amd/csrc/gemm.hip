@@ -859,16 +859,32 @@ __device__ __forceinline__ void swiglu_epilogue(const LinearArgs &a, const v16f 
         for (int jp = 0; jp < FN / 2; jp++) {
             const int64_t hc0 = hb + jp * 32;
             if (hc0 >= Kd) continue;  // wave-uniform: columns past the product
-            float h[16], S[16], dq[16], R[16];
-#pragma unroll
-            for (int k = 0; k < 16; k++) h[k] = silu_times(acc[i][2 * jp][k], acc[i][2 * jp + 1][k]);
-            const uint32_t keep = select_in_lane<M>(h, a.p_n) | (select_in_lane<M>(h + 8, a.p_n) << 8);
-            float am = 0.0f;
+            float gv[16], uv[16], h[16], S[16], dq[16], R[16];
 #pragma unroll
             for (int k = 0; k < 16; k++) {
-                S[k] = (keep >> k) & 1u ? h[k] : 0.0f;
-                am = fmaxf(am, fabsf(S[k]));
+                gv[k] = acc[i][2 * jp][k];
+                uv[k] = acc[i][2 * jp + 1][k];
             }
+            silu_times_n<16>(gv, uv, h);
+            uint32_t keep = 0;
+            if (M == 4 && a.p_n == 2) {  // 2:4 on wave-wide lane masks (uniform branch)
+                uint64_t km[16];
+                select_2of4(h, km);
+                select_2of4(h + 8, km + 8);
+#pragma unroll
+                for (int k = 0; k < 16; k++) {
+                    const bool b = __builtin_amdgcn_inverse_ballot_w64(km[k]);
+                    S[k] = b ? h[k] : 0.0f;
+                    keep |= (b ? 1u : 0u) << k;
+                }
+            } else {
+                keep = select_in_lane<M>(h, a.p_n) | (select_in_lane<M>(h + 8, a.p_n) << 8);
+#pragma unroll
+                for (int k = 0; k < 16; k++) S[k] = (keep >> k) & 1u ? h[k] : 0.0f;
+            }
+            float am = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 16; k++) am = fmaxf(am, fabsf(S[k]));
             am = fmaxf(am, __shfl_xor(am, 32, 64));
             const int Eb = mx_shared_exp(am);
             const float sb = e8m0_operand(Eb);

@@ -40,7 +40,7 @@ struct RowStats {  // per-row statistics written by the NVFP4 pre-pass
 };
 
 // ---------------------------------------------------------------- selection
-// (select_in_lane: device_util.h)
+// (select_in_lane, select_2of4: device_util.h)
 
 // M = 16: a group spans the lane and its quad neighbour (lane ^ 1); the lower
 // lane of the pair holds group elements 0..7.
@@ -65,29 +65,6 @@ __device__ __forceinline__ uint32_t select_m16(const float v[8], int n, int lane
         keep |= (rank < n ? 1u : 0u) << i;
     }
     return keep;
-}
-
-// 2:4 (the workloads' pattern): element i is kept iff it beats at least two
-// of the three others.  The six magnitude comparisons (|a| >= |b| on floats,
-// which orders finite values, subnormals and +-0 exactly like the bit
-// patterns without sign) are taken as wave-wide lane masks (ballot), the
-// majority logic runs on those masks in scalar registers, and each lane reads
-// its keep flags back as lane masks (inverse ballot) to select the kept
-// values, so no per-lane 0/1 values are materialized.  Inactive lanes
-// contribute 0 bits and never read theirs.
-__device__ __forceinline__ void select_2of4(const float v[8], uint64_t km[8]) {
-#pragma unroll
-    for (int g = 0; g < 8; g += 4) {
-        const float a0 = fabsf(v[g]), a1 = fabsf(v[g + 1]), a2 = fabsf(v[g + 2]), a3 = fabsf(v[g + 3]);
-        // lower index wins ties
-        const uint64_t c01 = __builtin_amdgcn_ballot_w64(a0 >= a1), c02 = __builtin_amdgcn_ballot_w64(a0 >= a2);
-        const uint64_t c03 = __builtin_amdgcn_ballot_w64(a0 >= a3), c12 = __builtin_amdgcn_ballot_w64(a1 >= a2);
-        const uint64_t c13 = __builtin_amdgcn_ballot_w64(a1 >= a3), c23 = __builtin_amdgcn_ballot_w64(a2 >= a3);
-        km[g] = (c01 & c02) | (c01 & c03) | (c02 & c03);
-        km[g + 1] = (~c01 & c12) | (~c01 & c13) | (c12 & c13);
-        km[g + 2] = (~c02 & ~c12) | (~c02 & c23) | (~c12 & c23);
-        km[g + 3] = (~c03 & ~c13) | (~c03 & ~c23) | (~c13 & ~c23);
-    }
 }
 
 // FAST24: 1 = the 2:4 fast path, 0 = runtime N with M-wide groups.  keep[i]
@@ -624,7 +601,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_prep_stream(PrepArgs a, 
 }
 
 // ---------------------------------------------------------------- SiLU(gate) * up source
-// (exp32_fixed, silu_times: device_util.h)
+// (exp32_fixed, silu_times, silu_times_n: device_util.h)
 
 // Eight activations at element e0 of a row from its gate and up words.
 __device__ __forceinline__ void swiglu8(const float *row, int64_t K, int64_t e0, float v[8]) {
@@ -632,10 +609,9 @@ __device__ __forceinline__ void swiglu8(const float *row, int64_t K, int64_t e0,
     const float4 g1 = *reinterpret_cast<const float4 *>(row + e0 + 4);
     const float4 u0 = *reinterpret_cast<const float4 *>(row + K + e0);
     const float4 u1 = *reinterpret_cast<const float4 *>(row + K + e0 + 4);
-    v[0] = silu_times(g0.x, u0.x); v[1] = silu_times(g0.y, u0.y);
-    v[2] = silu_times(g0.z, u0.z); v[3] = silu_times(g0.w, u0.w);
-    v[4] = silu_times(g1.x, u1.x); v[5] = silu_times(g1.y, u1.y);
-    v[6] = silu_times(g1.z, u1.z); v[7] = silu_times(g1.w, u1.w);
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    silu_times_n<8>(g, u, v);
 }
 
 // (row, kSwiChunks chunks) tasks, one per wave: one 512-element chunk per

@@ -3,8 +3,9 @@ of their domain: the E2M1 conversion (the gfx950 FP32 -> FP4 conversion
 instruction with scale 1, followed by the canonical-zero fix; oracle:
 nearest E2M1 value, ties to the even code, saturating at 6, zero magnitude
 as code 0x0) on all 2^32 bit patterns (NaN inputs lie outside the method's
-domain and are only counted), and the E4M3 block-scale encoder and MX
-shared exponent on every non-negative finite float32."""
+domain and are only counted), the E4M3 block-scale encoder and MX
+shared exponent on every non-negative finite float32, and the device SiLU on
+all 2^32 patterns."""
 import ctypes
 import os
 import sys
@@ -89,3 +90,45 @@ def test_device_scale_encoders_match_oracle_on_every_nonnegative_float32():
         if (base // CHUNK) % 8 == 7:
             print(f"scale encoders: {base + n:#x} patterns, {bad4} + {bad8} mismatches", flush=True)
     assert bad4 == 0 and bad8 == 0, examples[:10]
+
+
+@pytest.mark.gpu
+def test_device_silu_matches_oracle_on_every_float32():
+    """SiLU(g) = g / (1 + e^-g) of the library's device code against the
+    oracle on all 2^32 float32 patterns g: the function the SwiGLU epilogue
+    and the SiLU(gate)*up prep call (silu_times_n, which takes a shorter
+    instruction sequence when a wave's values all lie in [-80, 80]), and that
+    short sequence itself on every g of the range (a refined hardware
+    reciprocal and one remainder correction in place of the division
+    routine).  Equal bit patterns are required, NaN results only have to be
+    NaN on both sides (their payloads are not part of the definition)."""
+    import concurrent.futures as cf
+    import torch
+    if not os.path.exists(PROBE):
+        pytest.fail(f"{PROBE} not built (python tests/hwprobe/build.py)")
+    lib = ctypes.CDLL(PROBE)
+    lib.probe_silu.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_silu.restype = ctypes.c_int
+    outs = [torch.empty(CHUNK, dtype=torch.float32, device="cuda") for _ in range(2)]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    low = np.arange(CHUNK, dtype=np.uint32)
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    bad, examples = [0, 0], []
+    with cf.ThreadPoolExecutor(workers) as ex:
+        for c in range((1 << 32) // CHUNK):
+            base = c * CHUNK
+            for mode in (0, 1):
+                rc = lib.probe_silu(base, CHUNK, mode, ctypes.c_void_p(outs[mode].data_ptr()), stream)
+                assert rc == 0, rc
+            g = (low + np.uint32(base)).view(np.float32)
+            want = np.concatenate(list(ex.map(oracle.silu32_array, np.array_split(g, workers))))
+            wnan = np.isnan(want)
+            for mode in (0, 1):
+                got = outs[mode].cpu().numpy()
+                ok = (got.view(np.uint32) == want.view(np.uint32)) | (np.isnan(got) & wnan)
+                d = np.flatnonzero(~ok)
+                bad[mode] += d.size
+                examples += [(mode, hex(int(g.view(np.uint32)[i])), float(got[i]), float(want[i])) for i in d[:3]]
+            if c % 16 == 15:
+                print(f"silu exhaustive: {(c + 1) * CHUNK:#x} patterns, mismatches {bad}", flush=True)
+    assert bad == [0, 0], examples[:10]

@@ -894,6 +894,20 @@ def test_linear_swiglu(case):
     _check_swiglu(pg, qw, n, m, str(case), out_rows=out_rows)
 
 
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 2)])
+def test_linear_swiglu_large_gates(n, m):
+    """Gate values far outside [-80, 80] in part of the tile (weights scaled
+    by 2^9, products of a few hundred): waves whose gates all lie inside that
+    range and waves that take the general SiLU sequence in one launch."""
+    T, K, nout = 300, 512, 1024
+    x = synth.small_case(K, T, "bf16", outliers=3, tag=95)
+    pg = gpu_prepare(x, "bf16", K, 0, None, None, 0.0, 2, 4, 0)
+    wf = synth.bits_to_f32(synth.small_weight(nout, K, tag=96), "bf16")
+    wf[:, : nout // 4] *= 512.0  # gate rows of the first half of the hidden columns
+    qw = sq().quantize_weight(dev16(synth.to_bits(wf, "bf16"), "bf16"), fmt=0, gate_up=True)
+    _check_swiglu(pg, qw, n, m, f"large gates {n}:{m}")
+
+
 @pytest.mark.parametrize("E", [5, 24], ids=["grouped", "persistent"])
 def test_linear_swiglu_grouped(E):
     """Expert products over gathered rows (five experts: one workgroup per

@@ -316,11 +316,12 @@ __device__ __forceinline__ float silu_times(float g, float u) {
 // tests (-g lies inside [-87, 88]), and y - n * ln2_head as one fused
 // multiply-add, the same number because n * ln2_head is exact (|n| <= 116
 // and a 15-bit head).  g / d (1 <= d <= 1 + e^80, far from overflow and
-// underflow): the hardware reciprocal refined by one Newton step, the
-// product with g corrected once by its exact remainder (Markstein's
-// correction), which gives the correctly rounded quotient, its sign taken
-// from g; the device results equal the oracle's on every float32 g of the
-// range.
+// underflow): the product of g and the hardware reciprocal (within 1 ulp of
+// 1/d), corrected once by its exact remainder g - q0 * d, sign taken from g.
+// That is not a correctly rounded division for arbitrary operands, but for
+// the divisors 1 + e^-g it is: the result equals the oracle's correctly
+// rounded quotient on every float32 g of the range (checked exhaustively on
+// the GPU).
 __device__ __forceinline__ float silu_times_inrange(float g, float u) {
     const float y = -g;
     const float n = __builtin_rintf(__fmul_rn(y, 1.44269504f));
@@ -333,8 +334,7 @@ __device__ __forceinline__ float silu_times_inrange(float g, float u) {
     p = __fadd_rn(__fmul_rn(p, r), 1.0f);
     p = __fadd_rn(__fmul_rn(p, r), 1.0f);
     const float d = __fadd_rn(1.0f, __builtin_ldexpf(p, (int)n));
-    float z = __builtin_amdgcn_rcpf(d);
-    z = __builtin_fmaf(__builtin_fmaf(-d, z, 1.0f), z, z);
+    const float z = __builtin_amdgcn_rcpf(d);
     const float q0 = __fmul_rn(g, z);
     const float q = __builtin_fmaf(__builtin_fmaf(-q0, d, g), z, q0);
     return __fmul_rn(__builtin_copysignf(q, g), u);  // g = -0: the correction's sum gives +0

@@ -98,9 +98,9 @@ def test_device_silu_matches_oracle_on_every_float32():
     oracle on all 2^32 float32 patterns g: the function the SwiGLU epilogue
     and the SiLU(gate)*up prep call (silu_times_n, which takes a shorter
     instruction sequence when a wave's values all lie in [-80, 80]), and that
-    short sequence itself on every g of the range (a refined hardware
-    reciprocal and one remainder correction in place of the division
-    routine).  Equal bit patterns are required, NaN results only have to be
+    short sequence itself on every g of the range (the hardware reciprocal
+    and one remainder correction in place of the division routine: exact for
+    these divisors only, which this test is what shows).  Equal bit patterns are required, NaN results only have to be
     NaN on both sides (their payloads are not part of the definition)."""
     import concurrent.futures as cf
     import torch

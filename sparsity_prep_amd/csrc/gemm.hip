@@ -1311,10 +1311,10 @@ static hipError_t launch_prefill(const LinearArgs &a, hipStream_t st, int64_t n_
     } else {
         n_mtiles = (a.rows + BM - 1) / BM;
         blocks = ((n_ntiles * n_mtiles + 7) / 8) * 8;
-        // MXFP4 launches of more than one round: XCD bands of two row tiles,
+        // MXFP4 launches of more than one round: XCD bands of 512 token rows,
         // when 2 or 4 bands split the rows (each band then shared by 4 or 2
         // XCDs, so no XCD streams the whole weight)
-        constexpr int64_t RB = 2;
+        constexpr int64_t RB = BM >= 512 ? 1 : 512 / BM;
         if (FMT == kFmtMx && a.ksplit_tiles == 0 && n_ntiles * n_mtiles > (int64_t)device_cus() * OCC &&
             (n_mtiles == 2 * RB || n_mtiles == 4 * RB)) {
             const int64_t G = 8 / (n_mtiles / RB);

@@ -879,6 +879,7 @@ SWIGLU_LINEAR_CASES = [
     (257, 512, 2304, 2, 2), (130, 256, 512, 1, 1), (96, 256, 512, 4, 4), (2049, 256, 8448, 2, 4),
     (40, 256, 512, 0, 4), (4096, 128, 1024, 3, 4),
     (2100, 128, 16384, 2, 4),  # two or more rounds of 128x256 tiles at two workgroups per CU, ragged rows
+    (1024, 128, 32768, 2, 4),  # the same tiles in two XCD bands of 512 token rows
 ]
 
 

@@ -29,6 +29,11 @@ FP8 GEMMs.
     python bench.py [--gpus 1] [--steps 30] [--warmup 5]
                     [--workload llama|decode1|decode8|decode64|qwen|moe]
                     [--graph on|off] [--no-extras] [--no-cpu-baseline]
+                    [--no-other-workloads]
+
+The default workload's line also carries other_workloads: the step and
+roofline figures of the decode, Qwen2.5-7B NVFP4 and Qwen3-30B-A3B MoE
+workloads, each from a child run of this script after the timed region.
 """
 from __future__ import annotations
 
@@ -52,7 +57,7 @@ INFINITY_CACHE_BYTES = 256 << 20
 # clock under that load (about 1.6 GHz, against 2.1-2.3 GHz with constant operands)
 MFMA_RANDOM_FP4_TFLOPS = 6250.0
 ERROR_ROWS = 32                 # rows per linear in the error report
-CPU_ROWS = 256                  # rows per linear (per thread for the threaded prep) in the CPU baseline
+CPU_ROWS = 2048                 # rows per linear (per thread for the threaded prep) in the CPU baseline
 
 
 def parse():
@@ -75,6 +80,9 @@ def parse():
                     help="MXFP4 batches of more than 32 tokens: the gate_up product prepares the down "
                          "projection's input in its epilogue (sharq_linear_swiglu); off: gate_up's FP32 output, "
                          "then the SiLU(gate)*up prep; all: the epilogue at every batch size")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="default workload only: skip the short runs of the other workloads that the line "
+                         "reports under other_workloads")
     ap.add_argument("--nv-backbone", choices=["sp24", "dense"], default="sp24",
                     help="NVFP4 2:4 workloads: store the backbone in the compressed 2:4 form and multiply it on "
                          "the sparse f16 matrix instruction (sp24), or zero-filled on the dense one (dense)")
@@ -837,7 +845,43 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layers)
         result["error_report"] = error_report(layers)
+    if args.workload == "llama" and not args.no_extras and not args.no_other_workloads:
+        torch.cuda.synchronize()
+        result["other_workloads"] = other_workloads(args)
     print(json.dumps(result), flush=True)
+
+
+OTHER_WORKLOADS = ("decode1", "decode8", "decode64", "qwen", "moe")
+
+
+def other_workloads(args):
+    """The other workloads, each a child run of this script after the timed
+    region of the default one (own process, own buffers): the step and
+    roofline figures of its line.  A child that fails is reported with its
+    exit status; the default workload's figures do not depend on these."""
+    import subprocess
+    keep = ("ms_per_step", "value", "unit", "dtype", "prep_GBps", "prep_frac_hbm", "gemm_TFLOPs",
+            "gemm_frac_peak")
+    out = {}
+    for w in OTHER_WORKLOADS:
+        cmd = [sys.executable, os.path.abspath(__file__), "--workload", w, "--steps", str(args.steps),
+               "--warmup", str(args.warmup), "--no-extras", "--no-cpu-baseline"]
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=600)
+        lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+        if r.returncode != 0 or not lines:
+            out[w] = {"status": r.returncode, "stderr_tail": r.stderr[-400:]}
+            continue
+        d = json.loads(lines[-1])
+        res = {k: d[k] for k in keep if k in d}
+        res["workload"] = d["config"]["workload"]
+        res["per_linear_us"] = {k: {"prep": v["prep_in_step_us"], "product": v["gemm_us"]}
+                                for k, v in d["per_linear"].items()}
+        rf = d["roofline"]
+        res["roofline"] = {k: rf[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic",
+                                               "frac_of_f16_peak") if k in rf}
+        res["roofline_prep_frac"] = d["roofline_prep"]["frac"]
+        out[w] = res
+    return out
 
 
 if __name__ == "__main__":

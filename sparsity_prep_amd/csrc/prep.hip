@@ -821,8 +821,19 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void k_nv_rowstats(PrepArgs a, 
 // Tensor scale G = fl32(amax / 2688), or 1 when that is not positive.
 __global__ __launch_bounds__(1024) void k_nv_tensor_scale(const RowStats *stats, int64_t T, float *G) {
     __shared__ float part[1024 / kWave];
+    // eight independent loads in flight per thread (max is exact in any order)
+    constexpr int kU = 8;
     float m = 0.0f;
-    for (int64_t i = threadIdx.x; i < T; i += blockDim.x) m = fmaxf(m, stats[i].amax);
+    for (int64_t i = threadIdx.x; i < T; i += kU * (int64_t)blockDim.x) {
+        float v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; u++) {
+            const int64_t j = i + u * (int64_t)blockDim.x;
+            v[u] = j < T ? stats[j].amax : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; u++) m = fmaxf(m, v[u]);
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;

@@ -191,6 +191,18 @@ __device__ __forceinline__ void e2m1_dec8(uint32_t p, float scale, float q[8]) {
 // E8M0 exponent E as the scale operand of the conversions above.
 __device__ __forceinline__ float e8m0_operand(int E) { return __uint_as_float((uint32_t)(E + 127) << 23); }
 
+// Double reciprocal of a positive finite double d whose inverse is a normal
+// double (every positive float qualifies): the hardware reciprocal refined
+// by two Newton steps r <- r + r(1 - dr), each an FMA pair.  From a start
+// within 2^-20 the first step leaves about 2^-40 and the second the final
+// rounding (2^-53) plus 2^-79, so the result is within one ulp of the
+// correctly rounded 1/d.  No range scaling is needed for such d.
+__device__ __forceinline__ double rcp_f64_refined(double d) {
+    double r = __builtin_amdgcn_rcp(d);
+    r = __fma_rn(r, __fma_rn(-d, r, 1.0), r);
+    return __fma_rn(r, __fma_rn(-d, r, 1.0), r);
+}
+
 // ---------------------------------------------------------------- E8M0 (MX)
 // OCP MX shared exponent for E2M1 elements: floor(log2 amax) - 2, or -127
 // for amax == 0 (never below -127; at most 125 for finite floats).  The

@@ -110,8 +110,17 @@ __device__ __forceinline__ uint32_t quant_mx8(const float s[8], uint32_t &codes,
 // adjacent floats: v = M*D would make the 24-bit significand of v a
 // multiple of M's odd 25-bit one, and otherwise v and M*D differ by at least
 // one unit of their common bit grid.  The double product is within 2^-52 of
-// the quotient, so both round to the same float.  A zero divisor gives the
-// same infinities and NaNs as the division.
+// the quotient (plus 2^-79 from the reciprocal below), so both round to the
+// same float.  (Quotients below the normal range can part at an exact tie
+// of the subnormal grid; they lie far below the smallest E2M1 step and the
+// smallest E4M3 scale and encode as zero either way.)  A zero divisor gives
+// the same infinities and NaNs as the division.
+//
+// The element reciprocal 1/D is rcp_f64_refined (the hardware reciprocal
+// after two Newton steps, within the final rounding plus 2^-79 of 1/D).  A
+// block whose scale code is 0 (D = 0) takes r = 0: every quotient is then
+// +-0, which the E2M1 conversion encodes as the canonical zero code.
+
 __device__ __forceinline__ uint32_t quant_nv8(const float s[8], float G, double rG6, uint32_t &codes,
                                               float deq[8]) {
     float m = 0.0f;
@@ -120,10 +129,10 @@ __device__ __forceinline__ uint32_t quant_nv8(const float s[8], float G, double 
     m = pair_max_nonneg(m);
     const uint32_t sb = e4m3_encode_sat((float)((double)m * rG6));
     const float D = __fmul_rn(e4m3_value(sb), G);
-    const double rD = 1.0 / (double)D;
+    const double rD = sb != 0u ? rcp_f64_refined((double)D) : 0.0;
     float u[8], q[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) u[i] = sb != 0u ? (float)((double)s[i] * rD) : 0.0f;
+    for (int i = 0; i < 8; i++) u[i] = (float)((double)s[i] * rD);
     codes = e2m1_cvt8(u, 1.0f);
     e2m1_dec8(codes, 1.0f, q);
 #pragma unroll

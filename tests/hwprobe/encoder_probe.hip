@@ -6,7 +6,8 @@
 // encoder (sharq::e4m3_encode_sat), the MX shared exponent
 // (sharq::mx_shared_exp, written as the E8M0 byte E + 127), and SiLU(g)
 // (sharq::silu_times_n and sharq::silu_times_inrange with u = 1, which
-// returns the quotient itself).
+// returns the quotient itself), and the NVFP4 element quotient
+// float(double(x) * sharq::rcp_f64_refined(d)).
 #include "../../sparsity_prep_amd/csrc/device_util.h"
 
 __global__ void k_probe_e2m1(uint32_t base, uint32_t n, uint8_t *out) {
@@ -87,5 +88,24 @@ extern "C" __attribute__((visibility("default"))) int probe_silu(uint32_t base, 
     const uint32_t threads = n / 8u, block = 256u;
     hipLaunchKernelGGL(k_probe_silu, dim3((threads + block - 1) / block), dim3(block), 0, (hipStream_t)stream, base,
                        n, mode, out);
+    return (int)hipGetLastError();
+}
+
+// NVFP4 element quotients q[i] = float(double(x[i]) * rcp_f64_refined(d[i]))
+// as the prep kernels form them (d[i] positive finite floats).
+__global__ void k_probe_quotient(const float *x, const float *d, uint32_t n, float *q) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    q[i] = (float)((double)x[i] * sharq::rcp_f64_refined((double)d[i]));
+}
+
+// Quotients of the n pairs (x[i], d[i]) into q[0 .. n) (n at most 2^31);
+// returns the HIP error code.
+extern "C" __attribute__((visibility("default"))) int probe_quotient(const float *x, const float *d, uint32_t n,
+                                                                      float *q, void *stream) {
+    if (n > (1u << 31) || x == nullptr || d == nullptr || q == nullptr) return (int)hipErrorInvalidValue;
+    const uint32_t block = 256u;
+    hipLaunchKernelGGL(k_probe_quotient, dim3((n + block - 1) / block), dim3(block), 0, (hipStream_t)stream, x, d,
+                       n, q);
     return (int)hipGetLastError();
 }

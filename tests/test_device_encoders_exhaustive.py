@@ -4,8 +4,9 @@ instruction with scale 1, followed by the canonical-zero fix; oracle:
 nearest E2M1 value, ties to the even code, saturating at 6, zero magnitude
 as code 0x0) on all 2^32 bit patterns (NaN inputs lie outside the method's
 domain and are only counted), the E4M3 block-scale encoder and MX
-shared exponent on every non-negative finite float32, and the device SiLU on
-all 2^32 patterns."""
+shared exponent on every non-negative finite float32, the device SiLU on
+all 2^32 patterns, and the NVFP4 element quotient against float division on
+quotients next to the float midpoints."""
 import ctypes
 import os
 import sys
@@ -132,3 +133,65 @@ def test_device_silu_matches_oracle_on_every_float32():
             if c % 16 == 15:
                 print(f"silu exhaustive: {(c + 1) * CHUNK:#x} patterns, mismatches {bad}", flush=True)
     assert bad == [0, 0], examples[:10]
+
+
+def _near_midpoint_pairs(rng, n):
+    """Float pairs (x, d), d > 0, whose quotients lie as close as floats allow
+    to the midpoints between adjacent floats (x = fl32(mid * d) and its two
+    neighbours), divisors across the subnormal and normal range."""
+    xs, ds = [], []
+    for lo, hi in ((-149, -126), (-126, 0), (0, 127)):
+        d = (rng.uniform(1, 2, n) * 2.0 ** rng.integers(lo, hi, n)).astype(np.float32)
+        d = d[(d > 0) & np.isfinite(d)]
+        q = (rng.uniform(1, 2, d.size) * 2.0 ** rng.integers(-12, 10, d.size)).astype(np.float32)
+        mid = (q.astype(np.float64) + np.nextafter(q, np.float32(np.inf)).astype(np.float64)) / 2
+        with np.errstate(over="ignore"):
+            x = (mid * d.astype(np.float64)).astype(np.float32)
+        for xx in (x, np.nextafter(x, np.float32(np.inf)), np.nextafter(x, np.float32(-np.inf))):
+            keep = np.isfinite(xx)
+            xs.append(np.where(rng.random(xx.size) < 0.5, xx, -xx)[keep])
+            ds.append(d[keep])
+    return np.concatenate(xs), np.concatenate(ds)
+
+
+@pytest.mark.gpu
+def test_device_nvfp4_quotient_matches_float_division():
+    """The NVFP4 element quotient as the prep kernels form it,
+    float(double(x) * r) with r the hardware double reciprocal of the
+    positive float divisor refined by two Newton steps, against IEEE float
+    division (numpy's, correctly rounded: the definition) on quotients next to
+    the float midpoints, where a reciprocal off by more than the argument
+    allows would show, and on random pairs with positive finite divisors and
+    quotients in the normal range or zero."""
+    import torch
+    if not os.path.exists(PROBE):
+        pytest.fail(f"{PROBE} not built (python tests/hwprobe/build.py)")
+    lib = ctypes.CDLL(PROBE)
+    lib.probe_quotient.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.probe_quotient.restype = ctypes.c_int
+    rng = np.random.default_rng(7)
+    x0, d0 = _near_midpoint_pairs(rng, 1_000_000)
+    bits = rng.integers(0, 2 ** 32, size=(2, 4_000_000), dtype=np.uint64).astype(np.uint32)
+    x1, d1 = bits[0].view(np.float32), np.abs(bits[1].view(np.float32))
+    with np.errstate(over="ignore", under="ignore", invalid="ignore"):
+        q64 = np.abs(x1.astype(np.float64) / d1.astype(np.float64))
+    # quotients below the normal float range are left out: on the subnormal
+    # grid an exact tie can part from a reciprocal-based product, but every
+    # such quotient lies far below the smallest E2M1 step (0.25) and
+    # quantizes to zero either way
+    ok = np.isfinite(x1) & np.isfinite(d1) & (d1 > 0) & ((q64 == 0) | (q64 >= 2.0 ** -126))
+    x = np.concatenate([x0, x1[ok]]).astype(np.float32)
+    d = np.concatenate([d0, d1[ok]]).astype(np.float32)
+    assert x.size > 9_000_000
+    xt, dt = torch.from_numpy(x).cuda(), torch.from_numpy(d).cuda()
+    qt = torch.empty_like(xt)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rc = lib.probe_quotient(ctypes.c_void_p(xt.data_ptr()), ctypes.c_void_p(dt.data_ptr()), x.size,
+                            ctypes.c_void_p(qt.data_ptr()), stream)
+    assert rc == 0, rc
+    got = qt.cpu().numpy()
+    with np.errstate(over="ignore", under="ignore"):
+        want = np.divide(x, d, dtype=np.float32)
+    bad = np.flatnonzero(got.view(np.uint32) != want.view(np.uint32))
+    assert bad.size == 0, [(float(x[i]), float(d[i]), float(got[i]), float(want[i])) for i in bad[:5]]

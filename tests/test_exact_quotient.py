@@ -1,22 +1,28 @@
 """The NVFP4 prep kernels form every quotient the format defines (block
-amax / fl32(6G), and each element / D) as float(double(x) * (1 / double(d)))
-instead of a float division.  This pins the identity that makes the two
-equal, float(x/d) == float(double(x) * (1/double(d))) for floats x, d, on
-quotients placed as close as floats allow to the midpoints between adjacent
-floats (the only places where two roundings could part), with divisors
-across the normal and subnormal range, next to plain random pairs.  numpy's
-float32 division is IEEE correctly rounded, so it is the definition."""
+amax / fl32(6G), and each element / D) as float(double(x) * r) with r a
+double reciprocal of the float divisor instead of a float division: the
+correctly rounded 1 / double(d) for the block scale, and for the elements
+the hardware reciprocal refined by two Newton steps, which lies within one
+double ulp of it.  This pins the identity that makes them equal,
+float(x/d) == float(double(x) * r) for floats x, d and for r = 1/double(d)
+and its two neighbouring doubles, on quotients placed as close as floats
+allow to the midpoints between adjacent floats (the only places where two
+roundings could part), with divisors across the normal and subnormal range,
+next to plain random pairs.  numpy's float32 division is IEEE correctly
+rounded, so it is the definition."""
 import numpy as np
 
 
 def _check(x, d):
     ok = np.isfinite(x) & (d != 0) & np.isfinite(d)
     x, d = x[ok], d[ok]
+    r = 1.0 / d.astype(np.float64)
     with np.errstate(over="ignore"):   # quotients beyond the float range: inf on both sides
         want = np.divide(x, d, dtype=np.float32)
-        got = (x.astype(np.float64) * (1.0 / d.astype(np.float64))).astype(np.float32)
-    bad = np.flatnonzero(want.view(np.uint32) != got.view(np.uint32))
-    assert bad.size == 0, (x[bad[:5]], d[bad[:5]])
+        for rr in (r, np.nextafter(r, np.inf), np.nextafter(r, -np.inf)):
+            got = (x.astype(np.float64) * rr).astype(np.float32)
+            bad = np.flatnonzero(want.view(np.uint32) != got.view(np.uint32))
+            assert bad.size == 0, (x[bad[:5]], d[bad[:5]])
     return x.size
 
 

@@ -866,7 +866,11 @@ def other_workloads(args):
     for w in OTHER_WORKLOADS:
         cmd = [sys.executable, os.path.abspath(__file__), "--workload", w, "--steps", str(args.steps),
                "--warmup", str(args.warmup), "--no-extras", "--no-cpu-baseline"]
-        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=600)
+        try:
+            r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=300)
+        except (subprocess.TimeoutExpired, OSError) as e:
+            out[w] = {"status": "not run to the end", "error": str(e)[-400:]}
+            continue
         lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
         if r.returncode != 0 or not lines:
             out[w] = {"status": r.returncode, "stderr_tail": r.stderr[-400:]}

@@ -71,3 +71,39 @@ def test_layer_workloads_have_four_linears_with_fused_down():
     moe = {lin.name: lin for lin in synth.WORKLOADS[4].linears}
     assert moe["expert_down"].swiglu_of == "expert_gate_up"
     assert moe["expert_gate_up"].nout == 2 * moe["expert_down"].k
+
+
+def test_other_workloads_parses_child_lines_and_reports_failures(monkeypatch):
+    """The default line's other_workloads: each child's JSON line is reduced
+    to its step and roofline figures; a child that fails, times out or
+    cannot start is reported with its status, and the others still run."""
+    import json
+    import types
+
+    line = {"ms_per_step": 1.5, "value": 10.0, "unit": "TFLOP/s", "dtype": "x", "prep_GBps": 1.0,
+            "prep_frac_hbm": 0.1, "gemm_TFLOPs": 2.0, "gemm_frac_peak": 0.2,
+            "config": {"workload": "wl"},
+            "per_linear": {"qkv": {"prep_in_step_us": 3.0, "gemm_us": 4.0}},
+            "roofline": {"bound": "mfma", "achieved": 2.0, "peak": 10.0, "unit": "TFLOP/s", "frac": 0.2,
+                         "traffic": None},
+            "roofline_prep": {"frac": 0.1}}
+    calls = []
+
+    def fake_run(cmd, **kw):
+        w = cmd[cmd.index("--workload") + 1]
+        calls.append(w)
+        assert "--no-extras" in cmd and "--no-cpu-baseline" in cmd
+        if w == "qwen":
+            return types.SimpleNamespace(returncode=1, stdout="", stderr="boom")
+        if w == "moe":
+            raise subprocess.TimeoutExpired(cmd, kw.get("timeout"))
+        return types.SimpleNamespace(returncode=0, stdout="log line\n" + json.dumps(line) + "\n", stderr="")
+
+    monkeypatch.setattr(subprocess, "run", fake_run)
+    out = bench.other_workloads(types.SimpleNamespace(steps=3, warmup=1))
+    assert calls == list(bench.OTHER_WORKLOADS)
+    assert out["decode1"]["ms_per_step"] == 1.5 and out["decode1"]["workload"] == "wl"
+    assert out["decode1"]["per_linear_us"] == {"qkv": {"prep": 3.0, "product": 4.0}}
+    assert out["decode1"]["roofline"]["frac"] == 0.2 and out["decode1"]["roofline_prep_frac"] == 0.1
+    assert out["qwen"]["status"] == 1 and "boom" in out["qwen"]["stderr_tail"]
+    assert out["moe"]["status"] == "not run to the end"

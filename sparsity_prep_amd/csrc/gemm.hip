@@ -1568,10 +1568,12 @@ static hipError_t launch_linear_mx(const LinearArgs &a, void *ws, size_t ws_byte
 // MI355X 10-18% faster once there are enough tiles), whichever takes fewer
 // rounds of tiles, weighted by the measured cost per output element
 // (1.17 : 1); when 256x256 tiles fill some rounds and leave a partial one,
-// the columns of the full rounds run as 256x256 tiles and the rest as
-// 128x128 tiles in a second launch.  Grouped expert products use 128x256
-// tiles.  NVFP4_SP24 (backbone on the 2:4 sparse f16 MFMA) uses the same
-// shapes.
+// the columns of the full rounds run as 256x256 tiles and the rest in a
+// second launch of 64x128 tiles at three workgroups per CU, which spreads
+// those few columns over every CU (Qwen2.5-7B qkv, 4096 x 4608 x 3584, on
+// MI355X: 214 -> 196 us against 128x128 tiles at two per CU; 128x64 tiles
+// 206-208).  Grouped expert products use 128x256 tiles.  NVFP4_SP24
+// (backbone on the 2:4 sparse f16 MFMA) uses the same shapes.
 static double nv_cost128(int64_t rows, int64_t cols, int64_t cus) {
     const int64_t t = ((rows + 127) / 128) * ((cols + 127) / 128);
     return (double)((t + 2 * cus - 1) / (2 * cus)) * 2.0 * 128 * 128 * 1.17;
@@ -1594,7 +1596,7 @@ static hipError_t launch_linear_nv(const LinearArgs &a, hipStream_t st) {
         if (split < 0.97 * (c128 < c256 ? c128 : c256)) {  // a second launch costs a little
             const hipError_t e = launch_prefill<FMT, 256, 256, 2, 2, 2, 1, 0, 1>(a, st, 0, n_split);
             if (e != hipSuccess) return e;
-            return launch_prefill<FMT, 128, 128, 2, 2, 2, 2, 0, 1>(a, st, n_split, a.nout);
+            return launch_prefill<FMT, 64, 128, 2, 2, 2, 3, 0, 1>(a, st, n_split, a.nout);
         }
     }
     if (c256 < c128) return launch_prefill<FMT, 256, 256, 2, 2, 2, 1, 0, 1>(a, st);

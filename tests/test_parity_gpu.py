@@ -285,8 +285,10 @@ LINEAR_CASES = [
     (0, 64, 1024, 2128), (0, 40, 1024, 3000), (0, 9, 1024, 8240),  # few rows as 64x64 tiles
     (0, 64, 14336, 2050), (0, 24, 14336, 3000), (0, 17, 14336, 4096),  # few rows over 8 / 8 / 4 K ranges, summed
     (1, 16, 256, 256), (1, 300, 640, 272), (1, 1, 512, 64), (1, 70, 1024, 130), (1, 257, 3584, 256),
-    (1, 2049, 256, 4224),  # NVFP4 256x256 tiles (128x128 per wave), ragged rows and columns
-    (1, 2049, 256, 8616),  # NVFP4 column split: 256x256 tiles for full rounds, 128x128 for the rest
+    (1, 2049, 256, 4224),  # NVFP4 256x224 tiles (64x224 per wave), ragged rows and columns
+    (1, 4001, 256, 3500),  # NVFP4 256x224 tiles filling a round, ragged rows and columns
+    (1, 4000, 256, 4090),  # NVFP4 256x256 tiles (128x128 per wave), ragged rows and columns
+    (1, 2049, 256, 8616),  # NVFP4 column split: 256x256 tiles for full rounds, 64x128 for the rest
 ]
 
 

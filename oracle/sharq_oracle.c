@@ -339,21 +339,22 @@ static void decompose_row(const float *xh, int64_t K, int N, int M, int fmt, flo
  * (so any IEEE implementation of the same steps gives the same bits):
  * Cody-Waite reduction y = n ln2 + r with n = rint(y log2 e) and ln2 split
  * into a 15-bit head and a tail, e^r by its degree-6 Taylor polynomial in
- * Horner form, then scaling by 2^n.  Defined as 0 below -87 (so results are
- * never subnormal) and +inf above 88.  About 2 ulp from the true e^y. */
+ * Horner form with each step one fused multiply-add (one rounding), then
+ * scaling by 2^n.  Defined as 0 below -87 (so results are never subnormal)
+ * and +inf above 88.  About 2 ulp from the true e^y. */
 float or_exp32(float y)
 {
     if (!(y <= 88.0f)) return INFINITY;
     if (y < -87.0f) return 0.0f;
     float n = nearbyintf(y * 1.44269504f);
     float r = (y - n * 0.693145752f) - n * 1.42860677e-6f;
-    float p = 0.00138888889f;          /* 1/720 */
-    p = p * r + 0.00833333333f;        /* 1/120 */
-    p = p * r + 0.0416666667f;         /* 1/24 */
-    p = p * r + 0.166666667f;          /* 1/6 */
-    p = p * r + 0.5f;
-    p = p * r + 1.0f;
-    p = p * r + 1.0f;
+    float p = 0.00138888889f;              /* 1/720 */
+    p = fmaf(p, r, 0.00833333333f);        /* 1/120 */
+    p = fmaf(p, r, 0.0416666667f);         /* 1/24 */
+    p = fmaf(p, r, 0.166666667f);          /* 1/6 */
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
     return ldexpf(p, (int)n);
 }
 

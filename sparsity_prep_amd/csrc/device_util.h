@@ -302,20 +302,21 @@ __device__ __forceinline__ void select_2of4(const float v[8], uint64_t km[8]) {
 // float rows: x = fl32(SiLU(gate) * up), SiLU(g) = g / (1 + e^-g), with e^y
 // evaluated by fixed correctly rounded float steps: Cody-Waite reduction
 // y = n ln2 + r (n = rint(y log2 e), ln2 as a 15-bit head plus a tail), the
-// degree-6 Taylor polynomial of e^r in Horner form, scaling by 2^n; 0 below
+// degree-6 Taylor polynomial of e^r in Horner form (one fused multiply-add
+// per step), scaling by 2^n; 0 below
 // -87 (never subnormal), +inf above 88.
 __device__ __forceinline__ float exp32_fixed(float y) {
     if (!(y <= 88.0f)) return __builtin_inff();
     if (y < -87.0f) return 0.0f;
     const float n = __builtin_rintf(__fmul_rn(y, 1.44269504f));
     const float r = __fsub_rn(__fsub_rn(y, __fmul_rn(n, 0.693145752f)), __fmul_rn(n, 1.42860677e-6f));
-    float p = 0.00138888889f;                      // 1/720
-    p = __fadd_rn(__fmul_rn(p, r), 0.00833333333f);  // 1/120
-    p = __fadd_rn(__fmul_rn(p, r), 0.0416666667f);   // 1/24
-    p = __fadd_rn(__fmul_rn(p, r), 0.166666667f);    // 1/6
-    p = __fadd_rn(__fmul_rn(p, r), 0.5f);
-    p = __fadd_rn(__fmul_rn(p, r), 1.0f);
-    p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+    float p = 0.00138888889f;                 // 1/720
+    p = __builtin_fmaf(p, r, 0.00833333333f);  // 1/120
+    p = __builtin_fmaf(p, r, 0.0416666667f);   // 1/24
+    p = __builtin_fmaf(p, r, 0.166666667f);    // 1/6
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
     return __builtin_ldexpf(p, (int)n);
 }
 
@@ -339,12 +340,12 @@ __device__ __forceinline__ float silu_times_inrange(float g, float u) {
     const float n = __builtin_rintf(__fmul_rn(y, 1.44269504f));
     const float r = __fsub_rn(__builtin_fmaf(-n, 0.693145752f, y), __fmul_rn(n, 1.42860677e-6f));
     float p = 0.00138888889f;
-    p = __fadd_rn(__fmul_rn(p, r), 0.00833333333f);
-    p = __fadd_rn(__fmul_rn(p, r), 0.0416666667f);
-    p = __fadd_rn(__fmul_rn(p, r), 0.166666667f);
-    p = __fadd_rn(__fmul_rn(p, r), 0.5f);
-    p = __fadd_rn(__fmul_rn(p, r), 1.0f);
-    p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+    p = __builtin_fmaf(p, r, 0.00833333333f);
+    p = __builtin_fmaf(p, r, 0.0416666667f);
+    p = __builtin_fmaf(p, r, 0.166666667f);
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
     const float d = __fadd_rn(1.0f, __builtin_ldexpf(p, (int)n));
     const float z = __builtin_amdgcn_rcpf(d);
     const float q0 = __fmul_rn(g, z);
